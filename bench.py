@@ -1,0 +1,244 @@
+"""Benchmark of the fused multi-tensor AdamW step on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one apexw_step call over the whole parameter list of the workload
+(default: 8 bf16 [8192,8192] parameters with fp32 grads and fp32 moments,
+536,870,912 params), with parameters, grads and state already resident in
+HBM.  W untimed steps, then K timed steps between a barrier-free
+torch.cuda.synchronize() on both sides.  Prints one JSON line: params/s
+(value), achieved HBM GB/s on the algorithmic byte count and its fraction of
+the 8 TB/s peak, the roofline object of the update kernel (its average
+duration from HIP events recorded on the stream the kernel runs on), and the
+oracle's throughput on a bounded sample, timed on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "params updated/sec + achieved HBM GB/s (% of peak) per AdamW step, 1 MI355X"
+HBM_PEAK_GBPS = 8000.0
+
+# algorithmic bytes per element: read theta, g, m, v; write theta, m, v
+ELEM = {"f32": 4, "bf16": 2}
+MOMENT = {"f32": 4, "bf16": 2, "q8": 1}
+
+
+def algorithmic_bytes(w) -> int:
+    """Bytes the method must move per step: each of theta, g, m, v read once,
+    theta, m, v written once, plus (8-bit) the two block scales read and
+    written and the 4-byte step counter read and written per tensor."""
+    total = 0
+    for n, pd, gd in zip(w.numels, w.param_dtype, w.grad_dtype):
+        mb = MOMENT[w.state_fmt]
+        total += n * (2 * ELEM[pd] + ELEM[gd] + 4 * mb)
+        if w.state_fmt == "q8":
+            total += 2 * 2 * 4 * ((n + 255) // 256)
+        total += 8
+    return total
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in ("tensor_adamw_optimizer_amd/csrc/apexw.hip",
+                "tensor_adamw_optimizer_amd/csrc/apexw_kernels.hpp", "include/apexw.h"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s: float = 12.0):
+    """The oracle (scalar C, one thread) on a bounded sample of the workload:
+    a prefix of the first tensor, as many calls as fit in about budget_s."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import workloads as W
+
+    n_full = w.numels[0]
+    n = min(n_full, 1 << 24)
+    gen = torch.Generator().manual_seed(123)
+    th = (torch.randn(n, generator=gen) * w.theta_std).to(W.TORCH_DTYPE[w.param_dtype[0]])
+    th = W.to_numpy_bits(th)
+    g = (torch.randn(n, generator=gen) * w.grad_std).to(W.TORCH_DTYPE[w.grad_dtype[0]])
+    g = W.to_numpy_bits(g)
+    ref = oracle.OracleAdamW([n], w.param_dtype[:1], w.grad_dtype[:1], [0], w.state_fmt)
+    grp = [w.groups[w.group_of[0]]]
+    ref.step([th], [g], grp)                                  # warm-up call
+    calls, t0 = 0, time.perf_counter()
+    while True:
+        ref.step([th], [g], grp)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or calls >= 50:
+            break
+    return {
+        "value": n * calls / el,
+        "unit": "params/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": "%d of the %d params (prefix of tensor 0, %s params / %s grads / %s state), "
+                  "%d calls in %.1f s, single-threaded scalar C oracle (gcc -O2, no contraction)"
+                  % (n, w.n_params, w.param_dtype[0], w.grad_dtype[0], w.state_fmt, calls, el),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="few_large",
+                    choices=["few_large", "many_small", "bf16_state", "lora_q8", "tiny"])
+    ap.add_argument("--workgroups", type=int, default=0, help="persistent grid override")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="after timing, run a 1 GiB device copy 3x (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the optimizer step is benchmarked on a "
+              "single MI355X (--gpus 1); multi-GPU runs are not part of this build.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import workloads as W
+    from tensor_adamw_optimizer_amd import _lib as L
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    L.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = W.WORKLOADS[args.workload]()
+    print("bench: workload %s, %d tensors, %d params" % (w.name, len(w.shapes), w.n_params),
+          file=sys.stderr, flush=True)
+
+    dt = {W.F32: L.APEXW_F32, W.BF16: L.APEXW_BF16}
+    fmt = {W.STATE_F32: L.APEXW_STATE_F32, W.STATE_BF16: L.APEXW_STATE_BF16,
+           W.STATE_Q8: L.APEXW_STATE_Q8}[w.state_fmt]
+    params = W.init_params(w, dev)
+    grads = W.grads_for_call(w, 1, dev)
+    state_bytes = L.apexw_state_bytes(w.numels, fmt)
+    ws_bytes = L.apexw_workspace_bytes(w.numels)
+    state = torch.empty(state_bytes, dtype=torch.uint8, device=dev)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    h = L.apexw_create(w.numels, [dt[d] for d in w.param_dtype], [dt[d] for d in w.grad_dtype],
+                       w.group_of, len(w.groups), fmt, state.data_ptr(), state_bytes,
+                       ws.data_ptr(), ws_bytes, stream.cuda_stream)
+    if args.workgroups:
+        L.apexw_set_workgroups(h, args.workgroups)
+    tile, n_tiles, wgs = L.apexw_launch_info(h)
+    params_arr = L.make_ptrs([p.data_ptr() for p in params])
+    grads_arr = L.make_ptrs([g.data_ptr() for g in grads])
+    groups_arr = L.make_groups(w.groups)
+    found_inf = torch.zeros(1, dtype=torch.float32, device=dev)
+
+    def step():
+        L.apexw_step(h, groups_arr, len(w.groups), params_arr, grads_arr, found_inf.data_ptr(),
+                     stream.cuda_stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print("bench: warm-up done", file=sys.stderr, flush=True)
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for k in range(args.steps):
+        step()
+        ev[k + 1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kernel_ms = [ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps)]
+    avg_kernel_s = sum(kernel_ms) / len(kernel_ms) / 1e3
+    print("bench: timed %d steps" % args.steps, file=sys.stderr, flush=True)
+
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    ab = algorithmic_bytes(w)
+    gbps = ab / avg_kernel_s / 1e9
+    traffic = measured_traffic(w.name)
+    out = {
+        "metric": METRIC,
+        "value": w.n_params * args.steps / elapsed,
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "tensors": len(w.shapes),
+            "params": w.n_params,
+            "param_dtype": "+".join(sorted(set(w.param_dtype))),
+            "grad_dtype": "+".join(sorted(set(w.grad_dtype))),
+            "state": w.state_fmt,
+            "groups": len(w.groups),
+        },
+        "hbm_gbps": (ab / (elapsed / args.steps)) / 1e9,
+        "hbm_frac_of_peak": (ab / (elapsed / args.steps)) / 1e9 / HBM_PEAK_GBPS,
+        "kernel_ms": {"avg": sum(kernel_ms) / len(kernel_ms), "min": min(kernel_ms),
+                      "max": max(kernel_ms)},
+        "launch": {"tile_elems": tile, "tiles": n_tiles, "workgroups": wgs},
+        "state_bytes": state_bytes,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": gbps,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": gbps / HBM_PEAK_GBPS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": ab,
+            "kernel": "adamw_step_kernel",
+        },
+    }
+    L.apexw_destroy(h)
+    del params, grads, state, ws
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,204 @@
+/*
+ * apexw.h -- C ABI of a fused multi-tensor AdamW step for AMD MI355X (gfx950).
+ *
+ * One call of apexw_step updates every parameter of an optimizer, in one GPU
+ * launch per (parameter dtype, grad dtype) pair present, with the AdamW rule
+ * of "Fused optimizers and state precision" (ai-infra-kb M041), section 02:
+ *
+ *     t += 1
+ *     m  = beta1*m + (1-beta1)*g
+ *     v  = beta2*v + (1-beta2)*g*g
+ *     m_hat = m / (1-beta1^t),   v_hat = v / (1-beta2^t)
+ *     theta = theta*(1-lr*weight_decay) - lr*m_hat / (sqrt(v_hat) + eps)
+ *
+ * with decoupled weight decay, no AMSGrad, and the bias corrections applied as
+ * per-tensor scalars (section 04: m_hat and v_hat are never stored).  Moments
+ * are kept in one of three formats (section 05): fp32, bf16, or 8-bit codes
+ * with one fp32 absmax scale per 256-element block.  Per parameter group lr,
+ * betas, eps and weight decay are honoured (section 03); a parameter whose
+ * grad is absent is left completely alone (section 03), and a step for which
+ * the device flag found_inf is set changes nothing (section 06; the Apex
+ * fused-optimizer guide, section 4.3, capturable mode) -- decided on the
+ * device, without a host synchronisation.
+ *
+ * Arithmetic: fp32, every operation separately rounded in the order printed
+ * above (left to right), correctly rounded division and square root; the
+ * scalars (1-beta1), (1-beta2), (1-lr*wd), lr, eps are formed in fp64 and
+ * rounded once to fp32; beta^t is fp64 square-and-multiply over the bits of t
+ * from the least significant end and 1-beta^t is rounded once to fp32.  bf16
+ * values are widened exactly and narrowed round-to-nearest-even.
+ *
+ * Ownership: the caller owns every device buffer -- parameters, grads, the
+ * state buffer (apexw_state_bytes), the workspace (apexw_workspace_bytes) and
+ * the found_inf flag -- and the stream.  The library allocates no device
+ * memory; it keeps a small host handle and a pinned host staging area for
+ * table uploads.  Buffers must stay valid while work that uses them is queued.
+ *
+ * Errors: every function returns APEXW_OK (0) or a negative APEXW_E* code; on
+ * error nothing has been written to device memory, and apexw_last_error()
+ * gives a message (per thread).  Functions are thread-safe on distinct
+ * handles; one handle must not be used from two threads at once.
+ */
+#ifndef APEXW_H
+#define APEXW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- return codes */
+#define APEXW_OK 0
+#define APEXW_EINVAL (-1)  /* bad size, count, pointer or hyperparameter */
+#define APEXW_EDTYPE (-2)  /* unsupported element type or state format */
+#define APEXW_ENOSPC (-3)  /* state or workspace buffer smaller than needed */
+#define APEXW_EHIP (-4)    /* a HIP runtime call failed */
+#define APEXW_ENOMEM (-5)  /* host allocation failed */
+
+/* ---- element types of parameters and grads (dense, contiguous) */
+#define APEXW_F32 0
+#define APEXW_BF16 1
+
+/* ---- moment storage formats (section 05 of the M041 page) */
+#define APEXW_STATE_F32 0   /* m, v fp32: 8 bytes per element */
+#define APEXW_STATE_BF16 1  /* m, v bf16, rounded to nearest even: 4 bytes */
+#define APEXW_STATE_Q8 2    /* m int8 codes (scale absmax|m|/127), v uint8
+                               codes (scale max v/255), one fp32 scale each
+                               per 256-element block: 2 bytes + 8/256 */
+
+#define APEXW_Q8_BLOCK 256
+#define APEXW_MAX_GROUPS 32
+
+typedef struct apexw_opt *apexw_t;
+
+/* Hyperparameters of one parameter group for one call (Apex guide, section
+ * 4.2 parameter table; M041 section 03).  0 <= beta1, beta2 < 1; lr, eps and
+ * weight_decay finite and >= 0. */
+typedef struct {
+    double lr;
+    double beta1;
+    double beta2;
+    double eps;
+    double weight_decay;
+} apexw_group;
+
+/* Byte offsets of one tensor's state inside the state buffer.  m and v hold
+ * numel elements of the format's moment type (fp32, bf16 bits, int8, uint8);
+ * m_scale / v_scale hold ceil(numel/256) fp32 scales for APEXW_STATE_Q8 and
+ * are -1 otherwise. */
+typedef struct {
+    int64_t m;
+    int64_t v;
+    int64_t m_scale;
+    int64_t v_scale;
+} apexw_tensor_state;
+
+/*
+ * Bytes of optimizer state for n_tensors tensors of numel[i] elements in
+ * format fmt: the moment payload (8, 4 or 2 bytes per element), for Q8 two
+ * fp32 scales per 256-element block (blocks never span tensors), and one
+ * int32 step counter per tensor, plus padding that keeps each tensor's moment
+ * arrays 16-byte aligned (none when every numel is a multiple of 16).
+ * For the 392-tensor LoRA set of the "ApexW measured in Unsloth" page this is
+ * 185.5015 / 92.7515 / 47.1011 MiB for F32 / BF16 / Q8, the page's
+ * 185.501 / 92.751 / 47.101 MB optimizer-state figures.
+ * Returns APEXW_EINVAL for n_tensors < 0, a NULL pointer with n_tensors > 0,
+ * or a negative numel; APEXW_EDTYPE for an unknown fmt.
+ */
+int apexw_state_bytes(int32_t n_tensors, const int64_t *numel, int32_t fmt,
+                      size_t *out_bytes);
+
+/*
+ * Where each tensor's state lives in the state buffer: out_tensors[i] for
+ * i < n_tensors (caller-allocated array), and *out_steps the byte offset of
+ * the int32[n_tensors] step counters.  Layout: all m arrays (tensor order),
+ * then all v arrays, then (Q8) all m scales and all v scales, then the step
+ * counters.  Same argument rules as apexw_state_bytes.
+ */
+int apexw_state_layout(int32_t n_tensors, const int64_t *numel, int32_t fmt,
+                       apexw_tensor_state *out_tensors, int64_t *out_steps);
+
+/*
+ * Bytes of device workspace apexw_create needs for this tensor list (tensor
+ * and tile tables, grad-pointer table, launch counters).  Same argument rules
+ * as apexw_state_bytes, minus fmt.
+ */
+int apexw_workspace_bytes(int32_t n_tensors, const int64_t *numel,
+                          size_t *out_bytes);
+
+/*
+ * Create an optimizer over n_tensors tensors.
+ *   numel[i]        element count of tensor i (>= 0)
+ *   param_dtype[i]  APEXW_F32 or APEXW_BF16
+ *   grad_dtype[i]   APEXW_F32 or APEXW_BF16
+ *   group_of[i]     parameter group of tensor i, 0 <= group_of[i] < n_groups
+ *   n_groups        1 .. APEXW_MAX_GROUPS
+ *   fmt             APEXW_STATE_F32 / _BF16 / _Q8
+ *   state_dev       device buffer of state_bytes >= apexw_state_bytes(...)
+ *                   bytes, 256-byte aligned; zero-filled here on `stream`
+ *                   (m = v = 0, scales 0, step counters 0)
+ *   workspace_dev   device buffer of >= apexw_workspace_bytes(...) bytes,
+ *                   256-byte aligned, used only by this handle
+ *   stream          hipStream_t (NULL: the default stream); create queues its
+ *                   table uploads and the zero fill there and waits for them
+ * The arrays are copied; they need not outlive the call.  Returns
+ * APEXW_EINVAL / APEXW_EDTYPE / APEXW_ENOSPC on bad arguments (nothing
+ * written), APEXW_EHIP if a HIP call fails, APEXW_ENOMEM if host memory runs
+ * out.
+ */
+int apexw_create(int32_t n_tensors, const int64_t *numel,
+                 const int32_t *param_dtype, const int32_t *grad_dtype,
+                 const int32_t *group_of, int32_t n_groups, int32_t fmt,
+                 void *state_dev, size_t state_bytes, void *workspace_dev,
+                 size_t workspace_bytes, void *stream, apexw_t *out);
+
+/*
+ * Queue one optimizer step on `stream` (hipStream_t; NULL: default stream).
+ *   groups[g]     hyperparameters of group g for this call, n_groups entries
+ *                 (must equal the count given to apexw_create)
+ *   params[i]     device pointer to tensor i's values (param_dtype[i]); may
+ *                 be NULL only when numel[i] == 0
+ *   grads[i]      device pointer to tensor i's grad (grad_dtype[i]), or NULL
+ *                 when the tensor has no grad this call: then its values,
+ *                 moments and step counter are not touched
+ *   found_inf_dev device pointer to one float, read by the GPU when the step
+ *                 runs; nonzero (or NaN) skips the whole step -- nothing is
+ *                 written; NULL means never skip
+ * Never synchronises with the host.  The pointer tables are re-uploaded (one
+ * asynchronous copy) only when params or grads differ from the previous call.
+ * All calls on one handle must be ordered on the GPU (one stream, or streams
+ * the caller orders).  Non-finite grads with found_inf unset are not checked
+ * and propagate into theta, m and v.
+ */
+int apexw_step(apexw_t h, const apexw_group *groups, int32_t n_groups,
+               void *const *params, const void *const *grads,
+               const float *found_inf_dev, void *stream);
+
+/*
+ * Launch geometry of the handle: tile size in elements, number of tiles, and
+ * the workgroup count used per launch (persistent grid).  Any pointer may be
+ * NULL.
+ */
+int apexw_launch_info(apexw_t h, int32_t *tile_elems, int32_t *n_tiles,
+                      int32_t *workgroups);
+
+/*
+ * Override the persistent grid size (workgroups per launch); 0 restores the
+ * default (enough workgroups to fill every compute unit at the kernel's
+ * occupancy).  Results do not depend on it.
+ */
+int apexw_set_workgroups(apexw_t h, int32_t workgroups);
+
+/* Release the handle (host memory only; waits for nothing). */
+int apexw_destroy(apexw_t h);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char *apexw_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* APEXW_H */

@@ -90,7 +90,9 @@ def _ptr(a: Optional[np.ndarray]) -> int:
 
 
 def _ptr_array(arrs: Sequence[Optional[np.ndarray]]):
-    return (ctypes.c_void_p * max(1, len(arrs)))(*[_ptr(a) for a in arrs])
+    # a present but empty array still needs a non-NULL pointer ("present")
+    return (ctypes.c_void_p * max(1, len(arrs)))(
+        *[None if a is None else (_ptr(a) or 16) for a in arrs])
 
 
 def _groups(groups) -> ctypes.Array:

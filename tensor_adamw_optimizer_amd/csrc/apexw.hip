@@ -1,0 +1,527 @@
+// apexw.hip -- host engine and C ABI of the fused multi-tensor AdamW step.
+//
+// The engine turns a parameter list into device tables once (tensor
+// descriptors, a 4096-element tile table, per-launch tensor lists, launch
+// tickets), lays the optimizer state out in one caller-owned buffer, and on
+// every step queues one persistent kernel per (parameter dtype, grad dtype)
+// pair present.  Per call it only compares the param / grad pointer arrays
+// with the previous call's (one asynchronous upload when they differ) and
+// forms the per-group fp32 scalars, which travel in the kernel arguments.
+// It never synchronises with the host inside a step and allocates no device
+// memory.
+//
+// Sources: "Fused optimizers and state precision" (ai-infra-kb M041),
+// sections 02-06; "Apex fused optimizers" guide (qwbw.cn), sections 二/三
+// (dtype rules, multi-tensor launches) and 4.2-4.3 (parameter groups, device
+// overflow flag, step advanced only without overflow); "ApexW measured in
+// Unsloth" (kongchang.com), results table (state bytes per format).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "apexw.h"
+#include "apexw_kernels.hpp"
+
+using namespace apexw;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+#define HIP_TRY(call)                                                        \
+    do {                                                                     \
+        hipError_t e_ = (call);                                              \
+        if (e_ != hipSuccess)                                                \
+            return fail(APEXW_EHIP, "%s failed: %s", #call,                  \
+                        hipGetErrorString(e_));                              \
+    } while (0)
+
+constexpr int64_t kMomentAlign = 16;   // 128-bit loads of every moment array
+constexpr int64_t kTableAlign = 256;
+
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+int64_t ceil_div(int64_t x, int64_t a) { return (x + a - 1) / a; }
+
+int moment_bytes(int32_t fmt) {
+    switch (fmt) {
+    case APEXW_STATE_F32: return 4;
+    case APEXW_STATE_BF16: return 2;
+    case APEXW_STATE_Q8: return 1;
+    default: return 0;
+    }
+}
+
+int check_list(int32_t n, const int64_t *numel) {
+    if (n < 0) return fail(APEXW_EINVAL, "n_tensors must be >= 0 (got %d)", n);
+    if (n > 0 && numel == nullptr) return fail(APEXW_EINVAL, "numel is NULL");
+    for (int32_t i = 0; i < n; ++i)
+        if (numel[i] < 0)
+            return fail(APEXW_EINVAL, "numel[%d] is negative (%lld)", i,
+                        (long long)numel[i]);
+    return APEXW_OK;
+}
+
+// State layout: every m array, every v array, (Q8) every m scale array and
+// every v scale array, then the int32 step counters.  Moment arrays start on
+// 16-byte boundaries.
+int compute_layout(int32_t n, const int64_t *numel, int32_t fmt,
+                   apexw_tensor_state *per_tensor, int64_t *steps_off,
+                   int64_t *total) {
+    const int eb = moment_bytes(fmt);
+    if (eb == 0) return fail(APEXW_EDTYPE, "unknown state format %d", fmt);
+    int rc = check_list(n, numel);
+    if (rc) return rc;
+    int64_t off = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        if (per_tensor) per_tensor[i].m = off;
+        off += round_up(numel[i] * eb, kMomentAlign);
+    }
+    for (int32_t i = 0; i < n; ++i) {
+        if (per_tensor) per_tensor[i].v = off;
+        off += round_up(numel[i] * eb, kMomentAlign);
+    }
+    if (fmt == APEXW_STATE_Q8) {
+        for (int32_t i = 0; i < n; ++i) {
+            if (per_tensor) per_tensor[i].m_scale = off;
+            off += ceil_div(numel[i], APEXW_Q8_BLOCK) * 4;
+        }
+        for (int32_t i = 0; i < n; ++i) {
+            if (per_tensor) per_tensor[i].v_scale = off;
+            off += ceil_div(numel[i], APEXW_Q8_BLOCK) * 4;
+        }
+    } else if (per_tensor) {
+        for (int32_t i = 0; i < n; ++i) per_tensor[i].m_scale = per_tensor[i].v_scale = -1;
+    }
+    if (steps_off) *steps_off = off;
+    off += 4 * (int64_t)n;
+    if (total) *total = off;
+    return APEXW_OK;
+}
+
+// Workspace layout: descriptors | grad pointers | tiles | launch tensor lists
+// | tickets, each on a 256-byte boundary.
+struct WsLayout {
+    int64_t desc, grads, tiles, tensors, tickets, total;
+    int64_t n_tiles;
+};
+
+constexpr int kMaxLaunches = 4;   // (param, grad) dtype pairs
+
+WsLayout ws_layout(int32_t n, const int64_t *numel) {
+    WsLayout w;
+    w.n_tiles = 0;
+    for (int32_t i = 0; i < n; ++i) w.n_tiles += ceil_div(numel[i], kTile);
+    w.desc = 0;
+    w.grads = w.desc + round_up((int64_t)n * (int64_t)sizeof(TensorDesc), kTableAlign);
+    w.tiles = w.grads + round_up((int64_t)n * 8, kTableAlign);
+    w.tensors = w.tiles + round_up(w.n_tiles * (int64_t)sizeof(TileRef), kTableAlign);
+    w.tickets = w.tensors + round_up((int64_t)n * 4, kTableAlign);
+    w.total = w.tickets + kTableAlign;
+    return w;
+}
+
+bool finite_nonneg(double x) { return std::isfinite(x) && x >= 0.0; }
+
+struct Launch {
+    int pt, gt;
+    int32_t tile_begin, tile_count;
+    int32_t tensor_begin, tensor_count;
+    int max_workgroups;            // occupancy x compute units
+};
+
+typedef void (*kernel_fn)(KernelArgs);
+
+template <int ST>
+kernel_fn pick_kernel(int pt, int gt) {
+    // non-temporal hints keep the single-use streams out of the caches
+    if (pt == APEXW_F32 && gt == APEXW_F32) return adamw_step_kernel<ST, APEXW_F32, APEXW_F32, true>;
+    if (pt == APEXW_F32 && gt == APEXW_BF16) return adamw_step_kernel<ST, APEXW_F32, APEXW_BF16, true>;
+    if (pt == APEXW_BF16 && gt == APEXW_F32) return adamw_step_kernel<ST, APEXW_BF16, APEXW_F32, true>;
+    return adamw_step_kernel<ST, APEXW_BF16, APEXW_BF16, true>;
+}
+
+kernel_fn kernel_for(int fmt, int pt, int gt) {
+    if (fmt == APEXW_STATE_F32) return pick_kernel<APEXW_STATE_F32>(pt, gt);
+    if (fmt == APEXW_STATE_BF16) return pick_kernel<APEXW_STATE_BF16>(pt, gt);
+    return pick_kernel<APEXW_STATE_Q8>(pt, gt);
+}
+
+}  // namespace
+
+struct apexw_opt {
+    int device = 0;
+    int32_t n = 0, n_groups = 0, fmt = 0;
+    std::vector<int64_t> numel;
+    std::vector<int32_t> pdt, gdt, group_of;
+    std::vector<apexw_tensor_state> layout;
+    int64_t steps_off = 0;
+    char *state = nullptr;
+    char *ws = nullptr;
+    WsLayout wl{};
+    std::vector<Launch> launches;
+    std::vector<int32_t> tensor_list;   // host copy of the launch tensor lists
+    // host mirrors of the per-call tables
+    std::vector<TensorDesc> desc;
+    std::vector<void *> last_params;
+    std::vector<const void *> last_grads;
+    bool have_params = false, have_grads = false;
+    // pinned staging ring for table uploads
+    static constexpr int kRing = 4;
+    char *pinned = nullptr;
+    int64_t slot_bytes = 0;
+    hipEvent_t ev[kRing] = {};
+    bool ev_pending[kRing] = {};
+    int next_slot = 0;
+    int cu_count = 0;
+    int32_t wg_override = 0;
+};
+
+namespace {
+
+struct DeviceGuard {
+    int prev = -1;
+    explicit DeviceGuard(int dev) {
+        int cur = 0;
+        if (hipGetDevice(&cur) == hipSuccess && cur != dev) {
+            prev = cur;
+            (void)hipSetDevice(dev);
+        }
+    }
+    ~DeviceGuard() {
+        if (prev >= 0) (void)hipSetDevice(prev);
+    }
+};
+
+void release(apexw_opt *h) {
+    if (!h) return;
+    for (int s = 0; s < apexw_opt::kRing; ++s) {
+        if (h->ev[s]) {
+            if (h->ev_pending[s]) (void)hipEventSynchronize(h->ev[s]);
+            (void)hipEventDestroy(h->ev[s]);
+        }
+    }
+    if (h->pinned) (void)hipHostFree(h->pinned);
+    delete h;
+}
+
+}  // namespace
+
+// ======================================================================= ABI
+
+extern "C" {
+
+const char *apexw_last_error(void) { return g_err; }
+
+int apexw_state_bytes(int32_t n_tensors, const int64_t *numel, int32_t fmt,
+                      size_t *out_bytes) {
+    if (!out_bytes) return fail(APEXW_EINVAL, "out_bytes is NULL");
+    int64_t total = 0;
+    int rc = compute_layout(n_tensors, numel, fmt, nullptr, nullptr, &total);
+    if (rc) return rc;
+    *out_bytes = (size_t)total;
+    return APEXW_OK;
+}
+
+int apexw_state_layout(int32_t n_tensors, const int64_t *numel, int32_t fmt,
+                       apexw_tensor_state *out_tensors, int64_t *out_steps) {
+    if (n_tensors > 0 && !out_tensors) return fail(APEXW_EINVAL, "out_tensors is NULL");
+    if (!out_steps) return fail(APEXW_EINVAL, "out_steps is NULL");
+    return compute_layout(n_tensors, numel, fmt, out_tensors, out_steps, nullptr);
+}
+
+int apexw_workspace_bytes(int32_t n_tensors, const int64_t *numel, size_t *out_bytes) {
+    if (!out_bytes) return fail(APEXW_EINVAL, "out_bytes is NULL");
+    int rc = check_list(n_tensors, numel);
+    if (rc) return rc;
+    *out_bytes = (size_t)ws_layout(n_tensors, numel).total;
+    return APEXW_OK;
+}
+
+int apexw_create(int32_t n_tensors, const int64_t *numel, const int32_t *param_dtype,
+                 const int32_t *grad_dtype, const int32_t *group_of, int32_t n_groups,
+                 int32_t fmt, void *state_dev, size_t state_bytes, void *workspace_dev,
+                 size_t workspace_bytes, void *stream, apexw_t *out) {
+    if (!out) return fail(APEXW_EINVAL, "out is NULL");
+    *out = nullptr;
+    int rc = check_list(n_tensors, numel);
+    if (rc) return rc;
+    if (moment_bytes(fmt) == 0) return fail(APEXW_EDTYPE, "unknown state format %d", fmt);
+    if (n_groups < 1 || n_groups > APEXW_MAX_GROUPS)
+        return fail(APEXW_EINVAL, "n_groups must be in 1..%d (got %d)", APEXW_MAX_GROUPS, n_groups);
+    if (n_tensors > 0 && (!param_dtype || !grad_dtype || !group_of))
+        return fail(APEXW_EINVAL, "param_dtype, grad_dtype and group_of must not be NULL");
+    for (int32_t i = 0; i < n_tensors; ++i) {
+        if (param_dtype[i] != APEXW_F32 && param_dtype[i] != APEXW_BF16)
+            return fail(APEXW_EDTYPE, "param_dtype[%d] = %d is not fp32 or bf16", i, param_dtype[i]);
+        if (grad_dtype[i] != APEXW_F32 && grad_dtype[i] != APEXW_BF16)
+            return fail(APEXW_EDTYPE, "grad_dtype[%d] = %d is not fp32 or bf16", i, grad_dtype[i]);
+        if (group_of[i] < 0 || group_of[i] >= n_groups)
+            return fail(APEXW_EINVAL, "group_of[%d] = %d outside 0..%d", i, group_of[i], n_groups - 1);
+        if (numel[i] > ((int64_t)1 << 31) * kTile)
+            return fail(APEXW_EINVAL, "numel[%d] too large", i);
+    }
+    int64_t need_state = 0;
+    compute_layout(n_tensors, numel, fmt, nullptr, nullptr, &need_state);
+    const WsLayout wl = ws_layout(n_tensors, numel);
+    if (wl.n_tiles > INT32_MAX) return fail(APEXW_EINVAL, "too many tiles");
+    if (!state_dev || !workspace_dev)
+        return fail(APEXW_EINVAL, "state_dev and workspace_dev must not be NULL");
+    if (((uintptr_t)state_dev | (uintptr_t)workspace_dev) & (kTableAlign - 1))
+        return fail(APEXW_EINVAL, "state_dev and workspace_dev must be 256-byte aligned");
+    if ((int64_t)state_bytes < need_state)
+        return fail(APEXW_ENOSPC, "state buffer has %zu bytes, needs %lld", state_bytes,
+                    (long long)need_state);
+    if ((int64_t)workspace_bytes < wl.total)
+        return fail(APEXW_ENOSPC, "workspace has %zu bytes, needs %lld", workspace_bytes,
+                    (long long)wl.total);
+
+    apexw_opt *h = new (std::nothrow) apexw_opt;
+    if (!h) return fail(APEXW_ENOMEM, "host allocation failed");
+    try {
+        h->n = n_tensors;
+        h->n_groups = n_groups;
+        h->fmt = fmt;
+        h->numel.assign(numel, numel + n_tensors);
+        h->pdt.assign(param_dtype, param_dtype + n_tensors);
+        h->gdt.assign(grad_dtype, grad_dtype + n_tensors);
+        h->group_of.assign(group_of, group_of + n_tensors);
+        h->layout.resize(n_tensors);
+        compute_layout(n_tensors, numel, fmt, h->layout.data(), &h->steps_off, nullptr);
+        h->desc.resize(n_tensors);
+        h->last_params.resize(n_tensors);
+        h->last_grads.resize(n_tensors);
+    } catch (const std::bad_alloc &) {
+        delete h;
+        return fail(APEXW_ENOMEM, "host allocation failed");
+    }
+    h->state = static_cast<char *>(state_dev);
+    h->ws = static_cast<char *>(workspace_dev);
+    h->wl = wl;
+
+    auto bail = [&](int code) { release(h); return code; };
+#define TRY(call)                                                             \
+    do {                                                                      \
+        hipError_t e_ = (call);                                               \
+        if (e_ != hipSuccess)                                                 \
+            return bail(fail(APEXW_EHIP, "%s failed: %s", #call,              \
+                             hipGetErrorString(e_)));                         \
+    } while (0)
+
+    TRY(hipGetDevice(&h->device));
+    TRY(hipDeviceGetAttribute(&h->cu_count, hipDeviceAttributeMultiprocessorCount, h->device));
+
+    // static tables: tiles and launch tensor lists grouped by dtype pair
+    std::vector<TileRef> tiles;
+    std::vector<int32_t> tensors;
+    try {
+        tiles.reserve((size_t)wl.n_tiles);
+        tensors.reserve(n_tensors);
+        const int pairs[kMaxLaunches][2] = {{APEXW_F32, APEXW_F32}, {APEXW_F32, APEXW_BF16},
+                                           {APEXW_BF16, APEXW_F32}, {APEXW_BF16, APEXW_BF16}};
+        for (int p = 0; p < kMaxLaunches; ++p) {
+            Launch L{pairs[p][0], pairs[p][1], (int32_t)tiles.size(), 0,
+                     (int32_t)tensors.size(), 0, 0};
+            for (int32_t i = 0; i < n_tensors; ++i) {
+                if (param_dtype[i] != L.pt || grad_dtype[i] != L.gt) continue;
+                tensors.push_back(i);
+                const int64_t nt = ceil_div(numel[i], kTile);
+                for (int64_t k = 0; k < nt; ++k) tiles.push_back(TileRef{i, (int32_t)k});
+            }
+            L.tile_count = (int32_t)tiles.size() - L.tile_begin;
+            L.tensor_count = (int32_t)tensors.size() - L.tensor_begin;
+            if (L.tensor_count == 0) continue;
+            int occ = 0;
+            TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &occ, reinterpret_cast<const void *>(kernel_for(fmt, L.pt, L.gt)), kThreads, 0));
+            L.max_workgroups = std::max(1, occ) * h->cu_count;
+            h->launches.push_back(L);
+        }
+    } catch (const std::bad_alloc &) {
+        return bail(fail(APEXW_ENOMEM, "host allocation failed"));
+    }
+
+    // pinned staging: the ring for per-call uploads, also used once here
+    const int64_t per_call = wl.tiles;        // descriptors + grad pointers
+    const int64_t static_bytes = wl.total - wl.tiles;
+    h->slot_bytes = std::max<int64_t>(per_call, kTableAlign);
+    const int64_t pinned_bytes =
+        std::max<int64_t>(h->slot_bytes * apexw_opt::kRing, static_bytes);
+    TRY(hipHostMalloc((void **)&h->pinned, (size_t)pinned_bytes, hipHostMallocDefault));
+    for (int s = 0; s < apexw_opt::kRing; ++s) TRY(hipEventCreateWithFlags(&h->ev[s], hipEventDisableTiming));
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char *stage = h->pinned;
+    std::memset(stage, 0, (size_t)static_bytes);
+    if (!tiles.empty())
+        std::memcpy(stage, tiles.data(), tiles.size() * sizeof(TileRef));
+    if (!tensors.empty())
+        std::memcpy(stage + (wl.tensors - wl.tiles), tensors.data(), tensors.size() * 4);
+    // tickets are zero in the staged copy
+    TRY(hipMemcpyAsync(h->ws + wl.tiles, stage, (size_t)static_bytes, hipMemcpyHostToDevice, st));
+    const int64_t words = need_state / 4;
+    if (words > 0) {
+        const int64_t blocks = std::min<int64_t>(ceil_div(words, kThreads), 8 * (int64_t)h->cu_count);
+        hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, st,
+                           reinterpret_cast<uint32_t *>(h->state), words);
+        TRY(hipGetLastError());
+    }
+    TRY(hipStreamSynchronize(st));
+#undef TRY
+    try {
+        h->tensor_list = tensors;
+    } catch (const std::bad_alloc &) {
+        release(h);
+        return fail(APEXW_ENOMEM, "host allocation failed");
+    }
+    *out = h;
+    return APEXW_OK;
+}
+
+int apexw_step(apexw_t h, const apexw_group *groups, int32_t n_groups, void *const *params,
+               const void *const *grads, const float *found_inf_dev, void *stream) {
+    if (!h) return fail(APEXW_EINVAL, "handle is NULL");
+    if (n_groups != h->n_groups)
+        return fail(APEXW_EINVAL, "n_groups is %d, the handle was created with %d", n_groups,
+                    h->n_groups);
+    if (!groups) return fail(APEXW_EINVAL, "groups is NULL");
+    if (h->n > 0 && (!params || !grads)) return fail(APEXW_EINVAL, "params and grads must not be NULL");
+
+    KernelArgs a;
+    std::memset(&a, 0, sizeof a);
+    for (int32_t g = 0; g < n_groups; ++g) {
+        const apexw_group &G = groups[g];
+        if (!finite_nonneg(G.lr) || !finite_nonneg(G.eps) || !finite_nonneg(G.weight_decay) ||
+            !(G.beta1 >= 0.0 && G.beta1 < 1.0) || !(G.beta2 >= 0.0 && G.beta2 < 1.0))
+            return fail(APEXW_EINVAL,
+                        "group %d: need lr, eps, weight_decay finite and >= 0 and 0 <= beta < 1", g);
+        // scalars formed in fp64 and rounded once to fp32
+        GroupScalars &S = a.groups[g];
+        S.beta1 = (float)G.beta1;
+        S.one_minus_beta1 = (float)(1.0 - G.beta1);
+        S.beta2 = (float)G.beta2;
+        S.one_minus_beta2 = (float)(1.0 - G.beta2);
+        S.lr = (float)G.lr;
+        S.decay = (float)(1.0 - G.lr * G.weight_decay);
+        S.eps = (float)G.eps;
+        S.beta1_d = G.beta1;
+        S.beta2_d = G.beta2;
+    }
+    for (int32_t i = 0; i < h->n; ++i)
+        if (params[i] == nullptr && h->numel[i] > 0)
+            return fail(APEXW_EINVAL, "params[%d] is NULL", i);
+
+    const size_t n = (size_t)h->n;
+    const bool params_changed =
+        !h->have_params || (n && std::memcmp(h->last_params.data(), params, n * sizeof(void *)));
+    const bool grads_changed =
+        !h->have_grads || (n && std::memcmp(h->last_grads.data(), grads, n * sizeof(void *)));
+
+    DeviceGuard guard(h->device);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (n && (params_changed || grads_changed)) {
+        const int s = h->next_slot;
+        if (h->ev_pending[s]) HIP_TRY(hipEventSynchronize(h->ev[s]));
+        char *slot = h->pinned + (int64_t)s * h->slot_bytes;
+        int64_t begin = h->wl.grads, end = h->wl.grads + (int64_t)n * 8;
+        if (params_changed) {
+            for (int32_t i = 0; i < h->n; ++i) {
+                TensorDesc &d = h->desc[i];
+                std::memset(&d, 0, sizeof d);
+                d.param = params[i];
+                d.m = h->state + h->layout[i].m;
+                d.v = h->state + h->layout[i].v;
+                d.m_scale = h->layout[i].m_scale >= 0
+                                ? reinterpret_cast<float *>(h->state + h->layout[i].m_scale)
+                                : nullptr;
+                d.v_scale = h->layout[i].v_scale >= 0
+                                ? reinterpret_cast<float *>(h->state + h->layout[i].v_scale)
+                                : nullptr;
+                d.numel = h->numel[i];
+                d.group = h->group_of[i];
+            }
+            std::memcpy(slot + h->wl.desc, h->desc.data(), n * sizeof(TensorDesc));
+            begin = h->wl.desc;
+        }
+        std::memcpy(slot + h->wl.grads, grads, n * sizeof(void *));
+        HIP_TRY(hipMemcpyAsync(h->ws + begin, slot + begin, (size_t)(end - begin),
+                               hipMemcpyHostToDevice, st));
+        HIP_TRY(hipEventRecord(h->ev[s], st));
+        h->ev_pending[s] = true;
+        h->next_slot = (s + 1) % apexw_opt::kRing;
+        std::memcpy(h->last_params.data(), params, n * sizeof(void *));
+        std::memcpy(h->last_grads.data(), grads, n * sizeof(void *));
+        h->have_params = h->have_grads = true;
+    }
+
+    a.desc = reinterpret_cast<const TensorDesc *>(h->ws + h->wl.desc);
+    a.grads = reinterpret_cast<const void *const *>(h->ws + h->wl.grads);
+    a.steps = reinterpret_cast<int32_t *>(h->state + h->steps_off);
+    a.found_inf = found_inf_dev;
+    const TileRef *tiles = reinterpret_cast<const TileRef *>(h->ws + h->wl.tiles);
+    const int32_t *tensors = reinterpret_cast<const int32_t *>(h->ws + h->wl.tensors);
+    uint32_t *tickets = reinterpret_cast<uint32_t *>(h->ws + h->wl.tickets);
+    for (size_t li = 0; li < h->launches.size(); ++li) {
+        const Launch &L = h->launches[li];
+        bool any = false;   // skip a launch none of whose tensors has a grad
+        for (int32_t j = 0; j < L.tensor_count && !any; ++j)
+            any = grads[h->tensor_list[L.tensor_begin + j]] != nullptr;
+        if (!any) continue;
+        a.tiles = tiles + L.tile_begin;
+        a.n_tiles = L.tile_count;
+        a.tensors = tensors + L.tensor_begin;
+        a.n_tensors = L.tensor_count;
+        a.ticket = tickets + L.pt * 2 + L.gt;
+        int wg = h->wg_override > 0 ? h->wg_override : L.max_workgroups;
+        wg = std::max(1, std::min(wg, std::max(1, L.tile_count)));
+        hipLaunchKernelGGL(kernel_for(h->fmt, L.pt, L.gt), dim3((unsigned)wg), dim3(kThreads), 0,
+                           st, a);
+        HIP_TRY(hipGetLastError());
+    }
+    return APEXW_OK;
+}
+
+int apexw_launch_info(apexw_t h, int32_t *tile_elems, int32_t *n_tiles, int32_t *workgroups) {
+    if (!h) return fail(APEXW_EINVAL, "handle is NULL");
+    if (tile_elems) *tile_elems = kTile;
+    if (n_tiles) *n_tiles = (int32_t)h->wl.n_tiles;
+    if (workgroups) {
+        int32_t wg = 0;
+        for (const Launch &L : h->launches) {
+            int w = h->wg_override > 0 ? h->wg_override : L.max_workgroups;
+            wg = std::max<int32_t>(wg, std::max(1, std::min(w, std::max(1, L.tile_count))));
+        }
+        *workgroups = wg;
+    }
+    return APEXW_OK;
+}
+
+int apexw_set_workgroups(apexw_t h, int32_t workgroups) {
+    if (!h) return fail(APEXW_EINVAL, "handle is NULL");
+    if (workgroups < 0) return fail(APEXW_EINVAL, "workgroups must be >= 0");
+    h->wg_override = workgroups;
+    return APEXW_OK;
+}
+
+int apexw_destroy(apexw_t h) {
+    if (!h) return fail(APEXW_EINVAL, "handle is NULL");
+    DeviceGuard guard(h->device);
+    release(h);
+    return APEXW_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,410 @@
+"""GPU parity: the HIP library, called through its C ABI, against the oracle
+on the same seeded inputs.
+
+Bars: fp32 state -- elementwise relative error <= 1e-5 on theta, m, v after
+every call (the design target, and what is observed, is a bitwise match);
+bf16 state -- bitwise against the oracle's bf16-state mode and <= 1e-2
+(normwise) against the fp32-state oracle on the moments; 8-bit state --
+codes equal or within 1, scales within 1e-6 relative; step counters and the
+skip / grad=None behaviour bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_helpers import (GpuOpt, as_f32, assert_fp32_state_parity, bits, n_bit_mismatch,
+                         normwise_err, rel_err_elementwise, say)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+
+
+def _oracle_for(w: W.Workload, idx=None, state_fmt=None):
+    idx = range(len(w.shapes)) if idx is None else idx
+    return oracle.OracleAdamW([w.numels[i] for i in idx], [w.param_dtype[i] for i in idx],
+                              [w.grad_dtype[i] for i in idx], [w.group_of[i] for i in idx],
+                              state_fmt or w.state_fmt)
+
+
+# =================================================================== tiny
+
+def test_tiny_every_call_against_oracle():
+    """525,315 fp32 params, 20 calls, call 7 skipped, [3] has no grad on odd
+    calls: theta, m, v and t compared after every call."""
+    _need_gpu()
+    w = W.tiny()
+    say("case: tiny", w.describe())
+    p_cpu = W.init_params(w, "cpu")
+    params = [p.to(DEV) for p in p_cpu]
+    grads = [torch.empty(s, dtype=torch.float32, device=DEV) for s in w.shapes]
+    opt = GpuOpt(w.numels, w.param_dtype, w.grad_dtype, w.group_of, len(w.groups), w.state_fmt)
+    ref = _oracle_for(w)
+    th_ref = [bits(p) for p in p_cpu]
+    fi = torch.zeros(1, dtype=torch.float32, device=DEV)
+    total_mismatch = 0
+    for k in range(1, w.steps + 1):
+        g_cpu = W.grads_for_call(w, k, "cpu")
+        for gb, g in zip(grads, g_cpu):
+            if g is not None:
+                gb.copy_(g)
+        skip = w.skip_call(k)
+        fi.fill_(1.0 if skip else 0.0)
+        opt.step(w.groups, params, [gb if g is not None else None for gb, g in zip(grads, g_cpu)],
+                 found_inf=fi)
+        ref.step(th_ref, [None if g is None else bits(g) for g in g_cpu], w.groups, found_inf=skip)
+        torch.cuda.synchronize()
+        for i in range(len(w.shapes)):
+            m, v = opt.moments(i)
+            total_mismatch += assert_fp32_state_parity("theta%d@%d" % (i, k), bits(params[i]), th_ref[i])
+            total_mismatch += assert_fp32_state_parity("m%d@%d" % (i, k), bits(m), ref.m[i])
+            total_mismatch += assert_fp32_state_parity("v%d@%d" % (i, k), bits(v), ref.v[i])
+        assert np.array_equal(bits(opt.steps()), ref.t), (bits(opt.steps()), ref.t)
+    assert list(ref.t) == [19, 19, 19, 9]
+    assert total_mismatch == 0
+    opt.close()
+
+
+# =================================================================== edge cases
+
+EDGE_SIZES = [1, 3, 5, 255, 256, 257, 1023, 4095, 4096, 4097, 8191, 12289, 0, 100003]
+
+
+@pytest.mark.parametrize("fmt", [W.STATE_F32, W.STATE_BF16, W.STATE_Q8])
+def test_ragged_mixed_dtypes_groups_and_misalignment(fmt):
+    """Every (param, grad) dtype pair in one optimizer (one launch each), ragged
+    sizes, an empty tensor, three groups, a parameter and a grad that are not
+    16-byte aligned, grads absent on some calls, one skipped call."""
+    _need_gpu()
+    say("case: ragged", fmt)
+    sizes = EDGE_SIZES * 2
+    n = len(sizes)
+    pdt = [(W.F32, W.BF16)[(i // 2) % 2] for i in range(n)]
+    gdt = [(W.F32, W.BF16)[i % 2] for i in range(n)]
+    group_of = [i % 3 for i in range(n)]
+    groups = [W.Group(lr=1e-2, weight_decay=0.1), W.Group(lr=3e-3, beta1=0.8, beta2=0.99, eps=1e-6),
+              W.Group(lr=5e-4, weight_decay=0.01)]
+    gen = torch.Generator().manual_seed(7)
+    p_cpu = [(torch.randn(s, generator=gen) * 0.02).to(W.TORCH_DTYPE[d]) for s, d in zip(sizes, pdt)]
+    # tensor 3 and 10 live one element into a larger buffer: not 16-byte aligned
+    bases = {}
+    params = []
+    for i, p in enumerate(p_cpu):
+        if i in (3, 10):
+            buf = torch.zeros(p.numel() + 1, dtype=p.dtype, device=DEV)
+            buf[1:].copy_(p)
+            bases[i] = buf
+            params.append(buf[1:])
+        else:
+            params.append(p.to(DEV))
+    opt = GpuOpt(sizes, pdt, gdt, group_of, 3, fmt)
+    ref = oracle.OracleAdamW(sizes, pdt, gdt, group_of, fmt)
+    th_ref = [bits(p) for p in p_cpu]
+    fi = torch.zeros(1, device=DEV)
+    for k in range(1, 9):
+        g_cpu = [(torch.randn(s, generator=gen) * 1e-3).to(W.TORCH_DTYPE[d]) for s, d in zip(sizes, gdt)]
+        present = [not ((i + k) % 5 == 0) for i in range(n)]
+        gdev = []
+        for i, (g, ok) in enumerate(zip(g_cpu, present)):
+            if not ok:
+                gdev.append(None)
+            elif i == 5:
+                gb = torch.zeros(g.numel() + 3, dtype=g.dtype, device=DEV)
+                gb[3:].copy_(g)
+                gdev.append(gb[3:])
+            else:
+                gdev.append(g.to(DEV))
+        skip = k == 4
+        fi.fill_(1.0 if skip else 0.0)
+        opt.step(groups, params, gdev, found_inf=fi)
+        ref.step(th_ref, [bits(g) if ok else None for g, ok in zip(g_cpu, present)], groups,
+                 found_inf=skip)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(opt.steps()), ref.t)
+    for i in range(n):
+        assert n_bit_mismatch(bits(params[i]), th_ref[i]) == 0, i
+        m, v = opt.moments(i)
+        assert n_bit_mismatch(bits(m), ref.m[i]) == 0, i
+        assert n_bit_mismatch(bits(v), ref.v[i]) == 0, i
+        if fmt == W.STATE_Q8:
+            ms, vs = opt.scales(i)
+            assert n_bit_mismatch(bits(ms), ref.m_scale[i]) == 0, i
+            assert n_bit_mismatch(bits(vs), ref.v_scale[i]) == 0, i
+    opt.close()
+
+
+@pytest.mark.parametrize("fmt", [W.STATE_F32, W.STATE_BF16, W.STATE_Q8])
+def test_found_inf_leaves_everything_bitwise(fmt):
+    _need_gpu()
+    say("case: found_inf", fmt)
+    sizes = [5000, 4096, 77]
+    opt = GpuOpt(sizes, [W.BF16, W.F32, W.F32], [W.F32, W.BF16, W.F32], [0, 0, 0], 1, fmt)
+    params = [torch.randn(sizes[0], device=DEV).to(torch.bfloat16), torch.randn(sizes[1], device=DEV),
+              torch.randn(sizes[2], device=DEV)]
+    grads = [torch.randn(sizes[0], device=DEV) * 1e-3,
+             (torch.randn(sizes[1], device=DEV) * 1e-3).to(torch.bfloat16),
+             torch.randn(sizes[2], device=DEV) * 1e-3]
+    g = [W.Group(lr=1e-3, weight_decay=0.1)]
+    for _ in range(3):
+        opt.step(g, params, grads)
+    torch.cuda.synchronize()
+    before = [bits(p) for p in params] + [bits(opt.state)]
+    fi = torch.ones(1, device=DEV)
+    for val in (1.0, float("inf"), float("nan"), -2.0):
+        fi.fill_(val)
+        opt.step(g, params, grads, found_inf=fi)
+    torch.cuda.synchronize()
+    after = [bits(p) for p in params] + [bits(opt.state)]
+    for a, b in zip(before, after):
+        assert np.array_equal(a, b)
+    assert list(bits(opt.steps())) == [3, 3, 3]
+    fi.fill_(0.0)
+    opt.step(g, params, grads, found_inf=fi)
+    torch.cuda.synchronize()
+    assert list(bits(opt.steps())) == [4, 4, 4]
+    opt.close()
+
+
+def test_all_grads_absent_and_pointer_changes():
+    """No grads at all: nothing changes.  Grads moved to new buffers between
+    calls: the library follows the new pointers."""
+    _need_gpu()
+    say("case: absent grads / moved grads")
+    w = W.tiny()
+    p_cpu = W.init_params(w, "cpu")
+    params = [p.to(DEV) for p in p_cpu]
+    opt = GpuOpt(w.numels, w.param_dtype, w.grad_dtype, w.group_of, 1, w.state_fmt)
+    ref = _oracle_for(w)
+    th_ref = [bits(p) for p in p_cpu]
+    opt.step(w.groups, params, [None] * 4)
+    ref.step(th_ref, [None] * 4, w.groups)
+    for k in range(1, 6):
+        g_cpu = W.grads_for_call(w, k, "cpu")
+        g_cpu = [g if g is not None else torch.zeros(s) for g, s in zip(g_cpu, w.shapes)]
+        g_dev = [g.to(DEV) for g in g_cpu]      # fresh allocations every call
+        keep = [torch.empty(1 << 20, device=DEV) for _ in range(k)]  # shift the allocator
+        opt.step(w.groups, params, g_dev)
+        ref.step(th_ref, [bits(g) for g in g_cpu], w.groups)
+        del keep
+    torch.cuda.synchronize()
+    for i in range(4):
+        assert n_bit_mismatch(bits(params[i]), th_ref[i]) == 0
+    assert list(bits(opt.steps())) == [5, 5, 5, 5]
+    opt.close()
+
+
+@pytest.mark.parametrize("wg", [1, 7, 300, 0])
+def test_results_do_not_depend_on_grid(wg):
+    _need_gpu()
+    say("case: grid", wg)
+    w = W.many_small(n_tensors=300)
+    outs = []
+    for setting in (wg, 0):
+        params = W.init_params(w, DEV)
+        opt = GpuOpt(w.numels, w.param_dtype, w.grad_dtype, w.group_of, 3, w.state_fmt)
+        from tensor_adamw_optimizer_amd import _lib as L
+        L.apexw_set_workgroups(opt.h, setting)
+        for k in range(1, 4):
+            opt.step(w.groups, params, W.grads_for_call(w, k, DEV))
+        torch.cuda.synchronize()
+        outs.append((torch.cat([p.reshape(-1) for p in params]).cpu(), opt.state.cpu()))
+        opt.close()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+# =================================================================== configs
+
+def _sampled_run(w: W.Workload, sample_tensors, elems=None, seed=0, every=None,
+                 ref_fmt=None, calls=None):
+    """Run the whole workload on the GPU; run the oracle on a sample: whole
+    tensors ``sample_tensors`` or, with ``elems`` (dict i -> index array), the
+    given elements (for fp32 / bf16 state, where elements are independent).
+    Returns (opt, params, ref, th_ref, idx)."""
+    calls = calls or w.steps
+    params = W.init_params(w, DEV)
+    grads = [torch.empty(s, dtype=W.TORCH_DTYPE[d], device=DEV) for s, d in zip(w.shapes, w.grad_dtype)]
+    opt = GpuOpt(w.numels, w.param_dtype, w.grad_dtype, w.group_of, len(w.groups), w.state_fmt)
+    idx = {}
+    for i in sample_tensors:
+        idx[i] = (torch.arange(w.numels[i]) if elems is None or i not in elems
+                  else torch.as_tensor(elems[i]))
+    sel = list(sample_tensors)
+    sub_n = [int(idx[i].numel()) for i in sel]
+    ref = oracle.OracleAdamW(sub_n, [w.param_dtype[i] for i in sel], [w.grad_dtype[i] for i in sel],
+                             [w.group_of[i] for i in sel], ref_fmt or w.state_fmt)
+    idx_dev = {i: idx[i].to(DEV) for i in sel}
+    th_ref = [bits(params[i].reshape(-1)[idx_dev[i]]) for i in sel]
+    fi = torch.zeros(1, device=DEV)
+    for k in range(1, calls + 1):
+        g_list = W.grads_for_call(w, k, DEV, out=grads)
+        skip = w.skip_call(k)
+        fi.fill_(1.0 if skip else 0.0)
+        opt.step(w.groups, params, g_list, found_inf=fi)
+        ref.step(th_ref, [None if g_list[i] is None else bits(g_list[i].reshape(-1)[idx_dev[i]])
+                          for i in sel], w.groups, found_inf=skip)
+        if every and k % every == 0:
+            say("  call", k)
+    torch.cuda.synchronize()
+    return opt, params, ref, th_ref, idx_dev
+
+
+def _spread_indices(n, count, rng):
+    """Sorted sample of element indices: the first and last tile plus random
+    elements in between."""
+    head = np.arange(min(n, 4096))
+    tail = np.arange(max(0, n - 4096), n)
+    mid = rng.choice(n, size=min(n, count), replace=False)
+    return np.unique(np.concatenate([head, tail, mid]))
+
+
+def test_many_small_reduced_full_oracle():
+    """2,000 log-uniform tensors (3 groups round-robin), 10 calls, every
+    element against the oracle."""
+    _need_gpu()
+    w = W.many_small(n_tensors=2000)
+    say("case: many_small reduced", w.describe())
+    opt, params, ref, th_ref, idx = _sampled_run(w, range(len(w.shapes)))
+    mism = 0
+    for j, i in enumerate(range(len(w.shapes))):
+        m, v = opt.moments(i)
+        for name, a, b in (("theta", bits(params[i]), th_ref[j]), ("m", bits(m), ref.m[j]),
+                           ("v", bits(v), ref.v[j])):
+            assert rel_err_elementwise(a, b) <= 1e-5, (name, i)
+            mism += n_bit_mismatch(a, b)
+    assert np.array_equal(bits(opt.steps()), ref.t)
+    say("  bit mismatches:", mism)
+    assert mism == 0
+    opt.close()
+
+
+def test_many_small_full_size_sampled():
+    """The 20,000-tensor list (about 189M params), 10 calls; 400 whole tensors
+    (the smallest, the largest, random) against the oracle."""
+    _need_gpu()
+    w = W.many_small()
+    say("case: many_small full", w.describe())
+    rng = np.random.default_rng(0)
+    order = np.argsort(w.numels)
+    pick = sorted(set(order[:50].tolist() + order[-50:].tolist() +
+                      rng.choice(len(w.shapes), 300, replace=False).tolist()))
+    opt, params, ref, th_ref, idx = _sampled_run(w, pick)
+    for j, i in enumerate(pick):
+        m, v = opt.moments(i)
+        assert rel_err_elementwise(bits(params[i]), th_ref[j]) <= 1e-5
+        assert rel_err_elementwise(bits(m), ref.m[j]) <= 1e-5
+        assert rel_err_elementwise(bits(v), ref.v[j]) <= 1e-5
+        assert n_bit_mismatch(bits(params[i]), th_ref[j]) == 0
+    st = bits(opt.steps())
+    assert np.all(st == 10)
+    opt.close()
+
+
+def _few_large_check(w):
+    rng = np.random.default_rng(1)
+    elems = {i: _spread_indices(w.numels[i], 60000, rng) for i in range(len(w.shapes))}
+    opt, params, ref, th_ref, idx = _sampled_run(w, range(len(w.shapes)), elems=elems)
+    for i in range(len(w.shapes)):
+        m, v = opt.moments(i)
+        gm, gv = bits(m[idx[i]]), bits(v[idx[i]])
+        gth = bits(params[i].reshape(-1)[idx[i]])
+        nb = n_bit_mismatch(gth, th_ref[i]) + n_bit_mismatch(gm, ref.m[i]) + n_bit_mismatch(gv, ref.v[i])
+        say("  tensor %d: theta rel %.3g, m rel %.3g, v rel %.3g, bit mismatches %d / %d" % (
+            i, rel_err_elementwise(gth, th_ref[i]), rel_err_elementwise(gm, ref.m[i]),
+            rel_err_elementwise(gv, ref.v[i]), nb, 3 * gth.size))
+        if w.state_fmt == W.STATE_F32:
+            assert rel_err_elementwise(gm, ref.m[i]) <= 1e-5
+            assert rel_err_elementwise(gv, ref.v[i]) <= 1e-5
+            assert rel_err_elementwise(gth, th_ref[i]) <= 1e-5
+        assert nb == 0
+    assert np.all(bits(opt.steps()) == w.steps)
+    return opt, params, idx
+
+
+def test_few_large_full_size_sampled():
+    """8 bf16 [8192,8192] params, fp32 grads and state, 10 calls (the
+    benchmark's launch configuration); 60k+ elements per tensor, including the
+    first and last tiles, against the oracle."""
+    _need_gpu()
+    w = W.few_large()
+    say("case: few_large", w.describe())
+    opt, _, _ = _few_large_check(w)
+    opt.close()
+
+
+def test_bf16_state_full_size_sampled_and_against_fp32_state():
+    """The same list with bf16 moments: bitwise against the oracle's bf16
+    mode, and within 1e-2 (normwise) of the fp32-state oracle on m and v."""
+    _need_gpu()
+    w = W.bf16_state()
+    say("case: bf16_state", w.describe())
+    rng = np.random.default_rng(2)
+    pick = [0, 7]
+    elems = {i: _spread_indices(w.numels[i], 30000, rng) for i in pick}
+    opt, params, ref, th_ref, idx = _sampled_run(w, pick, elems=elems)
+    # fp32-state oracle on the same inputs
+    ref32 = oracle.OracleAdamW([len(elems[i]) for i in pick], [W.BF16] * 2, [W.F32] * 2, [0, 0], "f32")
+    p0 = W.init_params(w, DEV)
+    th32 = [bits(p0[i].reshape(-1)[idx[i]]) for i in pick]
+    del p0
+    for k in range(1, w.steps + 1):
+        g = W.grads_for_call(w, k, DEV)
+        ref32.step(th32, [bits(g[i].reshape(-1)[idx[i]]) for i in pick], w.groups)
+        del g
+    for j, i in enumerate(pick):
+        m, v = opt.moments(i)
+        gm, gv = bits(m[idx[i]]), bits(v[idx[i]])
+        assert n_bit_mismatch(gm, ref.m[j]) == 0 and n_bit_mismatch(gv, ref.v[j]) == 0
+        assert n_bit_mismatch(bits(params[i].reshape(-1)[idx[i]]), th_ref[j]) == 0
+        em, ev = normwise_err(gm, ref32.m[j]), normwise_err(gv, ref32.v[j])
+        eth = normwise_err(bits(params[i].reshape(-1)[idx[i]]), th32[j])
+        say("  tensor %d vs fp32-state oracle: m %.3g v %.3g theta %.3g (normwise)" % (i, em, ev, eth))
+        assert em <= 1e-2 and ev <= 1e-2
+    opt.close()
+
+
+def _q8_check(opt, params, ref, th_ref, pick, label):
+    worst_code, worst_scale = 0, 0.0
+    for j, i in enumerate(pick):
+        m, v = opt.moments(i)
+        ms, vs = opt.scales(i)
+        dm = np.abs(bits(m).astype(np.int32) - ref.m[j].astype(np.int32))
+        dv = np.abs(bits(v).astype(np.int32) - ref.v[j].astype(np.int32))
+        worst_code = max(worst_code, int(dm.max(initial=0)), int(dv.max(initial=0)))
+        for a, b in ((bits(ms), ref.m_scale[j]), (bits(vs), ref.v_scale[j])):
+            worst_scale = max(worst_scale, rel_err_elementwise(a, b))
+        assert n_bit_mismatch(bits(params[i]), th_ref[j]) == 0, i
+        assert n_bit_mismatch(bits(m), ref.m[j]) == 0 and n_bit_mismatch(bits(v), ref.v[j]) == 0, i
+    say("  %s: worst code diff %d, worst scale rel %.3g" % (label, worst_code, worst_scale))
+    assert worst_code <= 1 and worst_scale <= 1e-6
+
+
+def test_lora_q8_reduced_full_oracle():
+    """Two LoRA layers (28 tensors), 40 calls, every code and scale."""
+    _need_gpu()
+    w = W.lora_q8(layers=2)
+    say("case: lora_q8 reduced", w.describe())
+    pick = list(range(len(w.shapes)))
+    opt, params, ref, th_ref, _ = _sampled_run(w, pick, calls=40)
+    _q8_check(opt, params, ref, th_ref, pick, "2 layers, 40 calls")
+    assert np.all(bits(opt.steps()) == 40)
+    opt.close()
+
+
+def test_lora_q8_full_size_sampled():
+    """392 LoRA tensors (24.3M params), 250 calls; 30 whole tensors (each
+    shape class) against the oracle."""
+    _need_gpu()
+    w = W.lora_q8()
+    say("case: lora_q8 full", w.describe())
+    pick = list(range(0, 14)) + list(range(14 * 27, 14 * 28)) + [150, 151]
+    opt, params, ref, th_ref, _ = _sampled_run(w, pick, every=50)
+    _q8_check(opt, params, ref, th_ref, pick, "28 layers, 250 calls")
+    assert np.all(bits(opt.steps()) == 250)
+    opt.close()

@@ -1,0 +1,136 @@
+"""C ABI host logic, no GPU: the library loads and exports every entry point
+include/apexw.h declares, the state-size function reproduces the pages'
+optimizer-state figures, the layout is consistent, and bad arguments are
+rejected before any device work."""
+import json
+import os
+import re
+
+import pytest
+
+from tensor_adamw_optimizer_amd import _lib as L
+from workloads import lora_shapes, log_uniform_sizes
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "apexw.h")
+GOLDEN = json.load(open(os.path.join(ROOT, "tests", "golden", "state_memory.json")))
+MIB = 2 ** 20
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(apexw_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) >= 9
+    lib = L.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(L.ENTRY_POINTS)
+
+
+def _lora_numels():
+    return [a * b for a, b in lora_shapes()]
+
+
+def test_state_bytes_reproduce_unsloth_table():
+    numel = _lora_numels()
+    assert len(numel) == 392 and sum(numel) == 24_313_856
+    g = GOLDEN["unsloth_lora"]
+    assert abs(sum(numel) - g["trainable_params_approx"]) < 0.05e6
+    got = {fmt: L.apexw_state_bytes(numel, code) / MIB for fmt, code in
+           (("f32", L.APEXW_STATE_F32), ("bf16", L.APEXW_STATE_BF16), ("q8", L.APEXW_STATE_Q8))}
+    assert round(got["f32"], 3) == g["AdamW"]
+    assert round(got["bf16"], 3) == g["ApexW Compact"]
+    assert round(got["q8"], 3) == g["ApexW 8bit"]
+    # exact byte counts: payload + two fp32 scales per 256 block + 4 B step
+    assert L.apexw_state_bytes(numel, L.APEXW_STATE_F32) == 8 * 24_313_856 + 4 * 392
+    assert L.apexw_state_bytes(numel, L.APEXW_STATE_Q8) == \
+        2 * 24_313_856 + 8 * (24_313_856 // 256) + 4 * 392
+
+
+def test_state_bytes_hundred_million_and_seven_billion():
+    g = GOLDEN["hundred_million"]
+    n = [g["params"]]
+    assert L.apexw_state_bytes(n, L.APEXW_STATE_F32) == g["fp32_MB"] * 10 ** 6 + 4
+    assert L.apexw_state_bytes(n, L.APEXW_STATE_BF16) == g["16bit_MB"] * 10 ** 6 + 4
+    q8 = L.apexw_state_bytes(n, L.APEXW_STATE_Q8)
+    assert q8 == g["8bit_MB"] * 10 ** 6 + 2 * 4 * (-(-10 ** 8 // 256)) + 4
+    s = GOLDEN["seven_billion"]
+    # 7B in tensors of 2^27 elements (tensor sizes do not change the payload)
+    sizes = [2 ** 27] * (s["params"] // 2 ** 27) + [s["params"] % 2 ** 27]
+    b = L.apexw_state_bytes(sizes, L.APEXW_STATE_F32)
+    assert b == s["fp32_GB"] * 10 ** 9 + 4 * len(sizes)
+
+
+@pytest.mark.parametrize("fmt", [L.APEXW_STATE_F32, L.APEXW_STATE_BF16, L.APEXW_STATE_Q8])
+def test_layout_is_disjoint_aligned_and_complete(fmt):
+    numel = [3, 0, 1024, 4097, 255, 256, 65536, 1] + log_uniform_sizes(50, 64, 65536, 1)
+    per, steps = L.apexw_state_layout(numel, fmt)
+    total = L.apexw_state_bytes(numel, fmt)
+    eb = {L.APEXW_STATE_F32: 4, L.APEXW_STATE_BF16: 2, L.APEXW_STATE_Q8: 1}[fmt]
+    spans = []
+    for (m, v, ms, vs), n in zip(per, numel):
+        assert m % 16 == 0 and v % 16 == 0
+        spans += [(m, m + n * eb), (v, v + n * eb)]
+        nb = (n + 255) // 256
+        if fmt == L.APEXW_STATE_Q8:
+            assert ms % 4 == 0 and vs % 4 == 0
+            spans += [(ms, ms + 4 * nb), (vs, vs + 4 * nb)]
+        else:
+            assert ms == -1 and vs == -1
+    spans.append((steps, steps + 4 * len(numel)))
+    spans = sorted(s for s in spans if s[1] > s[0])
+    for (a0, a1), (b0, b1) in zip(spans, spans[1:]):
+        assert a1 <= b0
+    assert spans[-1][1] == total == steps + 4 * len(numel)
+    assert steps % 4 == 0
+
+
+def test_workspace_grows_with_tiles():
+    a = L.apexw_workspace_bytes([4096])
+    b = L.apexw_workspace_bytes([4096 * 1000])
+    assert b - a >= 999 * 8 - 256   # 8-byte tile records, 256-byte rounding
+    assert L.apexw_workspace_bytes([]) > 0
+
+
+def test_argument_errors_are_reported():
+    with pytest.raises(L.ApexwError) as e:
+        L.apexw_state_bytes([10], 7)
+    assert e.value.code == L.APEXW_EDTYPE and "format" in L.apexw_last_error()
+    with pytest.raises(L.ApexwError) as e:
+        L.apexw_state_bytes([10, -1], L.APEXW_STATE_F32)
+    assert e.value.code == L.APEXW_EINVAL
+    with pytest.raises(L.ApexwError) as e:
+        L.apexw_workspace_bytes([-5])
+    assert e.value.code == L.APEXW_EINVAL
+    ok = dict(numel=[100], param_dtype=[L.APEXW_F32], grad_dtype=[L.APEXW_F32],
+              group_of=[0], n_groups=1, fmt=L.APEXW_STATE_F32, state_ptr=256,
+              state_bytes=1 << 20, workspace_ptr=1 << 20, workspace_bytes=1 << 20)
+    bad = [
+        (dict(param_dtype=[5]), L.APEXW_EDTYPE),
+        (dict(grad_dtype=[2]), L.APEXW_EDTYPE),
+        (dict(fmt=9), L.APEXW_EDTYPE),
+        (dict(group_of=[1]), L.APEXW_EINVAL),
+        (dict(n_groups=0), L.APEXW_EINVAL),
+        (dict(n_groups=L.APEXW_MAX_GROUPS + 1), L.APEXW_EINVAL),
+        (dict(state_bytes=100), L.APEXW_ENOSPC),
+        (dict(workspace_bytes=16), L.APEXW_ENOSPC),
+        (dict(state_ptr=0), L.APEXW_EINVAL),
+        (dict(state_ptr=260), L.APEXW_EINVAL),
+    ]
+    for change, code in bad:
+        args = dict(ok, **change)
+        with pytest.raises(L.ApexwError) as e:
+            L.apexw_create(**args)
+        assert e.value.code == code, (change, L.apexw_last_error())
+
+
+def test_null_handle_rejected():
+    with pytest.raises(L.ApexwError):
+        L.apexw_destroy(0)
+    with pytest.raises(L.ApexwError):
+        L.apexw_launch_info(0)
