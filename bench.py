@@ -142,7 +142,10 @@ def main() -> int:
     fmt = {W.STATE_F32: L.APEXW_STATE_F32, W.STATE_BF16: L.APEXW_STATE_BF16,
            W.STATE_Q8: L.APEXW_STATE_Q8}[w.state_fmt]
     params = W.init_params(w, dev)
-    grads = W.grads_for_call(w, 1, dev)
+    # every tensor gets a grad in the timed steps (a full update)
+    grads = [g if g is not None else torch.randn(s, device=dev).mul_(w.grad_std)
+             .to(W.TORCH_DTYPE[d])
+             for g, s, d in zip(W.grads_for_call(w, 1, dev), w.shapes, w.grad_dtype)]
     state_bytes = L.apexw_state_bytes(w.numels, fmt)
     ws_bytes = L.apexw_workspace_bytes(w.numels)
     state = torch.empty(state_bytes, dtype=torch.uint8, device=dev)

@@ -1,8 +1,9 @@
 /*
  * apexw.h -- C ABI of a fused multi-tensor AdamW step for AMD MI355X (gfx950).
  *
- * One call of apexw_step updates every parameter of an optimizer, in one GPU
- * launch per (parameter dtype, grad dtype) pair present, with the AdamW rule
+ * One call of apexw_step updates every parameter of an optimizer -- a small
+ * per-tensor prepare launch, then one streaming launch per (parameter dtype,
+ * grad dtype) pair present -- with the AdamW rule
  * of "Fused optimizers and state precision" (ai-infra-kb M041), section 02:
  *
  *     t += 1
@@ -122,7 +123,7 @@ int apexw_state_layout(int32_t n_tensors, const int64_t *numel, int32_t fmt,
 
 /*
  * Bytes of device workspace apexw_create needs for this tensor list (tensor
- * and tile tables, grad-pointer table, launch counters).  Same argument rules
+ * table, grad-pointer table, per-tensor bias corrections, tile table).  Same argument rules
  * as apexw_state_bytes, minus fmt.
  */
 int apexw_workspace_bytes(int32_t n_tensors, const int64_t *numel,
@@ -177,17 +178,17 @@ int apexw_step(apexw_t h, const apexw_group *groups, int32_t n_groups,
                const float *found_inf_dev, void *stream);
 
 /*
- * Launch geometry of the handle: tile size in elements, number of tiles, and
- * the workgroup count used per launch (persistent grid).  Any pointer may be
- * NULL.
+ * Launch geometry of the handle: tile size in elements (256; one workgroup of
+ * one wave64 per tile), number of tiles, and the largest workgroup count of
+ * its update launches.  Any pointer may be NULL.
  */
 int apexw_launch_info(apexw_t h, int32_t *tile_elems, int32_t *n_tiles,
                       int32_t *workgroups);
 
 /*
- * Override the persistent grid size (workgroups per launch); 0 restores the
- * default (enough workgroups to fill every compute unit at the kernel's
- * occupancy).  Results do not depend on it.
+ * Cap the workgroups of each update launch (0 restores the default: one per
+ * tile, at most 2^24); under the cap a workgroup walks several tiles.
+ * Results do not depend on it.
  */
 int apexw_set_workgroups(apexw_t h, int32_t workgroups);
 

@@ -1,14 +1,15 @@
 // apexw.hip -- host engine and C ABI of the fused multi-tensor AdamW step.
 //
 // The engine turns a parameter list into device tables once (tensor
-// descriptors, a 4096-element tile table, per-launch tensor lists, launch
-// tickets), lays the optimizer state out in one caller-owned buffer, and on
-// every step queues one persistent kernel per (parameter dtype, grad dtype)
-// pair present.  Per call it only compares the param / grad pointer arrays
-// with the previous call's (one asynchronous upload when they differ) and
-// forms the per-group fp32 scalars, which travel in the kernel arguments.
-// It never synchronises with the host inside a step and allocates no device
-// memory.
+// descriptors, a table giving the tensor of every 256-element tile, a
+// per-tensor bias-correction slot), lays the optimizer state out in one
+// caller-owned buffer, and on every step queues a small prepare kernel
+// (step counters and bias corrections) followed by one update kernel per
+// (parameter dtype, grad dtype) pair present, each with one workgroup per
+// tile.  Per call it only compares the param / grad pointer arrays with the
+// previous call's (one asynchronous upload when they differ) and forms the
+// per-group fp32 scalars, which travel in the kernel arguments.  It never
+// synchronises with the host inside a step and allocates no device memory.
 //
 // Sources: "Fused optimizers and state precision" (ai-infra-kb M041),
 // sections 02-06; "Apex fused optimizers" guide (qwbw.cn), sections 二/三
@@ -113,14 +114,15 @@ int compute_layout(int32_t n, const int64_t *numel, int32_t fmt,
     return APEXW_OK;
 }
 
-// Workspace layout: descriptors | grad pointers | tiles | launch tensor lists
-// | tickets, each on a 256-byte boundary.
+// Workspace layout: descriptors | grad pointers | bias corrections | tile
+// table, each on a 256-byte boundary.
 struct WsLayout {
-    int64_t desc, grads, tiles, tensors, tickets, total;
+    int64_t desc, grads, bias, tiles, total;
     int64_t n_tiles;
 };
 
-constexpr int kMaxLaunches = 4;   // (param, grad) dtype pairs
+constexpr int kMaxLaunches = 4;      // (param, grad) dtype pairs
+constexpr int64_t kMaxGrid = 1 << 24;  // workgroups per launch (grid-stride above)
 
 WsLayout ws_layout(int32_t n, const int64_t *numel) {
     WsLayout w;
@@ -128,10 +130,9 @@ WsLayout ws_layout(int32_t n, const int64_t *numel) {
     for (int32_t i = 0; i < n; ++i) w.n_tiles += ceil_div(numel[i], kTile);
     w.desc = 0;
     w.grads = w.desc + round_up((int64_t)n * (int64_t)sizeof(TensorDesc), kTableAlign);
-    w.tiles = w.grads + round_up((int64_t)n * 8, kTableAlign);
-    w.tensors = w.tiles + round_up(w.n_tiles * (int64_t)sizeof(TileRef), kTableAlign);
-    w.tickets = w.tensors + round_up((int64_t)n * 4, kTableAlign);
-    w.total = w.tickets + kTableAlign;
+    w.bias = w.grads + round_up((int64_t)n * 8, kTableAlign);
+    w.tiles = w.bias + round_up((int64_t)n * 8, kTableAlign);
+    w.total = w.tiles + round_up(w.n_tiles * 4, kTableAlign);
     return w;
 }
 
@@ -139,9 +140,8 @@ bool finite_nonneg(double x) { return std::isfinite(x) && x >= 0.0; }
 
 struct Launch {
     int pt, gt;
-    int32_t tile_begin, tile_count;
+    int64_t tile_begin, tile_count;
     int32_t tensor_begin, tensor_count;
-    int max_workgroups;            // occupancy x compute units
 };
 
 typedef void (*kernel_fn)(KernelArgs);
@@ -174,7 +174,8 @@ struct apexw_opt {
     char *ws = nullptr;
     WsLayout wl{};
     std::vector<Launch> launches;
-    std::vector<int32_t> tensor_list;   // host copy of the launch tensor lists
+    std::vector<int32_t> tensor_list;   // tensors of each launch, launch by launch
+    std::vector<int64_t> first_tile;    // per tensor
     // host mirrors of the per-call tables
     std::vector<TensorDesc> desc;
     std::vector<void *> last_params;
@@ -272,14 +273,14 @@ int apexw_create(int32_t n_tensors, const int64_t *numel, const int32_t *param_d
             return fail(APEXW_EDTYPE, "grad_dtype[%d] = %d is not fp32 or bf16", i, grad_dtype[i]);
         if (group_of[i] < 0 || group_of[i] >= n_groups)
             return fail(APEXW_EINVAL, "group_of[%d] = %d outside 0..%d", i, group_of[i], n_groups - 1);
-        if (numel[i] > ((int64_t)1 << 31) * kTile)
+        if (numel[i] > ((int64_t)1 << 40))
             return fail(APEXW_EINVAL, "numel[%d] too large", i);
     }
     int64_t need_state = 0;
     compute_layout(n_tensors, numel, fmt, nullptr, nullptr, &need_state);
     const WsLayout wl = ws_layout(n_tensors, numel);
     if (wl.n_tiles > INT32_MAX) return fail(APEXW_EINVAL, "too many tiles");
-    if (!state_dev || !workspace_dev)
+    if ((!state_dev && need_state > 0) || (!workspace_dev && wl.total > 0))
         return fail(APEXW_EINVAL, "state_dev and workspace_dev must not be NULL");
     if (((uintptr_t)state_dev | (uintptr_t)workspace_dev) & (kTableAlign - 1))
         return fail(APEXW_EINVAL, "state_dev and workspace_dev must be 256-byte aligned");
@@ -325,39 +326,35 @@ int apexw_create(int32_t n_tensors, const int64_t *numel, const int32_t *param_d
     TRY(hipGetDevice(&h->device));
     TRY(hipDeviceGetAttribute(&h->cu_count, hipDeviceAttributeMultiprocessorCount, h->device));
 
-    // static tables: tiles and launch tensor lists grouped by dtype pair
-    std::vector<TileRef> tiles;
-    std::vector<int32_t> tensors;
+    // static tables: the tensor of every tile, tiles grouped by dtype pair
+    std::vector<int32_t> tiles;
     try {
         tiles.reserve((size_t)wl.n_tiles);
-        tensors.reserve(n_tensors);
+        h->tensor_list.reserve(n_tensors);
+        h->first_tile.assign(n_tensors, 0);
         const int pairs[kMaxLaunches][2] = {{APEXW_F32, APEXW_F32}, {APEXW_F32, APEXW_BF16},
                                            {APEXW_BF16, APEXW_F32}, {APEXW_BF16, APEXW_BF16}};
         for (int p = 0; p < kMaxLaunches; ++p) {
-            Launch L{pairs[p][0], pairs[p][1], (int32_t)tiles.size(), 0,
-                     (int32_t)tensors.size(), 0, 0};
+            Launch L{pairs[p][0], pairs[p][1], (int64_t)tiles.size(), 0,
+                     (int32_t)h->tensor_list.size(), 0};
             for (int32_t i = 0; i < n_tensors; ++i) {
                 if (param_dtype[i] != L.pt || grad_dtype[i] != L.gt) continue;
-                tensors.push_back(i);
-                const int64_t nt = ceil_div(numel[i], kTile);
-                for (int64_t k = 0; k < nt; ++k) tiles.push_back(TileRef{i, (int32_t)k});
+                h->tensor_list.push_back(i);
+                h->first_tile[i] = (int64_t)tiles.size();
+                tiles.insert(tiles.end(), (size_t)ceil_div(numel[i], kTile), i);
             }
-            L.tile_count = (int32_t)tiles.size() - L.tile_begin;
-            L.tensor_count = (int32_t)tensors.size() - L.tensor_begin;
-            if (L.tensor_count == 0) continue;
-            int occ = 0;
-            TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &occ, reinterpret_cast<const void *>(kernel_for(fmt, L.pt, L.gt)), kThreads, 0));
-            L.max_workgroups = std::max(1, occ) * h->cu_count;
-            h->launches.push_back(L);
+            L.tile_count = (int64_t)tiles.size() - L.tile_begin;
+            L.tensor_count = (int32_t)h->tensor_list.size() - L.tensor_begin;
+            if (L.tensor_count > 0) h->launches.push_back(L);
         }
     } catch (const std::bad_alloc &) {
         return bail(fail(APEXW_ENOMEM, "host allocation failed"));
     }
 
-    // pinned staging: the ring for per-call uploads, also used once here
-    const int64_t per_call = wl.tiles;        // descriptors + grad pointers
-    const int64_t static_bytes = wl.total - wl.tiles;
+    // pinned staging: the ring for per-call uploads (descriptors + grad
+    // pointers), also used once here for the bias slots and the tile table
+    const int64_t per_call = wl.bias;
+    const int64_t static_bytes = wl.total - wl.bias;
     h->slot_bytes = std::max<int64_t>(per_call, kTableAlign);
     const int64_t pinned_bytes =
         std::max<int64_t>(h->slot_bytes * apexw_opt::kRing, static_bytes);
@@ -368,26 +365,17 @@ int apexw_create(int32_t n_tensors, const int64_t *numel, const int32_t *param_d
     char *stage = h->pinned;
     std::memset(stage, 0, (size_t)static_bytes);
     if (!tiles.empty())
-        std::memcpy(stage, tiles.data(), tiles.size() * sizeof(TileRef));
-    if (!tensors.empty())
-        std::memcpy(stage + (wl.tensors - wl.tiles), tensors.data(), tensors.size() * 4);
-    // tickets are zero in the staged copy
-    TRY(hipMemcpyAsync(h->ws + wl.tiles, stage, (size_t)static_bytes, hipMemcpyHostToDevice, st));
+        std::memcpy(stage + (wl.tiles - wl.bias), tiles.data(), tiles.size() * 4);
+    TRY(hipMemcpyAsync(h->ws + wl.bias, stage, (size_t)static_bytes, hipMemcpyHostToDevice, st));
     const int64_t words = need_state / 4;
     if (words > 0) {
-        const int64_t blocks = std::min<int64_t>(ceil_div(words, kThreads), 8 * (int64_t)h->cu_count);
-        hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, st,
+        const int64_t blocks = std::min<int64_t>(ceil_div(words, 256), 8 * (int64_t)h->cu_count);
+        hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
                            reinterpret_cast<uint32_t *>(h->state), words);
         TRY(hipGetLastError());
     }
     TRY(hipStreamSynchronize(st));
 #undef TRY
-    try {
-        h->tensor_list = tensors;
-    } catch (const std::bad_alloc &) {
-        release(h);
-        return fail(APEXW_ENOMEM, "host allocation failed");
-    }
     *out = h;
     return APEXW_OK;
 }
@@ -452,6 +440,7 @@ int apexw_step(apexw_t h, const apexw_group *groups, int32_t n_groups, void *con
                                 ? reinterpret_cast<float *>(h->state + h->layout[i].v_scale)
                                 : nullptr;
                 d.numel = h->numel[i];
+                d.first_tile = h->first_tile[i];
                 d.group = h->group_of[i];
             }
             std::memcpy(slot + h->wl.desc, h->desc.data(), n * sizeof(TensorDesc));
@@ -468,26 +457,30 @@ int apexw_step(apexw_t h, const apexw_group *groups, int32_t n_groups, void *con
         h->have_params = h->have_grads = true;
     }
 
+    bool any_grad = false;
+    for (int32_t i = 0; i < h->n && !any_grad; ++i) any_grad = grads[i] != nullptr;
+    if (!any_grad) return APEXW_OK;           // nothing to update, nothing advances
+
     a.desc = reinterpret_cast<const TensorDesc *>(h->ws + h->wl.desc);
     a.grads = reinterpret_cast<const void *const *>(h->ws + h->wl.grads);
+    a.tile_tensor = reinterpret_cast<const int32_t *>(h->ws + h->wl.tiles);
+    a.bias = reinterpret_cast<const float2 *>(h->ws + h->wl.bias);
     a.steps = reinterpret_cast<int32_t *>(h->state + h->steps_off);
     a.found_inf = found_inf_dev;
-    const TileRef *tiles = reinterpret_cast<const TileRef *>(h->ws + h->wl.tiles);
-    const int32_t *tensors = reinterpret_cast<const int32_t *>(h->ws + h->wl.tensors);
-    uint32_t *tickets = reinterpret_cast<uint32_t *>(h->ws + h->wl.tickets);
-    for (size_t li = 0; li < h->launches.size(); ++li) {
-        const Launch &L = h->launches[li];
-        bool any = false;   // skip a launch none of whose tensors has a grad
+    a.n_tensors = h->n;
+    hipLaunchKernelGGL(adamw_prepare_kernel, dim3((unsigned)ceil_div(h->n, kPrepThreads)),
+                       dim3(kPrepThreads), 0, st, a);
+    HIP_TRY(hipGetLastError());
+    const int64_t cap = h->wg_override > 0 ? h->wg_override : kMaxGrid;
+    for (const Launch &L : h->launches) {
+        if (L.tile_count == 0) continue;      // only empty tensors: t advanced above
+        bool any = false;                     // no grads in this launch: skip it
         for (int32_t j = 0; j < L.tensor_count && !any; ++j)
             any = grads[h->tensor_list[L.tensor_begin + j]] != nullptr;
         if (!any) continue;
-        a.tiles = tiles + L.tile_begin;
-        a.n_tiles = L.tile_count;
-        a.tensors = tensors + L.tensor_begin;
-        a.n_tensors = L.tensor_count;
-        a.ticket = tickets + L.pt * 2 + L.gt;
-        int wg = h->wg_override > 0 ? h->wg_override : L.max_workgroups;
-        wg = std::max(1, std::min(wg, std::max(1, L.tile_count)));
+        a.tile_begin = L.tile_begin;
+        a.tile_count = L.tile_count;
+        const int64_t wg = std::min(L.tile_count, cap);
         hipLaunchKernelGGL(kernel_for(h->fmt, L.pt, L.gt), dim3((unsigned)wg), dim3(kThreads), 0,
                            st, a);
         HIP_TRY(hipGetLastError());
@@ -500,12 +493,10 @@ int apexw_launch_info(apexw_t h, int32_t *tile_elems, int32_t *n_tiles, int32_t 
     if (tile_elems) *tile_elems = kTile;
     if (n_tiles) *n_tiles = (int32_t)h->wl.n_tiles;
     if (workgroups) {
-        int32_t wg = 0;
-        for (const Launch &L : h->launches) {
-            int w = h->wg_override > 0 ? h->wg_override : L.max_workgroups;
-            wg = std::max<int32_t>(wg, std::max(1, std::min(w, std::max(1, L.tile_count))));
-        }
-        *workgroups = wg;
+        const int64_t cap = h->wg_override > 0 ? h->wg_override : kMaxGrid;
+        int64_t wg = 0;
+        for (const Launch &L : h->launches) wg = std::max(wg, std::min(L.tile_count, cap));
+        *workgroups = (int32_t)wg;
     }
     return APEXW_OK;
 }

@@ -1,16 +1,22 @@
 // apexw_kernels.hpp -- gfx950 device code of the fused multi-tensor AdamW step.
 //
-// One persistent, grid-stride kernel per moment format walks a table of
-// 4096-element tiles (a tile never spans two tensors).  A workgroup of 256
-// lanes (four wave64s) owns a tile: lane l of wave w takes, in each of four
-// slots s, the 4 contiguous elements starting at s*1024 + w*256 + l*4, so
-// each load instruction of a wave covers one contiguous 256-element run
-// (fp32: 1 KiB as dwordx4, bf16: 512 B as dwordx2, 8-bit codes: 256 B), and
-// in the 8-bit format that run is exactly one 256-element quantisation block.
-// Every element is read once and written once: theta, g, m, v in; theta, m, v
-// out (M041 section 04 ledger: 28 B per fp32 element).  The path is
-// HBM-bandwidth bound, so there is no matrix-core work; the arithmetic is
-// ordinary fp32 VALU code compiled without contraction.
+// Two kernels per step:
+//  * adamw_prepare_kernel -- one lane per tensor: unless found_inf is set,
+//    advances the step counter of every tensor that has a grad and writes
+//    that tensor's fp32 bias corrections 1-beta1^t, 1-beta2^t (fp64
+//    square-and-multiply) to the workspace;
+//  * adamw_step_kernel -- the streaming update.  The parameter list is cut
+//    into 256-element tiles (a tile never spans two tensors) and each tile is
+//    one workgroup of one wave64: lane l owns the 4 contiguous elements
+//    4l..4l+3, so every load instruction of the wave covers one contiguous
+//    256-element run (fp32: 1 KiB as dwordx4, bf16: 512 B as dwordx2, 8-bit
+//    codes: 256 B as dword), and in the 8-bit format the tile is exactly one
+//    quantisation block.  Every element is read once and written once:
+//    theta, g, m, v in; theta, m, v out (28 B per fp32 element, the one-pass
+//    ledger of the M041 page, section 04).  Small one-tile workgroups keep
+//    many independent read and write streams in flight; the path is
+//    HBM-bandwidth bound, so there is no matrix-core work and the arithmetic
+//    is ordinary fp32 VALU code compiled without contraction.
 //
 // Sources: "Fused optimizers and state precision" (ai-infra-kb M041),
 // sections 02 (update), 03 (groups, missing grads), 04 (scalar bias
@@ -26,13 +32,11 @@
 
 namespace apexw {
 
-constexpr int kThreads = 256;                 // lanes per workgroup
-constexpr int kVec = 4;                       // contiguous elements per lane per slot
-constexpr int kSlots = 4;                     // slots per tile
-constexpr int kSlotElems = kThreads * kVec;   // 1024
-constexpr int kTile = kSlotElems * kSlots;    // 4096 elements per tile
-constexpr int kWaveElems = 64 * kVec;         // 256: one q8 block per wave-slot
-static_assert(kWaveElems == APEXW_Q8_BLOCK, "a wave-slot is one 8-bit block");
+constexpr int kThreads = 64;                  // one wave64 per workgroup
+constexpr int kVec = 4;                       // contiguous elements per lane
+constexpr int kTile = kThreads * kVec;        // 256 elements per tile
+constexpr int kPrepThreads = 256;             // lanes per prepare workgroup
+static_assert(kTile == APEXW_Q8_BLOCK, "a tile is one 8-bit block");
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -52,26 +56,23 @@ struct TensorDesc {
     float *m_scale;
     float *v_scale;
     int64_t numel;
+    int64_t first_tile;  // index of the tensor's first tile in the tile table
     int32_t group;
-    int32_t pad_[3];
+    int32_t pad_;
 };
 static_assert(sizeof(TensorDesc) == 64, "descriptor is one 64-byte record");
-
-struct TileRef {
-    int32_t tensor;      // index into the descriptor table
-    int32_t index;       // tile number within the tensor
-};
 
 struct KernelArgs {
     const TensorDesc *desc;
     const void *const *grads;        // grads[i] == nullptr: no grad this call
-    const TileRef *tiles;            // this launch's tiles
-    const int32_t *tensors;          // this launch's tensors (step epilogue)
+    const int32_t *tile_tensor;      // tensor of each tile (whole table)
+    const float2 *bias;              // per tensor: 1-beta1^t, 1-beta2^t
     int32_t *steps;                  // int32 step counter per tensor
-    uint32_t *ticket;                // workgroups finished (reset by the last)
     const float *found_inf;          // nullptr: never skip
-    int32_t n_tiles;
+    int64_t tile_begin;              // this launch's tiles: [begin, begin+count)
+    int64_t tile_count;
     int32_t n_tensors;
+    int32_t pad_;
     GroupScalars groups[APEXW_MAX_GROUPS];
 };
 
@@ -93,8 +94,7 @@ __device__ __forceinline__ double pow_uint(double b, uint32_t n) {
     return r;
 }
 
-__device__ __forceinline__ StepScalars step_scalars(const GroupScalars &g,
-                                                    int32_t t) {
+__device__ __forceinline__ StepScalars step_scalars(const GroupScalars &g, float2 bias) {
     StepScalars s;
     s.beta1 = g.beta1;
     s.one_minus_beta1 = g.one_minus_beta1;
@@ -103,8 +103,8 @@ __device__ __forceinline__ StepScalars step_scalars(const GroupScalars &g,
     s.lr = g.lr;
     s.decay = g.decay;
     s.eps = g.eps;
-    s.bc1 = (float)(1.0 - pow_uint(g.beta1_d, (uint32_t)t));
-    s.bc2 = (float)(1.0 - pow_uint(g.beta2_d, (uint32_t)t));
+    s.bc1 = bias.x;
+    s.bc2 = bias.y;
     return s;
 }
 
@@ -139,11 +139,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 // ---------------------------------------------------------------- loads
 
-// Element types: 0 = fp32, 1 = bf16 (APEXW_F32 / APEXW_BF16).
-template <int DT> struct Elem;
-template <> struct Elem<APEXW_F32> { typedef float storage; };
-template <> struct Elem<APEXW_BF16> { typedef uint16_t storage; };
-
+// Element types: APEXW_F32 (fp32) or APEXW_BF16 (bf16 bit patterns).
 template <int DT, bool NT>
 __device__ __forceinline__ void load4(const void *base, int64_t e, float (&x)[kVec]) {
     if constexpr (DT == APEXW_F32) {
@@ -169,6 +165,18 @@ __device__ __forceinline__ void store4(void *base, int64_t e, const float (&x)[k
         u32x2 w = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
         if (NT) __builtin_nontemporal_store(w, p); else *p = w;
     }
+}
+
+template <bool NT>
+__device__ __forceinline__ uint32_t load_u32(const void *base, int64_t byte_off) {
+    const uint32_t *p = reinterpret_cast<const uint32_t *>(static_cast<const char *>(base) + byte_off);
+    return NT ? __builtin_nontemporal_load(p) : *p;
+}
+
+template <bool NT>
+__device__ __forceinline__ void store_u32(void *base, int64_t byte_off, uint32_t w) {
+    uint32_t *p = reinterpret_cast<uint32_t *>(static_cast<char *>(base) + byte_off);
+    if (NT) __builtin_nontemporal_store(w, p); else *p = w;
 }
 
 template <int DT>
@@ -201,63 +209,43 @@ __device__ __forceinline__ float wave_max(float x) {
 
 // ---------------------------------------------------------------- tiles
 
-// One tile of a dense-state tensor (fp32 or bf16 moments).
+// One 256-element tile of a tensor with fp32 or bf16 moments (ST = element
+// type of m and v).  n = valid elements in this tile (1..256).
 template <int PT, int GT, int ST, bool NT>
 __device__ __forceinline__ void tile_dense(const TensorDesc &d, const void *grad,
-                                           int64_t base, int n,
-                                           const StepScalars &s) {
-    const int lane = threadIdx.x;
-    const bool vec_ok =
-        (((uintptr_t)d.param | (uintptr_t)grad) & 15u) == 0u;
-    float th[kSlots][kVec], g[kSlots][kVec], m[kSlots][kVec], v[kSlots][kVec];
+                                           int64_t base, int n, const StepScalars &s) {
+    const int off = threadIdx.x * kVec;
+    const int64_t e = base + off;
+    const bool vec_ok = (((uintptr_t)d.param | (uintptr_t)grad) & 15u) == 0u;
+    float th[kVec], g[kVec], m[kVec], v[kVec];
+    if (vec_ok && off + kVec <= n) {
+        load4<ST, NT>(d.m, e, m);
+        load4<ST, NT>(d.v, e, v);
+        load4<GT, NT>(grad, e, g);
+        load4<PT, NT>(d.param, e, th);
 #pragma unroll
-    for (int k = 0; k < kSlots; ++k) {
-        const int off = k * kSlotElems + lane * kVec;
-        const int64_t e = base + off;
-        if (vec_ok && off + kVec <= n) {
-            load4<PT, NT>(d.param, e, th[k]);
-            load4<GT, NT>(grad, e, g[k]);
-            load4<ST, NT>(d.m, e, m[k]);
-            load4<ST, NT>(d.v, e, v[k]);
-        } else {
+        for (int j = 0; j < kVec; ++j) adamw_update(th[j], g[j], m[j], v[j], s);
+        store4<PT, NT>(d.param, e, th);
+        store4<ST, NT>(d.m, e, m);
+        store4<ST, NT>(d.v, e, v);
+    } else {
 #pragma unroll
-            for (int j = 0; j < kVec; ++j) {
-                const bool ok = off + j < n;
-                th[k][j] = ok ? load1<PT>(d.param, e + j) : 0.0f;
-                g[k][j] = ok ? load1<GT>(grad, e + j) : 0.0f;
-                m[k][j] = ok ? load1<ST>(d.m, e + j) : 0.0f;
-                v[k][j] = ok ? load1<ST>(d.v, e + j) : 0.0f;
-            }
-        }
-    }
-#pragma unroll
-    for (int k = 0; k < kSlots; ++k)
-#pragma unroll
-        for (int j = 0; j < kVec; ++j)
-            adamw_update(th[k][j], g[k][j], m[k][j], v[k][j], s);
-#pragma unroll
-    for (int k = 0; k < kSlots; ++k) {
-        const int off = k * kSlotElems + lane * kVec;
-        const int64_t e = base + off;
-        if (vec_ok && off + kVec <= n) {
-            store4<PT, NT>(d.param, e, th[k]);
-            store4<ST, NT>(d.m, e, m[k]);
-            store4<ST, NT>(d.v, e, v[k]);
-        } else {
-#pragma unroll
-            for (int j = 0; j < kVec; ++j) {
-                if (off + j < n) {
-                    store1<PT>(d.param, e + j, th[k][j]);
-                    store1<ST>(d.m, e + j, m[k][j]);
-                    store1<ST>(d.v, e + j, v[k][j]);
-                }
+        for (int j = 0; j < kVec; ++j) {
+            if (off + j < n) {
+                float t = load1<PT>(d.param, e + j);
+                float mm = load1<ST>(d.m, e + j);
+                float vv = load1<ST>(d.v, e + j);
+                adamw_update(t, load1<GT>(grad, e + j), mm, vv, s);
+                store1<PT>(d.param, e + j, t);
+                store1<ST>(d.m, e + j, mm);
+                store1<ST>(d.v, e + j, vv);
             }
         }
     }
 }
 
 // 8-bit codes: m signed (scale absmax|m|/127), v unsigned (scale max v/255),
-// one scale per 256-element block; all-zero block -> scale 0, codes 0.
+// one scale per 256-element block; an all-zero block has scale 0, codes 0.
 __device__ __forceinline__ uint32_t encode_signed(float x, float s) {
     if (s == 0.0f) return 0u;
     float r = rintf(x / s);
@@ -272,131 +260,128 @@ __device__ __forceinline__ uint32_t encode_unsigned(float x, float s) {
     return (uint32_t)(int)r;
 }
 
-// One tile of an 8-bit-state tensor.  Wave w, slot k handles block
-// (base + k*1024 + w*256) / 256 of the tensor.
+// One tile = one 8-bit block (block index base/256 of the tensor): decode
+// with the stored scales, update in fp32, reduce the block maxima over the
+// wave, re-encode.  theta uses this step's fp32 moments.
 template <int PT, int GT, bool NT>
 __device__ __forceinline__ void tile_q8(const TensorDesc &d, const void *grad,
-                                        int64_t base, int n,
-                                        const StepScalars &s) {
-    const int lane = threadIdx.x;
-    const int wave = lane >> 6;
-    const bool vec_ok =
-        (((uintptr_t)d.param | (uintptr_t)grad) & 15u) == 0u;
+                                        int64_t base, int n, const StepScalars &s) {
+    const int off = threadIdx.x * kVec;
+    const int64_t e = base + off;
+    const int64_t blk = base / APEXW_Q8_BLOCK;
+    const bool vec_ok = (((uintptr_t)d.param | (uintptr_t)grad) & 15u) == 0u;
     const int8_t *mq = static_cast<const int8_t *>(d.m);
     const uint8_t *vq = static_cast<const uint8_t *>(d.v);
-    float th[kSlots][kVec], g[kSlots][kVec], m[kSlots][kVec], v[kSlots][kVec];
+    const float sm_old = d.m_scale[blk];
+    const float sv_old = d.v_scale[blk];
+    float th[kVec], g[kVec], m[kVec], v[kVec];
+    const bool full = off + kVec <= n;
+    if (full) {
+        const uint32_t cm = load_u32<NT>(d.m, e);
+        const uint32_t cv = load_u32<NT>(d.v, e);
 #pragma unroll
-    for (int k = 0; k < kSlots; ++k) {
-        const int off = k * kSlotElems + lane * kVec;
-        const int64_t e = base + off;
-        const int64_t blk = (base + k * kSlotElems + wave * kWaveElems) / APEXW_Q8_BLOCK;
-        const bool block_live = k * kSlotElems + wave * kWaveElems < n;
-        const float sm = block_live ? d.m_scale[blk] : 0.0f;
-        const float sv = block_live ? d.v_scale[blk] : 0.0f;
-        if (off + kVec <= n) {
-            const uint32_t cm = *reinterpret_cast<const uint32_t *>(mq + e);
-            const uint32_t cv = *reinterpret_cast<const uint32_t *>(vq + e);
-#pragma unroll
-            for (int j = 0; j < kVec; ++j) {
-                m[k][j] = (float)(int8_t)(cm >> (8 * j)) * sm;
-                v[k][j] = (float)(uint8_t)(cv >> (8 * j)) * sv;
-            }
-            if (vec_ok) {
-                load4<PT, NT>(d.param, e, th[k]);
-                load4<GT, NT>(grad, e, g[k]);
-            } else {
-#pragma unroll
-                for (int j = 0; j < kVec; ++j) {
-                    th[k][j] = load1<PT>(d.param, e + j);
-                    g[k][j] = load1<GT>(grad, e + j);
-                }
-            }
+        for (int j = 0; j < kVec; ++j) {
+            m[j] = (float)(int8_t)(cm >> (8 * j)) * sm_old;
+            v[j] = (float)(uint8_t)(cv >> (8 * j)) * sv_old;
+        }
+        if (vec_ok) {
+            load4<GT, NT>(grad, e, g);
+            load4<PT, NT>(d.param, e, th);
         } else {
 #pragma unroll
             for (int j = 0; j < kVec; ++j) {
-                const bool ok = off + j < n;
-                m[k][j] = ok ? (float)mq[e + j] * sm : 0.0f;
-                v[k][j] = ok ? (float)vq[e + j] * sv : 0.0f;
-                th[k][j] = ok ? load1<PT>(d.param, e + j) : 0.0f;
-                g[k][j] = ok ? load1<GT>(grad, e + j) : 0.0f;
+                g[j] = load1<GT>(grad, e + j);
+                th[j] = load1<PT>(d.param, e + j);
             }
         }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) {
+            const bool ok = off + j < n;
+            m[j] = ok ? (float)mq[e + j] * sm_old : 0.0f;
+            v[j] = ok ? (float)vq[e + j] * sv_old : 0.0f;
+            g[j] = ok ? load1<GT>(grad, e + j) : 0.0f;
+            th[j] = ok ? load1<PT>(d.param, e + j) : 0.0f;
+        }
     }
+    float am = 0.0f, av = 0.0f;
 #pragma unroll
-    for (int k = 0; k < kSlots; ++k)
+    for (int j = 0; j < kVec; ++j) {
+        adamw_update(th[j], g[j], m[j], v[j], s);
+        if (off + j < n) {                    // lanes past the end do not count
+            am = fmaxf(am, fabsf(m[j]));
+            av = fmaxf(av, v[j]);
+        }
+    }
+    am = wave_max(am);
+    av = wave_max(av);
+    const float sm = am / 127.0f;
+    const float sv = av / 255.0f;
+    if (threadIdx.x == 0) {
+        d.m_scale[blk] = sm;
+        d.v_scale[blk] = sv;
+    }
+    if (full) {
+        uint32_t cm = 0, cv = 0;
 #pragma unroll
-        for (int j = 0; j < kVec; ++j)
-            adamw_update(th[k][j], g[k][j], m[k][j], v[k][j], s);
+        for (int j = 0; j < kVec; ++j) {
+            cm |= encode_signed(m[j], sm) << (8 * j);
+            cv |= encode_unsigned(v[j], sv) << (8 * j);
+        }
+        store_u32<NT>(d.m, e, cm);
+        store_u32<NT>(d.v, e, cv);
+        if (vec_ok) {
+            store4<PT, NT>(d.param, e, th);
+        } else {
 #pragma unroll
-    for (int k = 0; k < kSlots; ++k) {
-        const int off = k * kSlotElems + lane * kVec;
-        const int64_t e = base + off;
-        const int64_t blk = (base + k * kSlotElems + wave * kWaveElems) / APEXW_Q8_BLOCK;
-        const bool block_live = k * kSlotElems + wave * kWaveElems < n;
-        // lanes past the end hold m = v = 0 after the update only if their
-        // inputs were 0 and g = 0: mask them out of the block maxima
-        float am = 0.0f, av = 0.0f;
+            for (int j = 0; j < kVec; ++j) store1<PT>(d.param, e + j, th[j]);
+        }
+    } else {
 #pragma unroll
         for (int j = 0; j < kVec; ++j) {
             if (off + j < n) {
-                am = fmaxf(am, fabsf(m[k][j]));
-                av = fmaxf(av, v[k][j]);
-            }
-        }
-        am = wave_max(am);
-        av = wave_max(av);
-        if (!block_live) continue;             // uniform per wave
-        const float sm = am / 127.0f;
-        const float sv = av / 255.0f;
-        if ((lane & 63) == 0) {
-            d.m_scale[blk] = sm;
-            d.v_scale[blk] = sv;
-        }
-        if (off + kVec <= n) {
-            uint32_t cm = 0, cv = 0;
-#pragma unroll
-            for (int j = 0; j < kVec; ++j) {
-                cm |= encode_signed(m[k][j], sm) << (8 * j);
-                cv |= encode_unsigned(v[k][j], sv) << (8 * j);
-            }
-            *reinterpret_cast<uint32_t *>(const_cast<int8_t *>(mq) + e) = cm;
-            *reinterpret_cast<uint32_t *>(const_cast<uint8_t *>(vq) + e) = cv;
-            if (vec_ok) {
-                store4<PT, NT>(d.param, e, th[k]);
-            } else {
-#pragma unroll
-                for (int j = 0; j < kVec; ++j) store1<PT>(d.param, e + j, th[k][j]);
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < kVec; ++j) {
-                if (off + j < n) {
-                    const_cast<int8_t *>(mq)[e + j] = (int8_t)encode_signed(m[k][j], sm);
-                    const_cast<uint8_t *>(vq)[e + j] = (uint8_t)encode_unsigned(v[k][j], sv);
-                    store1<PT>(d.param, e + j, th[k][j]);
-                }
+                const_cast<int8_t *>(mq)[e + j] = (int8_t)encode_signed(m[j], sm);
+                const_cast<uint8_t *>(vq)[e + j] = (uint8_t)encode_unsigned(v[j], sv);
+                store1<PT>(d.param, e + j, th[j]);
             }
         }
     }
 }
 
-// ---------------------------------------------------------------- kernel
+// ---------------------------------------------------------------- kernels
 
+// Before the update: advance t of each tensor with a grad (only when the
+// step is not skipped) and form its bias corrections.
+__global__ __launch_bounds__(kPrepThreads) void adamw_prepare_kernel(KernelArgs a) {
+    const int32_t i = blockIdx.x * kPrepThreads + threadIdx.x;
+    if (i >= a.n_tensors) return;
+    if (a.found_inf != nullptr && *a.found_inf != 0.0f) return;
+    if (a.grads[i] == nullptr) return;
+    const int32_t t = a.steps[i] + 1;
+    a.steps[i] = t;
+    const GroupScalars &g = a.groups[a.desc[i].group];
+    float2 b;
+    b.x = (float)(1.0 - pow_uint(g.beta1_d, (uint32_t)t));
+    b.y = (float)(1.0 - pow_uint(g.beta2_d, (uint32_t)t));
+    const_cast<float2 *>(a.bias)[i] = b;
+}
+
+// The update: one 256-element tile per workgroup (the grid-stride loop only
+// runs more than once when the tile count exceeds the grid).
 // ST: APEXW_STATE_F32 / _BF16 / _Q8.  PT, GT: parameter and grad types.
 template <int ST, int PT, int GT, bool NT>
 __global__ __launch_bounds__(kThreads) void adamw_step_kernel(KernelArgs a) {
     // found_inf (M041 section 06, Apex guide 4.3): the whole step is skipped
     // on the device; every workgroup reads the same flag, so all leave.
     if (a.found_inf != nullptr && *a.found_inf != 0.0f) return;
-
-    for (int32_t tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x) {
-        const TileRef tr = a.tiles[tile];
-        const void *grad = a.grads[tr.tensor];
+    for (int64_t k = blockIdx.x; k < a.tile_count; k += gridDim.x) {
+        const int64_t tile = a.tile_begin + k;
+        const int32_t i = a.tile_tensor[tile];
+        const void *grad = a.grads[i];
         if (grad == nullptr) continue;          // no grad: tensor untouched
-        const TensorDesc d = a.desc[tr.tensor];
-        const int32_t t = a.steps[tr.tensor] + 1;
-        const StepScalars s = step_scalars(a.groups[d.group], t);
-        const int64_t base = (int64_t)tr.index * kTile;
+        const TensorDesc d = a.desc[i];
+        const StepScalars s = step_scalars(a.groups[d.group], a.bias[i]);
+        const int64_t base = (tile - d.first_tile) * kTile;
         const int64_t left = d.numel - base;
         const int n = left < kTile ? (int)left : kTile;
         if constexpr (ST == APEXW_STATE_F32)
@@ -406,32 +391,12 @@ __global__ __launch_bounds__(kThreads) void adamw_step_kernel(KernelArgs a) {
         else
             tile_q8<PT, GT, NT>(d, grad, base, n, s);
     }
-
-    // Step counters advance once every workgroup has read them: the last
-    // workgroup to finish bumps t for this launch's tensors that had a grad
-    // and re-arms the ticket for the next launch.
-    __shared__ bool last;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        __threadfence();
-        const uint32_t done = atomicAdd(a.ticket, 1u);
-        last = (done == gridDim.x - 1);
-    }
-    __syncthreads();
-    if (last) {
-        __threadfence();
-        for (int j = threadIdx.x; j < a.n_tensors; j += kThreads) {
-            const int32_t i = a.tensors[j];
-            if (a.grads[i] != nullptr) a.steps[i] += 1;
-        }
-        if (threadIdx.x == 0) atomicExch(a.ticket, 0u);
-    }
 }
 
 // Zero fill of the state buffer (used once, at creation).
-__global__ __launch_bounds__(kThreads) void fill_zero_kernel(uint32_t *p, int64_t n_words) {
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n_words;
-         i += (int64_t)gridDim.x * kThreads)
+__global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t *p, int64_t n_words) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n_words;
+         i += (int64_t)gridDim.x * 256)
         p[i] = 0u;
 }
 

@@ -113,6 +113,7 @@ def assert_fp32_state_parity(name, gpu, ref, rtol=1e-5):
     """fp32 bar: elementwise relative error <= rtol (expected: bitwise)."""
     e = rel_err_elementwise(gpu, ref)
     nb = n_bit_mismatch(gpu, ref)
-    say("  %-10s max_rel=%.3g bit_mismatch=%d/%d" % (name, e, nb, gpu.size))
+    if e > 0 or nb:
+        say("  %-10s max_rel=%.3g bit_mismatch=%d/%d" % (name, e, nb, gpu.size))
     assert e <= rtol, (name, e, nb)
     return nb

@@ -67,7 +67,8 @@ def test_tiny_every_call_against_oracle():
             total_mismatch += assert_fp32_state_parity("m%d@%d" % (i, k), bits(m), ref.m[i])
             total_mismatch += assert_fp32_state_parity("v%d@%d" % (i, k), bits(v), ref.v[i])
         assert np.array_equal(bits(opt.steps()), ref.t), (bits(opt.steps()), ref.t)
-    assert list(ref.t) == [19, 19, 19, 9]
+    # 20 calls minus the skipped call 7; the [3] tensor has grads on the 10 even calls
+    assert list(ref.t) == [19, 19, 19, 10]
     assert total_mismatch == 0
     opt.close()
 
