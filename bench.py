@@ -112,7 +112,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="few_large",
                     choices=["few_large", "many_small", "bf16_state", "lora_q8", "tiny"])
-    ap.add_argument("--workgroups", type=int, default=0, help="persistent grid override")
+    ap.add_argument("--workgroups", type=int, default=0, help="cap on workgroups per launch")
+    ap.add_argument("--occupancy", type=int, default=0,
+                    help="update workgroups per CU (0: the format's default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, run a 1 GiB device copy 3x (counter calibration)")
@@ -156,6 +158,9 @@ def main() -> int:
                        ws.data_ptr(), ws_bytes, stream.cuda_stream)
     if args.workgroups:
         L.apexw_set_workgroups(h, args.workgroups)
+    if args.occupancy:
+        L.apexw_set_occupancy(h, args.occupancy)
+    occupancy = L.apexw_get_occupancy(h)
     tile, n_tiles, wgs = L.apexw_launch_info(h)
     params_arr = L.make_ptrs([p.data_ptr() for p in params])
     grads_arr = L.make_ptrs([g.data_ptr() for g in grads])
@@ -221,7 +226,8 @@ def main() -> int:
         "hbm_frac_of_peak": (ab / (elapsed / args.steps)) / 1e9 / HBM_PEAK_GBPS,
         "kernel_ms": {"avg": sum(kernel_ms) / len(kernel_ms), "min": min(kernel_ms),
                       "max": max(kernel_ms)},
-        "launch": {"tile_elems": tile, "tiles": n_tiles, "workgroups": wgs},
+        "launch": {"tile_elems": tile, "tiles": n_tiles, "workgroups": wgs,
+                   "workgroups_per_cu_cap": occupancy},
         "state_bytes": state_bytes,
         "roofline": {
             "bound": "hbm",

@@ -123,7 +123,7 @@ int apexw_state_layout(int32_t n_tensors, const int64_t *numel, int32_t fmt,
 
 /*
  * Bytes of device workspace apexw_create needs for this tensor list (tensor
- * table, grad-pointer table, per-tensor bias corrections, tile table).  Same argument rules
+ * table, grad-pointer table, per-tensor step records, tile table).  Same argument rules
  * as apexw_state_bytes, minus fmt.
  */
 int apexw_workspace_bytes(int32_t n_tensors, const int64_t *numel,
@@ -187,10 +187,23 @@ int apexw_launch_info(apexw_t h, int32_t *tile_elems, int32_t *n_tiles,
 
 /*
  * Cap the workgroups of each update launch (0 restores the default: one per
- * tile, at most 2^24); under the cap a workgroup walks several tiles.
+ * tile, at most 2^24); under the cap a workgroup walks several tiles.  A cap
+ * that is a multiple of 8 keeps each XCD on its own tile-table lines.
  * Results do not depend on it.
  */
 int apexw_set_workgroups(apexw_t h, int32_t workgroups);
+
+/*
+ * Cap how many update workgroups may be resident on one compute unit at a
+ * time (enforced through the dynamic LDS each workgroup reserves; the kernel
+ * uses none).  0 restores the format's default (fp32 moments: 28; bf16 and
+ * 8-bit: no cap).  Fewer concurrent streams can keep the HBM read/write mix
+ * more efficient; results do not depend on it.
+ */
+int apexw_set_occupancy(apexw_t h, int32_t workgroups_per_cu);
+
+/* The cap in force (0: none). */
+int apexw_get_occupancy(apexw_t h, int32_t *workgroups_per_cu);
 
 /* Release the handle (host memory only; waits for nothing). */
 int apexw_destroy(apexw_t h);

@@ -1,15 +1,15 @@
 // apexw.hip -- host engine and C ABI of the fused multi-tensor AdamW step.
 //
 // The engine turns a parameter list into device tables once (tensor
-// descriptors, a table giving the tensor of every 256-element tile, a
-// per-tensor bias-correction slot), lays the optimizer state out in one
-// caller-owned buffer, and on every step queues a small prepare kernel
-// (step counters and bias corrections) followed by one update kernel per
-// (parameter dtype, grad dtype) pair present, each with one workgroup per
-// tile.  Per call it only compares the param / grad pointer arrays with the
-// previous call's (one asynchronous upload when they differ) and forms the
-// per-group fp32 scalars, which travel in the kernel arguments.  It never
-// synchronises with the host inside a step and allocates no device memory.
+// descriptors, a table giving the tensor of every 256-element tile), lays the
+// optimizer state out in one caller-owned buffer, and on every step queues a
+// small prepare kernel (step counters, per-tensor step records) followed by
+// one update kernel per (parameter dtype, grad dtype) pair present, each with
+// one workgroup per tile.  Per call it only compares the param / grad pointer
+// arrays with the previous call's (one asynchronous upload when they differ)
+// and forms the per-group fp32 scalars, which travel in the kernel arguments.
+// It never synchronises with the host inside a step and allocates no device
+// memory.
 //
 // Sources: "Fused optimizers and state precision" (ai-infra-kb M041),
 // sections 02-06; "Apex fused optimizers" guide (qwbw.cn), sections 二/三
@@ -114,10 +114,10 @@ int compute_layout(int32_t n, const int64_t *numel, int32_t fmt,
     return APEXW_OK;
 }
 
-// Workspace layout: descriptors | grad pointers | bias corrections | tile
-// table, each on a 256-byte boundary.
+// Workspace layout: descriptors | grad pointers | step records | tile table,
+// each on a 256-byte boundary.
 struct WsLayout {
-    int64_t desc, grads, bias, tiles, total;
+    int64_t desc, grads, records, tiles, total;
     int64_t n_tiles;
 };
 
@@ -130,9 +130,10 @@ WsLayout ws_layout(int32_t n, const int64_t *numel) {
     for (int32_t i = 0; i < n; ++i) w.n_tiles += ceil_div(numel[i], kTile);
     w.desc = 0;
     w.grads = w.desc + round_up((int64_t)n * (int64_t)sizeof(TensorDesc), kTableAlign);
-    w.bias = w.grads + round_up((int64_t)n * 8, kTableAlign);
-    w.tiles = w.bias + round_up((int64_t)n * 8, kTableAlign);
-    w.total = w.tiles + round_up(w.n_tiles * 4, kTableAlign);
+    w.records = w.grads + round_up((int64_t)n * 8, kTableAlign);
+    w.tiles = w.records + round_up((int64_t)n * (int64_t)sizeof(StepRecord), kTableAlign);
+    // each launch's table is padded to a multiple of kXcds entries
+    w.total = n == 0 ? 0 : w.tiles + round_up((w.n_tiles + kMaxLaunches * kXcds) * 4, kTableAlign);
     return w;
 }
 
@@ -140,9 +141,21 @@ bool finite_nonneg(double x) { return std::isfinite(x) && x >= 0.0; }
 
 struct Launch {
     int pt, gt;
-    int64_t tile_begin, tile_count;
+    int64_t tile_begin, tile_count;     // logical tiles [begin, begin+count)
+    int64_t table_begin, table_stride;  // XCD-major table slice
     int32_t tensor_begin, tensor_count;
 };
+
+// Default cap on update workgroups resident per compute unit, per moment
+// format (0: no cap).  Fewer, longer-lived one-wave streams per CU keep the
+// HBM read/write mix efficient for the 28/24-byte fp32-state update; the
+// leaner formats want every stream they can get.
+int default_occupancy(int32_t fmt) {
+    switch (fmt) {
+    case APEXW_STATE_F32: return 28;
+    default: return 0;
+    }
+}
 
 typedef void (*kernel_fn)(KernelArgs);
 
@@ -189,7 +202,9 @@ struct apexw_opt {
     bool ev_pending[kRing] = {};
     int next_slot = 0;
     int cu_count = 0;
+    int lds_per_cu = 0, lds_per_block = 0;
     int32_t wg_override = 0;
+    int32_t occupancy = 0;              // update workgroups per CU (0: no cap)
 };
 
 namespace {
@@ -325,36 +340,52 @@ int apexw_create(int32_t n_tensors, const int64_t *numel, const int32_t *param_d
 
     TRY(hipGetDevice(&h->device));
     TRY(hipDeviceGetAttribute(&h->cu_count, hipDeviceAttributeMultiprocessorCount, h->device));
+    TRY(hipDeviceGetAttribute(&h->lds_per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor,
+                              h->device));
+    TRY(hipDeviceGetAttribute(&h->lds_per_block, hipDeviceAttributeMaxSharedMemoryPerBlock,
+                              h->device));
+    h->occupancy = default_occupancy(fmt);
 
-    // static tables: the tensor of every tile, tiles grouped by dtype pair
+    // static tables: the tensor of every tile, tiles grouped by dtype pair;
+    // logical tile k of a launch is stored at (k % kXcds) * stride + k / kXcds
     std::vector<int32_t> tiles;
     try {
-        tiles.reserve((size_t)wl.n_tiles);
+        tiles.reserve((size_t)(wl.n_tiles + kMaxLaunches * kXcds));
         h->tensor_list.reserve(n_tensors);
         h->first_tile.assign(n_tensors, 0);
         const int pairs[kMaxLaunches][2] = {{APEXW_F32, APEXW_F32}, {APEXW_F32, APEXW_BF16},
                                            {APEXW_BF16, APEXW_F32}, {APEXW_BF16, APEXW_BF16}};
+        int64_t logical = 0;
+        std::vector<int32_t> order;
         for (int p = 0; p < kMaxLaunches; ++p) {
-            Launch L{pairs[p][0], pairs[p][1], (int64_t)tiles.size(), 0,
+            Launch L{pairs[p][0], pairs[p][1], logical, 0, (int64_t)tiles.size(), 0,
                      (int32_t)h->tensor_list.size(), 0};
+            order.clear();
             for (int32_t i = 0; i < n_tensors; ++i) {
                 if (param_dtype[i] != L.pt || grad_dtype[i] != L.gt) continue;
                 h->tensor_list.push_back(i);
-                h->first_tile[i] = (int64_t)tiles.size();
-                tiles.insert(tiles.end(), (size_t)ceil_div(numel[i], kTile), i);
+                h->first_tile[i] = logical + (int64_t)order.size();
+                order.insert(order.end(), (size_t)ceil_div(numel[i], kTile), i);
             }
-            L.tile_count = (int64_t)tiles.size() - L.tile_begin;
+            L.tile_count = (int64_t)order.size();
             L.tensor_count = (int32_t)h->tensor_list.size() - L.tensor_begin;
-            if (L.tensor_count > 0) h->launches.push_back(L);
+            if (L.tensor_count == 0) continue;
+            L.table_stride = ceil_div(L.tile_count, kXcds);
+            tiles.resize(tiles.size() + (size_t)(L.table_stride * kXcds), 0);
+            for (int64_t k = 0; k < L.tile_count; ++k)
+                tiles[(size_t)(L.table_begin + (k % kXcds) * L.table_stride + k / kXcds)] =
+                    order[(size_t)k];
+            logical += L.tile_count;
+            h->launches.push_back(L);
         }
     } catch (const std::bad_alloc &) {
         return bail(fail(APEXW_ENOMEM, "host allocation failed"));
     }
 
     // pinned staging: the ring for per-call uploads (descriptors + grad
-    // pointers), also used once here for the bias slots and the tile table
-    const int64_t per_call = wl.bias;
-    const int64_t static_bytes = wl.total - wl.bias;
+    // pointers), also used once here for the step records and the tile table
+    const int64_t per_call = wl.records;
+    const int64_t static_bytes = wl.total - wl.records;
     h->slot_bytes = std::max<int64_t>(per_call, kTableAlign);
     const int64_t pinned_bytes =
         std::max<int64_t>(h->slot_bytes * apexw_opt::kRing, static_bytes);
@@ -365,8 +396,8 @@ int apexw_create(int32_t n_tensors, const int64_t *numel, const int32_t *param_d
     char *stage = h->pinned;
     std::memset(stage, 0, (size_t)static_bytes);
     if (!tiles.empty())
-        std::memcpy(stage + (wl.tiles - wl.bias), tiles.data(), tiles.size() * 4);
-    TRY(hipMemcpyAsync(h->ws + wl.bias, stage, (size_t)static_bytes, hipMemcpyHostToDevice, st));
+        std::memcpy(stage + (wl.tiles - wl.records), tiles.data(), tiles.size() * 4);
+    TRY(hipMemcpyAsync(h->ws + wl.records, stage, (size_t)static_bytes, hipMemcpyHostToDevice, st));
     const int64_t words = need_state / 4;
     if (words > 0) {
         const int64_t blocks = std::min<int64_t>(ceil_div(words, 256), 8 * (int64_t)h->cu_count);
@@ -464,7 +495,7 @@ int apexw_step(apexw_t h, const apexw_group *groups, int32_t n_groups, void *con
     a.desc = reinterpret_cast<const TensorDesc *>(h->ws + h->wl.desc);
     a.grads = reinterpret_cast<const void *const *>(h->ws + h->wl.grads);
     a.tile_tensor = reinterpret_cast<const int32_t *>(h->ws + h->wl.tiles);
-    a.bias = reinterpret_cast<const float2 *>(h->ws + h->wl.bias);
+    a.records = reinterpret_cast<StepRecord *>(h->ws + h->wl.records);
     a.steps = reinterpret_cast<int32_t *>(h->state + h->steps_off);
     a.found_inf = found_inf_dev;
     a.n_tensors = h->n;
@@ -472,6 +503,9 @@ int apexw_step(apexw_t h, const apexw_group *groups, int32_t n_groups, void *con
                        dim3(kPrepThreads), 0, st, a);
     HIP_TRY(hipGetLastError());
     const int64_t cap = h->wg_override > 0 ? h->wg_override : kMaxGrid;
+    // residency cap: the dynamic LDS a workgroup reserves (it uses none)
+    const unsigned lds =
+        h->occupancy > 0 ? (unsigned)std::min(h->lds_per_cu / h->occupancy, h->lds_per_block) : 0u;
     for (const Launch &L : h->launches) {
         if (L.tile_count == 0) continue;      // only empty tensors: t advanced above
         bool any = false;                     // no grads in this launch: skip it
@@ -480,9 +514,11 @@ int apexw_step(apexw_t h, const apexw_group *groups, int32_t n_groups, void *con
         if (!any) continue;
         a.tile_begin = L.tile_begin;
         a.tile_count = L.tile_count;
+        a.table_begin = L.table_begin;
+        a.table_stride = L.table_stride;
         const int64_t wg = std::min(L.tile_count, cap);
-        hipLaunchKernelGGL(kernel_for(h->fmt, L.pt, L.gt), dim3((unsigned)wg), dim3(kThreads), 0,
-                           st, a);
+        hipLaunchKernelGGL(kernel_for(h->fmt, L.pt, L.gt), dim3((unsigned)wg), dim3(kThreads),
+                           lds, st, a);
         HIP_TRY(hipGetLastError());
     }
     return APEXW_OK;
@@ -505,6 +541,19 @@ int apexw_set_workgroups(apexw_t h, int32_t workgroups) {
     if (!h) return fail(APEXW_EINVAL, "handle is NULL");
     if (workgroups < 0) return fail(APEXW_EINVAL, "workgroups must be >= 0");
     h->wg_override = workgroups;
+    return APEXW_OK;
+}
+
+int apexw_set_occupancy(apexw_t h, int32_t workgroups_per_cu) {
+    if (!h) return fail(APEXW_EINVAL, "handle is NULL");
+    if (workgroups_per_cu < 0) return fail(APEXW_EINVAL, "workgroups_per_cu must be >= 0");
+    h->occupancy = workgroups_per_cu == 0 ? default_occupancy(h->fmt) : workgroups_per_cu;
+    return APEXW_OK;
+}
+
+int apexw_get_occupancy(apexw_t h, int32_t *workgroups_per_cu) {
+    if (!h || !workgroups_per_cu) return fail(APEXW_EINVAL, "NULL argument");
+    *workgroups_per_cu = h->occupancy;
     return APEXW_OK;
 }
 

@@ -3,8 +3,10 @@
 // Two kernels per step:
 //  * adamw_prepare_kernel -- one lane per tensor: unless found_inf is set,
 //    advances the step counter of every tensor that has a grad and writes
-//    that tensor's fp32 bias corrections 1-beta1^t, 1-beta2^t (fp64
-//    square-and-multiply) to the workspace;
+//    that tensor's step record (grad pointer, fp32 group scalars and bias
+//    corrections 1-beta1^t, 1-beta2^t from fp64 square-and-multiply) to the
+//    workspace; a tensor without a grad, or every tensor when found_inf is
+//    set, gets a record without a grad and no counter moves;
 //  * adamw_step_kernel -- the streaming update.  The parameter list is cut
 //    into 256-element tiles (a tile never spans two tensors) and each tile is
 //    one workgroup of one wave64: lane l owns the 4 contiguous elements
@@ -36,10 +38,31 @@ constexpr int kThreads = 64;                  // one wave64 per workgroup
 constexpr int kVec = 4;                       // contiguous elements per lane
 constexpr int kTile = kThreads * kVec;        // 256 elements per tile
 constexpr int kPrepThreads = 256;             // lanes per prepare workgroup
+constexpr int kXcds = 8;                      // gfx950: 8 XCDs, workgroups dealt round-robin
 static_assert(kTile == APEXW_Q8_BLOCK, "a tile is one 8-bit block");
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Address spaces.  Data pointers arrive through tables as generic pointers;
+// casting them to the global space gives global_load/global_store (with the
+// non-temporal bit) instead of flat accesses.  The per-tile metadata (tile
+// table, descriptors, step records) is read-only for the whole
+// update launch, so it is read through the constant space, which lets the
+// compiler use scalar loads (scalar cache) for these wave-uniform values.
+#define APEXW_GLOBAL __attribute__((address_space(1)))
+#define APEXW_CONST __attribute__((address_space(4)))
+
+template <typename T>
+__device__ __forceinline__ APEXW_GLOBAL T *gptr(void *p) { return (APEXW_GLOBAL T *)p; }
+template <typename T>
+__device__ __forceinline__ const APEXW_GLOBAL T *gptr(const void *p) {
+    return (const APEXW_GLOBAL T *)p;
+}
+template <typename T>
+__device__ __forceinline__ const APEXW_CONST T *cptr(const void *p) {
+    return (const APEXW_CONST T *)p;
+}
 
 // Per-group scalars, formed on the host once per call.
 struct GroupScalars {
@@ -62,15 +85,30 @@ struct TensorDesc {
 };
 static_assert(sizeof(TensorDesc) == 64, "descriptor is one 64-byte record");
 
+// Per-tensor record of one step, written by the prepare kernel: the grad to
+// apply (nullptr: leave the tensor alone -- no grad, or the step is skipped)
+// and every scalar the update needs, so the update kernel reads one record
+// per tensor and nothing else besides the descriptor.
+struct StepRecord {
+    const void *grad;
+    float beta1, one_minus_beta1, beta2, one_minus_beta2;
+    float lr, decay, eps;
+    float bc1, bc2;                  // 1 - beta1^t, 1 - beta2^t
+    float pad_[5];
+};
+static_assert(sizeof(StepRecord) == 64, "step record is one 64-byte record");
+
 struct KernelArgs {
     const TensorDesc *desc;
     const void *const *grads;        // grads[i] == nullptr: no grad this call
-    const int32_t *tile_tensor;      // tensor of each tile (whole table)
-    const float2 *bias;              // per tensor: 1-beta1^t, 1-beta2^t
+    const int32_t *tile_tensor;      // tensor of each tile, XCD-major per launch
+    StepRecord *records;             // per tensor, rewritten every step
     int32_t *steps;                  // int32 step counter per tensor
     const float *found_inf;          // nullptr: never skip
     int64_t tile_begin;              // this launch's tiles: [begin, begin+count)
     int64_t tile_count;
+    int64_t table_begin;             // this launch's part of tile_tensor
+    int64_t table_stride;            // ceil(tile_count / kXcds)
     int32_t n_tensors;
     int32_t pad_;
     GroupScalars groups[APEXW_MAX_GROUPS];
@@ -94,17 +132,17 @@ __device__ __forceinline__ double pow_uint(double b, uint32_t n) {
     return r;
 }
 
-__device__ __forceinline__ StepScalars step_scalars(const GroupScalars &g, float2 bias) {
+__device__ __forceinline__ StepScalars step_scalars(const StepRecord &r) {
     StepScalars s;
-    s.beta1 = g.beta1;
-    s.one_minus_beta1 = g.one_minus_beta1;
-    s.beta2 = g.beta2;
-    s.one_minus_beta2 = g.one_minus_beta2;
-    s.lr = g.lr;
-    s.decay = g.decay;
-    s.eps = g.eps;
-    s.bc1 = bias.x;
-    s.bc2 = bias.y;
+    s.beta1 = r.beta1;
+    s.one_minus_beta1 = r.one_minus_beta1;
+    s.beta2 = r.beta2;
+    s.one_minus_beta2 = r.one_minus_beta2;
+    s.lr = r.lr;
+    s.decay = r.decay;
+    s.eps = r.eps;
+    s.bc1 = r.bc1;
+    s.bc2 = r.bc2;
     return s;
 }
 
@@ -143,11 +181,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 template <int DT, bool NT>
 __device__ __forceinline__ void load4(const void *base, int64_t e, float (&x)[kVec]) {
     if constexpr (DT == APEXW_F32) {
-        const f32x4 *p = reinterpret_cast<const f32x4 *>(static_cast<const float *>(base) + e);
+        const APEXW_GLOBAL f32x4 *p = gptr<f32x4>(static_cast<const float *>(base) + e);
         f32x4 w = NT ? __builtin_nontemporal_load(p) : *p;
         x[0] = w.x; x[1] = w.y; x[2] = w.z; x[3] = w.w;
     } else {
-        const u32x2 *p = reinterpret_cast<const u32x2 *>(static_cast<const uint16_t *>(base) + e);
+        const APEXW_GLOBAL u32x2 *p = gptr<u32x2>(static_cast<const uint16_t *>(base) + e);
         u32x2 w = NT ? __builtin_nontemporal_load(p) : *p;
         x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x);
         x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
@@ -157,11 +195,11 @@ __device__ __forceinline__ void load4(const void *base, int64_t e, float (&x)[kV
 template <int DT, bool NT>
 __device__ __forceinline__ void store4(void *base, int64_t e, const float (&x)[kVec]) {
     if constexpr (DT == APEXW_F32) {
-        f32x4 *p = reinterpret_cast<f32x4 *>(static_cast<float *>(base) + e);
+        APEXW_GLOBAL f32x4 *p = gptr<f32x4>(static_cast<float *>(base) + e);
         f32x4 w = {x[0], x[1], x[2], x[3]};
         if (NT) __builtin_nontemporal_store(w, p); else *p = w;
     } else {
-        u32x2 *p = reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(base) + e);
+        APEXW_GLOBAL u32x2 *p = gptr<u32x2>(static_cast<uint16_t *>(base) + e);
         u32x2 w = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
         if (NT) __builtin_nontemporal_store(w, p); else *p = w;
     }
@@ -169,26 +207,26 @@ __device__ __forceinline__ void store4(void *base, int64_t e, const float (&x)[k
 
 template <bool NT>
 __device__ __forceinline__ uint32_t load_u32(const void *base, int64_t byte_off) {
-    const uint32_t *p = reinterpret_cast<const uint32_t *>(static_cast<const char *>(base) + byte_off);
+    const APEXW_GLOBAL uint32_t *p = gptr<uint32_t>(static_cast<const char *>(base) + byte_off);
     return NT ? __builtin_nontemporal_load(p) : *p;
 }
 
 template <bool NT>
 __device__ __forceinline__ void store_u32(void *base, int64_t byte_off, uint32_t w) {
-    uint32_t *p = reinterpret_cast<uint32_t *>(static_cast<char *>(base) + byte_off);
+    APEXW_GLOBAL uint32_t *p = gptr<uint32_t>(static_cast<char *>(base) + byte_off);
     if (NT) __builtin_nontemporal_store(w, p); else *p = w;
 }
 
 template <int DT>
 __device__ __forceinline__ float load1(const void *base, int64_t e) {
-    if constexpr (DT == APEXW_F32) return static_cast<const float *>(base)[e];
-    else return __uint_as_float((uint32_t)static_cast<const uint16_t *>(base)[e] << 16);
+    if constexpr (DT == APEXW_F32) return gptr<float>(base)[e];
+    else return __uint_as_float((uint32_t)gptr<uint16_t>(base)[e] << 16);
 }
 
 template <int DT>
 __device__ __forceinline__ void store1(void *base, int64_t e, float x) {
-    if constexpr (DT == APEXW_F32) static_cast<float *>(base)[e] = x;
-    else static_cast<uint16_t *>(base)[e] = (uint16_t)f32_to_bf16_bits(x);
+    if constexpr (DT == APEXW_F32) gptr<float>(base)[e] = x;
+    else gptr<uint16_t>(base)[e] = (uint16_t)f32_to_bf16_bits(x);
 }
 
 // ---------------------------------------------------------------- wave max
@@ -270,10 +308,10 @@ __device__ __forceinline__ void tile_q8(const TensorDesc &d, const void *grad,
     const int64_t e = base + off;
     const int64_t blk = base / APEXW_Q8_BLOCK;
     const bool vec_ok = (((uintptr_t)d.param | (uintptr_t)grad) & 15u) == 0u;
-    const int8_t *mq = static_cast<const int8_t *>(d.m);
-    const uint8_t *vq = static_cast<const uint8_t *>(d.v);
-    const float sm_old = d.m_scale[blk];
-    const float sv_old = d.v_scale[blk];
+    const APEXW_GLOBAL int8_t *mq = gptr<int8_t>(static_cast<const void *>(d.m));
+    const APEXW_GLOBAL uint8_t *vq = gptr<uint8_t>(static_cast<const void *>(d.v));
+    const float sm_old = gptr<float>(static_cast<const void *>(d.m_scale))[blk];
+    const float sv_old = gptr<float>(static_cast<const void *>(d.v_scale))[blk];
     float th[kVec], g[kVec], m[kVec], v[kVec];
     const bool full = off + kVec <= n;
     if (full) {
@@ -318,8 +356,8 @@ __device__ __forceinline__ void tile_q8(const TensorDesc &d, const void *grad,
     const float sm = am / 127.0f;
     const float sv = av / 255.0f;
     if (threadIdx.x == 0) {
-        d.m_scale[blk] = sm;
-        d.v_scale[blk] = sv;
+        gptr<float>(static_cast<void *>(d.m_scale))[blk] = sm;
+        gptr<float>(static_cast<void *>(d.v_scale))[blk] = sv;
     }
     if (full) {
         uint32_t cm = 0, cv = 0;
@@ -340,8 +378,8 @@ __device__ __forceinline__ void tile_q8(const TensorDesc &d, const void *grad,
 #pragma unroll
         for (int j = 0; j < kVec; ++j) {
             if (off + j < n) {
-                const_cast<int8_t *>(mq)[e + j] = (int8_t)encode_signed(m[j], sm);
-                const_cast<uint8_t *>(vq)[e + j] = (uint8_t)encode_unsigned(v[j], sv);
+                gptr<int8_t>(d.m)[e + j] = (int8_t)encode_signed(m[j], sm);
+                gptr<uint8_t>(d.v)[e + j] = (uint8_t)encode_unsigned(v[j], sv);
                 store1<PT>(d.param, e + j, th[j]);
             }
         }
@@ -350,20 +388,56 @@ __device__ __forceinline__ void tile_q8(const TensorDesc &d, const void *grad,
 
 // ---------------------------------------------------------------- kernels
 
-// Before the update: advance t of each tensor with a grad (only when the
-// step is not skipped) and form its bias corrections.
+// Before the update, one lane per tensor: unless found_inf is set (M041
+// section 06, Apex guide 4.3), advance t of each tensor with a grad and write
+// its step record (grad pointer, group scalars, bias corrections from fp64
+// square-and-multiply); a tensor without a grad, or every tensor when
+// found_inf is set, gets a record with no grad and no counter moves.  The
+// flag is thus read once per tensor here instead of once per workgroup.
 __global__ __launch_bounds__(kPrepThreads) void adamw_prepare_kernel(KernelArgs a) {
     const int32_t i = blockIdx.x * kPrepThreads + threadIdx.x;
     if (i >= a.n_tensors) return;
-    if (a.found_inf != nullptr && *a.found_inf != 0.0f) return;
-    if (a.grads[i] == nullptr) return;
-    const int32_t t = a.steps[i] + 1;
-    a.steps[i] = t;
-    const GroupScalars &g = a.groups[a.desc[i].group];
-    float2 b;
-    b.x = (float)(1.0 - pow_uint(g.beta1_d, (uint32_t)t));
-    b.y = (float)(1.0 - pow_uint(g.beta2_d, (uint32_t)t));
-    const_cast<float2 *>(a.bias)[i] = b;
+    StepRecord r = {};
+    const bool skip = a.found_inf != nullptr && *a.found_inf != 0.0f;
+    const void *grad = skip ? nullptr : a.grads[i];
+    if (grad != nullptr) {
+        const int32_t t = a.steps[i] + 1;
+        a.steps[i] = t;
+        const GroupScalars &g = a.groups[a.desc[i].group];
+        r.grad = grad;
+        r.beta1 = g.beta1;
+        r.one_minus_beta1 = g.one_minus_beta1;
+        r.beta2 = g.beta2;
+        r.one_minus_beta2 = g.one_minus_beta2;
+        r.lr = g.lr;
+        r.decay = g.decay;
+        r.eps = g.eps;
+        r.bc1 = (float)(1.0 - pow_uint(g.beta1_d, (uint32_t)t));
+        r.bc2 = (float)(1.0 - pow_uint(g.beta2_d, (uint32_t)t));
+    }
+    a.records[i] = r;
+}
+
+// Wave-uniform metadata reads through the constant space (scalar loads),
+// copied out word by word.
+template <typename T>
+__device__ __forceinline__ T load_uniform(const T *tab, int32_t i) {
+    static_assert(sizeof(T) % 8 == 0, "64-bit words");
+    const APEXW_CONST uint64_t *p = cptr<uint64_t>(tab + i);
+    uint64_t w[sizeof(T) / 8];
+#pragma unroll
+    for (int j = 0; j < (int)(sizeof(T) / 8); ++j) w[j] = p[j];
+    T out;
+    __builtin_memcpy(&out, w, sizeof out);
+    return out;
+}
+
+// Position of tile k of a launch in its tile table.  The table is stored
+// XCD-major: the dispatcher deals workgroups to the XCDs round-robin, so the
+// workgroups one XCD runs (k, k+8, k+16, ...) read consecutive entries and
+// share the XCD's L2 lines.
+__device__ __forceinline__ int64_t table_pos(const KernelArgs &a, int64_t k) {
+    return a.table_begin + (k % kXcds) * a.table_stride + k / kXcds;
 }
 
 // The update: one 256-element tile per workgroup (the grid-stride loop only
@@ -371,25 +445,34 @@ __global__ __launch_bounds__(kPrepThreads) void adamw_prepare_kernel(KernelArgs 
 // ST: APEXW_STATE_F32 / _BF16 / _Q8.  PT, GT: parameter and grad types.
 template <int ST, int PT, int GT, bool NT>
 __global__ __launch_bounds__(kThreads) void adamw_step_kernel(KernelArgs a) {
-    // found_inf (M041 section 06, Apex guide 4.3): the whole step is skipped
-    // on the device; every workgroup reads the same flag, so all leave.
-    if (a.found_inf != nullptr && *a.found_inf != 0.0f) return;
-    for (int64_t k = blockIdx.x; k < a.tile_count; k += gridDim.x) {
-        const int64_t tile = a.tile_begin + k;
-        const int32_t i = a.tile_tensor[tile];
-        const void *grad = a.grads[i];
-        if (grad == nullptr) continue;          // no grad: tensor untouched
-        const TensorDesc d = a.desc[i];
-        const StepScalars s = step_scalars(a.groups[d.group], a.bias[i]);
-        const int64_t base = (tile - d.first_tile) * kTile;
+    const APEXW_CONST int32_t *tile_tensor = cptr<int32_t>(a.tile_tensor);
+    int64_t k = blockIdx.x;                    // < tile_count: grid <= tiles
+    int32_t i = tile_tensor[table_pos(a, k)];
+    for (;;) {
+        const StepRecord r = load_uniform(a.records, i);
+        const TensorDesc d = load_uniform(a.desc, i);
+        const int64_t base = (a.tile_begin + k - d.first_tile) * kTile;
         const int64_t left = d.numel - base;
         const int n = left < kTile ? (int)left : kTile;
-        if constexpr (ST == APEXW_STATE_F32)
-            tile_dense<PT, GT, APEXW_F32, NT>(d, grad, base, n, s);
-        else if constexpr (ST == APEXW_STATE_BF16)
-            tile_dense<PT, GT, APEXW_BF16, NT>(d, grad, base, n, s);
-        else
-            tile_q8<PT, GT, NT>(d, grad, base, n, s);
+        // Issue every metadata load before the branch (the compiler would
+        // otherwise fetch the data pointers only after it, one more
+        // round trip before the first data load); the empty asm only names
+        // the values, it emits no instruction.
+        asm volatile("" ::"s"(r.grad), "s"(d.param), "s"(d.m), "s"(d.v));
+        if constexpr (ST == APEXW_STATE_Q8) asm volatile("" ::"s"(d.m_scale), "s"(d.v_scale));
+        // no grad (absent, or the step is skipped): tensor untouched
+        if (r.grad != nullptr && n > 0) {
+            const StepScalars s = step_scalars(r);
+            if constexpr (ST == APEXW_STATE_F32)
+                tile_dense<PT, GT, APEXW_F32, NT>(d, r.grad, base, n, s);
+            else if constexpr (ST == APEXW_STATE_BF16)
+                tile_dense<PT, GT, APEXW_BF16, NT>(d, r.grad, base, n, s);
+            else
+                tile_q8<PT, GT, NT>(d, r.grad, base, n, s);
+        }
+        k += gridDim.x;
+        if (k >= a.tile_count) break;
+        i = tile_tensor[table_pos(a, k)];
     }
 }
 
