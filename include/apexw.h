@@ -195,14 +195,16 @@ int apexw_set_workgroups(apexw_t h, int32_t workgroups);
 
 /*
  * Cap how many update workgroups may be resident on one compute unit at a
- * time (enforced through the dynamic LDS each workgroup reserves; the kernel
- * uses none).  0 restores the format's default (fp32 moments: 28; bf16 and
- * 8-bit: no cap).  Fewer concurrent streams can keep the HBM read/write mix
- * more efficient; results do not depend on it.
+ * time, for every update launch (enforced through the dynamic LDS each
+ * workgroup reserves; the kernel uses none).  0 restores the defaults, which
+ * depend on the bytes each element moves (fp32 params and moments, 28 B: 12;
+ * bf16 params, fp32 grads and moments, 24 B: 16; bf16 or 8-bit moments: no
+ * cap).  Fewer concurrent streams can keep the HBM read/write mix more
+ * efficient; results do not depend on it.
  */
 int apexw_set_occupancy(apexw_t h, int32_t workgroups_per_cu);
 
-/* The cap in force (0: none). */
+/* The largest cap in force over the handle's update launches (0: none). */
 int apexw_get_occupancy(apexw_t h, int32_t *workgroups_per_cu);
 
 /* Release the handle (host memory only; waits for nothing). */

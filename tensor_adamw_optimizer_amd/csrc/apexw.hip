@@ -146,15 +146,24 @@ struct Launch {
     int32_t tensor_begin, tensor_count;
 };
 
-// Default cap on update workgroups resident per compute unit, per moment
-// format (0: no cap).  Fewer, longer-lived one-wave streams per CU keep the
-// HBM read/write mix efficient for the 28/24-byte fp32-state update; the
-// leaner formats want every stream they can get.
-int default_occupancy(int32_t fmt) {
-    switch (fmt) {
-    case APEXW_STATE_F32: return 28;
-    default: return 0;
-    }
+// Default cap on update workgroups resident per compute unit for one launch
+// (0: no cap), from the bytes each element moves.  Measured on MI355X: the
+// heavier the per-tile traffic, the fewer one-wave streams per CU keep the
+// HBM read/write mix most efficient (28 B/elem: 12, 24 B/elem: 16); the lean
+// bf16 and 8-bit formats want every stream they can get.
+
+int element_bytes(int32_t fmt, int pt, int gt) {
+    const int p = pt == APEXW_F32 ? 4 : 2, g = gt == APEXW_F32 ? 4 : 2;
+    return 2 * p + g + 4 * moment_bytes(fmt);
+}
+
+int default_occupancy(int32_t fmt, int pt, int gt) {
+    const int b = element_bytes(fmt, pt, gt);
+    if (b >= 27) return 12;
+    if (b >= 25) return 14;
+    if (b >= 23) return 16;
+    if (b >= 21) return 20;
+    return 0;
 }
 
 typedef void (*kernel_fn)(KernelArgs);
@@ -204,7 +213,7 @@ struct apexw_opt {
     int cu_count = 0;
     int lds_per_cu = 0, lds_per_block = 0;
     int32_t wg_override = 0;
-    int32_t occupancy = 0;              // update workgroups per CU (0: no cap)
+    int32_t occupancy = 0;              // override for every launch (0: defaults)
 };
 
 namespace {
@@ -344,7 +353,6 @@ int apexw_create(int32_t n_tensors, const int64_t *numel, const int32_t *param_d
                               h->device));
     TRY(hipDeviceGetAttribute(&h->lds_per_block, hipDeviceAttributeMaxSharedMemoryPerBlock,
                               h->device));
-    h->occupancy = default_occupancy(fmt);
 
     // static tables: the tensor of every tile, tiles grouped by dtype pair;
     // logical tile k of a launch is stored at (k % kXcds) * stride + k / kXcds
@@ -503,10 +511,10 @@ int apexw_step(apexw_t h, const apexw_group *groups, int32_t n_groups, void *con
                        dim3(kPrepThreads), 0, st, a);
     HIP_TRY(hipGetLastError());
     const int64_t cap = h->wg_override > 0 ? h->wg_override : kMaxGrid;
-    // residency cap: the dynamic LDS a workgroup reserves (it uses none)
-    const unsigned lds =
-        h->occupancy > 0 ? (unsigned)std::min(h->lds_per_cu / h->occupancy, h->lds_per_block) : 0u;
     for (const Launch &L : h->launches) {
+        // residency cap: the dynamic LDS a workgroup reserves (it uses none)
+        const int occ = h->occupancy > 0 ? h->occupancy : default_occupancy(h->fmt, L.pt, L.gt);
+        const unsigned lds = occ > 0 ? (unsigned)std::min(h->lds_per_cu / occ, h->lds_per_block) : 0u;
         if (L.tile_count == 0) continue;      // only empty tensors: t advanced above
         bool any = false;                     // no grads in this launch: skip it
         for (int32_t j = 0; j < L.tensor_count && !any; ++j)
@@ -547,13 +555,17 @@ int apexw_set_workgroups(apexw_t h, int32_t workgroups) {
 int apexw_set_occupancy(apexw_t h, int32_t workgroups_per_cu) {
     if (!h) return fail(APEXW_EINVAL, "handle is NULL");
     if (workgroups_per_cu < 0) return fail(APEXW_EINVAL, "workgroups_per_cu must be >= 0");
-    h->occupancy = workgroups_per_cu == 0 ? default_occupancy(h->fmt) : workgroups_per_cu;
+    h->occupancy = workgroups_per_cu;
     return APEXW_OK;
 }
 
 int apexw_get_occupancy(apexw_t h, int32_t *workgroups_per_cu) {
     if (!h || !workgroups_per_cu) return fail(APEXW_EINVAL, "NULL argument");
-    *workgroups_per_cu = h->occupancy;
+    int32_t occ = 0;
+    for (const Launch &L : h->launches)
+        occ = std::max<int32_t>(occ, h->occupancy > 0 ? h->occupancy
+                                                      : default_occupancy(h->fmt, L.pt, L.gt));
+    *workgroups_per_cu = occ;
     return APEXW_OK;
 }
 
