@@ -115,6 +115,8 @@ def main() -> int:
     ap.add_argument("--workgroups", type=int, default=0, help="cap on workgroups per launch")
     ap.add_argument("--occupancy", type=int, default=0,
                     help="update workgroups per CU (0: the format's default)")
+    ap.add_argument("--cache-policy", type=int, default=0,
+                    help="0 auto, 1 streaming (non-temporal), 2 cached")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, run a 1 GiB device copy 3x (counter calibration)")
@@ -160,6 +162,8 @@ def main() -> int:
         L.apexw_set_workgroups(h, args.workgroups)
     if args.occupancy:
         L.apexw_set_occupancy(h, args.occupancy)
+    if args.cache_policy:
+        L.apexw_set_cache_policy(h, args.cache_policy)
     occupancy = L.apexw_get_occupancy(h)
     tile, n_tiles, wgs = L.apexw_launch_info(h)
     params_arr = L.make_ptrs([p.data_ptr() for p in params])

@@ -204,6 +204,15 @@ int apexw_set_workgroups(apexw_t h, int32_t workgroups);
  */
 int apexw_set_occupancy(apexw_t h, int32_t workgroups_per_cu);
 
+/*
+ * Cache policy of the update kernel: 0 (default) chooses by size -- lists
+ * whose parameters, grads and state together reach 192 MiB stream with
+ * non-temporal loads and stores, smaller ones use ordinary (cached) accesses
+ * so they can stay in the 256 MB Infinity Cache from step to step; 1 forces
+ * streaming, 2 forces cached.  Results do not depend on it.
+ */
+int apexw_set_cache_policy(apexw_t h, int32_t policy);
+
 /* The largest cap in force over the handle's update launches (0: none). */
 int apexw_get_occupancy(apexw_t h, int32_t *workgroups_per_cu);
 

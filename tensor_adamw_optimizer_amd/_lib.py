@@ -36,7 +36,8 @@ APEXW_MAX_GROUPS = 32
 ENTRY_POINTS = (
     "apexw_state_bytes", "apexw_state_layout", "apexw_workspace_bytes",
     "apexw_create", "apexw_step", "apexw_launch_info", "apexw_set_workgroups",
-    "apexw_set_occupancy", "apexw_get_occupancy", "apexw_destroy", "apexw_last_error",
+    "apexw_set_occupancy", "apexw_get_occupancy", "apexw_set_cache_policy",
+    "apexw_destroy", "apexw_last_error",
 )
 
 
@@ -82,6 +83,7 @@ def lib() -> ctypes.CDLL:
         L.apexw_set_workgroups.argtypes = [P, I32]
         L.apexw_set_occupancy.argtypes = [P, I32]
         L.apexw_get_occupancy.argtypes = [P, ctypes.POINTER(I32)]
+        L.apexw_set_cache_policy.argtypes = [P, I32]
         L.apexw_destroy.argtypes = [P]
         L.apexw_last_error.argtypes = []
         L.apexw_last_error.restype = ctypes.c_char_p
@@ -183,6 +185,10 @@ def apexw_get_occupancy(handle: int) -> int:
     out = ctypes.c_int32(0)
     _check(lib().apexw_get_occupancy(handle, ctypes.byref(out)), "apexw_get_occupancy")
     return out.value
+
+
+def apexw_set_cache_policy(handle: int, policy: int) -> None:
+    _check(lib().apexw_set_cache_policy(handle, policy), "apexw_set_cache_policy")
 
 
 def apexw_destroy(handle: int) -> None:

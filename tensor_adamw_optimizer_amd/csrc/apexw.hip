@@ -168,20 +168,31 @@ int default_occupancy(int32_t fmt, int pt, int gt) {
 
 typedef void (*kernel_fn)(KernelArgs);
 
-template <int ST>
+template <int ST, bool NT>
 kernel_fn pick_kernel(int pt, int gt) {
-    // non-temporal hints keep the single-use streams out of the caches
-    if (pt == APEXW_F32 && gt == APEXW_F32) return adamw_step_kernel<ST, APEXW_F32, APEXW_F32, true>;
-    if (pt == APEXW_F32 && gt == APEXW_BF16) return adamw_step_kernel<ST, APEXW_F32, APEXW_BF16, true>;
-    if (pt == APEXW_BF16 && gt == APEXW_F32) return adamw_step_kernel<ST, APEXW_BF16, APEXW_F32, true>;
-    return adamw_step_kernel<ST, APEXW_BF16, APEXW_BF16, true>;
+    if (pt == APEXW_F32 && gt == APEXW_F32) return adamw_step_kernel<ST, APEXW_F32, APEXW_F32, NT>;
+    if (pt == APEXW_F32 && gt == APEXW_BF16) return adamw_step_kernel<ST, APEXW_F32, APEXW_BF16, NT>;
+    if (pt == APEXW_BF16 && gt == APEXW_F32) return adamw_step_kernel<ST, APEXW_BF16, APEXW_F32, NT>;
+    return adamw_step_kernel<ST, APEXW_BF16, APEXW_BF16, NT>;
 }
 
-kernel_fn kernel_for(int fmt, int pt, int gt) {
-    if (fmt == APEXW_STATE_F32) return pick_kernel<APEXW_STATE_F32>(pt, gt);
-    if (fmt == APEXW_STATE_BF16) return pick_kernel<APEXW_STATE_BF16>(pt, gt);
-    return pick_kernel<APEXW_STATE_Q8>(pt, gt);
+// streaming = non-temporal loads and stores (the single-use streams of a
+// list far larger than the caches); a list whose parameters, grads and state
+// fit the 256 MB Infinity Cache many times over keeps them cached instead.
+kernel_fn kernel_for(int fmt, int pt, int gt, bool streaming) {
+    if (streaming) {
+        if (fmt == APEXW_STATE_F32) return pick_kernel<APEXW_STATE_F32, true>(pt, gt);
+        if (fmt == APEXW_STATE_BF16) return pick_kernel<APEXW_STATE_BF16, true>(pt, gt);
+        return pick_kernel<APEXW_STATE_Q8, true>(pt, gt);
+    }
+    if (fmt == APEXW_STATE_F32) return pick_kernel<APEXW_STATE_F32, false>(pt, gt);
+    if (fmt == APEXW_STATE_BF16) return pick_kernel<APEXW_STATE_BF16, false>(pt, gt);
+    return pick_kernel<APEXW_STATE_Q8, false>(pt, gt);
 }
+
+// Bytes an optimizer touches per step (parameters, grads, state): above this
+// the update streams past the caches.
+constexpr int64_t kStreamingBytes = (int64_t)192 << 20;
 
 }  // namespace
 
@@ -214,6 +225,8 @@ struct apexw_opt {
     int lds_per_cu = 0, lds_per_block = 0;
     int32_t wg_override = 0;
     int32_t occupancy = 0;              // override for every launch (0: defaults)
+    int cache_policy = 0;               // 0 auto, 1 streaming, 2 cached
+    bool streaming_auto = true;
 };
 
 namespace {
@@ -356,6 +369,13 @@ int apexw_create(int32_t n_tensors, const int64_t *numel, const int32_t *param_d
 
     // static tables: the tensor of every tile, tiles grouped by dtype pair;
     // logical tile k of a launch is stored at (k % kXcds) * stride + k / kXcds
+    {
+        int64_t touched = need_state;
+        for (int32_t i = 0; i < n_tensors; ++i)
+            touched += numel[i] * ((param_dtype[i] == APEXW_F32 ? 4 : 2) +
+                                   (grad_dtype[i] == APEXW_F32 ? 4 : 2));
+        h->streaming_auto = touched >= kStreamingBytes;
+    }
     std::vector<int32_t> tiles;
     try {
         tiles.reserve((size_t)(wl.n_tiles + kMaxLaunches * kXcds));
@@ -525,7 +545,8 @@ int apexw_step(apexw_t h, const apexw_group *groups, int32_t n_groups, void *con
         a.table_begin = L.table_begin;
         a.table_stride = L.table_stride;
         const int64_t wg = std::min(L.tile_count, cap);
-        hipLaunchKernelGGL(kernel_for(h->fmt, L.pt, L.gt), dim3((unsigned)wg), dim3(kThreads),
+        const bool streaming = h->cache_policy == 0 ? h->streaming_auto : h->cache_policy == 1;
+        hipLaunchKernelGGL(kernel_for(h->fmt, L.pt, L.gt, streaming), dim3((unsigned)wg), dim3(kThreads),
                            lds, st, a);
         HIP_TRY(hipGetLastError());
     }
@@ -556,6 +577,13 @@ int apexw_set_occupancy(apexw_t h, int32_t workgroups_per_cu) {
     if (!h) return fail(APEXW_EINVAL, "handle is NULL");
     if (workgroups_per_cu < 0) return fail(APEXW_EINVAL, "workgroups_per_cu must be >= 0");
     h->occupancy = workgroups_per_cu;
+    return APEXW_OK;
+}
+
+int apexw_set_cache_policy(apexw_t h, int32_t policy) {
+    if (!h) return fail(APEXW_EINVAL, "handle is NULL");
+    if (policy < 0 || policy > 2) return fail(APEXW_EINVAL, "policy must be 0, 1 or 2");
+    h->cache_policy = policy;
     return APEXW_OK;
 }
 

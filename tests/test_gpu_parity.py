@@ -14,6 +14,7 @@ import torch
 
 import oracle
 import workloads as W
+from tensor_adamw_optimizer_amd import _lib as L
 from gpu_helpers import (GpuOpt, as_f32, assert_fp32_state_parity, bits, n_bit_mismatch,
                          normwise_err, rel_err_elementwise, say)
 
@@ -78,13 +79,15 @@ def test_tiny_every_call_against_oracle():
 EDGE_SIZES = [1, 3, 5, 255, 256, 257, 1023, 4095, 4096, 4097, 8191, 12289, 0, 100003]
 
 
+@pytest.mark.parametrize("policy", [0, 1])
 @pytest.mark.parametrize("fmt", [W.STATE_F32, W.STATE_BF16, W.STATE_Q8])
-def test_ragged_mixed_dtypes_groups_and_misalignment(fmt):
+def test_ragged_mixed_dtypes_groups_and_misalignment(fmt, policy):
     """Every (param, grad) dtype pair in one optimizer (one launch each), ragged
     sizes, an empty tensor, three groups, a parameter and a grad that are not
-    16-byte aligned, grads absent on some calls, one skipped call."""
+    16-byte aligned, grads absent on some calls, one skipped call; cached
+    (the small list's default) and streaming accesses."""
     _need_gpu()
-    say("case: ragged", fmt)
+    say("case: ragged", fmt, "policy", policy)
     sizes = EDGE_SIZES * 2
     n = len(sizes)
     pdt = [(W.F32, W.BF16)[(i // 2) % 2] for i in range(n)]
@@ -106,6 +109,7 @@ def test_ragged_mixed_dtypes_groups_and_misalignment(fmt):
         else:
             params.append(p.to(DEV))
     opt = GpuOpt(sizes, pdt, gdt, group_of, 3, fmt)
+    L.apexw_set_cache_policy(opt.h, policy)
     ref = oracle.OracleAdamW(sizes, pdt, gdt, group_of, fmt)
     th_ref = [bits(p) for p in p_cpu]
     fi = torch.zeros(1, device=DEV)
@@ -210,7 +214,6 @@ def test_results_do_not_depend_on_grid(wg):
     for setting in (wg, 0):
         params = W.init_params(w, DEV)
         opt = GpuOpt(w.numels, w.param_dtype, w.grad_dtype, w.group_of, 3, w.state_fmt)
-        from tensor_adamw_optimizer_amd import _lib as L
         L.apexw_set_workgroups(opt.h, setting)
         for k in range(1, 4):
             opt.step(w.groups, params, W.grads_for_call(w, k, DEV))
