@@ -77,6 +77,12 @@ def lib():
         L.oracle_adamw_step.argtypes = [
             ctypes.c_int32, P, P, P, P, P, P, P, ctypes.c_int32, ctypes.c_int32,
             P, P, P, P, P, ctypes.c_int32]
+        L.oracle_adamw_step_scaled.restype = ctypes.c_int32
+        L.oracle_adamw_step_scaled.argtypes = [
+            ctypes.c_int32, P, P, P, P, P, P, P, ctypes.c_int32, ctypes.c_int32,
+            P, P, P, P, P, ctypes.c_float, ctypes.c_int32]
+        L.oracle_unscale_check.restype = ctypes.c_int32
+        L.oracle_unscale_check.argtypes = [ctypes.c_int32, P, P, P, ctypes.c_float]
         L.oracle_adamw_step_three_loops.restype = ctypes.c_int32
         L.oracle_adamw_step_three_loops.argtypes = [
             ctypes.c_int32, P, P, P, P, P, ctypes.c_int32, P, P, P,
@@ -216,10 +222,18 @@ class OracleAdamW:
             v[lo:hi] = dequantize_unsigned(self.v[i][lo:hi], float(self.v_scale[i][b]))
         return m, v
 
+    def unscale_check(self, grads: Sequence[Optional[np.ndarray]],
+                      inv_scale: float) -> bool:
+        """True if any present grad value times inv_scale (fp32) is not finite."""
+        assert len(grads) == self.n
+        return bool(lib().oracle_unscale_check(self.n, _ptr(self._numel), _ptr(self._gdt),
+                                               _ptr_array(grads), inv_scale))
+
     def step(self, thetas: Sequence[np.ndarray],
              grads: Sequence[Optional[np.ndarray]], groups,
-             found_inf: bool = False) -> None:
-        """Update ``thetas`` (in place) and the held state by one call."""
+             found_inf: bool = False, inv_scale: Optional[float] = None) -> None:
+        """Update ``thetas`` (in place) and the held state by one call; with
+        ``inv_scale`` the grads are unscaled (g * inv_scale in fp32) first."""
         assert len(thetas) == self.n and len(grads) == self.n
         for i, th in enumerate(thetas):
             want = np.uint16 if self.param_dtype[i] == "bf16" else np.float32
@@ -228,12 +242,15 @@ class OracleAdamW:
             if g is not None:
                 want = np.uint16 if self.grad_dtype[i] == "bf16" else np.float32
                 assert g.dtype == want and g.flags.c_contiguous and g.size == self.numels[i]
-        rc = lib().oracle_adamw_step(
-            self.n, _ptr(self._numel), _ptr(self._pdt), _ptr_array(thetas),
-            _ptr(self._gdt), _ptr_array(grads), _ptr(self._grp),
-            _groups(groups), len(groups), STATE_CODE[self.state_fmt],
-            _ptr_array(self.m), _ptr_array(self.v), _ptr_array(self.m_scale),
-            _ptr_array(self.v_scale), _ptr(self.t), int(bool(found_inf)))
+        args = (self.n, _ptr(self._numel), _ptr(self._pdt), _ptr_array(thetas),
+                _ptr(self._gdt), _ptr_array(grads), _ptr(self._grp),
+                _groups(groups), len(groups), STATE_CODE[self.state_fmt],
+                _ptr_array(self.m), _ptr_array(self.v), _ptr_array(self.m_scale),
+                _ptr_array(self.v_scale), _ptr(self.t))
+        if inv_scale is None:
+            rc = lib().oracle_adamw_step(*args, int(bool(found_inf)))
+        else:
+            rc = lib().oracle_adamw_step_scaled(*args, inv_scale, int(bool(found_inf)))
         if rc != 0:
             raise ValueError("oracle_adamw_step rejected its arguments")
 

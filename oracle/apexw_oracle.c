@@ -222,11 +222,12 @@ static void store_value(int32_t dtype, void *base, int64_t i, float x)
 
 static void update_tensor_dense(int64_t n, int32_t pdt, void *theta,
                                 int32_t gdt, const void *grad, int32_t sdt,
-                                void *m, void *v, const step_scalars *s)
+                                void *m, void *v, const step_scalars *s,
+                                float inv_scale)
 {
     for (int64_t i = 0; i < n; ++i) {
         float th = load_value(pdt, theta, i);
-        float g = load_value(gdt, grad, i);
+        float g = load_value(gdt, grad, i) * inv_scale;
         float mi = load_value(sdt, m, i);
         float vi = load_value(sdt, v, i);
         adamw_element(&th, g, &mi, &vi, s);
@@ -239,7 +240,8 @@ static void update_tensor_dense(int64_t n, int32_t pdt, void *theta,
 /* R5: decode a block, update it, re-encode it. */
 static void update_tensor_q8(int64_t n, int32_t pdt, void *theta, int32_t gdt,
                              const void *grad, int8_t *mq, uint8_t *vq,
-                             float *ms, float *vs, const step_scalars *s)
+                             float *ms, float *vs, const step_scalars *s,
+                             float inv_scale)
 {
     float mf[ORACLE_BLOCK], vf[ORACLE_BLOCK];
     int64_t nblocks = (n + ORACLE_BLOCK - 1) / ORACLE_BLOCK;
@@ -250,7 +252,7 @@ static void update_tensor_q8(int64_t n, int32_t pdt, void *theta, int32_t gdt,
         oracle_dequantize_unsigned(len, vq + lo, vs[b], vf);
         for (int64_t j = 0; j < len; ++j) {
             float th = load_value(pdt, theta, lo + j);
-            float g = load_value(gdt, grad, lo + j);
+            float g = load_value(gdt, grad, lo + j) * inv_scale;
             adamw_element(&th, g, &mf[j], &vf[j], s);
             store_value(pdt, theta, lo + j, th);
         }
@@ -260,24 +262,49 @@ static void update_tensor_q8(int64_t n, int32_t pdt, void *theta, int32_t gdt,
 }
 
 /*
- * One optimizer step over a tensor list.
+ * Mixed-precision recipe step before the update ([M041 §06]; [Apex §4.3]):
+ * the grads are unscaled by inv_scale (one rounded fp32 multiply per element)
+ * and checked for non-finite values.  Returns 1 if any unscaled value of any
+ * present grad is an infinity or a NaN, else 0.
+ */
+int32_t oracle_unscale_check(int32_t n_tensors, const int64_t *numel,
+                             const int32_t *grad_dtype, const void *const *grad,
+                             float inv_scale)
+{
+    for (int32_t i = 0; i < n_tensors; ++i) {
+        if (grad[i] == NULL)
+            continue;
+        for (int64_t e = 0; e < numel[i]; ++e) {
+            float g = load_value(grad_dtype[i], grad[i], e) * inv_scale;
+            if (isnan(g) || isinf(g))
+                return 1;
+        }
+    }
+    return 0;
+}
+
+/*
+ * One optimizer step over a tensor list, on unscaled grads g * inv_scale
+ * (inv_scale = 1 is the plain step: multiplying by one is exact).
  *
  *   theta[i]      parameter values, fp32 or bf16 bits (param_dtype[i])
  *   grad[i]       gradient values, fp32 or bf16 bits, or NULL for "no grad"
  *   m[i], v[i]    state: fp32, bf16 bits, or int8 / uint8 codes (state_fmt)
  *   m_scale[i], v_scale[i]  per-256-block fp32 scales (8-bit state only)
  *   t[i]          int32 step counter per tensor
+ *   inv_scale     fp32 factor applied to every grad value first
  *   found_inf     nonzero: the whole step is skipped, nothing is written
  *
  * Returns 0, or -1 on an argument it does not understand.
  */
-int oracle_adamw_step(int32_t n_tensors, const int64_t *numel,
-                      const int32_t *param_dtype, void *const *theta,
-                      const int32_t *grad_dtype, const void *const *grad,
-                      const int32_t *group_of, const oracle_group *groups,
-                      int32_t n_groups, int32_t state_fmt, void *const *m,
-                      void *const *v, float *const *m_scale,
-                      float *const *v_scale, int32_t *t, int32_t found_inf)
+int oracle_adamw_step_scaled(int32_t n_tensors, const int64_t *numel,
+                             const int32_t *param_dtype, void *const *theta,
+                             const int32_t *grad_dtype, const void *const *grad,
+                             const int32_t *group_of, const oracle_group *groups,
+                             int32_t n_groups, int32_t state_fmt, void *const *m,
+                             void *const *v, float *const *m_scale,
+                             float *const *v_scale, int32_t *t, float inv_scale,
+                             int32_t found_inf)
 {
     if (found_inf)
         return 0;                                   /* R3: skip everything */
@@ -291,16 +318,32 @@ int oracle_adamw_step(int32_t n_tensors, const int64_t *numel,
         if (state_fmt == ORACLE_STATE_F32 || state_fmt == ORACLE_STATE_BF16) {
             int32_t sdt = state_fmt == ORACLE_STATE_F32 ? ORACLE_F32 : ORACLE_BF16;
             update_tensor_dense(numel[i], param_dtype[i], theta[i],
-                                grad_dtype[i], grad[i], sdt, m[i], v[i], &s);
+                                grad_dtype[i], grad[i], sdt, m[i], v[i], &s,
+                                inv_scale);
         } else if (state_fmt == ORACLE_STATE_Q8) {
             update_tensor_q8(numel[i], param_dtype[i], theta[i], grad_dtype[i],
                              grad[i], (int8_t *)m[i], (uint8_t *)v[i],
-                             m_scale[i], v_scale[i], &s);
+                             m_scale[i], v_scale[i], &s, inv_scale);
         } else {
             return -1;
         }
     }
     return 0;
+}
+
+/* The plain step: oracle_adamw_step_scaled with inv_scale = 1. */
+int oracle_adamw_step(int32_t n_tensors, const int64_t *numel,
+                      const int32_t *param_dtype, void *const *theta,
+                      const int32_t *grad_dtype, const void *const *grad,
+                      const int32_t *group_of, const oracle_group *groups,
+                      int32_t n_groups, int32_t state_fmt, void *const *m,
+                      void *const *v, float *const *m_scale,
+                      float *const *v_scale, int32_t *t, int32_t found_inf)
+{
+    return oracle_adamw_step_scaled(n_tensors, numel, param_dtype, theta,
+                                    grad_dtype, grad, group_of, groups,
+                                    n_groups, state_fmt, m, v, m_scale, v_scale,
+                                    t, 1.0f, found_inf);
 }
 
 /*

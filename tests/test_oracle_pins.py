@@ -405,3 +405,109 @@ def test_bf16_state_is_fp32_update_rounded():
         assert np.array_equal(th, th_ref)
         assert np.array_equal(b.m[0], oracle.f32_to_bf16(ref.m[0]))
         assert np.array_equal(b.v[0], oracle.f32_to_bf16(ref.v[0]))
+
+
+# ------------------------------------------------------------ unscale / check
+
+def _run_fmt(fmt, sizes, pdt, gdt, grads_per_call, group, inv_scale=None, seed=20):
+    rng = np.random.default_rng(seed)
+    o = OracleAdamW(sizes, pdt, gdt, [0] * len(sizes), fmt)
+    th = []
+    for n, d in zip(sizes, pdt):
+        x = f32(rng.normal(0, 0.02, n))
+        th.append(oracle.f32_to_bf16(x) if d == "bf16" else x)
+    for gs in grads_per_call:
+        o.step(th, gs, [group], inv_scale=inv_scale)
+    return th, o
+
+
+def _as_dtype(x, d):
+    return oracle.f32_to_bf16(x) if d == "bf16" else f32(x)
+
+
+@pytest.mark.parametrize("fmt", ["f32", "bf16", "q8"])
+def test_unscale_by_power_of_two_is_exact(fmt):
+    """Grads stored multiplied by 2^k and unscaled by 2^-k give bit for bit the
+    plain step on the unscaled grads (the scaling is exact), and inv_scale = 1
+    is the plain step; a multiply placed anywhere else would differ."""
+    rng = np.random.default_rng(21)
+    sizes, pdt, gdt = [700, 300], ["bf16", "f32"], ["f32", "bf16"]
+    grp = Group(lr=1e-3, weight_decay=0.05)
+    calls = [[f32(rng.normal(0, 1e-3, n)) for n in sizes] for _ in range(4)]
+    plain = [[_as_dtype(g, d) for g, d in zip(c, gdt)] for c in calls]
+    scaled = [[_as_dtype(g * 65536.0, d) for g, d in zip(c, gdt)] for c in calls]
+    th_a, a = _run_fmt(fmt, sizes, pdt, gdt, plain, grp)
+    th_b, b = _run_fmt(fmt, sizes, pdt, gdt, scaled, grp, inv_scale=1.0 / 65536.0)
+    th_c, c = _run_fmt(fmt, sizes, pdt, gdt, plain, grp, inv_scale=1.0)
+    for i in range(2):
+        for other_th, other in ((th_b, b), (th_c, c)):
+            assert np.array_equal(th_a[i], other_th[i])
+            assert np.array_equal(a.m[i], other.m[i]) and np.array_equal(a.v[i], other.v[i])
+
+
+def test_unscale_general_factor_against_fp64():
+    rng = np.random.default_rng(22)
+    n, inv = 513, 1.0 / 3.0
+    grp = Group(lr=1e-2, weight_decay=0.1)
+    theta = f32(rng.normal(0, 0.02, n))
+    o = OracleAdamW([n], ["f32"], ["f32"], [0], "f32")
+    th = theta.copy()
+    st = [theta.astype(np.float64), np.zeros(n), np.zeros(n), 0]
+    for _ in range(10):
+        g = f32(rng.normal(0, 3e-3, n))
+        o.step([th], [g], [grp], inv_scale=inv)
+        g64 = (g * np.float32(inv)).astype(np.float64)
+        st = list(ref64.adamw_fp64(st[0], g64, st[1], st[2], st[3], grp.lr, grp.beta1,
+                                   grp.beta2, grp.eps, grp.weight_decay))
+    assert np.max(np.abs(th - st[0])) / np.max(np.abs(st[0])) <= 1e-5
+    m, v = o.moments_f32(0)
+    assert np.max(np.abs(m - st[1])) / np.max(np.abs(st[1])) <= 1e-5
+
+
+@pytest.mark.parametrize("inv", [1.0 / 65536.0, 1.0, 4.0, 3.0e30])
+def test_unscale_check_matches_numpy_isfinite(inv):
+    rng = np.random.default_rng(23)
+    sizes, gdt = [1000, 257, 64], ["f32", "bf16", "f32"]
+    o = OracleAdamW(sizes, ["f32"] * 3, gdt, [0, 0, 0], "f32")
+    for trial in range(30):
+        gs = [f32(rng.normal(0, 1.0, n) * np.exp(rng.uniform(-10, 10, n))) for n in sizes]
+        if trial % 3 == 1:
+            t = rng.integers(0, 3)
+            gs[t][rng.integers(0, sizes[t])] = [np.inf, -np.inf, np.nan][trial % 3]
+        if trial % 5 == 4:
+            gs[0][5] = np.float32(3.0e38)          # finite, overflows when inv > 1
+        absent = trial % 4 == 2
+        stored = [_as_dtype(g, d) for g, d in zip(gs, gdt)]
+        if absent:
+            stored[0] = None
+        want = False
+        for g, d in zip(stored, gdt):
+            if g is None:
+                continue
+            v = oracle.bf16_to_f32(g) if d == "bf16" else g
+            with np.errstate(over="ignore", invalid="ignore"):
+                want |= bool(np.any(~np.isfinite(v * np.float32(inv))))
+        assert o.unscale_check(stored, inv) == want
+
+
+def test_amp_recipe_skip_on_overflow():
+    """Scale 2^16: grads arrive scaled; an overflow in any tensor makes the
+    check report it and the step with that flag change nothing."""
+    rng = np.random.default_rng(24)
+    sizes = [400, 90]
+    grp = Group(lr=1e-3, weight_decay=0.1)
+    o = OracleAdamW(sizes, ["f32", "f32"], ["f32", "f32"], [0, 0], "f32")
+    th = [f32(rng.normal(0, 0.02, n)) for n in sizes]
+    scale = 65536.0
+    for k in range(1, 7):
+        gs = [f32(rng.normal(0, 1e-3, n) * scale) for n in sizes]
+        if k == 4:
+            gs[1][7] = np.inf
+        found = o.unscale_check(gs, 1.0 / scale)
+        assert found == (k == 4)
+        before = [x.copy() for x in th] + [o.t.copy()]
+        o.step(th, gs, [grp], found_inf=found, inv_scale=1.0 / scale)
+        if found:
+            after = [x.copy() for x in th] + [o.t.copy()]
+            assert all(np.array_equal(a, b) for a, b in zip(before, after))
+    assert list(o.t) == [5, 5]
