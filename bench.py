@@ -117,6 +117,9 @@ def main() -> int:
                     help="update workgroups per CU (0: the format's default)")
     ap.add_argument("--cache-policy", type=int, default=0,
                     help="0 auto, 1 streaming (non-temporal), 2 cached")
+    ap.add_argument("--amp", action="store_true",
+                    help="time the mixed-precision recipe: zero found_inf, unscale-and-check "
+                         "pass, update on grads scaled by 2^16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, run a 1 GiB device copy 3x (counter calibration)")
@@ -170,10 +173,21 @@ def main() -> int:
     grads_arr = L.make_ptrs([g.data_ptr() for g in grads])
     groups_arr = L.make_groups(w.groups)
     found_inf = torch.zeros(1, dtype=torch.float32, device=dev)
+    inv_scale = torch.tensor([1.0 / 65536.0], dtype=torch.float32, device=dev)
+    if args.amp:
+        for g in grads:
+            g.mul_(65536.0)
 
     def step():
-        L.apexw_step(h, groups_arr, len(w.groups), params_arr, grads_arr, found_inf.data_ptr(),
-                     stream.cuda_stream)
+        if args.amp:
+            found_inf.zero_()
+            L.apexw_unscale_check(h, grads_arr, inv_scale.data_ptr(), found_inf.data_ptr(),
+                                  stream.cuda_stream)
+            L.apexw_step_scaled(h, groups_arr, len(w.groups), params_arr, grads_arr,
+                                inv_scale.data_ptr(), found_inf.data_ptr(), stream.cuda_stream)
+        else:
+            L.apexw_step(h, groups_arr, len(w.groups), params_arr, grads_arr,
+                         found_inf.data_ptr(), stream.cuda_stream)
 
     for _ in range(args.warmup):
         step()
@@ -202,8 +216,10 @@ def main() -> int:
         del src, dst
 
     ab = algorithmic_bytes(w)
+    if args.amp:        # the check pass reads every grad once more
+        ab += sum(n * ELEM[d] for n, d in zip(w.numels, w.grad_dtype))
     gbps = ab / avg_kernel_s / 1e9
-    traffic = measured_traffic(w.name)
+    traffic = None if args.amp else measured_traffic(w.name)
     out = {
         "metric": METRIC,
         "value": w.n_params * args.steps / elapsed,
@@ -218,7 +234,7 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": w.name,
+            "workload": w.name + ("+amp" if args.amp else ""),
             "tensors": len(w.shapes),
             "params": w.n_params,
             "param_dtype": "+".join(sorted(set(w.param_dtype))),
@@ -241,7 +257,7 @@ def main() -> int:
             "frac": gbps / HBM_PEAK_GBPS,
             "traffic": traffic,
             "algorithmic_bytes_per_launch": ab,
-            "kernel": "adamw_step_kernel",
+            "kernel": "adamw_step_kernel" + (" + unscale_check_kernel" if args.amp else ""),
         },
     }
     L.apexw_destroy(h)

@@ -178,6 +178,37 @@ int apexw_step(apexw_t h, const apexw_group *groups, int32_t n_groups,
                const float *found_inf_dev, void *stream);
 
 /*
+ * apexw_step on grads that arrive multiplied by a loss scale: every grad
+ * value is first unscaled, g * (*inv_scale_dev) as one rounded fp32
+ * multiply, then updated exactly as by apexw_step (the mixed-precision
+ * recipe of the M041 page, section 06; the Apex guide, section 4.3, passes
+ * inv_scale = 1/scale to its kernel the same way, with no host sync).
+ *   inv_scale_dev  device pointer to one float, read by the GPU when the step
+ *                  runs; NULL means 1 (then this is apexw_step).
+ * Other arguments, errors and ordering as apexw_step.
+ */
+int apexw_step_scaled(apexw_t h, const apexw_group *groups, int32_t n_groups,
+                      void *const *params, const void *const *grads,
+                      const float *inv_scale_dev, const float *found_inf_dev,
+                      void *stream);
+
+/*
+ * Unscale-and-check pass of the mixed-precision recipe (M041 section 06):
+ * reads every present grad once and sets *found_inf_dev = 1.0f if any value
+ * g * (*inv_scale_dev) (one rounded fp32 multiply; NULL inv_scale_dev means 1)
+ * is an infinity or a NaN.  It never clears the flag (the caller zeroes it
+ * before the first check of a step, so several checks can accumulate) and
+ * never rewrites the grads: pass the same inv_scale to apexw_step_scaled,
+ * which applies it inside the update.  grads: as for apexw_step (NULL entries
+ * are skipped); found_inf_dev must not be NULL.  Queued on `stream`, no host
+ * synchronisation.  Errors: APEXW_EINVAL for a NULL handle, grads or
+ * found_inf_dev; APEXW_EHIP if a launch fails.
+ */
+int apexw_unscale_check(apexw_t h, const void *const *grads,
+                        const float *inv_scale_dev, float *found_inf_dev,
+                        void *stream);
+
+/*
  * Launch geometry of the handle: tile size in elements (256; one workgroup of
  * one wave64 per tile), number of tiles, and the largest workgroup count of
  * its update launches.  Any pointer may be NULL.

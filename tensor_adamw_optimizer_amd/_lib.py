@@ -35,7 +35,8 @@ APEXW_MAX_GROUPS = 32
 # the entry points include/apexw.h declares
 ENTRY_POINTS = (
     "apexw_state_bytes", "apexw_state_layout", "apexw_workspace_bytes",
-    "apexw_create", "apexw_step", "apexw_launch_info", "apexw_set_workgroups",
+    "apexw_create", "apexw_step", "apexw_step_scaled", "apexw_unscale_check",
+    "apexw_launch_info", "apexw_set_workgroups",
     "apexw_set_occupancy", "apexw_get_occupancy", "apexw_set_cache_policy",
     "apexw_destroy", "apexw_last_error",
 )
@@ -78,6 +79,8 @@ def lib() -> ctypes.CDLL:
         L.apexw_create.argtypes = [I32, P, P, P, P, I32, I32, P, SZ, P, SZ, P,
                                    ctypes.POINTER(P)]
         L.apexw_step.argtypes = [P, P, I32, P, P, P, P]
+        L.apexw_step_scaled.argtypes = [P, P, I32, P, P, P, P, P]
+        L.apexw_unscale_check.argtypes = [P, P, P, P, P]
         L.apexw_launch_info.argtypes = [P, ctypes.POINTER(I32), ctypes.POINTER(I32),
                                         ctypes.POINTER(I32)]
         L.apexw_set_workgroups.argtypes = [P, I32]
@@ -164,6 +167,20 @@ def apexw_step(handle: int, groups_arr, n_groups: int, params_arr, grads_arr,
     """groups_arr / params_arr / grads_arr: arrays from make_groups / make_ptrs."""
     _check(lib().apexw_step(handle, groups_arr, n_groups, params_arr, grads_arr,
                             found_inf_ptr or None, stream or None), "apexw_step")
+
+
+def apexw_step_scaled(handle: int, groups_arr, n_groups: int, params_arr, grads_arr,
+                      inv_scale_ptr: int = 0, found_inf_ptr: int = 0, stream: int = 0) -> None:
+    _check(lib().apexw_step_scaled(handle, groups_arr, n_groups, params_arr, grads_arr,
+                                   inv_scale_ptr or None, found_inf_ptr or None, stream or None),
+           "apexw_step_scaled")
+
+
+def apexw_unscale_check(handle: int, grads_arr, inv_scale_ptr: int, found_inf_ptr: int,
+                        stream: int = 0) -> None:
+    _check(lib().apexw_unscale_check(handle, grads_arr, inv_scale_ptr or None,
+                                     found_inf_ptr or None, stream or None),
+           "apexw_unscale_check")
 
 
 def apexw_launch_info(handle: int):

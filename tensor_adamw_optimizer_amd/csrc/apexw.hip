@@ -257,6 +257,64 @@ void release(apexw_opt *h) {
     delete h;
 }
 
+// Host copy of the descriptor table for the given parameter pointers
+// (nullptr: none yet).
+void fill_descriptors(apexw_opt *h, void *const *params) {
+    for (int32_t i = 0; i < h->n; ++i) {
+        TensorDesc &d = h->desc[i];
+        std::memset(&d, 0, sizeof d);
+        d.param = params ? params[i] : nullptr;
+        d.m = h->state + h->layout[i].m;
+        d.v = h->state + h->layout[i].v;
+        d.m_scale = h->layout[i].m_scale >= 0
+                        ? reinterpret_cast<float *>(h->state + h->layout[i].m_scale)
+                        : nullptr;
+        d.v_scale = h->layout[i].v_scale >= 0
+                        ? reinterpret_cast<float *>(h->state + h->layout[i].v_scale)
+                        : nullptr;
+        d.numel = h->numel[i];
+        d.first_tile = h->first_tile[i];
+        d.group = h->group_of[i];
+    }
+}
+
+// Upload the grad-pointer table, and the descriptors when params is given
+// and differs from the last upload: one asynchronous copy from a pinned ring
+// slot, only when something changed.
+int upload_pointer_tables(apexw_opt *h, void *const *params, const void *const *grads,
+                          hipStream_t st) {
+    const size_t n = (size_t)h->n;
+    if (n == 0) return APEXW_OK;
+    const bool params_changed =
+        params && (!h->have_params || std::memcmp(h->last_params.data(), params, n * sizeof(void *)));
+    const bool grads_changed =
+        !h->have_grads || std::memcmp(h->last_grads.data(), grads, n * sizeof(void *));
+    if (!params_changed && !grads_changed) return APEXW_OK;
+    const int s = h->next_slot;
+    if (h->ev_pending[s]) HIP_TRY(hipEventSynchronize(h->ev[s]));
+    char *slot = h->pinned + (int64_t)s * h->slot_bytes;
+    int64_t begin = h->wl.grads;
+    const int64_t end = h->wl.grads + (int64_t)n * 8;
+    if (params_changed) {
+        fill_descriptors(h, params);
+        std::memcpy(slot + h->wl.desc, h->desc.data(), n * sizeof(TensorDesc));
+        begin = h->wl.desc;
+        std::memcpy(h->last_params.data(), params, n * sizeof(void *));
+        h->have_params = true;
+    }
+    std::memcpy(slot + h->wl.grads, grads, n * sizeof(void *));
+    HIP_TRY(hipMemcpyAsync(h->ws + begin, slot + begin, (size_t)(end - begin),
+                           hipMemcpyHostToDevice, st));
+    HIP_TRY(hipEventRecord(h->ev[s], st));
+    h->ev_pending[s] = true;
+    h->next_slot = (s + 1) % apexw_opt::kRing;
+    std::memcpy(h->last_grads.data(), grads, n * sizeof(void *));
+    h->have_grads = true;
+    return APEXW_OK;
+}
+
+int launch_cap(const apexw_opt *h) { return h->wg_override > 0 ? h->wg_override : (int)kMaxGrid; }
+
 }  // namespace
 
 // ======================================================================= ABI
@@ -411,21 +469,28 @@ int apexw_create(int32_t n_tensors, const int64_t *numel, const int32_t *param_d
     }
 
     // pinned staging: the ring for per-call uploads (descriptors + grad
-    // pointers), also used once here for the step records and the tile table
+    // pointers), also used once here for the whole workspace: descriptors
+    // (parameter pointers arrive with the first step), grad pointers and
+    // step records zero, the tile table
     const int64_t per_call = wl.records;
-    const int64_t static_bytes = wl.total - wl.records;
+    const int64_t static_bytes = wl.total;
     h->slot_bytes = std::max<int64_t>(per_call, kTableAlign);
     const int64_t pinned_bytes =
         std::max<int64_t>(h->slot_bytes * apexw_opt::kRing, static_bytes);
-    TRY(hipHostMalloc((void **)&h->pinned, (size_t)pinned_bytes, hipHostMallocDefault));
+    TRY(hipHostMalloc((void **)&h->pinned, (size_t)std::max<int64_t>(pinned_bytes, kTableAlign),
+                      hipHostMallocDefault));
     for (int s = 0; s < apexw_opt::kRing; ++s) TRY(hipEventCreateWithFlags(&h->ev[s], hipEventDisableTiming));
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     char *stage = h->pinned;
     std::memset(stage, 0, (size_t)static_bytes);
+    fill_descriptors(h, nullptr);
+    if (n_tensors > 0)
+        std::memcpy(stage + wl.desc, h->desc.data(), (size_t)n_tensors * sizeof(TensorDesc));
     if (!tiles.empty())
-        std::memcpy(stage + (wl.tiles - wl.records), tiles.data(), tiles.size() * 4);
-    TRY(hipMemcpyAsync(h->ws + wl.records, stage, (size_t)static_bytes, hipMemcpyHostToDevice, st));
+        std::memcpy(stage + wl.tiles, tiles.data(), tiles.size() * 4);
+    if (static_bytes > 0)
+        TRY(hipMemcpyAsync(h->ws, stage, (size_t)static_bytes, hipMemcpyHostToDevice, st));
     const int64_t words = need_state / 4;
     if (words > 0) {
         const int64_t blocks = std::min<int64_t>(ceil_div(words, 256), 8 * (int64_t)h->cu_count);
@@ -441,6 +506,12 @@ int apexw_create(int32_t n_tensors, const int64_t *numel, const int32_t *param_d
 
 int apexw_step(apexw_t h, const apexw_group *groups, int32_t n_groups, void *const *params,
                const void *const *grads, const float *found_inf_dev, void *stream) {
+    return apexw_step_scaled(h, groups, n_groups, params, grads, nullptr, found_inf_dev, stream);
+}
+
+int apexw_step_scaled(apexw_t h, const apexw_group *groups, int32_t n_groups,
+                      void *const *params, const void *const *grads,
+                      const float *inv_scale_dev, const float *found_inf_dev, void *stream) {
     if (!h) return fail(APEXW_EINVAL, "handle is NULL");
     if (n_groups != h->n_groups)
         return fail(APEXW_EINVAL, "n_groups is %d, the handle was created with %d", n_groups,
@@ -472,49 +543,10 @@ int apexw_step(apexw_t h, const apexw_group *groups, int32_t n_groups, void *con
         if (params[i] == nullptr && h->numel[i] > 0)
             return fail(APEXW_EINVAL, "params[%d] is NULL", i);
 
-    const size_t n = (size_t)h->n;
-    const bool params_changed =
-        !h->have_params || (n && std::memcmp(h->last_params.data(), params, n * sizeof(void *)));
-    const bool grads_changed =
-        !h->have_grads || (n && std::memcmp(h->last_grads.data(), grads, n * sizeof(void *)));
-
     DeviceGuard guard(h->device);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (n && (params_changed || grads_changed)) {
-        const int s = h->next_slot;
-        if (h->ev_pending[s]) HIP_TRY(hipEventSynchronize(h->ev[s]));
-        char *slot = h->pinned + (int64_t)s * h->slot_bytes;
-        int64_t begin = h->wl.grads, end = h->wl.grads + (int64_t)n * 8;
-        if (params_changed) {
-            for (int32_t i = 0; i < h->n; ++i) {
-                TensorDesc &d = h->desc[i];
-                std::memset(&d, 0, sizeof d);
-                d.param = params[i];
-                d.m = h->state + h->layout[i].m;
-                d.v = h->state + h->layout[i].v;
-                d.m_scale = h->layout[i].m_scale >= 0
-                                ? reinterpret_cast<float *>(h->state + h->layout[i].m_scale)
-                                : nullptr;
-                d.v_scale = h->layout[i].v_scale >= 0
-                                ? reinterpret_cast<float *>(h->state + h->layout[i].v_scale)
-                                : nullptr;
-                d.numel = h->numel[i];
-                d.first_tile = h->first_tile[i];
-                d.group = h->group_of[i];
-            }
-            std::memcpy(slot + h->wl.desc, h->desc.data(), n * sizeof(TensorDesc));
-            begin = h->wl.desc;
-        }
-        std::memcpy(slot + h->wl.grads, grads, n * sizeof(void *));
-        HIP_TRY(hipMemcpyAsync(h->ws + begin, slot + begin, (size_t)(end - begin),
-                               hipMemcpyHostToDevice, st));
-        HIP_TRY(hipEventRecord(h->ev[s], st));
-        h->ev_pending[s] = true;
-        h->next_slot = (s + 1) % apexw_opt::kRing;
-        std::memcpy(h->last_params.data(), params, n * sizeof(void *));
-        std::memcpy(h->last_grads.data(), grads, n * sizeof(void *));
-        h->have_params = h->have_grads = true;
-    }
+    int rc = upload_pointer_tables(h, params, grads, st);
+    if (rc) return rc;
 
     bool any_grad = false;
     for (int32_t i = 0; i < h->n && !any_grad; ++i) any_grad = grads[i] != nullptr;
@@ -526,11 +558,12 @@ int apexw_step(apexw_t h, const apexw_group *groups, int32_t n_groups, void *con
     a.records = reinterpret_cast<StepRecord *>(h->ws + h->wl.records);
     a.steps = reinterpret_cast<int32_t *>(h->state + h->steps_off);
     a.found_inf = found_inf_dev;
+    a.inv_scale = inv_scale_dev;
     a.n_tensors = h->n;
     hipLaunchKernelGGL(adamw_prepare_kernel, dim3((unsigned)ceil_div(h->n, kPrepThreads)),
                        dim3(kPrepThreads), 0, st, a);
     HIP_TRY(hipGetLastError());
-    const int64_t cap = h->wg_override > 0 ? h->wg_override : kMaxGrid;
+    const int64_t cap = launch_cap(h);
     for (const Launch &L : h->launches) {
         // residency cap: the dynamic LDS a workgroup reserves (it uses none)
         const int occ = h->occupancy > 0 ? h->occupancy : default_occupancy(h->fmt, L.pt, L.gt);
@@ -548,6 +581,43 @@ int apexw_step(apexw_t h, const apexw_group *groups, int32_t n_groups, void *con
         const bool streaming = h->cache_policy == 0 ? h->streaming_auto : h->cache_policy == 1;
         hipLaunchKernelGGL(kernel_for(h->fmt, L.pt, L.gt, streaming), dim3((unsigned)wg), dim3(kThreads),
                            lds, st, a);
+        HIP_TRY(hipGetLastError());
+    }
+    return APEXW_OK;
+}
+
+int apexw_unscale_check(apexw_t h, const void *const *grads, const float *inv_scale_dev,
+                        float *found_inf_dev, void *stream) {
+    if (!h) return fail(APEXW_EINVAL, "handle is NULL");
+    if (!found_inf_dev) return fail(APEXW_EINVAL, "found_inf_dev is NULL");
+    if (h->n > 0 && !grads) return fail(APEXW_EINVAL, "grads must not be NULL");
+    DeviceGuard guard(h->device);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int rc = upload_pointer_tables(h, nullptr, grads, st);
+    if (rc) return rc;
+    KernelArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.desc = reinterpret_cast<const TensorDesc *>(h->ws + h->wl.desc);
+    a.grads = reinterpret_cast<const void *const *>(h->ws + h->wl.grads);
+    a.tile_tensor = reinterpret_cast<const int32_t *>(h->ws + h->wl.tiles);
+    a.inv_scale = inv_scale_dev;
+    a.found_inf_out = found_inf_dev;
+    const bool streaming = h->cache_policy == 0 ? h->streaming_auto : h->cache_policy == 1;
+    for (const Launch &L : h->launches) {
+        if (L.tile_count == 0) continue;
+        bool any = false;
+        for (int32_t j = 0; j < L.tensor_count && !any; ++j)
+            any = grads[h->tensor_list[L.tensor_begin + j]] != nullptr;
+        if (!any) continue;
+        a.tile_begin = L.tile_begin;
+        a.tile_count = L.tile_count;
+        a.table_begin = L.table_begin;
+        a.table_stride = L.table_stride;
+        const int64_t wg = std::min<int64_t>(L.tile_count, launch_cap(h));
+        kernel_fn k = L.gt == APEXW_F32
+                          ? (streaming ? unscale_check_kernel<APEXW_F32, true> : unscale_check_kernel<APEXW_F32, false>)
+                          : (streaming ? unscale_check_kernel<APEXW_BF16, true> : unscale_check_kernel<APEXW_BF16, false>);
+        hipLaunchKernelGGL(k, dim3((unsigned)wg), dim3(kThreads), 0, st, a);
         HIP_TRY(hipGetLastError());
     }
     return APEXW_OK;

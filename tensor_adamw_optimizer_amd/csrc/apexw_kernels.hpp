@@ -94,7 +94,8 @@ struct StepRecord {
     float beta1, one_minus_beta1, beta2, one_minus_beta2;
     float lr, decay, eps;
     float bc1, bc2;                  // 1 - beta1^t, 1 - beta2^t
-    float pad_[5];
+    float inv_scale;                 // grads are unscaled by this first
+    float pad_[4];
 };
 static_assert(sizeof(StepRecord) == 64, "step record is one 64-byte record");
 
@@ -105,6 +106,8 @@ struct KernelArgs {
     StepRecord *records;             // per tensor, rewritten every step
     int32_t *steps;                  // int32 step counter per tensor
     const float *found_inf;          // nullptr: never skip
+    const float *inv_scale;          // nullptr: 1 (grads are not scaled)
+    float *found_inf_out;            // unscale check: set to 1 on a non-finite
     int64_t tile_begin;              // this launch's tiles: [begin, begin+count)
     int64_t tile_count;
     int64_t table_begin;             // this launch's part of tile_tensor
@@ -119,6 +122,7 @@ struct StepScalars {
     float beta1, one_minus_beta1, beta2, one_minus_beta2;
     float lr, decay, eps;
     float bc1, bc2;                  // 1 - beta1^t, 1 - beta2^t (fp32)
+    float inv_scale;                 // 1 unless grads arrive scaled
 };
 
 // beta^n in fp64: square-and-multiply from the least significant bit.
@@ -143,13 +147,16 @@ __device__ __forceinline__ StepScalars step_scalars(const StepRecord &r) {
     s.eps = r.eps;
     s.bc1 = r.bc1;
     s.bc2 = r.bc2;
+    s.inv_scale = r.inv_scale;
     return s;
 }
 
 // The AdamW update of one element (M041 section 02), fp32, each operation
-// rounded, evaluated left to right as printed.
-__device__ __forceinline__ void adamw_update(float &theta, float g, float &m,
+// rounded, evaluated left to right as printed, on the unscaled grad (the
+// mixed-precision recipe of M041 section 06; multiplying by 1 is exact).
+__device__ __forceinline__ void adamw_update(float &theta, float g_scaled, float &m,
                                              float &v, const StepScalars &s) {
+    const float g = g_scaled * s.inv_scale;
     m = s.beta1 * m + s.one_minus_beta1 * g;
     v = s.beta2 * v + (s.one_minus_beta2 * g) * g;
     const float m_hat = m / s.bc1;
@@ -414,6 +421,7 @@ __global__ __launch_bounds__(kPrepThreads) void adamw_prepare_kernel(KernelArgs 
         r.eps = g.eps;
         r.bc1 = (float)(1.0 - pow_uint(g.beta1_d, (uint32_t)t));
         r.bc2 = (float)(1.0 - pow_uint(g.beta2_d, (uint32_t)t));
+        r.inv_scale = a.inv_scale != nullptr ? *a.inv_scale : 1.0f;
     }
     a.records[i] = r;
 }
@@ -474,6 +482,48 @@ __global__ __launch_bounds__(kThreads) void adamw_step_kernel(KernelArgs a) {
         if (k >= a.tile_count) break;
         i = tile_tensor[table_pos(a, k)];
     }
+}
+
+// Mixed-precision recipe before the update (M041 section 06; Apex guide
+// 4.3): unscale every present grad by inv_scale and set *found_inf_out to 1
+// if any unscaled value is an infinity or a NaN.  The flag is only ever set
+// (the caller clears it), by plain stores of the same value; grads are not
+// rewritten -- the update applies inv_scale itself.  One wave per tile, the
+// tiles of one (param, grad) dtype launch.
+template <int GT, bool NT>
+__global__ __launch_bounds__(kThreads) void unscale_check_kernel(KernelArgs a) {
+    const APEXW_CONST int32_t *tile_tensor = cptr<int32_t>(a.tile_tensor);
+    const APEXW_CONST uint64_t *grads = cptr<uint64_t>(a.grads);
+    const float inv = a.inv_scale != nullptr ? *a.inv_scale : 1.0f;
+    int64_t k = blockIdx.x;
+    bool bad = false;
+    for (;;) {
+        const int32_t i = tile_tensor[table_pos(a, k)];
+        const void *grad = reinterpret_cast<const void *>(grads[i]);
+        const TensorDesc d = load_uniform(a.desc, i);
+        const int64_t base = (a.tile_begin + k - d.first_tile) * kTile;
+        const int64_t left = d.numel - base;
+        const int n = left < kTile ? (int)left : kTile;
+        asm volatile("" ::"s"(grad));
+        if (grad != nullptr && n > 0) {
+            const int off = threadIdx.x * kVec;
+            float g[kVec];
+            if ((((uintptr_t)grad) & 15u) == 0u && off + kVec <= n) {
+                load4<GT, NT>(grad, base + off, g);
+            } else {
+#pragma unroll
+                for (int j = 0; j < kVec; ++j) g[j] = off + j < n ? load1<GT>(grad, base + off + j) : 0.0f;
+            }
+#pragma unroll
+            for (int j = 0; j < kVec; ++j) {
+                const float u = g[j] * inv;
+                bad |= (off + j < n) && !(fabsf(u) <= 3.40282347e38f);   // inf or NaN
+            }
+        }
+        k += gridDim.x;
+        if (k >= a.tile_count) break;
+    }
+    if (__any(bad) && threadIdx.x == 0) *gptr<float>(static_cast<void *>(a.found_inf_out)) = 1.0f;
 }
 
 // Zero fill of the state buffer (used once, at creation).
