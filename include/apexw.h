@@ -209,6 +209,47 @@ int apexw_unscale_check(apexw_t h, const void *const *grads,
                         void *stream);
 
 /*
+ * apexw_step_scaled with the group hyperparameters in device memory:
+ * groups_dev points to n_groups apexw_group records that the GPU reads when
+ * the step runs, and the fp32 scalars are formed there exactly as the host
+ * forms them, so results are bit-identical to apexw_step_scaled with the same
+ * values.  This makes the whole step capturable in a hipGraph with a learning
+ * rate that changes between replays (capturable mode of the Apex guide,
+ * section 4.2; the step counters already live on the device).  The values are
+ * not validated (they are never read by the host): out-of-range
+ * hyperparameters give unspecified numbers, never a fault.  Under stream
+ * capture the parameter and grad pointers must equal those of the previous
+ * call on the handle (the pointer tables are uploaded only outside capture);
+ * otherwise APEXW_EINVAL.
+ */
+int apexw_step_device(apexw_t h, const apexw_group *groups_dev, int32_t n_groups,
+                      void *const *params, const void *const *grads,
+                      const float *inv_scale_dev, const float *found_inf_dev,
+                      void *stream);
+
+/*
+ * Checkpoint of the optimizer state (the M041 page, section 08: a checkpoint
+ * carries the state dtype and scales, the step counters and the recipe, not
+ * only the parameters).  apexw_export_bytes gives the size of the blob;
+ * apexw_export_state writes it to host memory dst_host: a header (format
+ * version, state format, tensor count, group count), every tensor's numel,
+ * parameter and grad dtype and group, the recipe `groups` (n_groups records,
+ * usually those of the last step), and the raw state buffer (moments, 8-bit
+ * scales, step counters).  It queues a device-to-host copy on `stream` and
+ * waits for it.  apexw_import_state checks that a blob was written for a
+ * handle of the same format, tensor sizes, dtypes and groups (APEXW_EINVAL
+ * otherwise, nothing written), copies its state into the handle's state
+ * buffer (waits for the copy), and returns the recipe in groups_out (may be
+ * NULL; else n_groups must match).  A run resumed from a blob continues
+ * bit for bit as the uninterrupted run.
+ */
+int apexw_export_bytes(apexw_t h, size_t *out_bytes);
+int apexw_export_state(apexw_t h, const apexw_group *groups, int32_t n_groups,
+                       void *dst_host, size_t dst_bytes, void *stream);
+int apexw_import_state(apexw_t h, const void *src_host, size_t src_bytes,
+                       apexw_group *groups_out, int32_t n_groups, void *stream);
+
+/*
  * Launch geometry of the handle: tile size in elements (256; one workgroup of
  * one wave64 per tile), number of tiles, and the largest workgroup count of
  * its update launches.  Any pointer may be NULL.

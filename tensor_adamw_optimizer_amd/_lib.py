@@ -36,6 +36,7 @@ APEXW_MAX_GROUPS = 32
 ENTRY_POINTS = (
     "apexw_state_bytes", "apexw_state_layout", "apexw_workspace_bytes",
     "apexw_create", "apexw_step", "apexw_step_scaled", "apexw_unscale_check",
+    "apexw_step_device", "apexw_export_bytes", "apexw_export_state", "apexw_import_state",
     "apexw_launch_info", "apexw_set_workgroups",
     "apexw_set_occupancy", "apexw_get_occupancy", "apexw_set_cache_policy",
     "apexw_destroy", "apexw_last_error",
@@ -81,6 +82,10 @@ def lib() -> ctypes.CDLL:
         L.apexw_step.argtypes = [P, P, I32, P, P, P, P]
         L.apexw_step_scaled.argtypes = [P, P, I32, P, P, P, P, P]
         L.apexw_unscale_check.argtypes = [P, P, P, P, P]
+        L.apexw_step_device.argtypes = [P, P, I32, P, P, P, P, P]
+        L.apexw_export_bytes.argtypes = [P, ctypes.POINTER(SZ)]
+        L.apexw_export_state.argtypes = [P, P, I32, P, SZ, P]
+        L.apexw_import_state.argtypes = [P, P, SZ, P, I32, P]
         L.apexw_launch_info.argtypes = [P, ctypes.POINTER(I32), ctypes.POINTER(I32),
                                         ctypes.POINTER(I32)]
         L.apexw_set_workgroups.argtypes = [P, I32]
@@ -181,6 +186,37 @@ def apexw_unscale_check(handle: int, grads_arr, inv_scale_ptr: int, found_inf_pt
     _check(lib().apexw_unscale_check(handle, grads_arr, inv_scale_ptr or None,
                                      found_inf_ptr or None, stream or None),
            "apexw_unscale_check")
+
+
+def apexw_step_device(handle: int, groups_dev_ptr: int, n_groups: int, params_arr, grads_arr,
+                      inv_scale_ptr: int = 0, found_inf_ptr: int = 0, stream: int = 0) -> None:
+    """groups_dev_ptr: device address of n_groups apexw_group records."""
+    _check(lib().apexw_step_device(handle, groups_dev_ptr, n_groups, params_arr, grads_arr,
+                                   inv_scale_ptr or None, found_inf_ptr or None, stream or None),
+           "apexw_step_device")
+
+
+def apexw_export_bytes(handle: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().apexw_export_bytes(handle, ctypes.byref(out)), "apexw_export_bytes")
+    return out.value
+
+
+def apexw_export_state(handle: int, groups_arr, n_groups: int, stream: int = 0) -> bytes:
+    """The checkpoint blob as bytes."""
+    size = apexw_export_bytes(handle)
+    buf = ctypes.create_string_buffer(size)
+    _check(lib().apexw_export_state(handle, groups_arr, n_groups, buf, size, stream or None),
+           "apexw_export_state")
+    return buf.raw
+
+
+def apexw_import_state(handle: int, blob: bytes, n_groups: int, stream: int = 0):
+    """Load a blob; returns the recipe as a list of apexw_group records."""
+    groups = (apexw_group * max(1, n_groups))()
+    _check(lib().apexw_import_state(handle, blob, len(blob), groups, n_groups, stream or None),
+           "apexw_import_state")
+    return list(groups[:n_groups])
 
 
 def apexw_launch_info(handle: int):

@@ -290,6 +290,11 @@ int upload_pointer_tables(apexw_opt *h, void *const *params, const void *const *
     const bool grads_changed =
         !h->have_grads || std::memcmp(h->last_grads.data(), grads, n * sizeof(void *));
     if (!params_changed && !grads_changed) return APEXW_OK;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    HIP_TRY(hipStreamIsCapturing(st, &cap));
+    if (cap != hipStreamCaptureStatusNone)
+        return fail(APEXW_EINVAL, "parameter or grad pointers changed while the stream is being "
+                                  "captured; call once with these pointers before capturing");
     const int s = h->next_slot;
     if (h->ev_pending[s]) HIP_TRY(hipEventSynchronize(h->ev[s]));
     char *slot = h->pinned + (int64_t)s * h->slot_bytes;
@@ -316,6 +321,10 @@ int upload_pointer_tables(apexw_opt *h, void *const *params, const void *const *
 int launch_cap(const apexw_opt *h) { return h->wg_override > 0 ? h->wg_override : (int)kMaxGrid; }
 
 }  // namespace
+
+static int step_impl(apexw_t h, const apexw_group *groups, const apexw_group *groups_dev,
+                     int32_t n_groups, void *const *params, const void *const *grads,
+                     const float *inv_scale_dev, const float *found_inf_dev, void *stream);
 
 // ======================================================================= ABI
 
@@ -512,16 +521,34 @@ int apexw_step(apexw_t h, const apexw_group *groups, int32_t n_groups, void *con
 int apexw_step_scaled(apexw_t h, const apexw_group *groups, int32_t n_groups,
                       void *const *params, const void *const *grads,
                       const float *inv_scale_dev, const float *found_inf_dev, void *stream) {
+    return step_impl(h, groups, nullptr, n_groups, params, grads, inv_scale_dev, found_inf_dev,
+                     stream);
+}
+
+int apexw_step_device(apexw_t h, const apexw_group *groups_dev, int32_t n_groups,
+                      void *const *params, const void *const *grads,
+                      const float *inv_scale_dev, const float *found_inf_dev, void *stream) {
+    if (!groups_dev) return fail(APEXW_EINVAL, "groups_dev is NULL");
+    return step_impl(h, nullptr, groups_dev, n_groups, params, grads, inv_scale_dev,
+                     found_inf_dev, stream);
+}
+
+}  // extern "C"
+
+static int step_impl(apexw_t h, const apexw_group *groups, const apexw_group *groups_dev,
+                     int32_t n_groups, void *const *params, const void *const *grads,
+                     const float *inv_scale_dev, const float *found_inf_dev, void *stream) {
     if (!h) return fail(APEXW_EINVAL, "handle is NULL");
     if (n_groups != h->n_groups)
         return fail(APEXW_EINVAL, "n_groups is %d, the handle was created with %d", n_groups,
                     h->n_groups);
-    if (!groups) return fail(APEXW_EINVAL, "groups is NULL");
+    if (!groups && !groups_dev) return fail(APEXW_EINVAL, "groups is NULL");
     if (h->n > 0 && (!params || !grads)) return fail(APEXW_EINVAL, "params and grads must not be NULL");
 
     KernelArgs a;
     std::memset(&a, 0, sizeof a);
-    for (int32_t g = 0; g < n_groups; ++g) {
+    a.groups_dev = groups_dev;
+    for (int32_t g = 0; groups && g < n_groups; ++g) {
         const apexw_group &G = groups[g];
         if (!finite_nonneg(G.lr) || !finite_nonneg(G.eps) || !finite_nonneg(G.weight_decay) ||
             !(G.beta1 >= 0.0 && G.beta1 < 1.0) || !(G.beta2 >= 0.0 && G.beta2 < 1.0))
@@ -586,6 +613,8 @@ int apexw_step_scaled(apexw_t h, const apexw_group *groups, int32_t n_groups,
     return APEXW_OK;
 }
 
+extern "C" {
+
 int apexw_unscale_check(apexw_t h, const void *const *grads, const float *inv_scale_dev,
                         float *found_inf_dev, void *stream) {
     if (!h) return fail(APEXW_EINVAL, "handle is NULL");
@@ -620,6 +649,111 @@ int apexw_unscale_check(apexw_t h, const void *const *grads, const float *inv_sc
         hipLaunchKernelGGL(k, dim3((unsigned)wg), dim3(kThreads), 0, st, a);
         HIP_TRY(hipGetLastError());
     }
+    return APEXW_OK;
+}
+
+// ---------------------------------------------------------------- checkpoint
+//
+// Blob: header | numel[n] int64 | param_dtype[n] int32 | grad_dtype[n] int32
+// | group_of[n] int32 | groups[n_groups] apexw_group | pad to 256 | the raw
+// state buffer (moments, block scales, step counters) in the layout of
+// apexw_state_layout.
+
+namespace {
+
+struct BlobHeader {
+    char magic[8];
+    uint32_t version;
+    int32_t fmt;
+    int32_t n_tensors;
+    int32_t n_groups;
+    uint64_t state_bytes;
+    uint64_t payload_offset;
+};
+const char kMagic[8] = {'A', 'P', 'E', 'X', 'W', 'S', 'T', '1'};
+
+uint64_t blob_payload_offset(const apexw_opt *h) {
+    const uint64_t n = (uint64_t)h->n;
+    const uint64_t meta = sizeof(BlobHeader) + n * (8 + 4 + 4 + 4) +
+                          (uint64_t)h->n_groups * sizeof(apexw_group);
+    return (uint64_t)round_up((int64_t)meta, kTableAlign);
+}
+
+uint64_t state_total(const apexw_opt *h) { return (uint64_t)(h->steps_off + 4 * (int64_t)h->n); }
+
+}  // namespace
+
+int apexw_export_bytes(apexw_t h, size_t *out_bytes) {
+    if (!h || !out_bytes) return fail(APEXW_EINVAL, "NULL argument");
+    *out_bytes = (size_t)(blob_payload_offset(h) + state_total(h));
+    return APEXW_OK;
+}
+
+int apexw_export_state(apexw_t h, const apexw_group *groups, int32_t n_groups, void *dst_host,
+                       size_t dst_bytes, void *stream) {
+    if (!h || !dst_host || !groups) return fail(APEXW_EINVAL, "NULL argument");
+    if (n_groups != h->n_groups)
+        return fail(APEXW_EINVAL, "n_groups is %d, the handle has %d", n_groups, h->n_groups);
+    const uint64_t off = blob_payload_offset(h), sb = state_total(h);
+    if (dst_bytes < off + sb)
+        return fail(APEXW_ENOSPC, "destination has %zu bytes, needs %llu", dst_bytes,
+                    (unsigned long long)(off + sb));
+    char *p = static_cast<char *>(dst_host);
+    std::memset(p, 0, (size_t)off);
+    BlobHeader hd;
+    std::memcpy(hd.magic, kMagic, 8);
+    hd.version = 1;
+    hd.fmt = h->fmt;
+    hd.n_tensors = h->n;
+    hd.n_groups = h->n_groups;
+    hd.state_bytes = sb;
+    hd.payload_offset = off;
+    std::memcpy(p, &hd, sizeof hd);
+    char *q = p + sizeof hd;
+    const size_t n = (size_t)h->n;
+    std::memcpy(q, h->numel.data(), n * 8); q += n * 8;
+    std::memcpy(q, h->pdt.data(), n * 4); q += n * 4;
+    std::memcpy(q, h->gdt.data(), n * 4); q += n * 4;
+    std::memcpy(q, h->group_of.data(), n * 4); q += n * 4;
+    std::memcpy(q, groups, (size_t)n_groups * sizeof(apexw_group));
+    DeviceGuard guard(h->device);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (sb > 0) HIP_TRY(hipMemcpyAsync(p + off, h->state, (size_t)sb, hipMemcpyDeviceToHost, st));
+    HIP_TRY(hipStreamSynchronize(st));
+    return APEXW_OK;
+}
+
+int apexw_import_state(apexw_t h, const void *src_host, size_t src_bytes, apexw_group *groups_out,
+                       int32_t n_groups, void *stream) {
+    if (!h || !src_host) return fail(APEXW_EINVAL, "NULL argument");
+    const char *p = static_cast<const char *>(src_host);
+    BlobHeader hd;
+    if (src_bytes < sizeof hd) return fail(APEXW_EINVAL, "blob too short for its header");
+    std::memcpy(&hd, p, sizeof hd);
+    if (std::memcmp(hd.magic, kMagic, 8) != 0 || hd.version != 1)
+        return fail(APEXW_EINVAL, "not an optimizer-state blob of this format");
+    if (hd.fmt != h->fmt || hd.n_tensors != h->n || hd.n_groups != h->n_groups)
+        return fail(APEXW_EINVAL, "blob is for format %d, %d tensors, %d groups; the handle has "
+                    "%d, %d, %d", hd.fmt, hd.n_tensors, hd.n_groups, h->fmt, h->n, h->n_groups);
+    const uint64_t off = blob_payload_offset(h), sb = state_total(h);
+    if (hd.payload_offset != off || hd.state_bytes != sb || src_bytes < off + sb)
+        return fail(APEXW_EINVAL, "blob sizes do not match the handle's state layout");
+    const char *q = p + sizeof hd;
+    const size_t n = (size_t)h->n;
+    if (std::memcmp(q, h->numel.data(), n * 8) != 0 ||
+        std::memcmp(q + n * 8, h->pdt.data(), n * 4) != 0 ||
+        std::memcmp(q + n * 12, h->gdt.data(), n * 4) != 0 ||
+        std::memcmp(q + n * 16, h->group_of.data(), n * 4) != 0)
+        return fail(APEXW_EINVAL, "blob's tensor sizes, dtypes or groups differ from the handle's");
+    if (groups_out) {
+        if (n_groups != h->n_groups)
+            return fail(APEXW_EINVAL, "n_groups is %d, the handle has %d", n_groups, h->n_groups);
+        std::memcpy(groups_out, q + n * 20, (size_t)n_groups * sizeof(apexw_group));
+    }
+    DeviceGuard guard(h->device);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (sb > 0) HIP_TRY(hipMemcpyAsync(h->state, p + off, (size_t)sb, hipMemcpyHostToDevice, st));
+    HIP_TRY(hipStreamSynchronize(st));
     return APEXW_OK;
 }
 

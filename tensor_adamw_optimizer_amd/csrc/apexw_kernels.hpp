@@ -108,6 +108,7 @@ struct KernelArgs {
     const float *found_inf;          // nullptr: never skip
     const float *inv_scale;          // nullptr: 1 (grads are not scaled)
     float *found_inf_out;            // unscale check: set to 1 on a non-finite
+    const apexw_group *groups_dev;   // non-null: hyperparameters read on the device
     int64_t tile_begin;              // this launch's tiles: [begin, begin+count)
     int64_t tile_count;
     int64_t table_begin;             // this launch's part of tile_tensor
@@ -395,6 +396,24 @@ __device__ __forceinline__ void tile_q8(const TensorDesc &d, const void *grad,
 
 // ---------------------------------------------------------------- kernels
 
+// The fp32 scalars of a group, formed from its fp64 hyperparameters exactly
+// as the host forms them (fp64 operations, then one rounding to fp32), for
+// hyperparameters that live in device memory (graph-capturable steps).
+__device__ __forceinline__ GroupScalars group_scalars(const apexw_group &G) {
+    GroupScalars S;
+    S.beta1 = (float)G.beta1;
+    S.one_minus_beta1 = (float)(1.0 - G.beta1);
+    S.beta2 = (float)G.beta2;
+    S.one_minus_beta2 = (float)(1.0 - G.beta2);
+    S.lr = (float)G.lr;
+    S.decay = (float)(1.0 - G.lr * G.weight_decay);
+    S.eps = (float)G.eps;
+    S.pad_ = 0.0f;
+    S.beta1_d = G.beta1;
+    S.beta2_d = G.beta2;
+    return S;
+}
+
 // Before the update, one lane per tensor: unless found_inf is set (M041
 // section 06, Apex guide 4.3), advance t of each tensor with a grad and write
 // its step record (grad pointer, group scalars, bias corrections from fp64
@@ -410,7 +429,8 @@ __global__ __launch_bounds__(kPrepThreads) void adamw_prepare_kernel(KernelArgs 
     if (grad != nullptr) {
         const int32_t t = a.steps[i] + 1;
         a.steps[i] = t;
-        const GroupScalars &g = a.groups[a.desc[i].group];
+        const int32_t gi = a.desc[i].group;
+        const GroupScalars g = a.groups_dev != nullptr ? group_scalars(a.groups_dev[gi]) : a.groups[gi];
         r.grad = grad;
         r.beta1 = g.beta1;
         r.one_minus_beta1 = g.one_minus_beta1;
