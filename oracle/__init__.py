@@ -81,6 +81,14 @@ def lib():
         L.oracle_adamw_step_scaled.argtypes = [
             ctypes.c_int32, P, P, P, P, P, P, P, ctypes.c_int32, ctypes.c_int32,
             P, P, P, P, P, ctypes.c_float, ctypes.c_int32]
+        L.oracle_adamw_step_clipped.restype = ctypes.c_int32
+        L.oracle_adamw_step_clipped.argtypes = [
+            ctypes.c_int32, P, P, P, P, P, P, P, ctypes.c_int32, ctypes.c_int32,
+            P, P, P, P, P, ctypes.c_float, ctypes.c_float, ctypes.c_int32]
+        L.oracle_grad_norm.restype = ctypes.c_double
+        L.oracle_grad_norm.argtypes = [ctypes.c_int32, P, P, P, ctypes.c_float]
+        L.oracle_clip_coef.restype = ctypes.c_float
+        L.oracle_clip_coef.argtypes = [ctypes.c_double, ctypes.c_double]
         L.oracle_unscale_check.restype = ctypes.c_int32
         L.oracle_unscale_check.argtypes = [ctypes.c_int32, P, P, P, ctypes.c_float]
         L.oracle_adamw_step_three_loops.restype = ctypes.c_int32
@@ -229,11 +237,23 @@ class OracleAdamW:
         return bool(lib().oracle_unscale_check(self.n, _ptr(self._numel), _ptr(self._gdt),
                                                _ptr_array(grads), inv_scale))
 
+    def grad_norm(self, grads: Sequence[Optional[np.ndarray]], inv_scale: float = 1.0) -> float:
+        """Euclidean norm of the unscaled present grads (fp64 accumulation)."""
+        assert len(grads) == self.n
+        return lib().oracle_grad_norm(self.n, _ptr(self._numel), _ptr(self._gdt),
+                                      _ptr_array(grads), inv_scale)
+
+    @staticmethod
+    def clip_coef(norm: float, max_norm: float) -> float:
+        return lib().oracle_clip_coef(norm, max_norm)
+
     def step(self, thetas: Sequence[np.ndarray],
              grads: Sequence[Optional[np.ndarray]], groups,
-             found_inf: bool = False, inv_scale: Optional[float] = None) -> None:
+             found_inf: bool = False, inv_scale: Optional[float] = None,
+             clip_coef: Optional[float] = None) -> None:
         """Update ``thetas`` (in place) and the held state by one call; with
-        ``inv_scale`` the grads are unscaled (g * inv_scale in fp32) first."""
+        ``inv_scale`` the grads are unscaled (g * inv_scale in fp32) first,
+        with ``clip_coef`` the unscaled grads are then multiplied by it."""
         assert len(thetas) == self.n and len(grads) == self.n
         for i, th in enumerate(thetas):
             want = np.uint16 if self.param_dtype[i] == "bf16" else np.float32
@@ -247,10 +267,13 @@ class OracleAdamW:
                 _groups(groups), len(groups), STATE_CODE[self.state_fmt],
                 _ptr_array(self.m), _ptr_array(self.v), _ptr_array(self.m_scale),
                 _ptr_array(self.v_scale), _ptr(self.t))
-        if inv_scale is None:
+        if inv_scale is None and clip_coef is None:
             rc = lib().oracle_adamw_step(*args, int(bool(found_inf)))
-        else:
+        elif clip_coef is None:
             rc = lib().oracle_adamw_step_scaled(*args, inv_scale, int(bool(found_inf)))
+        else:
+            rc = lib().oracle_adamw_step_clipped(
+                *args, 1.0 if inv_scale is None else inv_scale, clip_coef, int(bool(found_inf)))
         if rc != 0:
             raise ValueError("oracle_adamw_step rejected its arguments")
 

@@ -223,11 +223,11 @@ static void store_value(int32_t dtype, void *base, int64_t i, float x)
 static void update_tensor_dense(int64_t n, int32_t pdt, void *theta,
                                 int32_t gdt, const void *grad, int32_t sdt,
                                 void *m, void *v, const step_scalars *s,
-                                float inv_scale)
+                                float inv_scale, float clip_coef)
 {
     for (int64_t i = 0; i < n; ++i) {
         float th = load_value(pdt, theta, i);
-        float g = load_value(gdt, grad, i) * inv_scale;
+        float g = (load_value(gdt, grad, i) * inv_scale) * clip_coef;
         float mi = load_value(sdt, m, i);
         float vi = load_value(sdt, v, i);
         adamw_element(&th, g, &mi, &vi, s);
@@ -241,7 +241,7 @@ static void update_tensor_dense(int64_t n, int32_t pdt, void *theta,
 static void update_tensor_q8(int64_t n, int32_t pdt, void *theta, int32_t gdt,
                              const void *grad, int8_t *mq, uint8_t *vq,
                              float *ms, float *vs, const step_scalars *s,
-                             float inv_scale)
+                             float inv_scale, float clip_coef)
 {
     float mf[ORACLE_BLOCK], vf[ORACLE_BLOCK];
     int64_t nblocks = (n + ORACLE_BLOCK - 1) / ORACLE_BLOCK;
@@ -252,7 +252,7 @@ static void update_tensor_q8(int64_t n, int32_t pdt, void *theta, int32_t gdt,
         oracle_dequantize_unsigned(len, vq + lo, vs[b], vf);
         for (int64_t j = 0; j < len; ++j) {
             float th = load_value(pdt, theta, lo + j);
-            float g = load_value(gdt, grad, lo + j) * inv_scale;
+            float g = (load_value(gdt, grad, lo + j) * inv_scale) * clip_coef;
             adamw_element(&th, g, &mf[j], &vf[j], s);
             store_value(pdt, theta, lo + j, th);
         }
@@ -297,6 +297,15 @@ int32_t oracle_unscale_check(int32_t n_tensors, const int64_t *numel,
  *
  * Returns 0, or -1 on an argument it does not understand.
  */
+int oracle_adamw_step_clipped(int32_t n_tensors, const int64_t *numel,
+                              const int32_t *param_dtype, void *const *theta,
+                              const int32_t *grad_dtype, const void *const *grad,
+                              const int32_t *group_of, const oracle_group *groups,
+                              int32_t n_groups, int32_t state_fmt, void *const *m,
+                              void *const *v, float *const *m_scale,
+                              float *const *v_scale, int32_t *t, float inv_scale,
+                              float clip_coef, int32_t found_inf);
+
 int oracle_adamw_step_scaled(int32_t n_tensors, const int64_t *numel,
                              const int32_t *param_dtype, void *const *theta,
                              const int32_t *grad_dtype, const void *const *grad,
@@ -305,6 +314,58 @@ int oracle_adamw_step_scaled(int32_t n_tensors, const int64_t *numel,
                              void *const *v, float *const *m_scale,
                              float *const *v_scale, int32_t *t, float inv_scale,
                              int32_t found_inf)
+{
+    return oracle_adamw_step_clipped(n_tensors, numel, param_dtype, theta,
+                                     grad_dtype, grad, group_of, groups, n_groups,
+                                     state_fmt, m, v, m_scale, v_scale, t,
+                                     inv_scale, 1.0f, found_inf);
+}
+
+/*
+ * Global grad-norm clipping, the step the recipe of [M041 §06] places after
+ * the finite check (the pages name it but give no formula; reading: the
+ * plain one).  The norm is the Euclidean norm of all present unscaled grads,
+ * u = g * inv_scale rounded to fp32 as the update uses it, each square and
+ * the running sum in fp64, the square root in fp64.
+ */
+double oracle_grad_norm(int32_t n_tensors, const int64_t *numel,
+                        const int32_t *grad_dtype, const void *const *grad,
+                        float inv_scale)
+{
+    double sum = 0.0;
+    for (int32_t i = 0; i < n_tensors; ++i) {
+        if (grad[i] == NULL)
+            continue;
+        for (int64_t e = 0; e < numel[i]; ++e) {
+            double u = (double)(load_value(grad_dtype[i], grad[i], e) * inv_scale);
+            sum = sum + u * u;
+        }
+    }
+    return sqrt(sum);
+}
+
+/* Clip coefficient: max_norm / norm when the norm exceeds max_norm (fp64,
+ * rounded once to fp32), else 1 (also for a NaN norm). */
+float oracle_clip_coef(double norm, double max_norm)
+{
+    if (norm > max_norm)
+        return (float)(max_norm / norm);
+    return 1.0f;
+}
+
+/*
+ * One step on clipped, unscaled grads: every grad value becomes
+ * (g * inv_scale) * clip_coef, two rounded fp32 multiplies, before the
+ * update (inv_scale = clip_coef = 1 is the plain step).
+ */
+int oracle_adamw_step_clipped(int32_t n_tensors, const int64_t *numel,
+                              const int32_t *param_dtype, void *const *theta,
+                              const int32_t *grad_dtype, const void *const *grad,
+                              const int32_t *group_of, const oracle_group *groups,
+                              int32_t n_groups, int32_t state_fmt, void *const *m,
+                              void *const *v, float *const *m_scale,
+                              float *const *v_scale, int32_t *t, float inv_scale,
+                              float clip_coef, int32_t found_inf)
 {
     if (found_inf)
         return 0;                                   /* R3: skip everything */
@@ -319,11 +380,11 @@ int oracle_adamw_step_scaled(int32_t n_tensors, const int64_t *numel,
             int32_t sdt = state_fmt == ORACLE_STATE_F32 ? ORACLE_F32 : ORACLE_BF16;
             update_tensor_dense(numel[i], param_dtype[i], theta[i],
                                 grad_dtype[i], grad[i], sdt, m[i], v[i], &s,
-                                inv_scale);
+                                inv_scale, clip_coef);
         } else if (state_fmt == ORACLE_STATE_Q8) {
             update_tensor_q8(numel[i], param_dtype[i], theta[i], grad_dtype[i],
                              grad[i], (int8_t *)m[i], (uint8_t *)v[i],
-                             m_scale[i], v_scale[i], &s, inv_scale);
+                             m_scale[i], v_scale[i], &s, inv_scale, clip_coef);
         } else {
             return -1;
         }

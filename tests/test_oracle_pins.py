@@ -511,3 +511,89 @@ def test_amp_recipe_skip_on_overflow():
             after = [x.copy() for x in th] + [o.t.copy()]
             assert all(np.array_equal(a, b) for a, b in zip(before, after))
     assert list(o.t) == [5, 5]
+
+
+# ------------------------------------------------------------ clipping
+
+def test_grad_norm_against_exact_sum():
+    """The oracle's fp64 running sum against the exactly rounded sum of the
+    same fp32 products (math.fsum)."""
+    rng = np.random.default_rng(30)
+    sizes, gdt = [5000, 777, 1], ["f32", "bf16", "f32"]
+    o = OracleAdamW(sizes, ["f32"] * 3, gdt, [0, 0, 0], "f32")
+    for inv in (1.0, 1.0 / 1024.0, 1.0 / 3.0):
+        gs = [f32(rng.normal(0, 1, n) * np.exp(rng.uniform(-5, 5, n))) for n in sizes]
+        stored = [_as_dtype(g, d) for g, d in zip(gs, gdt)]
+        stored[2] = None if inv == 1.0 else stored[2]
+        u = []
+        for g, d in zip(stored, gdt):
+            if g is None:
+                continue
+            v = oracle.bf16_to_f32(g) if d == "bf16" else g
+            u.append((v * np.float32(inv)).astype(np.float64))
+        u = np.concatenate(u)
+        exact = math.sqrt(math.fsum((u * u).tolist()))
+        got = o.grad_norm(stored, inv)
+        assert abs(got - exact) <= 1e-13 * exact
+
+
+def test_clip_coef_cases():
+    c = OracleAdamW.clip_coef
+    assert c(0.0, 1.0) == 1.0                      # no grads: nothing to clip
+    assert c(0.5, 1.0) == 1.0 and c(1.0, 1.0) == 1.0
+    assert c(4.0, 1.0) == 0.25
+    assert c(3.0, 1.0) == np.float32(1.0 / 3.0)
+    assert c(float("nan"), 1.0) == 1.0
+    assert c(float("inf"), 1.0) == 0.0
+
+
+def test_clipped_step_scales_the_direction_only_through_g():
+    """With clip 2^-k (exact) the clipped step equals the plain step on grads
+    multiplied by 2^-k; a zero-grad-free first step is invariant to any clip
+    (m_hat / sqrt(v_hat) = sign(g)), which a clip applied to theta, m or the
+    update would break."""
+    rng = np.random.default_rng(31)
+    n = 900
+    grp = [Group(lr=1e-2, weight_decay=0.1)]
+    th0 = f32(rng.normal(0, 0.02, n))
+    g = f32(rng.normal(0, 1e-3, n))
+    a = OracleAdamW([n], ["f32"], ["f32"], [0], "f32")
+    b = OracleAdamW([n], ["f32"], ["f32"], [0], "f32")
+    tha, thb = th0.copy(), th0.copy()
+    a.step([tha], [g * np.float32(0.125)], grp)
+    b.step([thb], [g], grp, clip_coef=0.125)
+    assert np.array_equal(tha, thb) and np.array_equal(a.m[0], b.m[0])
+    grp0 = [Group(lr=1e-2, weight_decay=0.1, eps=0.0)]
+    c = OracleAdamW([n], ["f32"], ["f32"], [0], "f32")
+    thc = th0.copy()
+    c.step([thc], [g], grp0, clip_coef=0.3)
+    plain = OracleAdamW([n], ["f32"], ["f32"], [0], "f32")
+    thp = th0.copy()
+    plain.step([thp], [g], grp0)
+    # first step with eps = 0: the direction is sign(g) (to a few ulps),
+    # whatever the clip
+    assert np.max(np.abs(thc.astype(np.float64) - thp)) < 1e-8
+    assert not np.array_equal(c.m[0], plain.m[0])
+
+
+def test_clipped_amp_loop_against_fp64():
+    rng = np.random.default_rng(32)
+    n, inv, max_norm = 2000, 1.0 / 512.0, 0.02
+    grp = Group(lr=1e-2, weight_decay=0.01)
+    o = OracleAdamW([n], ["f32"], ["f32"], [0], "f32")
+    th = f32(rng.normal(0, 0.02, n))
+    st = [th.astype(np.float64), np.zeros(n), np.zeros(n), 0]
+    clipped = 0
+    for _ in range(12):
+        g = f32(rng.normal(0, 1e-3, n) * 512.0 * rng.uniform(0.2, 2.0))
+        norm = o.grad_norm([g], inv)
+        coef = OracleAdamW.clip_coef(norm, max_norm)
+        clipped += coef < 1.0
+        o.step([th], [g], [grp], inv_scale=inv, clip_coef=coef)
+        u = (g * np.float32(inv)).astype(np.float64)
+        un = np.sqrt(np.sum(u * u))
+        u64 = u * (max_norm / un if un > max_norm else 1.0)
+        st = list(ref64.adamw_fp64(st[0], u64, st[1], st[2], st[3], grp.lr, grp.beta1, grp.beta2,
+                                   grp.eps, grp.weight_decay))
+    assert 0 < clipped < 12
+    assert np.max(np.abs(th - st[0])) / np.max(np.abs(st[0])) <= 1e-5
