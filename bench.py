@@ -120,6 +120,8 @@ def main() -> int:
     ap.add_argument("--amp", action="store_true",
                     help="time the mixed-precision recipe: zero found_inf, unscale-and-check "
                          "pass, update on grads scaled by 2^16")
+    ap.add_argument("--clip", type=float, default=0.0,
+                    help="with --amp: also clip the global grad norm to this value")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, run a 1 GiB device copy 3x (counter calibration)")
@@ -178,8 +180,17 @@ def main() -> int:
         for g in grads:
             g.mul_(65536.0)
 
+    clip_coef = torch.ones(1, dtype=torch.float32, device=dev)
+
     def step():
-        if args.amp:
+        if args.amp and args.clip > 0:
+            found_inf.zero_()
+            L.apexw_clip_grad_norm(h, grads_arr, inv_scale.data_ptr(), args.clip,
+                                   found_inf.data_ptr(), 0, clip_coef.data_ptr(), stream.cuda_stream)
+            L.apexw_step_ex(h, groups_arr, len(w.groups), params_arr, grads_arr,
+                            inv_scale_ptr=inv_scale.data_ptr(), clip_coef_ptr=clip_coef.data_ptr(),
+                            found_inf_ptr=found_inf.data_ptr(), stream=stream.cuda_stream)
+        elif args.amp:
             found_inf.zero_()
             L.apexw_unscale_check(h, grads_arr, inv_scale.data_ptr(), found_inf.data_ptr(),
                                   stream.cuda_stream)
@@ -234,7 +245,7 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": w.name + ("+amp" if args.amp else ""),
+            "workload": w.name + ("+amp" if args.amp else "") + ("+clip" if args.amp and args.clip > 0 else ""),
             "tensors": len(w.shapes),
             "params": w.n_params,
             "param_dtype": "+".join(sorted(set(w.param_dtype))),
@@ -257,7 +268,7 @@ def main() -> int:
             "frac": gbps / HBM_PEAK_GBPS,
             "traffic": traffic,
             "algorithmic_bytes_per_launch": ab,
-            "kernel": "adamw_step_kernel" + (" + unscale_check_kernel" if args.amp else ""),
+            "kernel": "adamw_step_kernel" + ((" + grad_norm kernels" if args.clip > 0 else " + unscale_check_kernel") if args.amp else ""),
         },
     }
     L.apexw_destroy(h)

@@ -123,7 +123,8 @@ int apexw_state_layout(int32_t n_tensors, const int64_t *numel, int32_t fmt,
 
 /*
  * Bytes of device workspace apexw_create needs for this tensor list (tensor
- * table, grad-pointer table, per-tensor step records, tile table).  Same argument rules
+ * table, grad-pointer table, per-tensor step records, tile table, grad-norm
+ * partial sums).  Same argument rules
  * as apexw_state_bytes, minus fmt.
  */
 int apexw_workspace_bytes(int32_t n_tensors, const int64_t *numel,
@@ -176,6 +177,55 @@ int apexw_create(int32_t n_tensors, const int64_t *numel,
 int apexw_step(apexw_t h, const apexw_group *groups, int32_t n_groups,
                void *const *params, const void *const *grads,
                const float *found_inf_dev, void *stream);
+
+/*
+ * Options of apexw_step_ex; every pointer may be NULL.
+ *   inv_scale   device float: grads arrive multiplied by a loss scale and are
+ *               unscaled first, g * inv_scale (NULL: 1)
+ *   clip_coef   device float: the unscaled grads are then multiplied by it,
+ *               (g * inv_scale) * clip_coef, e.g. the coefficient written by
+ *               apexw_clip_grad_norm (NULL: 1)
+ *   found_inf   device float: nonzero or NaN skips the whole step (NULL:
+ *               never skip)
+ *   groups_dev  device array of n_groups apexw_group records read by the GPU
+ *               when the step runs (NULL: the host `groups` argument)
+ * Each factor is one rounded fp32 multiply; a factor of 1 changes nothing.
+ */
+typedef struct {
+    const float *inv_scale;
+    const float *clip_coef;
+    const float *found_inf;
+    const apexw_group *groups_dev;
+} apexw_step_options;
+
+/*
+ * The general step: apexw_step with the options above.  groups may be NULL
+ * when opts->groups_dev is set.  apexw_step, apexw_step_scaled and
+ * apexw_step_device are this call with some options fixed.
+ */
+int apexw_step_ex(apexw_t h, const apexw_group *groups, int32_t n_groups,
+                  void *const *params, const void *const *grads,
+                  const apexw_step_options *opts, void *stream);
+
+/*
+ * Global grad-norm clipping, the clip step of the mixed-precision recipe
+ * (M041 section 06; the pages give no formula -- the plain one is used).
+ * One pass reads every present grad: u = g * (*inv_scale_dev) in fp32 (NULL:
+ * 1); if found_inf_dev is not NULL, sets it to 1.0f when any u is an
+ * infinity or a NaN, exactly as apexw_unscale_check; sums u*u in fp64 into
+ * one partial per 256-element tile; then a fixed-order reduction (so the
+ * result does not depend on scheduling) writes the norm sqrt(sum) (fp64) to
+ * *norm_out_dev (may be NULL) and to *clip_coef_dev the factor
+ * max_norm / norm if norm > max_norm (fp64, rounded once to fp32), else 1.
+ * Pass clip_coef_dev (and the same inv_scale) in apexw_step_options.
+ * max_norm must be finite and > 0.  Queued on `stream`, no host sync.
+ * Errors: APEXW_EINVAL for a NULL handle, grads or clip_coef_dev or a bad
+ * max_norm; APEXW_EHIP if a launch fails.
+ */
+int apexw_clip_grad_norm(apexw_t h, const void *const *grads,
+                         const float *inv_scale_dev, double max_norm,
+                         float *found_inf_dev, double *norm_out_dev,
+                         float *clip_coef_dev, void *stream);
 
 /*
  * apexw_step on grads that arrive multiplied by a loss scale: every grad

@@ -36,7 +36,8 @@ APEXW_MAX_GROUPS = 32
 ENTRY_POINTS = (
     "apexw_state_bytes", "apexw_state_layout", "apexw_workspace_bytes",
     "apexw_create", "apexw_step", "apexw_step_scaled", "apexw_unscale_check",
-    "apexw_step_device", "apexw_export_bytes", "apexw_export_state", "apexw_import_state",
+    "apexw_step_device", "apexw_step_ex", "apexw_clip_grad_norm",
+    "apexw_export_bytes", "apexw_export_state", "apexw_import_state",
     "apexw_launch_info", "apexw_set_workgroups",
     "apexw_set_occupancy", "apexw_get_occupancy", "apexw_set_cache_policy",
     "apexw_destroy", "apexw_last_error",
@@ -53,6 +54,11 @@ class apexw_group(ctypes.Structure):
     _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double),
                 ("beta2", ctypes.c_double), ("eps", ctypes.c_double),
                 ("weight_decay", ctypes.c_double)]
+
+
+class apexw_step_options(ctypes.Structure):
+    _fields_ = [("inv_scale", ctypes.c_void_p), ("clip_coef", ctypes.c_void_p),
+                ("found_inf", ctypes.c_void_p), ("groups_dev", ctypes.c_void_p)]
 
 
 class apexw_tensor_state(ctypes.Structure):
@@ -83,6 +89,8 @@ def lib() -> ctypes.CDLL:
         L.apexw_step_scaled.argtypes = [P, P, I32, P, P, P, P, P]
         L.apexw_unscale_check.argtypes = [P, P, P, P, P]
         L.apexw_step_device.argtypes = [P, P, I32, P, P, P, P, P]
+        L.apexw_step_ex.argtypes = [P, P, I32, P, P, P, P]
+        L.apexw_clip_grad_norm.argtypes = [P, P, P, ctypes.c_double, P, P, P, P]
         L.apexw_export_bytes.argtypes = [P, ctypes.POINTER(SZ)]
         L.apexw_export_state.argtypes = [P, P, I32, P, SZ, P]
         L.apexw_import_state.argtypes = [P, P, SZ, P, I32, P]
@@ -194,6 +202,25 @@ def apexw_step_device(handle: int, groups_dev_ptr: int, n_groups: int, params_ar
     _check(lib().apexw_step_device(handle, groups_dev_ptr, n_groups, params_arr, grads_arr,
                                    inv_scale_ptr or None, found_inf_ptr or None, stream or None),
            "apexw_step_device")
+
+
+def apexw_step_ex(handle: int, groups_arr, n_groups: int, params_arr, grads_arr,
+                  inv_scale_ptr: int = 0, clip_coef_ptr: int = 0, found_inf_ptr: int = 0,
+                  groups_dev_ptr: int = 0, stream: int = 0) -> None:
+    """groups_arr may be None when groups_dev_ptr is given."""
+    o = apexw_step_options(inv_scale_ptr or None, clip_coef_ptr or None, found_inf_ptr or None,
+                           groups_dev_ptr or None)
+    _check(lib().apexw_step_ex(handle, groups_arr, n_groups, params_arr, grads_arr,
+                               ctypes.byref(o), stream or None), "apexw_step_ex")
+
+
+def apexw_clip_grad_norm(handle: int, grads_arr, inv_scale_ptr: int, max_norm: float,
+                         found_inf_ptr: int, norm_out_ptr: int, clip_coef_ptr: int,
+                         stream: int = 0) -> None:
+    _check(lib().apexw_clip_grad_norm(handle, grads_arr, inv_scale_ptr or None, max_norm,
+                                      found_inf_ptr or None, norm_out_ptr or None,
+                                      clip_coef_ptr or None, stream or None),
+           "apexw_clip_grad_norm")
 
 
 def apexw_export_bytes(handle: int) -> int:

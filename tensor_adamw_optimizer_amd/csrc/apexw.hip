@@ -114,10 +114,11 @@ int compute_layout(int32_t n, const int64_t *numel, int32_t fmt,
     return APEXW_OK;
 }
 
-// Workspace layout: descriptors | grad pointers | step records | tile table,
-// each on a 256-byte boundary.
+// Workspace layout: descriptors | grad pointers | step records | tile table |
+// grad-norm partial sums (one per tile, then one per reduce workgroup), each
+// on a 256-byte boundary.
 struct WsLayout {
-    int64_t desc, grads, records, tiles, total;
+    int64_t desc, grads, records, tiles, partials, partials2, total;
     int64_t n_tiles;
 };
 
@@ -133,7 +134,9 @@ WsLayout ws_layout(int32_t n, const int64_t *numel) {
     w.records = w.grads + round_up((int64_t)n * 8, kTableAlign);
     w.tiles = w.records + round_up((int64_t)n * (int64_t)sizeof(StepRecord), kTableAlign);
     // each launch's table is padded to a multiple of kXcds entries
-    w.total = n == 0 ? 0 : w.tiles + round_up((w.n_tiles + kMaxLaunches * kXcds) * 4, kTableAlign);
+    w.partials = w.tiles + round_up((w.n_tiles + kMaxLaunches * kXcds) * 4, kTableAlign);
+    w.partials2 = w.partials + round_up(w.n_tiles * 8, kTableAlign);
+    w.total = n == 0 ? 0 : w.partials2 + round_up(kReduceBlocks * 8, kTableAlign);
     return w;
 }
 
@@ -321,10 +324,6 @@ int upload_pointer_tables(apexw_opt *h, void *const *params, const void *const *
 int launch_cap(const apexw_opt *h) { return h->wg_override > 0 ? h->wg_override : (int)kMaxGrid; }
 
 }  // namespace
-
-static int step_impl(apexw_t h, const apexw_group *groups, const apexw_group *groups_dev,
-                     int32_t n_groups, void *const *params, const void *const *grads,
-                     const float *inv_scale_dev, const float *found_inf_dev, void *stream);
 
 // ======================================================================= ABI
 
@@ -515,39 +514,43 @@ int apexw_create(int32_t n_tensors, const int64_t *numel, const int32_t *param_d
 
 int apexw_step(apexw_t h, const apexw_group *groups, int32_t n_groups, void *const *params,
                const void *const *grads, const float *found_inf_dev, void *stream) {
-    return apexw_step_scaled(h, groups, n_groups, params, grads, nullptr, found_inf_dev, stream);
+    apexw_step_options o = {nullptr, nullptr, found_inf_dev, nullptr};
+    return apexw_step_ex(h, groups, n_groups, params, grads, &o, stream);
 }
 
 int apexw_step_scaled(apexw_t h, const apexw_group *groups, int32_t n_groups,
                       void *const *params, const void *const *grads,
                       const float *inv_scale_dev, const float *found_inf_dev, void *stream) {
-    return step_impl(h, groups, nullptr, n_groups, params, grads, inv_scale_dev, found_inf_dev,
-                     stream);
+    apexw_step_options o = {inv_scale_dev, nullptr, found_inf_dev, nullptr};
+    return apexw_step_ex(h, groups, n_groups, params, grads, &o, stream);
 }
 
 int apexw_step_device(apexw_t h, const apexw_group *groups_dev, int32_t n_groups,
                       void *const *params, const void *const *grads,
                       const float *inv_scale_dev, const float *found_inf_dev, void *stream) {
     if (!groups_dev) return fail(APEXW_EINVAL, "groups_dev is NULL");
-    return step_impl(h, nullptr, groups_dev, n_groups, params, grads, inv_scale_dev,
-                     found_inf_dev, stream);
+    apexw_step_options o = {inv_scale_dev, nullptr, found_inf_dev, groups_dev};
+    return apexw_step_ex(h, nullptr, n_groups, params, grads, &o, stream);
 }
 
-}  // extern "C"
-
-static int step_impl(apexw_t h, const apexw_group *groups, const apexw_group *groups_dev,
-                     int32_t n_groups, void *const *params, const void *const *grads,
-                     const float *inv_scale_dev, const float *found_inf_dev, void *stream) {
+int apexw_step_ex(apexw_t h, const apexw_group *groups, int32_t n_groups, void *const *params,
+                  const void *const *grads, const apexw_step_options *opts, void *stream) {
+    static const apexw_step_options none = {nullptr, nullptr, nullptr, nullptr};
+    const apexw_step_options &o = opts ? *opts : none;
     if (!h) return fail(APEXW_EINVAL, "handle is NULL");
     if (n_groups != h->n_groups)
         return fail(APEXW_EINVAL, "n_groups is %d, the handle was created with %d", n_groups,
                     h->n_groups);
-    if (!groups && !groups_dev) return fail(APEXW_EINVAL, "groups is NULL");
+    if (!groups && !o.groups_dev) return fail(APEXW_EINVAL, "groups is NULL");
     if (h->n > 0 && (!params || !grads)) return fail(APEXW_EINVAL, "params and grads must not be NULL");
+    const float *inv_scale_dev = o.inv_scale;
+    const float *found_inf_dev = o.found_inf;
+    if (o.groups_dev) groups = nullptr;
 
     KernelArgs a;
     std::memset(&a, 0, sizeof a);
-    a.groups_dev = groups_dev;
+    a.groups_dev = o.groups_dev;
+    a.clip_coef = o.clip_coef;
     for (int32_t g = 0; groups && g < n_groups; ++g) {
         const apexw_group &G = groups[g];
         if (!finite_nonneg(G.lr) || !finite_nonneg(G.eps) || !finite_nonneg(G.weight_decay) ||
@@ -613,8 +616,6 @@ static int step_impl(apexw_t h, const apexw_group *groups, const apexw_group *gr
     return APEXW_OK;
 }
 
-extern "C" {
-
 int apexw_unscale_check(apexw_t h, const void *const *grads, const float *inv_scale_dev,
                         float *found_inf_dev, void *stream) {
     if (!h) return fail(APEXW_EINVAL, "handle is NULL");
@@ -649,6 +650,60 @@ int apexw_unscale_check(apexw_t h, const void *const *grads, const float *inv_sc
         hipLaunchKernelGGL(k, dim3((unsigned)wg), dim3(kThreads), 0, st, a);
         HIP_TRY(hipGetLastError());
     }
+    return APEXW_OK;
+}
+
+int apexw_clip_grad_norm(apexw_t h, const void *const *grads, const float *inv_scale_dev,
+                         double max_norm, float *found_inf_dev, double *norm_out_dev,
+                         float *clip_coef_dev, void *stream) {
+    if (!h) return fail(APEXW_EINVAL, "handle is NULL");
+    if (!clip_coef_dev) return fail(APEXW_EINVAL, "clip_coef_dev is NULL");
+    if (!(max_norm > 0.0) || !std::isfinite(max_norm))
+        return fail(APEXW_EINVAL, "max_norm must be finite and > 0");
+    if (h->n > 0 && !grads) return fail(APEXW_EINVAL, "grads must not be NULL");
+    DeviceGuard guard(h->device);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int rc = upload_pointer_tables(h, nullptr, grads, st);
+    if (rc) return rc;
+    KernelArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.desc = reinterpret_cast<const TensorDesc *>(h->ws + h->wl.desc);
+    a.grads = reinterpret_cast<const void *const *>(h->ws + h->wl.grads);
+    a.tile_tensor = reinterpret_cast<const int32_t *>(h->ws + h->wl.tiles);
+    a.inv_scale = inv_scale_dev;
+    a.found_inf_out = found_inf_dev;
+    a.partials = reinterpret_cast<double *>(h->ws + h->wl.partials);
+    a.partials2 = reinterpret_cast<double *>(h->ws + h->wl.partials2);
+    a.norm_out = norm_out_dev;
+    a.clip_out = clip_coef_dev;
+    a.max_norm = max_norm;
+    a.n_tiles_total = h->wl.n_tiles;
+    const bool streaming = h->cache_policy == 0 ? h->streaming_auto : h->cache_policy == 1;
+    // every tile writes its partial (0 without a grad), so no launch is skipped
+    for (const Launch &L : h->launches) {
+        if (L.tile_count == 0) continue;
+        a.tile_begin = L.tile_begin;
+        a.tile_count = L.tile_count;
+        a.table_begin = L.table_begin;
+        a.table_stride = L.table_stride;
+        const int64_t wg = std::min<int64_t>(L.tile_count, launch_cap(h));
+        kernel_fn k = L.gt == APEXW_F32
+                          ? (streaming ? grad_norm_partials_kernel<APEXW_F32, true>
+                                       : grad_norm_partials_kernel<APEXW_F32, false>)
+                          : (streaming ? grad_norm_partials_kernel<APEXW_BF16, true>
+                                       : grad_norm_partials_kernel<APEXW_BF16, false>);
+        hipLaunchKernelGGL(k, dim3((unsigned)wg), dim3(kThreads), 0, st, a);
+        HIP_TRY(hipGetLastError());
+    }
+    if (h->n > 0) {
+        hipLaunchKernelGGL(grad_norm_reduce_kernel, dim3(kReduceBlocks), dim3(kReduceThreads), 0,
+                           st, a);
+        HIP_TRY(hipGetLastError());
+    } else {
+        a.partials2 = nullptr;                // no workspace: the norm is 0
+    }
+    hipLaunchKernelGGL(grad_norm_final_kernel, dim3(1), dim3(kReduceThreads), 0, st, a);
+    HIP_TRY(hipGetLastError());
     return APEXW_OK;
 }
 

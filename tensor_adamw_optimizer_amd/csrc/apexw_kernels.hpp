@@ -95,7 +95,8 @@ struct StepRecord {
     float lr, decay, eps;
     float bc1, bc2;                  // 1 - beta1^t, 1 - beta2^t
     float inv_scale;                 // grads are unscaled by this first
-    float pad_[4];
+    float clip_coef;                 // then multiplied by this (norm clipping)
+    float pad_[3];
 };
 static_assert(sizeof(StepRecord) == 64, "step record is one 64-byte record");
 
@@ -109,6 +110,13 @@ struct KernelArgs {
     const float *inv_scale;          // nullptr: 1 (grads are not scaled)
     float *found_inf_out;            // unscale check: set to 1 on a non-finite
     const apexw_group *groups_dev;   // non-null: hyperparameters read on the device
+    const float *clip_coef;          // nullptr: 1 (no clipping)
+    double *partials;                // grad-norm pass: fp64 sum of squares per tile
+    double *partials2;               // grad-norm finalize: one per first-stage workgroup
+    double *norm_out;                // grad-norm finalize: the norm (may be null)
+    float *clip_out;                 // grad-norm finalize: the clip coefficient
+    double max_norm;
+    int64_t n_tiles_total;           // logical tiles over all launches
     int64_t tile_begin;              // this launch's tiles: [begin, begin+count)
     int64_t tile_count;
     int64_t table_begin;             // this launch's part of tile_tensor
@@ -124,6 +132,7 @@ struct StepScalars {
     float lr, decay, eps;
     float bc1, bc2;                  // 1 - beta1^t, 1 - beta2^t (fp32)
     float inv_scale;                 // 1 unless grads arrive scaled
+    float clip_coef;                 // 1 unless the grad norm is clipped
 };
 
 // beta^n in fp64: square-and-multiply from the least significant bit.
@@ -149,15 +158,17 @@ __device__ __forceinline__ StepScalars step_scalars(const StepRecord &r) {
     s.bc1 = r.bc1;
     s.bc2 = r.bc2;
     s.inv_scale = r.inv_scale;
+    s.clip_coef = r.clip_coef;
     return s;
 }
 
 // The AdamW update of one element (M041 section 02), fp32, each operation
-// rounded, evaluated left to right as printed, on the unscaled grad (the
-// mixed-precision recipe of M041 section 06; multiplying by 1 is exact).
+// rounded, evaluated left to right as printed, on the unscaled and clipped
+// grad (the mixed-precision recipe of M041 section 06: unscale, check,
+// clip; multiplying by 1 is exact).
 __device__ __forceinline__ void adamw_update(float &theta, float g_scaled, float &m,
                                              float &v, const StepScalars &s) {
-    const float g = g_scaled * s.inv_scale;
+    const float g = (g_scaled * s.inv_scale) * s.clip_coef;
     m = s.beta1 * m + s.one_minus_beta1 * g;
     v = s.beta2 * v + (s.one_minus_beta2 * g) * g;
     const float m_hat = m / s.bc1;
@@ -442,6 +453,7 @@ __global__ __launch_bounds__(kPrepThreads) void adamw_prepare_kernel(KernelArgs 
         r.bc1 = (float)(1.0 - pow_uint(g.beta1_d, (uint32_t)t));
         r.bc2 = (float)(1.0 - pow_uint(g.beta2_d, (uint32_t)t));
         r.inv_scale = a.inv_scale != nullptr ? *a.inv_scale : 1.0f;
+        r.clip_coef = a.clip_coef != nullptr ? *a.clip_coef : 1.0f;
     }
     a.records[i] = r;
 }
@@ -544,6 +556,109 @@ __global__ __launch_bounds__(kThreads) void unscale_check_kernel(KernelArgs a) {
         if (k >= a.tile_count) break;
     }
     if (__any(bad) && threadIdx.x == 0) *gptr<float>(static_cast<void *>(a.found_inf_out)) = 1.0f;
+}
+
+// ---------------------------------------------------------------- grad norm
+//
+// Global grad-norm clipping (the clip step of the M041 section 06 recipe):
+// the norm of all present unscaled grads u = g * inv_scale (fp32, as the
+// update uses them), squares and sums in fp64, reduced in a fixed order so
+// the result does not depend on scheduling:
+//  1. grad_norm_partials_kernel: one wave per tile sums its lanes' squares
+//     (lane order, then a butterfly over the wave) into partials[tile]; tiles
+//     without a grad contribute 0; optionally sets found_inf_out like the
+//     unscale check;
+//  2. grad_norm_reduce_kernel: workgroup b sums partials[b*C .. (b+1)*C) with
+//     a strided loop and a tree in LDS into partials2[b];
+//  3. grad_norm_final_kernel: one workgroup sums partials2 the same way and
+//     writes the norm (fp64 sqrt) and the clip coefficient max_norm / norm
+//     when norm > max_norm (fp64, rounded once to fp32), else 1.
+
+__device__ __forceinline__ double wave_sum(double x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+template <int GT, bool NT>
+__global__ __launch_bounds__(kThreads) void grad_norm_partials_kernel(KernelArgs a) {
+    const APEXW_CONST int32_t *tile_tensor = cptr<int32_t>(a.tile_tensor);
+    const APEXW_CONST uint64_t *grads = cptr<uint64_t>(a.grads);
+    const float inv = a.inv_scale != nullptr ? *a.inv_scale : 1.0f;
+    int64_t k = blockIdx.x;
+    bool bad = false;
+    for (;;) {
+        const int32_t i = tile_tensor[table_pos(a, k)];
+        const void *grad = reinterpret_cast<const void *>(grads[i]);
+        const TensorDesc d = load_uniform(a.desc, i);
+        const int64_t base = (a.tile_begin + k - d.first_tile) * kTile;
+        const int64_t left = d.numel - base;
+        const int n = left < kTile ? (int)left : kTile;
+        asm volatile("" ::"s"(grad));
+        double sq = 0.0;
+        if (grad != nullptr && n > 0) {
+            const int off = threadIdx.x * kVec;
+            float g[kVec];
+            if ((((uintptr_t)grad) & 15u) == 0u && off + kVec <= n) {
+                load4<GT, NT>(grad, base + off, g);
+            } else {
+#pragma unroll
+                for (int j = 0; j < kVec; ++j) g[j] = off + j < n ? load1<GT>(grad, base + off + j) : 0.0f;
+            }
+#pragma unroll
+            for (int j = 0; j < kVec; ++j) {
+                const float u = g[j] * inv;
+                if (off + j < n) {
+                    bad |= !(fabsf(u) <= 3.40282347e38f);
+                    sq = sq + (double)u * (double)u;
+                }
+            }
+        }
+        sq = wave_sum(sq);
+        if (threadIdx.x == 0) gptr<double>(static_cast<void *>(a.partials))[a.tile_begin + k] = sq;
+        k += gridDim.x;
+        if (k >= a.tile_count) break;
+    }
+    if (a.found_inf_out != nullptr && __any(bad) && threadIdx.x == 0)
+        *gptr<float>(static_cast<void *>(a.found_inf_out)) = 1.0f;
+}
+
+constexpr int kReduceThreads = 256;
+constexpr int kReduceBlocks = 256;
+
+// Fixed-order sum of src[lo, hi) by one workgroup: strided per thread, then a
+// tree over the workgroup's threads in LDS.
+__device__ __forceinline__ double block_sum(const double *src, int64_t lo, int64_t hi) {
+    __shared__ double buf[kReduceThreads];
+    double acc = 0.0;
+    for (int64_t j = lo + threadIdx.x; j < hi; j += kReduceThreads)
+        acc = acc + gptr<double>(static_cast<const void *>(src))[j];
+    buf[threadIdx.x] = acc;
+    __syncthreads();
+    for (int w = kReduceThreads / 2; w >= 1; w >>= 1) {
+        if ((int)threadIdx.x < w) buf[threadIdx.x] = buf[threadIdx.x] + buf[threadIdx.x + w];
+        __syncthreads();
+    }
+    return buf[0];
+}
+
+__global__ __launch_bounds__(kReduceThreads) void grad_norm_reduce_kernel(KernelArgs a) {
+    const int64_t chunk = (a.n_tiles_total + kReduceBlocks - 1) / kReduceBlocks;
+    const int64_t lo = (int64_t)blockIdx.x * chunk;
+    const int64_t hi = lo + chunk < a.n_tiles_total ? lo + chunk : a.n_tiles_total;
+    const double sum = block_sum(a.partials, lo, hi > lo ? hi : lo);
+    if (threadIdx.x == 0) gptr<double>(static_cast<void *>(a.partials2))[blockIdx.x] = sum;
+}
+
+__global__ __launch_bounds__(kReduceThreads) void grad_norm_final_kernel(KernelArgs a) {
+    // no partials at all (an empty tensor list): the norm is 0
+    const double sum = a.partials2 != nullptr ? block_sum(a.partials2, 0, kReduceBlocks) : 0.0;
+    if (threadIdx.x == 0) {
+        const double norm = sqrt(sum);
+        const float coef = norm > a.max_norm ? (float)(a.max_norm / norm) : 1.0f;
+        if (a.norm_out != nullptr) *gptr<double>(static_cast<void *>(a.norm_out)) = norm;
+        *gptr<float>(static_cast<void *>(a.clip_out)) = coef;
+    }
 }
 
 // Zero fill of the state buffer (used once, at creation).
