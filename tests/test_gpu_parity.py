@@ -412,3 +412,50 @@ def test_lora_q8_full_size_sampled():
     _q8_check(opt, params, ref, th_ref, pick, "28 layers, 250 calls")
     assert np.all(bits(opt.steps()) == 250)
     opt.close()
+
+
+@pytest.mark.parametrize("fmt", [W.STATE_F32, W.STATE_Q8])
+def test_maximum_size_tensor_past_int32(fmt):
+    """One bf16 tensor of 2^31 + 4099 elements (64-bit element offsets, 8.4M
+    tiles, a 3-element final 8-bit block), bf16 grads, 2 calls; whole
+    256-element blocks sampled around element 2^31, at both ends and at
+    random, against the oracle."""
+    _need_gpu()
+    n = (1 << 31) + 4099
+    say("case: maximum size", fmt, n)
+    gen = torch.Generator(device=DEV).manual_seed(11)
+    theta = (torch.randn(n, generator=gen, device=DEV) * 0.02).to(torch.bfloat16)
+    grad = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    opt = GpuOpt([n], [W.BF16], [W.BF16], [0], 1, fmt)
+    rng = np.random.default_rng(12)
+    nblocks = (n + 255) // 256
+    picks = sorted(set([0, 1, (1 << 23) - 1, 1 << 23, (1 << 23) + 1, nblocks - 2, nblocks - 1] +
+                       rng.integers(0, nblocks, 40).tolist()))
+    spans = [(b * 256, min(n, b * 256 + 256)) for b in picks]
+    idx = torch.cat([torch.arange(lo, hi) for lo, hi in spans]).to(DEV)
+    sizes = [hi - lo for lo, hi in spans]
+    ref = oracle.OracleAdamW(sizes, [W.BF16] * len(sizes), [W.BF16] * len(sizes), [0] * len(sizes), fmt)
+    th0 = bits(theta[idx])
+    th_ref = np.split(th0, np.cumsum(sizes)[:-1])
+    th_ref = [x.copy() for x in th_ref]
+    groups = [W.Group(lr=1e-3, weight_decay=0.1)]
+    for k in range(2):
+        grad.copy_((torch.randn(n, generator=gen, device=DEV) * 1e-3).to(torch.bfloat16))
+        opt.step(groups, [theta], [grad])
+        gs = np.split(bits(grad[idx]), np.cumsum(sizes)[:-1])
+        ref.step(th_ref, [x.copy() for x in gs], groups)
+    torch.cuda.synchronize()
+    got = np.split(bits(theta[idx]), np.cumsum(sizes)[:-1])
+    m, v = opt.moments(0)
+    gm = np.split(bits(m[idx]), np.cumsum(sizes)[:-1])
+    gv = np.split(bits(v[idx]), np.cumsum(sizes)[:-1])
+    for j, b in enumerate(picks):
+        assert n_bit_mismatch(got[j], th_ref[j]) == 0, b
+        assert n_bit_mismatch(gm[j], ref.m[j]) == 0 and n_bit_mismatch(gv[j], ref.v[j]) == 0, b
+        if fmt == W.STATE_Q8:
+            ms, vs = opt.scales(0)
+            assert bits(ms[b:b + 1])[0] == ref.m_scale[j][0] and bits(vs[b:b + 1])[0] == ref.v_scale[j][0]
+    assert list(bits(opt.steps())) == [2]
+    opt.close()
+    del theta, grad
+    torch.cuda.empty_cache()
