@@ -89,10 +89,7 @@ class AdamW:
         self._params_arr = L.make_ptrs([p.data_ptr() for p in self._params])
 
     # ------------------------------------------------------------ stepping
-    def step(self, found_inf: Optional[torch.Tensor] = None) -> None:
-        """One update; a parameter whose .grad is None is left untouched.
-        found_inf: optional one-element float32 GPU tensor; nonzero skips the
-        step on the device."""
+    def _grads_arr(self):
         ptrs = []
         for p, gdt in zip(self._params, self._gdtype):
             g = p.grad
@@ -107,21 +104,89 @@ class AdamW:
                                  "parameter on %s" % (gdt, p.device))
             # an empty grad has no storage; any non-null pointer marks "present"
             ptrs.append(g.data_ptr() or 16)
-        self.step_pointers(L.make_ptrs(ptrs), found_inf)
+        return L.make_ptrs(ptrs)
 
-    def step_pointers(self, grads_arr, found_inf: Optional[torch.Tensor] = None) -> None:
+    def _dev_ptr(self, t: Optional[torch.Tensor], name: str, dtype=torch.float32) -> int:
+        if t is None:
+            return 0
+        if t.dtype != dtype or t.device != self.device or t.numel() < 1:
+            raise ValueError("%s must be a %s tensor on the parameters' device" % (name, dtype))
+        return t.data_ptr()
+
+    def _stream(self) -> int:
+        return torch.cuda.current_stream(self.device).cuda_stream
+
+    def step(self, found_inf: Optional[torch.Tensor] = None,
+             inv_scale: Optional[torch.Tensor] = None,
+             clip_coef: Optional[torch.Tensor] = None) -> None:
+        """One update; a parameter whose .grad is None is left untouched.
+        found_inf: one-element float32 GPU tensor, nonzero skips the step on
+        the device.  inv_scale: grads are unscaled by it first.  clip_coef:
+        then multiplied by it (see clip_grad_norm)."""
+        self.step_pointers(self._grads_arr(), found_inf, inv_scale, clip_coef)
+
+    def step_pointers(self, grads_arr, found_inf: Optional[torch.Tensor] = None,
+                      inv_scale: Optional[torch.Tensor] = None,
+                      clip_coef: Optional[torch.Tensor] = None) -> None:
         """Step with a prepared void*[] of grad pointers (see _lib.make_ptrs)."""
-        fi = 0
-        if found_inf is not None:
-            if found_inf.dtype != torch.float32 or found_inf.device != self.device \
-                    or found_inf.numel() < 1:
-                raise ValueError("found_inf must be a float32 tensor on the parameters' device")
-            fi = found_inf.data_ptr()
         groups = [_GroupView(g) for g in self.param_groups]
         with torch.cuda.device(self.device):
-            stream = torch.cuda.current_stream(self.device).cuda_stream
-            L.apexw_step(self._h, L.make_groups(groups), len(groups), self._params_arr,
-                         grads_arr, fi, stream)
+            L.apexw_step_ex(self._h, L.make_groups(groups), len(groups), self._params_arr,
+                            grads_arr, self._dev_ptr(inv_scale, "inv_scale"),
+                            self._dev_ptr(clip_coef, "clip_coef"),
+                            self._dev_ptr(found_inf, "found_inf"), 0, self._stream())
+
+    def unscale_check(self, inv_scale: Optional[torch.Tensor], found_inf: torch.Tensor) -> None:
+        """Set found_inf to 1 if any grad times inv_scale is not finite (never
+        clears it); grads are not rewritten -- pass inv_scale to step()."""
+        with torch.cuda.device(self.device):
+            L.apexw_unscale_check(self._h, self._grads_arr(), self._dev_ptr(inv_scale, "inv_scale"),
+                                  self._dev_ptr(found_inf, "found_inf"), self._stream())
+
+    def clip_grad_norm(self, max_norm: float, inv_scale: Optional[torch.Tensor] = None,
+                       found_inf: Optional[torch.Tensor] = None):
+        """Global norm of the (unscaled) grads and the clip coefficient, both
+        on the device: returns (norm fp64 tensor, coef fp32 tensor); pass coef
+        to step(clip_coef=...).  With found_inf the finite check runs too."""
+        norm = torch.empty(1, dtype=torch.float64, device=self.device)
+        coef = torch.empty(1, dtype=torch.float32, device=self.device)
+        with torch.cuda.device(self.device):
+            L.apexw_clip_grad_norm(self._h, self._grads_arr(), self._dev_ptr(inv_scale, "inv_scale"),
+                                   float(max_norm), self._dev_ptr(found_inf, "found_inf"),
+                                   norm.data_ptr(), coef.data_ptr(), self._stream())
+        return norm, coef
+
+    def zero_grad(self, set_to_none: bool = True) -> None:
+        for p in self._params:
+            if p.grad is None:
+                continue
+            if set_to_none:
+                p.grad = None
+            else:
+                p.grad.zero_()
+
+    # ------------------------------------------------------------ checkpoint
+    def state_dict(self) -> Dict:
+        """The optimizer checkpoint: the library's blob (format, tensor list,
+        recipe, moments, scales, step counters) as a CPU uint8 tensor, plus
+        the parameter-group hyperparameters; loadable with
+        torch.load(weights_only=True)."""
+        groups = [_GroupView(g) for g in self.param_groups]
+        with torch.cuda.device(self.device):
+            blob = L.apexw_export_state(self._h, L.make_groups(groups), len(groups), self._stream())
+        return {
+            "apexw_blob": torch.frombuffer(bytearray(blob), dtype=torch.uint8),
+            "param_groups": [{"lr": g["lr"], "betas": list(g["betas"]), "eps": g["eps"],
+                              "weight_decay": g["weight_decay"]} for g in self.param_groups],
+        }
+
+    def load_state_dict(self, sd: Dict) -> None:
+        blob = bytes(sd["apexw_blob"].cpu().numpy().tobytes())
+        with torch.cuda.device(self.device):
+            L.apexw_import_state(self._h, blob, len(self.param_groups), self._stream())
+        for g, h in zip(self.param_groups, sd["param_groups"]):
+            g["lr"], g["betas"] = h["lr"], tuple(h["betas"])
+            g["eps"], g["weight_decay"] = h["eps"], h["weight_decay"]
 
     # ------------------------------------------------------------ state views
     def moments(self, i: int):

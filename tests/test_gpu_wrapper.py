@@ -1,0 +1,77 @@
+"""The torch wrapper (tensor_adamw_optimizer_amd.AdamW) used the torch way:
+.grad attributes, parameter-group dicts, a learning-rate change, the AMP
+recipe with clipping, and a checkpoint through torch.save / torch.load
+(weights_only=True) -- against the oracle."""
+import io
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_helpers import bits, n_bit_mismatch, say
+from tensor_adamw_optimizer_amd import AdamW
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.mark.parametrize("state", ["f32", "q8"])
+def test_wrapper_amp_clip_checkpoint(state):
+    say("case: wrapper", state)
+    gen = torch.Generator().manual_seed(51)
+    shapes = [(64, 33), (1000,), (7,), (300, 3)]
+    dts = [torch.float32, torch.bfloat16, torch.float32, torch.bfloat16]
+    p_cpu = [(torch.randn(s, generator=gen) * 0.02).to(d) for s, d in zip(shapes, dts)]
+    params = [p.to(DEV) for p in p_cpu]
+    groups = [{"params": [params[0], params[2]], "lr": 1e-3, "weight_decay": 0.1},
+              {"params": [params[1], params[3]], "lr": 5e-4, "betas": (0.8, 0.99)}]
+    opt = AdamW(groups, lr=1e-3, state=state)
+    order = [0, 2, 1, 3]                          # the wrapper's tensor order (group by group)
+    gdef = [W.Group(lr=1e-3, weight_decay=0.1), W.Group(lr=5e-4, beta1=0.8, beta2=0.99)]
+    ref = oracle.OracleAdamW([p_cpu[i].numel() for i in order],
+                             ["f32" if dts[i] == torch.float32 else "bf16" for i in order],
+                             ["f32" if dts[i] == torch.float32 else "bf16" for i in order],
+                             [0, 0, 1, 1], state)
+    th_ref = [bits(p_cpu[i]) for i in order]
+    fi = torch.zeros(1, device=DEV)
+    scale = 1024.0
+    inv = torch.tensor([1.0 / scale], device=DEV)
+    max_norm = 0.02
+    blob = None
+    for k in range(1, 9):
+        if k == 5:
+            # checkpoint, then continue in a fresh optimizer over the same params
+            buf = io.BytesIO()
+            torch.save(opt.state_dict(), buf)
+            buf.seek(0)
+            sd = torch.load(buf, weights_only=True)
+            opt.close()
+            opt = AdamW(groups, lr=1e-3, state=state)
+            opt.load_state_dict(sd)
+        if k == 6:
+            opt.param_groups[0]["lr"] = 2e-3
+            gdef[0] = W.Group(lr=2e-3, weight_decay=0.1)
+        g_cpu = [(torch.randn(s, generator=gen) * 1e-3 * scale).to(d) for s, d in zip(shapes, dts)]
+        for p, g in zip(params, g_cpu):
+            p.grad = g.to(DEV)
+        if k == 3:
+            params[2].grad = None
+        fi.zero_()
+        norm, coef = opt.clip_grad_norm(max_norm, inv_scale=inv, found_inf=fi)
+        opt.step(found_inf=fi, inv_scale=inv, clip_coef=coef)
+        g_np = [None if (k == 3 and i == 2) else bits(g_cpu[i]) for i in order]
+        found = ref.unscale_check(g_np, 1.0 / scale)
+        c = ref.clip_coef(ref.grad_norm(g_np, 1.0 / scale), max_norm)
+        torch.cuda.synchronize()
+        assert coef.item() == c
+        ref.step(th_ref, g_np, gdef, found_inf=found, inv_scale=1.0 / scale, clip_coef=c)
+        opt.zero_grad()
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(opt.steps()), ref.t)
+    for j, i in enumerate(order):
+        assert n_bit_mismatch(bits(params[i]), th_ref[j]) == 0, i
+        m, v = opt.moments(j)
+        assert n_bit_mismatch(bits(m), ref.m[j]) == 0 and n_bit_mismatch(bits(v), ref.v[j]) == 0
+    opt.close()
