@@ -303,16 +303,33 @@ __device__ __forceinline__ void tile_dense(const TensorDesc &d, const void *grad
 
 // 8-bit codes: m signed (scale absmax|m|/127), v unsigned (scale max v/255),
 // one scale per 256-element block; an all-zero block has scale 0, codes 0.
-__device__ __forceinline__ uint32_t encode_signed(float x, float s) {
+//
+// The code is round-half-even of the correctly rounded quotient x/s.  The
+// quotient is not formed per element: with inv_s = RN(1/s) (one division per
+// block), r = RN(x*inv_s) differs from x/s by at most |x/s|*2^-23 (plus 2^-150
+// on underflow) and RN(x/s) by at most |x/s|*2^-24; for |x/s| <= 256 both
+// stay within 4.6e-5 of x/s.  So when r is more than 2.5e-4 away from every
+// half-integer, r and RN(x/s) round to the same integer; otherwise (rare),
+// or when r is not finite (a tiny scale), the quotient itself is rounded.
+// r - rint(r) is exact here (Sterbenz), so the distance test is exact too.
+__host__ __device__ __forceinline__ float round_quotient(float x, float s, float inv_s) {
+    const float r = x * inv_s;
+    const float q = rintf(r);
+    const float dist = fabsf(fabsf(r - q) - 0.5f);   // to the nearest half-integer
+    if (!(fabsf(r) <= 256.0f) || !(dist > 2.5e-4f)) return rintf(x / s);
+    return q;
+}
+
+__device__ __forceinline__ uint32_t encode_signed(float x, float s, float inv_s) {
     if (s == 0.0f) return 0u;
-    float r = rintf(x / s);
+    float r = round_quotient(x, s, inv_s);
     r = fminf(fmaxf(r, -127.0f), 127.0f);
     return (uint32_t)(uint8_t)(int8_t)(int)r;
 }
 
-__device__ __forceinline__ uint32_t encode_unsigned(float x, float s) {
+__device__ __forceinline__ uint32_t encode_unsigned(float x, float s, float inv_s) {
     if (s == 0.0f) return 0u;
-    float r = rintf(x / s);
+    float r = round_quotient(x, s, inv_s);
     r = fminf(fmaxf(r, 0.0f), 255.0f);
     return (uint32_t)(int)r;
 }
@@ -374,6 +391,8 @@ __device__ __forceinline__ void tile_q8(const TensorDesc &d, const void *grad,
     av = wave_max(av);
     const float sm = am / 127.0f;
     const float sv = av / 255.0f;
+    const float inv_sm = sm != 0.0f ? 1.0f / sm : 0.0f;
+    const float inv_sv = sv != 0.0f ? 1.0f / sv : 0.0f;
     if (threadIdx.x == 0) {
         gptr<float>(static_cast<void *>(d.m_scale))[blk] = sm;
         gptr<float>(static_cast<void *>(d.v_scale))[blk] = sv;
@@ -382,8 +401,8 @@ __device__ __forceinline__ void tile_q8(const TensorDesc &d, const void *grad,
         uint32_t cm = 0, cv = 0;
 #pragma unroll
         for (int j = 0; j < kVec; ++j) {
-            cm |= encode_signed(m[j], sm) << (8 * j);
-            cv |= encode_unsigned(v[j], sv) << (8 * j);
+            cm |= encode_signed(m[j], sm, inv_sm) << (8 * j);
+            cv |= encode_unsigned(v[j], sv, inv_sv) << (8 * j);
         }
         store_u32<NT>(d.m, e, cm);
         store_u32<NT>(d.v, e, cv);
@@ -397,8 +416,8 @@ __device__ __forceinline__ void tile_q8(const TensorDesc &d, const void *grad,
 #pragma unroll
         for (int j = 0; j < kVec; ++j) {
             if (off + j < n) {
-                gptr<int8_t>(d.m)[e + j] = (int8_t)encode_signed(m[j], sm);
-                gptr<uint8_t>(d.v)[e + j] = (uint8_t)encode_unsigned(v[j], sv);
+                gptr<int8_t>(d.m)[e + j] = (int8_t)encode_signed(m[j], sm, inv_sm);
+                gptr<uint8_t>(d.v)[e + j] = (uint8_t)encode_unsigned(v[j], sv, inv_sv);
                 store1<PT>(d.param, e + j, th[j]);
             }
         }
