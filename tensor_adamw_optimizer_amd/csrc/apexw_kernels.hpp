@@ -182,16 +182,20 @@ __device__ __forceinline__ void adamw_update(float &theta, float g_scaled, float
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Nearest bf16, ties to even (NaN kept quiet).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Nearest bf16 of two fp32 values, ties to even; a NaN stays a NaN with the
+// quiet bit set and the top 7 payload bits kept.  gfx950 converts a pair in
+// one instruction (v_cvt_pk_bf16_f32) whose result equals that rule for all
+// 2^32 inputs, denormals included (an exhaustive device check).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    return pack_bf16x2(f, 0.0f) & 0xffffu;
 }
 
 // ---------------------------------------------------------------- loads

@@ -8,6 +8,8 @@ bf16 state -- bitwise against the oracle's bf16-state mode and <= 1e-2
 codes equal or within 1, scales within 1e-6 relative; step counters and the
 skip / grad=None behaviour bit-exact.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -177,6 +179,54 @@ def test_found_inf_leaves_everything_bitwise(fmt):
     opt.close()
 
 
+def _bf16_rounding_patterns() -> np.ndarray:
+    """fp32 bit patterns covering every case of nearest-even rounding to
+    bf16: all 65536 low halves under each sign and exponent with an even and
+    an odd last kept bit (zeros, denormals, infinities and NaNs included),
+    and every high half under 16 low halves around the ties."""
+    sign_exp = np.arange(512, dtype=np.uint32) << 7
+    highs = np.concatenate([sign_exp | 0x00, sign_exp | 0x7F])
+    lows = np.arange(65536, dtype=np.uint32)
+    a = ((highs[:, None] << 16) | lows[None, :]).reshape(-1)
+    few_lows = np.array([0, 1, 0x3FFF, 0x7FFE, 0x7FFF, 0x8000, 0x8001, 0xBFFF, 0xC000, 0xFFFE,
+                         0xFFFF, 0x1234, 0x4321, 0x7000, 0x9000, 0xF00D], np.uint32)
+    b = ((np.arange(65536, dtype=np.uint32)[:, None] << 16) | few_lows[None, :]).reshape(-1)
+    return np.concatenate([a, b])
+
+
+def test_bf16_rounding_every_case_against_oracle():
+    """With beta1 = 0 the new m is the grad itself, so the bf16 m the library
+    stores is the grad rounded to bf16; m, v and the bf16 parameter after one
+    step match the oracle bit for bit on every rounding case (a NaN only has
+    to stay a NaN: payloads through the arithmetic are not compared)."""
+    _need_gpu()
+    say("case: bf16 rounding, all cases")
+    g_bits = _bf16_rounding_patterns()
+    n = int(g_bits.size)
+    grp = [W.Group(lr=1e-3, beta1=0.0, beta2=0.999, eps=1e-8, weight_decay=0.0)]
+    opt = GpuOpt([n], [W.BF16], [W.F32], [0], 1, W.STATE_BF16)
+    g_dev = torch.from_numpy(g_bits.view(np.int32)).to(DEV).view(torch.float32)
+    theta = torch.zeros(n, dtype=torch.bfloat16, device=DEV)
+    opt.step(grp, [theta], [g_dev])
+    torch.cuda.synchronize()
+    ref = oracle.OracleAdamW([n], [W.BF16], [W.F32], [0], W.STATE_BF16)
+    th_ref = [np.zeros(n, np.uint16)]
+    ref.step(th_ref, [g_bits.view(np.float32)], grp)
+    m_gpu, v_gpu = (bits(t) for t in opt.moments(0))
+    for name, got, want in (("m", m_gpu, ref.m[0]), ("v", v_gpu, ref.v[0]),
+                            ("theta", bits(theta), th_ref[0])):
+        got_nan = np.isnan(oracle.bf16_to_f32(got))
+        want_nan = np.isnan(oracle.bf16_to_f32(want))
+        assert np.array_equal(got_nan, want_nan), name
+        bad = int(np.count_nonzero(got[~got_nan] != want[~want_nan]))
+        assert bad == 0, "%s: %d of %d values differ" % (name, bad, n)
+    # the m path really is the plain conversion of the grad (0 + (-0) is +0)
+    g32 = g_bits.view(np.float32)
+    keep = ~np.isnan(g32) & (g_bits != 0x80000000)
+    assert np.array_equal(ref.m[0][keep], oracle.f32_to_bf16(g32)[keep])
+    opt.close()
+
+
 def test_all_grads_absent_and_pointer_changes():
     """No grads at all: nothing changes.  Grads moved to new buffers between
     calls: the library follows the new pointers."""
@@ -205,11 +255,12 @@ def test_all_grads_absent_and_pointer_changes():
     opt.close()
 
 
+@pytest.mark.parametrize("fmt", [W.STATE_F32, W.STATE_BF16, W.STATE_Q8])
 @pytest.mark.parametrize("wg", [1, 7, 300, 0])
-def test_results_do_not_depend_on_grid(wg):
+def test_results_do_not_depend_on_grid(wg, fmt):
     _need_gpu()
-    say("case: grid", wg)
-    w = W.many_small(n_tensors=300)
+    say("case: grid", wg, "fmt", fmt)
+    w = dataclasses.replace(W.many_small(n_tensors=300), state_fmt=fmt)
     outs = []
     for setting in (wg, 0):
         params = W.init_params(w, DEV)
