@@ -227,6 +227,88 @@ def test_bf16_rounding_every_case_against_oracle():
     opt.close()
 
 
+def _extreme_values(n: int, rng: np.random.Generator, finite: bool, max_abs: float) -> np.ndarray:
+    """fp32 values mixing the cases floating point treats specially: normal
+    N(0, 1e-3) values, signed zeros, denormals, tiny normals, large values up
+    to max_abs and, unless ``finite``, infinities and NaNs."""
+    x = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    kind = rng.integers(0, 20, n)
+    sign = np.where(rng.integers(0, 2, n) == 1, -1.0, 1.0).astype(np.float32)
+    den = (rng.integers(1, 1 << 23, n, dtype=np.uint32)).view(np.float32) * sign
+    tiny = (10.0 ** rng.uniform(-38, -25, n)).astype(np.float32) * sign
+    big = (10.0 ** rng.uniform(3, np.log10(max_abs), n)).astype(np.float32) * sign
+    x = np.where(kind == 0, np.float32(0.0) * sign, x)
+    x = np.where(kind == 1, den, x)
+    x = np.where(kind == 2, tiny, x)
+    x = np.where(kind == 3, big, x)
+    if not finite:
+        x = np.where(kind == 4, np.float32(np.inf) * sign, x)
+        x = np.where(kind == 5, np.float32(np.nan), x)
+    return x.astype(np.float32)
+
+
+def _same_bits_or_both_nan(name, got, want, as_float):
+    got_nan, want_nan = np.isnan(as_float(got)), np.isnan(as_float(want))
+    assert np.array_equal(got_nan, want_nan), "%s: NaN positions differ" % name
+    u = lambda a: a.view(np.uint32) if a.dtype == np.float32 else a     # compare bits
+    bad = int(np.count_nonzero(u(got)[~got_nan] != u(want)[~want_nan]))
+    assert bad == 0, "%s: %d of %d values differ" % (name, bad, got.size)
+
+
+@pytest.mark.parametrize("fmt", [W.STATE_F32, W.STATE_BF16, W.STATE_Q8])
+def test_extreme_values_against_oracle(fmt):
+    """Grads and parameters with signed zeros, denormals, tiny and huge values
+    (and, for the fp32 and bf16 moments, infinities and NaNs, which the
+    update simply propagates); groups with eps = 0 (0/0 appears) and with
+    beta1 = 0; six calls.  Every finite value bit-exact against the oracle,
+    NaNs in the same places.  The 8-bit codes are defined for finite moments
+    only, so that format gets finite inputs whose squares stay finite."""
+    _need_gpu()
+    say("case: extreme values", fmt)
+    rng = np.random.default_rng(11)
+    sizes = [4096, 4096, 1000, 777]
+    pdt = [W.F32, W.BF16, W.F32, W.BF16]
+    gdt = [W.F32, W.BF16, W.BF16, W.F32]
+    group_of = [0, 1, 2, 0]
+    groups = [W.Group(lr=1e-3, weight_decay=0.1), W.Group(lr=1e-2, eps=0.0),
+              W.Group(lr=1e-3, beta1=0.0, weight_decay=0.01)]
+    finite = fmt == W.STATE_Q8
+    max_abs = 1e18 if finite else 3e38
+
+    def host(x, dt):
+        return x.copy() if dt == W.F32 else oracle.f32_to_bf16(x)
+
+    def dev(h, dt):
+        t = torch.from_numpy(h.view(np.int32) if dt == W.F32 else h.view(np.int16)).to(DEV)
+        return t.view(torch.float32 if dt == W.F32 else torch.bfloat16)
+
+    th_ref = [host(_extreme_values(n, rng, finite, max_abs), d) for n, d in zip(sizes, pdt)]
+    params = [dev(h, d) for h, d in zip(th_ref, pdt)]
+    opt = GpuOpt(sizes, pdt, gdt, group_of, len(groups), fmt)
+    ref = oracle.OracleAdamW(sizes, pdt, gdt, group_of, fmt)
+    for k in range(6):
+        g_host = [host(_extreme_values(n, rng, finite, max_abs), d) for n, d in zip(sizes, gdt)]
+        opt.step(groups, params, [dev(h, d) for h, d in zip(g_host, gdt)])
+        ref.step(th_ref, g_host, groups)
+    torch.cuda.synchronize()
+    f32 = lambda a: a.view(np.float32)
+    for i in range(len(sizes)):
+        as_p = f32 if pdt[i] == W.F32 else oracle.bf16_to_f32
+        _same_bits_or_both_nan("theta%d" % i, bits(params[i]), th_ref[i], as_p)
+        m, v = (bits(t) for t in opt.moments(i))
+        if fmt == W.STATE_Q8:
+            assert np.array_equal(m, ref.m[i]) and np.array_equal(v, ref.v[i]), i
+            ms, vs = (bits(t) for t in opt.scales(i))
+            assert np.array_equal(ms.view(np.uint32), ref.m_scale[i].view(np.uint32)), i
+            assert np.array_equal(vs.view(np.uint32), ref.v_scale[i].view(np.uint32)), i
+        else:
+            as_s = f32 if fmt == W.STATE_F32 else oracle.bf16_to_f32
+            _same_bits_or_both_nan("m%d" % i, m, ref.m[i], as_s)
+            _same_bits_or_both_nan("v%d" % i, v, ref.v[i], as_s)
+    assert np.array_equal(bits(opt.steps()), ref.t)
+    opt.close()
+
+
 def test_all_grads_absent_and_pointer_changes():
     """No grads at all: nothing changes.  Grads moved to new buffers between
     calls: the library follows the new pointers."""
