@@ -162,6 +162,28 @@ __device__ __forceinline__ StepScalars step_scalars(const StepRecord &r) {
     return s;
 }
 
+// Square root rounded to nearest.  v_sqrt_f32 is within one ulp, so the
+// answer is it or a neighbour: the lower neighbour lo if x <= lo*s, the upper
+// hi if x > hi*s (the squares of the two midpoints lie strictly beyond those
+// products and no float falls in between), decided by the sign of one exact
+// fma residual each.  For x >= 2^-96 those residuals cannot underflow; 0,
+// +inf and NaN come out of the same steps unchanged.  A positive x below
+// 2^-96 takes the compiler's scaled sequence instead (rare).
+__device__ __forceinline__ float sqrt_rn(float x) {
+    const float s = __builtin_amdgcn_sqrtf(x);
+    const float lo = __uint_as_float(__float_as_uint(s) - 1u);
+    const float hi = __uint_as_float(__float_as_uint(s) + 1u);
+    float r = s;
+    if (fmaf(-lo, s, x) <= 0.0f) r = lo;
+    if (fmaf(-hi, s, x) > 0.0f) r = hi;
+    const bool tiny = x < 0x1p-96f && x > 0.0f;
+    if (__any(tiny)) {              // a wave-uniform branch keeps it off the common path
+        asm volatile("");           // (and stops the compiler from speculating it)
+        if (tiny) r = sqrtf(x);
+    }
+    return r;
+}
+
 // The AdamW update of one element (M041 section 02), fp32, each operation
 // rounded, evaluated left to right as printed, on the unscaled and clipped
 // grad (the mixed-precision recipe of M041 section 06: unscale, check,
@@ -173,7 +195,7 @@ __device__ __forceinline__ void adamw_update(float &theta, float g_scaled, float
     v = s.beta2 * v + (s.one_minus_beta2 * g) * g;
     const float m_hat = m / s.bc1;
     const float v_hat = v / s.bc2;
-    const float denom = sqrtf(v_hat) + s.eps;
+    const float denom = sqrt_rn(v_hat) + s.eps;
     theta = theta * s.decay - (s.lr * m_hat) / denom;
 }
 
@@ -308,34 +330,58 @@ __device__ __forceinline__ void tile_dense(const TensorDesc &d, const void *grad
 // 8-bit codes: m signed (scale absmax|m|/127), v unsigned (scale max v/255),
 // one scale per 256-element block; an all-zero block has scale 0, codes 0.
 //
-// The code is round-half-even of the correctly rounded quotient x/s.  The
-// quotient is not formed per element: with inv_s = RN(1/s) (one division per
-// block), r = RN(x*inv_s) differs from x/s by at most |x/s|*2^-23 (plus 2^-150
-// on underflow) and RN(x/s) by at most |x/s|*2^-24; for |x/s| <= 256 both
-// stay within 4.6e-5 of x/s.  So when r is more than 2.5e-4 away from every
-// half-integer, r and RN(x/s) round to the same integer; otherwise (rare),
-// or when r is not finite (a tiny scale), the quotient itself is rounded.
-// r - rint(r) is exact here (Sterbenz), so the distance test is exact too.
-__host__ __device__ __forceinline__ float round_quotient(float x, float s, float inv_s) {
-    const float r = x * inv_s;
-    const float q = rintf(r);
-    const float dist = fabsf(fabsf(r - q) - 0.5f);   // to the nearest half-integer
-    if (!(fabsf(r) <= 256.0f) || !(dist > 2.5e-4f)) return rintf(x / s);
+// The code is round-half-even of the correctly rounded quotient x/s, clamped
+// to the code range.  The quotient is not formed per element.  When s is a
+// normal number (the usual case), inv = v_rcp_f32(s) is within one ulp of
+// 1/s, so r = RN(x*inv) is within |x/s|*3*2^-24 of x/s, and RN(x/s) within
+// |x/s|*2^-24; every |x| <= amax has |x/s| <= 127/(1 - 2^-24) (resp. 255/..),
+// so both stay within 3e-5 of x/s and inside the code range.  When r is more
+// than 2.5e-4 away from every half-integer, r and RN(x/s) therefore round to
+// the same integer; otherwise (rare, or a NaN), or when s is zero, denormal
+// or infinite, the quotient itself is rounded and clamped.  r - rint(r) is
+// exact (Sterbenz), so the distance test is exact too.
+struct BlockScale {
+    float s, inv;
+    bool fast;      // s normal and finite: inv is usable
+};
+
+__device__ __forceinline__ BlockScale block_scale(float amax, float levels) {
+    BlockScale b;
+    b.s = amax / levels;
+    b.fast = b.s >= 0x1p-126f && b.s <= 0x1p126f;
+    b.inv = __builtin_amdgcn_rcpf(b.s);
+    return b;
+}
+
+// The code of x as an integer-valued float in [lo, hi].
+__device__ __forceinline__ float code_value(float x, const BlockScale &b, float lo, float hi) {
+    const float r = x * b.inv;
+    float q = rintf(r);
+    const bool exact = !b.fast || !(fabsf(fabsf(r - q) - 0.5f) > 2.5e-4f);
+    if (__any(exact)) {             // wave-uniform: rare except in degenerate blocks
+        asm volatile("");           // not speculated
+        if (exact) q = b.s == 0.0f ? 0.0f : fminf(fmaxf(rintf(x / b.s), lo), hi);
+    }
     return q;
 }
 
-__device__ __forceinline__ uint32_t encode_signed(float x, float s, float inv_s) {
-    if (s == 0.0f) return 0u;
-    float r = round_quotient(x, s, inv_s);
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    return (uint32_t)(uint8_t)(int8_t)(int)r;
+// Four codes packed little-endian into one word (v_cvt_pk_u8_f32 writes an
+// integer-valued float in [0, 255] into one byte); signed codes are packed
+// offset by 128 and flipped back, which is two's complement per byte.
+__device__ __forceinline__ uint32_t pack_codes_signed(const float (&x)[kVec], const BlockScale &b) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int j = 0; j < kVec; ++j)
+        w = __builtin_amdgcn_cvt_pk_u8_f32(code_value(x[j], b, -127.0f, 127.0f) + 128.0f, j, w);
+    return w ^ 0x80808080u;
 }
 
-__device__ __forceinline__ uint32_t encode_unsigned(float x, float s, float inv_s) {
-    if (s == 0.0f) return 0u;
-    float r = round_quotient(x, s, inv_s);
-    r = fminf(fmaxf(r, 0.0f), 255.0f);
-    return (uint32_t)(int)r;
+__device__ __forceinline__ uint32_t pack_codes_unsigned(const float (&x)[kVec], const BlockScale &b) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int j = 0; j < kVec; ++j)
+        w = __builtin_amdgcn_cvt_pk_u8_f32(code_value(x[j], b, 0.0f, 255.0f), j, w);
+    return w;
 }
 
 // One tile = one 8-bit block (block index base/256 of the tensor): decode
@@ -393,23 +439,15 @@ __device__ __forceinline__ void tile_q8(const TensorDesc &d, const void *grad,
     }
     am = wave_max(am);
     av = wave_max(av);
-    const float sm = am / 127.0f;
-    const float sv = av / 255.0f;
-    const float inv_sm = sm != 0.0f ? 1.0f / sm : 0.0f;
-    const float inv_sv = sv != 0.0f ? 1.0f / sv : 0.0f;
+    const BlockScale bm = block_scale(am, 127.0f);
+    const BlockScale bv = block_scale(av, 255.0f);
     if (threadIdx.x == 0) {
-        gptr<float>(static_cast<void *>(d.m_scale))[blk] = sm;
-        gptr<float>(static_cast<void *>(d.v_scale))[blk] = sv;
+        gptr<float>(static_cast<void *>(d.m_scale))[blk] = bm.s;
+        gptr<float>(static_cast<void *>(d.v_scale))[blk] = bv.s;
     }
     if (full) {
-        uint32_t cm = 0, cv = 0;
-#pragma unroll
-        for (int j = 0; j < kVec; ++j) {
-            cm |= encode_signed(m[j], sm, inv_sm) << (8 * j);
-            cv |= encode_unsigned(v[j], sv, inv_sv) << (8 * j);
-        }
-        store_u32<NT>(d.m, e, cm);
-        store_u32<NT>(d.v, e, cv);
+        store_u32<NT>(d.m, e, pack_codes_signed(m, bm));
+        store_u32<NT>(d.v, e, pack_codes_unsigned(v, bv));
         if (vec_ok) {
             store4<PT, NT>(d.param, e, th);
         } else {
@@ -420,8 +458,8 @@ __device__ __forceinline__ void tile_q8(const TensorDesc &d, const void *grad,
 #pragma unroll
         for (int j = 0; j < kVec; ++j) {
             if (off + j < n) {
-                gptr<int8_t>(d.m)[e + j] = (int8_t)encode_signed(m[j], sm, inv_sm);
-                gptr<uint8_t>(d.v)[e + j] = (uint8_t)encode_unsigned(v[j], sv, inv_sv);
+                gptr<int8_t>(d.m)[e + j] = (int8_t)(int)code_value(m[j], bm, -127.0f, 127.0f);
+                gptr<uint8_t>(d.v)[e + j] = (uint8_t)(int)code_value(v[j], bv, 0.0f, 255.0f);
                 store1<PT>(d.param, e + j, th[j]);
             }
         }

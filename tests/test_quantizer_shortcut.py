@@ -1,27 +1,51 @@
-"""The update kernel encodes 8-bit codes as rint(x * RN(1/s)) with a guard
-that falls back to rint(RN(x/s)) near half-integers (round_quotient in
-csrc/apexw_kernels.hpp).  This CPU test checks that rule, written out with
-numpy's IEEE fp32 arithmetic, against the definition rint(RN(x/s)) on ten
-million random pairs and on constructed near-ties.  (The GPU parity tests
-check the kernel itself bit for bit against the oracle.)"""
+"""CPU checks of the two rounding shortcuts the update kernel takes instead
+of a correctly rounded division or square root per element (code_value and
+sqrt_rn in csrc/apexw_kernels.hpp), written out with numpy's IEEE fp32
+arithmetic and checked against the definitions.  The hardware approximations
+they start from (v_rcp_f32, v_sqrt_f32: within one ulp) are modelled by
+trying the correctly rounded value and both of its neighbours.  (The GPU
+parity tests check the kernel itself bit for bit against the oracle.)"""
 import numpy as np
 
+F32 = np.float32
 
-def shortcut(x, s):
+
+def _neighbours(a):
+    return (np.nextafter(a, F32(-np.inf)), a, np.nextafter(a, F32(np.inf)))
+
+
+# ------------------------------------------------------------ 8-bit codes
+
+def code_rule(x, s, inv, lo, hi):
+    """The kernel's rule: r = x*inv rounded to even, unless the block scale
+    is not a normal number or r is within 2.5e-4 of a half-integer (or NaN);
+    then the correctly rounded quotient, rounded and clamped."""
     with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
-        inv = np.float32(1.0) / s
+        fast = (s >= F32(2.0 ** -126)) & (s <= F32(2.0 ** 126))
         r = x * inv
         q = np.rint(r)
-        dist = np.abs(np.abs(r - q) - np.float32(0.5))
-        slow = ~(np.abs(r) <= np.float32(256.0)) | ~(dist > np.float32(2.5e-4))
-        return np.where(slow, np.rint(x / s), q), slow
+        exact = ~fast | ~(np.abs(np.abs(r - q) - F32(0.5)) > F32(2.5e-4))
+        slow = np.where(s == 0, F32(0), np.clip(np.rint(x / s), lo, hi))
+        return np.where(exact, slow, q), exact
 
 
-def check(x, s):
-    got, slow = shortcut(x, s)
-    want = np.rint(x / s)
-    assert np.array_equal(got, want)
-    return slow.mean()
+def code_definition(x, s, lo, hi):
+    """The quantizer's definition (the oracle's): round-half-even of the
+    correctly rounded quotient, clamped; scale 0 gives code 0."""
+    with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
+        return np.where(s == 0, F32(0), np.clip(np.rint(x / s), lo, hi))
+
+
+def check_codes(x, s, lo, hi):
+    want = code_definition(x, s, lo, hi)
+    frac = []
+    with np.errstate(over="ignore", divide="ignore"):
+        inv0 = (F32(1.0) / s).astype(F32)
+    for inv in _neighbours(inv0):
+        got, exact = code_rule(x, s, inv, lo, hi)
+        assert np.array_equal(got, want)
+        frac.append(exact.mean())
+    return max(frac)
 
 
 def test_random_blocks_match_the_definition():
@@ -29,31 +53,75 @@ def test_random_blocks_match_the_definition():
     total_slow = 0.0
     for rep in range(10):
         n = 1_000_000
-        amax = np.float32(np.exp(rng.uniform(-80, 80, n))).astype(np.float32)
-        for div in (np.float32(127.0), np.float32(255.0)):
-            s = (amax / div).astype(np.float32)
-            x = (amax * rng.uniform(-1, 1, n).astype(np.float32)).astype(np.float32)
-            if div == 255.0:
+        amax = np.float32(np.exp(rng.uniform(-80, 80, n))).astype(F32)
+        for levels, lo in ((F32(127.0), F32(-127.0)), (F32(255.0), F32(0.0))):
+            s = (amax / levels).astype(F32)
+            x = (amax * rng.uniform(-1, 1, n).astype(F32)).astype(F32)
+            if lo == 0:
                 x = np.abs(x)
             x[:1000] = amax[:1000]                         # the block maximum itself
-            total_slow += check(x, s)
+            total_slow += check_codes(x, s, lo, levels)
     assert total_slow / 20 < 0.01
 
 
-def test_near_ties_match_the_definition():
+def test_near_ties_and_degenerate_scales_match_the_definition():
     rng = np.random.default_rng(1)
     n = 1_000_000
-    s = np.float32(np.exp(rng.uniform(-60, 60, n))).astype(np.float32)
-    k = rng.integers(-127, 127, n).astype(np.float32) + np.float32(0.5)
-    x = (k.astype(np.float64) * s.astype(np.float64)).astype(np.float32)
+    s = np.float32(np.exp(rng.uniform(-60, 60, n))).astype(F32)
+    k = rng.integers(-127, 127, n).astype(F32) + F32(0.5)
+    x = (k.astype(np.float64) * s.astype(np.float64)).astype(F32)
     # walk a few ulps either side of each near-tie
     for step in range(-3, 4):
-        xs = np.nextafter(x, np.float32(np.inf) if step > 0 else np.float32(-np.inf))
-        for _ in range(abs(step) - 1):
-            xs = np.nextafter(xs, np.float32(np.inf) if step > 0 else np.float32(-np.inf))
-        check(xs if step else x, s)
-    # tiny and denormal scales, zero values
-    s2 = np.array([1e-45, 1e-40, 1e-38, 3e-39, 1e38], np.float32)
-    for sv in s2:
-        xv = (np.float32(sv) * np.arange(-127, 128, dtype=np.float32)).astype(np.float32)
-        check(xv, np.full_like(xv, sv))
+        xs = x
+        for _ in range(abs(step)):
+            xs = np.nextafter(xs, F32(np.inf) if step > 0 else F32(-np.inf))
+        check_codes(xs, s, F32(-127.0), F32(127.0))
+    # zero, denormal, tiny, huge and infinite scales, every code value
+    for sv in (0.0, 1e-45, 1e-40, 1e-38, 3e-39, 1.2e-38, 1e38, 3e36, np.inf):
+        xv = (np.float32(sv if np.isfinite(sv) else 1.0) * np.arange(-127, 128, dtype=F32)).astype(F32)
+        check_codes(xv, np.full_like(xv, F32(sv)), F32(-127.0), F32(127.0))
+        check_codes(np.abs(xv), np.full_like(xv, F32(sv)), F32(0.0), F32(255.0))
+
+
+# ------------------------------------------------------------ square root
+
+def sqrt_rule(x, s0):
+    """The kernel's selection from an approximation s0 >= 0: the lower neighbour
+    if x <= lo*s0, the upper one if x > hi*s0 (signs of the fma residuals,
+    exact here: lo*s0 is exact in float64 and the float64 difference keeps
+    its sign)."""
+    lo = (s0.view(np.uint32) - np.uint32(1)).view(F32)      # the kernel steps the bits
+    hi = (s0.view(np.uint32) + np.uint32(1)).view(F32)      # (at 0: lo is a NaN)
+    x64 = x.astype(np.float64)
+    with np.errstate(invalid="ignore"):
+        r = np.where(x64 - lo.astype(np.float64) * s0.astype(np.float64) <= 0, lo, s0)
+        r = np.where(x64 - hi.astype(np.float64) * s0.astype(np.float64) > 0, hi, r)
+    return r
+
+
+def check_sqrt(x):
+    want = np.sqrt(x)                       # IEEE: correctly rounded
+    for s0 in _neighbours(want):
+        got = sqrt_rule(x, s0)
+        ok = (got == want) | (np.isnan(got) & np.isnan(want))
+        assert ok.all(), x[~ok][:5]
+
+
+def test_sqrt_selection_on_every_mantissa_of_two_binades():
+    m = np.arange(1 << 23, dtype=np.uint32)
+    for exp_bits in (127, 128):             # [1, 2) and [2, 4): both exponent parities
+        check_sqrt(((np.uint32(exp_bits) << 23) | m).view(F32))
+
+
+def test_sqrt_selection_over_the_range_it_is_used_on():
+    rng = np.random.default_rng(2)
+    x = np.exp2(rng.uniform(-96, 128, 5_000_000)).astype(F32)
+    x = x[np.isfinite(x)]
+    check_sqrt(x)
+    edges = np.array([2.0 ** -96, np.nextafter(F32(2.0 ** -96), F32(1)), 1.0, 4.0,
+                      np.finfo(F32).max, np.finfo(F32).tiny * 2 ** 30], F32)
+    check_sqrt(edges)
+    # zero and +inf come through the rule unchanged
+    for v in (F32(0.0), F32(np.inf)):
+        s0 = np.array([v], F32)
+        assert sqrt_rule(np.array([v], F32), s0)[0] == v
