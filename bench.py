@@ -92,7 +92,7 @@ def cpu_baseline(w, budget_s: float = 12.0):
         ref.step([th], [g], grp)
         calls += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or calls >= 50:
+        if el >= budget_s or calls >= 400:
             break
     return {
         "value": n * calls / el,
@@ -103,6 +103,83 @@ def cpu_baseline(w, budget_s: float = 12.0):
                   "%d calls in %.1f s, single-threaded scalar C oracle (gcc -O2, no contraction)"
                   % (n, w.n_params, w.param_dtype[0], w.grad_dtype[0], w.state_fmt, calls, el),
     }
+
+
+def device_copy_gbps(torch, dev, stream) -> float:
+    """A STREAM-style device copy for context: 1 GiB read + 1 GiB written."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    best = None
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        dst.copy_(src)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        best = ms if best is None else min(best, ms)
+    del src, dst
+    return 2 * (1 << 30) / (best / 1e3) / 1e9
+
+
+def torch_compare(torch, w, dev, steps, warmup):
+    """torch.optim.AdamW (fused and foreach) against this library on the
+    dtypes torch's fused kernel takes: grads and both moments in the
+    parameter's dtype.  Context only; the grads are the workload's, cast."""
+    import workloads as W
+    from tensor_adamw_optimizer_amd import _lib as L
+
+    res = {}
+    params = W.init_params(w, dev)
+    grads = [torch.randn(p.shape, device=dev).mul_(w.grad_std).to(p.dtype) for p in params]
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(steps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    groups = []
+    for gi, g in enumerate(w.groups):
+        ps = [p for p, j in zip(params, w.group_of) if j == gi]
+        groups.append({"params": ps, "lr": g.lr, "betas": (g.beta1, g.beta2), "eps": g.eps,
+                       "weight_decay": g.weight_decay})
+    for p, g in zip(params, grads):
+        p.grad = g
+    for mode in ("fused", "foreach"):
+        opt = torch.optim.AdamW(groups, **{mode: True})
+        ms = timed(opt.step)
+        res["torch_%s_adamw_ms" % mode] = ms
+        del opt
+        torch.cuda.empty_cache()
+    # this library on the same dtypes (moments in the parameter dtype)
+    same_fmt = {W.F32: L.APEXW_STATE_F32, W.BF16: L.APEXW_STATE_BF16}[w.param_dtype[0]]
+    dts = {W.F32: L.APEXW_F32, W.BF16: L.APEXW_BF16}
+    if len(set(w.param_dtype)) == 1:
+        sb = L.apexw_state_bytes(w.numels, same_fmt)
+        wb = L.apexw_workspace_bytes(w.numels)
+        state = torch.empty(sb, dtype=torch.uint8, device=dev)
+        ws = torch.empty(wb, dtype=torch.uint8, device=dev)
+        h = L.apexw_create(w.numels, [dts[d] for d in w.param_dtype], [dts[d] for d in w.param_dtype],
+                           w.group_of, len(w.groups), same_fmt, state.data_ptr(), sb,
+                           ws.data_ptr(), wb, stream.cuda_stream)
+        pa = L.make_ptrs([p.data_ptr() for p in params])
+        ga = L.make_ptrs([g.data_ptr() for g in grads])
+        ga_groups = L.make_groups(w.groups)
+        res["apexw_same_dtypes_ms"] = timed(
+            lambda: L.apexw_step(h, ga_groups, len(w.groups), pa, ga, 0, stream.cuda_stream))
+        L.apexw_destroy(h)
+    res["compare_dtypes"] = "params, grads and moments all %s" % "+".join(sorted(set(w.param_dtype)))
+    for p in params:
+        p.grad = None
+    return res
 
 
 def main() -> int:
@@ -125,6 +202,12 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, run a 1 GiB device copy 3x (counter calibration)")
+    ap.add_argument("--flush-mall", action="store_true",
+                    help="write 512 MiB between steps (evicts the 256 MB Infinity Cache) "
+                         "and time each step on its own")
+    ap.add_argument("--torch-compare", action="store_true",
+                    help="also time torch.optim.AdamW (fused and foreach) and this library on "
+                         "the dtypes torch supports for the workload (context only)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the optimizer step is benchmarked on a "
@@ -205,18 +288,35 @@ def main() -> int:
     torch.cuda.synchronize()
     print("bench: warm-up done", file=sys.stderr, flush=True)
 
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev[0].record(stream)
-    for k in range(args.steps):
-        step()
-        ev[k + 1].record(stream)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    kernel_ms = [ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps)]
+    if args.flush_mall:
+        # each step starts with a cold Infinity Cache; only the steps are timed
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for k in range(args.steps):
+            flush.fill_(k & 0xFF)
+            ev_a[k].record(stream)
+            step()
+            ev_b[k].record(stream)
+        torch.cuda.synchronize()
+        kernel_ms = [a.elapsed_time(b) for a, b in zip(ev_a, ev_b)]
+        elapsed = sum(kernel_ms) / 1e3
+        del flush
+    else:
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev[0].record(stream)
+        for k in range(args.steps):
+            step()
+            ev[k + 1].record(stream)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        kernel_ms = [ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps)]
     avg_kernel_s = sum(kernel_ms) / len(kernel_ms) / 1e3
     print("bench: timed %d steps" % args.steps, file=sys.stderr, flush=True)
+    max_mem = torch.cuda.max_memory_allocated(dev)
 
     if args.calib_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -225,6 +325,8 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    copy_gbps = device_copy_gbps(torch, dev, stream)
 
     ab = algorithmic_bytes(w)
     if args.amp:        # the check pass reads every grad once more
@@ -256,7 +358,12 @@ def main() -> int:
         "hbm_gbps": (ab / (elapsed / args.steps)) / 1e9,
         "hbm_frac_of_peak": (ab / (elapsed / args.steps)) / 1e9 / HBM_PEAK_GBPS,
         "kernel_ms": {"avg": sum(kernel_ms) / len(kernel_ms), "min": min(kernel_ms),
-                      "max": max(kernel_ms)},
+                      "median": sorted(kernel_ms)[len(kernel_ms) // 2], "max": max(kernel_ms)},
+        "residency": ("cache-resident (algorithmic bytes per step below the 256 MB "
+                      "Infinity Cache)" if ab < (256 << 20) and not args.flush_mall
+                      else "hbm" + (" (Infinity Cache flushed before each step)"
+                                    if args.flush_mall else "")),
+        "max_memory_allocated": max_mem,
         "launch": {"tile_elems": tile, "tiles": n_tiles, "workgroups": wgs,
                    "workgroups_per_cu_cap": occupancy},
         "state_bytes": state_bytes,
@@ -271,9 +378,13 @@ def main() -> int:
             "kernel": "adamw_step_kernel" + ((" + grad_norm kernels" if args.clip > 0 else " + unscale_check_kernel") if args.amp else ""),
         },
     }
+    out["context"] = {"device_copy_gbps": copy_gbps,
+                      "device_copy": "torch copy_ of 1 GiB, read + write bytes / time, best of 5"}
     L.apexw_destroy(h)
     del params, grads, state, ws
     torch.cuda.empty_cache()
+    if args.torch_compare:
+        out["context"].update(torch_compare(torch, w, dev, args.steps, args.warmup))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
