@@ -133,8 +133,9 @@ WsLayout ws_layout(int32_t n, const int64_t *numel) {
     w.grads = w.desc + round_up((int64_t)n * (int64_t)sizeof(TensorDesc), kTableAlign);
     w.records = w.grads + round_up((int64_t)n * 8, kTableAlign);
     w.tiles = w.records + round_up((int64_t)n * (int64_t)sizeof(StepRecord), kTableAlign);
-    // each launch's table is padded to a multiple of kXcds entries
-    w.partials = w.tiles + round_up((w.n_tiles + kMaxLaunches * kXcds) * 4, kTableAlign);
+    // each launch's table is padded to a multiple of kXcds entries; the read
+    // passes load table entries in fours and may read up to 3 past the end
+    w.partials = w.tiles + round_up((w.n_tiles + kMaxLaunches * kXcds + 4) * 4, kTableAlign);
     w.partials2 = w.partials + round_up(w.n_tiles * 8, kTableAlign);
     w.total = n == 0 ? 0 : w.partials2 + round_up(kReduceBlocks * 8, kTableAlign);
     return w;
@@ -327,10 +328,14 @@ int launch_cap(const apexw_opt *h) { return h->wg_override > 0 ? h->wg_override 
 // there each wave walks about 8 tiles (measured on MI355X: 7.4 TB/s for the
 // check against 4.7 TB/s with one tile per wave), keeping a multiple of 8
 // workgroups (one set per XCD) and at least 2048 of them.  Results do not depend on it.
+// Workgroups of a read pass over a launch of `tiles` tiles: a workgroup takes
+// groups of kReadBatch tiles (read_groups() of them in all), about two groups
+// each, at least 2048 workgroups, a multiple of the XCD count.
 int64_t read_pass_grid(const apexw_opt *h, int64_t tiles) {
-    if (h->wg_override > 0) return std::min<int64_t>(tiles, h->wg_override);
-    const int64_t g = round_up(std::max<int64_t>(ceil_div(tiles, 8), 2048), kXcds);
-    return std::min(tiles, g);
+    const int64_t groups = read_groups(ceil_div(tiles, kXcds));
+    if (h->wg_override > 0) return std::min<int64_t>(groups, h->wg_override);
+    const int64_t g = round_up(std::max<int64_t>(ceil_div(groups, 2), 2048), kXcds);
+    return std::min(groups, g);
 }
 
 }  // namespace

@@ -538,7 +538,8 @@ __device__ __forceinline__ T load_uniform(const T *tab, int32_t i) {
 // workgroups one XCD runs (k, k+8, k+16, ...) read consecutive entries and
 // share the XCD's L2 lines.
 __device__ __forceinline__ int64_t table_pos(const KernelArgs &a, int64_t k) {
-    return a.table_begin + (k % kXcds) * a.table_stride + k / kXcds;
+    const uint64_t uk = (uint64_t)k;                  // k >= 0: shifts, not divisions
+    return a.table_begin + (int64_t)(uk % kXcds) * a.table_stride + (int64_t)(uk / kXcds);
 }
 
 // The update: one 256-element tile per workgroup (the grid-stride loop only
@@ -583,38 +584,88 @@ __global__ __launch_bounds__(kThreads) void adamw_step_kernel(KernelArgs a) {
 // (the caller clears it), by plain stores of the same value; grads are not
 // rewritten -- the update applies inv_scale itself.  One wave per tile, the
 // tiles of one (param, grad) dtype launch.
+// The read passes below take their tiles in groups of kReadBatch: group j
+// is XCD stripe x = j % 8 of the launch's tile table, entries 4c .. 4c+3 with
+// c = j / 8, i.e. the logical tiles x + 8(4c + u), u = 0..3.  Its four table
+// entries are one 16-byte load, then the four grad pointers and descriptor
+// fields are fetched together, then every grad load of the group is issued
+// before any is used, so one wave keeps four tiles in flight.  What each
+// tile contributes does not depend on the grouping.
+constexpr int kReadBatch = 4;
+
+// Number of groups of a launch whose table stripes hold `stride` entries.
+__host__ __device__ __forceinline__ int64_t read_groups(int64_t stride) {
+    return kXcds * ((stride + kReadBatch - 1) / kReadBatch);
+}
+
+// A tile of a read group: grad (nullptr: absent), first element, valid
+// length (0 for a tile past the launch end), logical tile index.
+struct ReadTile {
+    const void *grad;
+    int64_t base;
+    int n;
+    int64_t k;
+};
+
+// The tiles of group j; false if the group starts past the launch end.  The
+// 16-byte table load may reach 3 entries past a stripe's end (the table
+// allocation is padded for it); such entries are never used.
+__device__ __forceinline__ bool read_group(const KernelArgs &a, int64_t j,
+                                           ReadTile (&t)[kReadBatch]) {
+    const int64_t x = j % kXcds, c = j / kXcds;
+    const int64_t k0 = x + (int64_t)kXcds * kReadBatch * c;
+    if (k0 >= a.tile_count) return false;
+    const APEXW_CONST int32_t *row =
+        cptr<int32_t>(a.tile_tensor) + a.table_begin + x * a.table_stride + kReadBatch * c;
+    int32_t ti[kReadBatch];
+#pragma unroll
+    for (int u = 0; u < kReadBatch; ++u) ti[u] = row[u];
+#pragma unroll
+    for (int u = 0; u < kReadBatch; ++u) {
+        t[u].k = k0 + (int64_t)kXcds * u;
+        const bool live = t[u].k < a.tile_count;
+        const int32_t i = live ? ti[u] : ti[0];
+        const APEXW_CONST int64_t *dd = cptr<int64_t>(&a.desc[i].numel);   // numel, first_tile
+        t[u].grad = reinterpret_cast<const void *>(cptr<uint64_t>(a.grads)[i]);
+        t[u].base = (a.tile_begin + (live ? t[u].k : k0) - dd[1]) * kTile;
+        const int64_t left = dd[0] - t[u].base;
+        t[u].n = !live ? 0 : left < kTile ? (int)left : kTile;
+    }
+    return true;
+}
+
+// The lane's 4 grad values of a tile (0 where absent or past the end).
+template <int GT, bool NT>
+__device__ __forceinline__ void load_tile_grads(const ReadTile &t, float (&g)[kVec]) {
+    const int off = threadIdx.x * kVec;
+    if (t.grad != nullptr && (((uintptr_t)t.grad) & 15u) == 0u && off + kVec <= t.n) {
+        load4<GT, NT>(t.grad, t.base + off, g);
+    } else {
+#pragma unroll
+        for (int j = 0; j < kVec; ++j)
+            g[j] = t.grad != nullptr && off + j < t.n ? load1<GT>(t.grad, t.base + off + j) : 0.0f;
+    }
+}
+
 template <int GT, bool NT>
 __global__ __launch_bounds__(kThreads) void unscale_check_kernel(KernelArgs a) {
-    const APEXW_CONST int32_t *tile_tensor = cptr<int32_t>(a.tile_tensor);
-    const APEXW_CONST uint64_t *grads = cptr<uint64_t>(a.grads);
     const float inv = a.inv_scale != nullptr ? *a.inv_scale : 1.0f;
-    int64_t k = blockIdx.x;
+    const int64_t groups = read_groups(a.table_stride);
+    const int off = threadIdx.x * kVec;
     bool bad = false;
-    for (;;) {
-        const int32_t i = tile_tensor[table_pos(a, k)];
-        const void *grad = reinterpret_cast<const void *>(grads[i]);
-        const TensorDesc d = load_uniform(a.desc, i);
-        const int64_t base = (a.tile_begin + k - d.first_tile) * kTile;
-        const int64_t left = d.numel - base;
-        const int n = left < kTile ? (int)left : kTile;
-        asm volatile("" ::"s"(grad));
-        if (grad != nullptr && n > 0) {
-            const int off = threadIdx.x * kVec;
-            float g[kVec];
-            if ((((uintptr_t)grad) & 15u) == 0u && off + kVec <= n) {
-                load4<GT, NT>(grad, base + off, g);
-            } else {
+    for (int64_t jg = blockIdx.x; jg < groups; jg += gridDim.x) {
+        ReadTile t[kReadBatch];
+        float g[kReadBatch][kVec];
+        if (!read_group(a, jg, t)) continue;
 #pragma unroll
-                for (int j = 0; j < kVec; ++j) g[j] = off + j < n ? load1<GT>(grad, base + off + j) : 0.0f;
-            }
+        for (int u = 0; u < kReadBatch; ++u) load_tile_grads<GT, NT>(t[u], g[u]);
+#pragma unroll
+        for (int u = 0; u < kReadBatch; ++u)
 #pragma unroll
             for (int j = 0; j < kVec; ++j) {
-                const float u = g[j] * inv;
-                bad |= (off + j < n) && !(fabsf(u) <= 3.40282347e38f);   // inf or NaN
+                const float x = g[u][j] * inv;
+                bad |= t[u].grad != nullptr && off + j < t[u].n && !(fabsf(x) <= 3.40282347e38f);
             }
-        }
-        k += gridDim.x;
-        if (k >= a.tile_count) break;
     }
     if (__any(bad) && threadIdx.x == 0) *gptr<float>(static_cast<void *>(a.found_inf_out)) = 1.0f;
 }
@@ -625,8 +676,8 @@ __global__ __launch_bounds__(kThreads) void unscale_check_kernel(KernelArgs a) {
 // the norm of all present unscaled grads u = g * inv_scale (fp32, as the
 // update uses them), squares and sums in fp64, reduced in a fixed order so
 // the result does not depend on scheduling:
-//  1. grad_norm_partials_kernel: one wave per tile sums its lanes' squares
-//     (lane order, then a butterfly over the wave) into partials[tile]; tiles
+//  1. grad_norm_partials_kernel: the squares of each tile are summed by one
+//     wave (lane order, then wave_sum's fixed order) into partials[tile]; tiles
 //     without a grad contribute 0; optionally sets found_inf_out like the
 //     unscale check;
 //  2. grad_norm_reduce_kernel: workgroup b sums partials[b*C .. (b+1)*C) with
@@ -635,50 +686,63 @@ __global__ __launch_bounds__(kThreads) void unscale_check_kernel(KernelArgs a) {
 //     writes the norm (fp64 sqrt) and the clip coefficient max_norm / norm
 //     when norm > max_norm (fp64, rounded once to fp32), else 1.
 
+// DPP move of a double (both halves) within 16-lane rows.
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+    const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(x), CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(x), CTRL, 0xF, 0xF, false);
+    return __hiloint2double(hi, lo);
+}
+
+__device__ __forceinline__ double lane_f64(double x, int lane) {
+    return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(x), lane),
+                            __builtin_amdgcn_readlane(__double2loint(x), lane));
+}
+
+// Sum over the 64 lanes, the same value in every lane, in a fixed order:
+// within each 16-lane row pairs at distance 1 and 2 (quad swaps), then the
+// two quads of each half-row and the two half-rows (mirrors) -- each lane
+// adds its partner's partial, and a + b == b + a, so the row's lanes agree
+// bit for bit -- then (row0 + row1) + (row2 + row3).
 __device__ __forceinline__ double wave_sum(double x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-    return x;
+    x = x + dpp_f64<0xB1>(x);     // quad_perm [1,0,3,2]
+    x = x + dpp_f64<0x4E>(x);     // quad_perm [2,3,0,1]
+    x = x + dpp_f64<0x141>(x);    // row_half_mirror
+    x = x + dpp_f64<0x140>(x);    // row_mirror
+    return (lane_f64(x, 0) + lane_f64(x, 16)) + (lane_f64(x, 32) + lane_f64(x, 48));
 }
 
 template <int GT, bool NT>
 __global__ __launch_bounds__(kThreads) void grad_norm_partials_kernel(KernelArgs a) {
-    const APEXW_CONST int32_t *tile_tensor = cptr<int32_t>(a.tile_tensor);
-    const APEXW_CONST uint64_t *grads = cptr<uint64_t>(a.grads);
     const float inv = a.inv_scale != nullptr ? *a.inv_scale : 1.0f;
-    int64_t k = blockIdx.x;
+    const int64_t groups = read_groups(a.table_stride);
+    const int off = threadIdx.x * kVec;
     bool bad = false;
-    for (;;) {
-        const int32_t i = tile_tensor[table_pos(a, k)];
-        const void *grad = reinterpret_cast<const void *>(grads[i]);
-        const TensorDesc d = load_uniform(a.desc, i);
-        const int64_t base = (a.tile_begin + k - d.first_tile) * kTile;
-        const int64_t left = d.numel - base;
-        const int n = left < kTile ? (int)left : kTile;
-        asm volatile("" ::"s"(grad));
-        double sq = 0.0;
-        if (grad != nullptr && n > 0) {
-            const int off = threadIdx.x * kVec;
-            float g[kVec];
-            if ((((uintptr_t)grad) & 15u) == 0u && off + kVec <= n) {
-                load4<GT, NT>(grad, base + off, g);
-            } else {
+    for (int64_t jg = blockIdx.x; jg < groups; jg += gridDim.x) {
+        ReadTile t[kReadBatch];
+        float g[kReadBatch][kVec];
+        if (!read_group(a, jg, t)) continue;
 #pragma unroll
-                for (int j = 0; j < kVec; ++j) g[j] = off + j < n ? load1<GT>(grad, base + off + j) : 0.0f;
-            }
+        for (int u = 0; u < kReadBatch; ++u) load_tile_grads<GT, NT>(t[u], g[u]);
+        double sq[kReadBatch];
+#pragma unroll
+        for (int u = 0; u < kReadBatch; ++u) {
+            sq[u] = 0.0;
 #pragma unroll
             for (int j = 0; j < kVec; ++j) {
-                const float u = g[j] * inv;
-                if (off + j < n) {
-                    bad |= !(fabsf(u) <= 3.40282347e38f);
-                    sq = sq + (double)u * (double)u;
+                const float x = g[u][j] * inv;
+                if (t[u].grad != nullptr && off + j < t[u].n) {
+                    bad |= !(fabsf(x) <= 3.40282347e38f);
+                    sq[u] = sq[u] + (double)x * (double)x;
                 }
             }
         }
-        sq = wave_sum(sq);
-        if (threadIdx.x == 0) gptr<double>(static_cast<void *>(a.partials))[a.tile_begin + k] = sq;
-        k += gridDim.x;
-        if (k >= a.tile_count) break;
+#pragma unroll
+        for (int u = 0; u < kReadBatch; ++u) sq[u] = wave_sum(sq[u]);
+#pragma unroll
+        for (int u = 0; u < kReadBatch; ++u)
+            if (threadIdx.x == 0 && t[u].k < a.tile_count)
+                gptr<double>(static_cast<void *>(a.partials))[a.tile_begin + t[u].k] = sq[u];
     }
     if (a.found_inf_out != nullptr && __any(bad) && threadIdx.x == 0)
         *gptr<float>(static_cast<void *>(a.found_inf_out)) = 1.0f;
