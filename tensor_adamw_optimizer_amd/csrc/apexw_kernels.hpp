@@ -274,6 +274,35 @@ __device__ __forceinline__ void store1(void *base, int64_t e, float x) {
     else gptr<uint16_t>(base)[e] = (uint16_t)f32_to_bf16_bits(x);
 }
 
+// A tile's element offsets are multiples of 4, so an array's 4-element
+// vector accesses are aligned exactly when its base pointer is (16 B for
+// fp32, 8 B for bf16).  Arrays that are not -- views into flat buffers at odd
+// offsets -- take 4 element accesses instead; the state arrays always align.
+template <int DT>
+__device__ __forceinline__ bool vec_aligned(const void *p) {
+    return ((uintptr_t)p & (DT == APEXW_F32 ? 15u : 7u)) == 0u;
+}
+
+template <int DT, bool NT>
+__device__ __forceinline__ void load4_any(const void *base, int64_t e, float (&x)[kVec], bool vec) {
+    if (vec) {
+        load4<DT, NT>(base, e, x);
+    } else {
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) x[j] = load1<DT>(base, e + j);
+    }
+}
+
+template <int DT, bool NT>
+__device__ __forceinline__ void store4_any(void *base, int64_t e, const float (&x)[kVec], bool vec) {
+    if (vec) {
+        store4<DT, NT>(base, e, x);
+    } else {
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) store1<DT>(base, e + j, x[j]);
+    }
+}
+
 // ---------------------------------------------------------------- wave max
 
 // Maximum over the 64 lanes of a wave, returned to every lane.
@@ -293,35 +322,45 @@ __device__ __forceinline__ float wave_max(float x) {
 // ---------------------------------------------------------------- tiles
 
 // One 256-element tile of a tensor with fp32 or bf16 moments (ST = element
-// type of m and v).  n = valid elements in this tile (1..256).
+// type of m and v).  n = valid elements in this tile (1..256).  A full tile
+// takes the vector path.  In a tensor's last, partial tile every lane loads
+// its valid elements one by one (zeros elsewhere), runs the update on all 4
+// values together -- one converged pass instead of one per element -- and
+// stores only the valid ones.
 template <int PT, int GT, int ST, bool NT>
 __device__ __forceinline__ void tile_dense(const TensorDesc &d, const void *grad,
                                            int64_t base, int n, const StepScalars &s) {
     const int off = threadIdx.x * kVec;
     const int64_t e = base + off;
-    const bool vec_ok = (((uintptr_t)d.param | (uintptr_t)grad) & 15u) == 0u;
     float th[kVec], g[kVec], m[kVec], v[kVec];
-    if (vec_ok && off + kVec <= n) {
+    if (n == kTile) {                                  // wave-uniform
+        const bool pv = vec_aligned<PT>(d.param), gv = vec_aligned<GT>(grad);
         load4<ST, NT>(d.m, e, m);
         load4<ST, NT>(d.v, e, v);
-        load4<GT, NT>(grad, e, g);
-        load4<PT, NT>(d.param, e, th);
+        load4_any<GT, NT>(grad, e, g, gv);
+        load4_any<PT, NT>(d.param, e, th, pv);
 #pragma unroll
         for (int j = 0; j < kVec; ++j) adamw_update(th[j], g[j], m[j], v[j], s);
-        store4<PT, NT>(d.param, e, th);
+        store4_any<PT, NT>(d.param, e, th, pv);
         store4<ST, NT>(d.m, e, m);
         store4<ST, NT>(d.v, e, v);
     } else {
 #pragma unroll
         for (int j = 0; j < kVec; ++j) {
+            const bool ok = off + j < n;
+            m[j] = ok ? load1<ST>(d.m, e + j) : 0.0f;
+            v[j] = ok ? load1<ST>(d.v, e + j) : 0.0f;
+            g[j] = ok ? load1<GT>(grad, e + j) : 0.0f;
+            th[j] = ok ? load1<PT>(d.param, e + j) : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) adamw_update(th[j], g[j], m[j], v[j], s);
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) {
             if (off + j < n) {
-                float t = load1<PT>(d.param, e + j);
-                float mm = load1<ST>(d.m, e + j);
-                float vv = load1<ST>(d.v, e + j);
-                adamw_update(t, load1<GT>(grad, e + j), mm, vv, s);
-                store1<PT>(d.param, e + j, t);
-                store1<ST>(d.m, e + j, mm);
-                store1<ST>(d.v, e + j, vv);
+                store1<PT>(d.param, e + j, th[j]);
+                store1<ST>(d.m, e + j, m[j]);
+                store1<ST>(d.v, e + j, v[j]);
             }
         }
     }
@@ -393,7 +432,7 @@ __device__ __forceinline__ void tile_q8(const TensorDesc &d, const void *grad,
     const int off = threadIdx.x * kVec;
     const int64_t e = base + off;
     const int64_t blk = base / APEXW_Q8_BLOCK;
-    const bool vec_ok = (((uintptr_t)d.param | (uintptr_t)grad) & 15u) == 0u;
+    const bool pv = vec_aligned<PT>(d.param), gv = vec_aligned<GT>(grad);
     const APEXW_GLOBAL int8_t *mq = gptr<int8_t>(static_cast<const void *>(d.m));
     const APEXW_GLOBAL uint8_t *vq = gptr<uint8_t>(static_cast<const void *>(d.v));
     const float sm_old = gptr<float>(static_cast<const void *>(d.m_scale))[blk];
@@ -408,16 +447,8 @@ __device__ __forceinline__ void tile_q8(const TensorDesc &d, const void *grad,
             m[j] = (float)(int8_t)(cm >> (8 * j)) * sm_old;
             v[j] = (float)(uint8_t)(cv >> (8 * j)) * sv_old;
         }
-        if (vec_ok) {
-            load4<GT, NT>(grad, e, g);
-            load4<PT, NT>(d.param, e, th);
-        } else {
-#pragma unroll
-            for (int j = 0; j < kVec; ++j) {
-                g[j] = load1<GT>(grad, e + j);
-                th[j] = load1<PT>(d.param, e + j);
-            }
-        }
+        load4_any<GT, NT>(grad, e, g, gv);
+        load4_any<PT, NT>(d.param, e, th, pv);
     } else {
 #pragma unroll
         for (int j = 0; j < kVec; ++j) {
@@ -448,12 +479,7 @@ __device__ __forceinline__ void tile_q8(const TensorDesc &d, const void *grad,
     if (full) {
         store_u32<NT>(d.m, e, pack_codes_signed(m, bm));
         store_u32<NT>(d.v, e, pack_codes_unsigned(v, bv));
-        if (vec_ok) {
-            store4<PT, NT>(d.param, e, th);
-        } else {
-#pragma unroll
-            for (int j = 0; j < kVec; ++j) store1<PT>(d.param, e + j, th[j]);
-        }
+        store4_any<PT, NT>(d.param, e, th, pv);
     } else {
 #pragma unroll
         for (int j = 0; j < kVec; ++j) {
@@ -638,8 +664,8 @@ __device__ __forceinline__ bool read_group(const KernelArgs &a, int64_t j,
 template <int GT, bool NT>
 __device__ __forceinline__ void load_tile_grads(const ReadTile &t, float (&g)[kVec]) {
     const int off = threadIdx.x * kVec;
-    if (t.grad != nullptr && (((uintptr_t)t.grad) & 15u) == 0u && off + kVec <= t.n) {
-        load4<GT, NT>(t.grad, t.base + off, g);
+    if (t.grad != nullptr && off + kVec <= t.n) {
+        load4_any<GT, NT>(t.grad, t.base + off, g, vec_aligned<GT>(t.grad));
     } else {
 #pragma unroll
         for (int j = 0; j < kVec; ++j)

@@ -309,6 +309,52 @@ def test_extreme_values_against_oracle(fmt):
     opt.close()
 
 
+@pytest.mark.parametrize("fmt", [W.STATE_F32, W.STATE_BF16, W.STATE_Q8])
+def test_views_into_flat_buffers_against_oracle(fmt):
+    """Parameters and grads that are views into flat buffers at arbitrary
+    element offsets (so most are not 16- or 8-byte aligned, and a parameter
+    and its grad are misaligned differently): bit-exact against the oracle
+    after three calls."""
+    _need_gpu()
+    say("case: flat-buffer views", fmt)
+    rng = np.random.default_rng(5)
+    sizes = [int(x) for x in rng.integers(1, 9000, 40)]
+    pdt = [(W.F32, W.BF16)[i % 2] for i in range(len(sizes))]
+    gdt = [(W.F32, W.BF16)[(i // 2) % 2] for i in range(len(sizes))]
+    groups = [W.Group(lr=1e-3, weight_decay=0.1), W.Group(lr=3e-3, beta1=0.8, eps=1e-6)]
+    group_of = [i % 2 for i in range(len(sizes))]
+    flat = {W.F32: torch.zeros(sum(sizes) + 7, device=DEV),
+            W.BF16: torch.zeros(sum(sizes) + 7, dtype=torch.bfloat16, device=DEV)}
+    gflat = {W.F32: torch.zeros(sum(sizes) + 7, device=DEV),
+             W.BF16: torch.zeros(sum(sizes) + 7, dtype=torch.bfloat16, device=DEV)}
+    params, poff, goff = [], {W.F32: 1, W.BF16: 3}, {W.F32: 2, W.BF16: 1}
+    views_g = []
+    for n, pd, gd in zip(sizes, pdt, gdt):
+        params.append(flat[pd][poff[pd]:poff[pd] + n])
+        poff[pd] += n
+        views_g.append(gflat[gd][goff[gd]:goff[gd] + n])
+        goff[gd] += n
+    gen = torch.Generator().manual_seed(9)
+    p_cpu = [(torch.randn(n, generator=gen) * 0.02).to(W.TORCH_DTYPE[d]) for n, d in zip(sizes, pdt)]
+    for p, c in zip(params, p_cpu):
+        p.copy_(c)
+    th_ref = [bits(c) for c in p_cpu]
+    opt = GpuOpt(sizes, pdt, gdt, group_of, len(groups), fmt)
+    ref = oracle.OracleAdamW(sizes, pdt, gdt, group_of, fmt)
+    for k in range(3):
+        g_cpu = [(torch.randn(n, generator=gen) * 1e-3).to(W.TORCH_DTYPE[d]) for n, d in zip(sizes, gdt)]
+        for v, c in zip(views_g, g_cpu):
+            v.copy_(c)
+        opt.step(groups, params, views_g)
+        ref.step(th_ref, [bits(c) for c in g_cpu], groups)
+    torch.cuda.synchronize()
+    for i in range(len(sizes)):
+        assert n_bit_mismatch(bits(params[i]), th_ref[i]) == 0, i
+        m, v = (bits(t) for t in opt.moments(i))
+        assert n_bit_mismatch(m, ref.m[i]) == 0 and n_bit_mismatch(v, ref.v[i]) == 0, i
+    opt.close()
+
+
 def test_all_grads_absent_and_pointer_changes():
     """No grads at all: nothing changes.  Grads moved to new buffers between
     calls: the library follows the new pointers."""
