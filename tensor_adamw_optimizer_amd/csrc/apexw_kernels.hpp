@@ -162,6 +162,10 @@ __device__ __forceinline__ StepScalars step_scalars(const StepRecord &r) {
     return s;
 }
 
+// True in every lane if p holds in any lane (the compare mask itself, read
+// as a scalar: no per-lane materialisation of p).
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
 // Square root rounded to nearest.  v_sqrt_f32 is within one ulp, so the
 // answer is it or a neighbour: the lower neighbour lo if x <= lo*s, the upper
 // hi if x > hi*s (the squares of the two midpoints lie strictly beyond those
@@ -176,10 +180,9 @@ __device__ __forceinline__ float sqrt_rn(float x) {
     float r = s;
     if (fmaf(-lo, s, x) <= 0.0f) r = lo;
     if (fmaf(-hi, s, x) > 0.0f) r = hi;
-    const bool tiny = x < 0x1p-96f && x > 0.0f;
-    if (__any(tiny)) {              // a wave-uniform branch keeps it off the common path
-        asm volatile("");           // (and stops the compiler from speculating it)
-        if (tiny) r = sqrtf(x);
+    if (x < 0x1p-96f && x > 0.0f) { // skipped by the whole wave unless a lane needs it
+        asm volatile("");           // (keeps the compiler from speculating it)
+        r = sqrtf(x);
     }
     return r;
 }
@@ -396,10 +399,9 @@ __device__ __forceinline__ BlockScale block_scale(float amax, float levels) {
 __device__ __forceinline__ float code_value(float x, const BlockScale &b, float lo, float hi) {
     const float r = x * b.inv;
     float q = rintf(r);
-    const bool exact = !b.fast || !(fabsf(fabsf(r - q) - 0.5f) > 2.5e-4f);
-    if (__any(exact)) {             // wave-uniform: rare except in degenerate blocks
-        asm volatile("");           // not speculated
-        if (exact) q = b.s == 0.0f ? 0.0f : fminf(fmaxf(rintf(x / b.s), lo), hi);
+    if (!b.fast || !(fabsf(fabsf(r - q) - 0.5f) > 2.5e-4f)) {   // rare: skipped by the wave
+        asm volatile("");                                          // not speculated
+        q = b.s == 0.0f ? 0.0f : fminf(fmaxf(rintf(x / b.s), lo), hi);
     }
     return q;
 }
@@ -693,7 +695,7 @@ __global__ __launch_bounds__(kThreads) void unscale_check_kernel(KernelArgs a) {
                 bad |= t[u].grad != nullptr && off + j < t[u].n && !(fabsf(x) <= 3.40282347e38f);
             }
     }
-    if (__any(bad) && threadIdx.x == 0) *gptr<float>(static_cast<void *>(a.found_inf_out)) = 1.0f;
+    if (wave_any(bad) && threadIdx.x == 0) *gptr<float>(static_cast<void *>(a.found_inf_out)) = 1.0f;
 }
 
 // ---------------------------------------------------------------- grad norm
@@ -770,7 +772,7 @@ __global__ __launch_bounds__(kThreads) void grad_norm_partials_kernel(KernelArgs
             if (threadIdx.x == 0 && t[u].k < a.tile_count)
                 gptr<double>(static_cast<void *>(a.partials))[a.tile_begin + t[u].k] = sq[u];
     }
-    if (a.found_inf_out != nullptr && __any(bad) && threadIdx.x == 0)
+    if (a.found_inf_out != nullptr && wave_any(bad) && threadIdx.x == 0)
         *gptr<float>(static_cast<void *>(a.found_inf_out)) = 1.0f;
 }
 
