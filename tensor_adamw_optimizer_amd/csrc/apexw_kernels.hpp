@@ -308,18 +308,27 @@ __device__ __forceinline__ void store4_any(void *base, int64_t e, const float (&
 
 // ---------------------------------------------------------------- wave max
 
-// Maximum over the 64 lanes of a wave, returned to every lane.
-__device__ __forceinline__ float wave_max(float x) {
-    // quad xor 1, quad xor 2, half-row mirror, row mirror: the max of each
-    // 16-lane row reaches all of its lanes through DPP moves
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false)));
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false)));
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false)));
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false)));
-    // across the four rows
-    x = fmaxf(x, __shfl_xor(x, 16, 64));
-    x = fmaxf(x, __shfl_xor(x, 32, 64));
-    return x;
+// Maximum over the 64 lanes of a wave of non-negative, NaN-free floats,
+// returned wave-uniform.  For such values the order of the bit patterns as
+// unsigned integers is the order of the numbers, so the reduction is integer:
+// quad swaps and the two row mirrors bring each 16-lane row's maximum to all
+// of its lanes (DPP), then the four row maxima are read by lane.
+template <int CTRL>
+__device__ __forceinline__ uint32_t max_dpp(uint32_t u) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, CTRL, 0xF, 0xF, false);
+    return u > o ? u : o;
+}
+
+__device__ __forceinline__ float wave_max_nonneg(float x) {
+    uint32_t u = __float_as_uint(x);
+    u = max_dpp<0xB1>(u);       // quad_perm [1,0,3,2]
+    u = max_dpp<0x4E>(u);       // quad_perm [2,3,0,1]
+    u = max_dpp<0x141>(u);      // row_half_mirror
+    u = max_dpp<0x140>(u);      // row_mirror
+    const uint32_t r0 = __builtin_amdgcn_readlane(u, 0), r1 = __builtin_amdgcn_readlane(u, 16);
+    const uint32_t r2 = __builtin_amdgcn_readlane(u, 32), r3 = __builtin_amdgcn_readlane(u, 48);
+    const uint32_t a = r0 > r1 ? r0 : r1, b = r2 > r3 ? r2 : r3;
+    return __uint_as_float(a > b ? a : b);
 }
 
 // ---------------------------------------------------------------- tiles
@@ -466,12 +475,12 @@ __device__ __forceinline__ void tile_q8(const TensorDesc &d, const void *grad,
     for (int j = 0; j < kVec; ++j) {
         adamw_update(th[j], g[j], m[j], v[j], s);
         if (off + j < n) {                    // lanes past the end do not count
-            am = fmaxf(am, fabsf(m[j]));
-            av = fmaxf(av, v[j]);
+            am = fmaxf(am, fabsf(m[j]));      // (a NaN moment is passed over)
+            av = fmaxf(av, fabsf(v[j]));      // v >= 0; fabs makes a -0 +0
         }
     }
-    am = wave_max(am);
-    av = wave_max(av);
+    am = wave_max_nonneg(am);
+    av = wave_max_nonneg(av);
     const BlockScale bm = block_scale(am, 127.0f);
     const BlockScale bv = block_scale(av, 255.0f);
     if (threadIdx.x == 0) {
