@@ -118,9 +118,14 @@ int compute_layout(int32_t n, const int64_t *numel, int32_t fmt,
 // grad-norm partial sums (one per tile, then one per reduce workgroup), each
 // on a 256-byte boundary.
 struct WsLayout {
-    int64_t desc, grads, records, tiles, partials, partials2, total;
+    int64_t desc, grads, records, tiles, partials, partials2, consts, total;
     int64_t n_tiles;
 };
+
+// The constants region: 0.0f and 1.0f, passed to the prepare kernel in place
+// of an absent found_inf flag, inv_scale or clip coefficient, so that it
+// loads all of them unconditionally.
+constexpr float kConsts[2] = {0.0f, 1.0f};
 
 constexpr int kMaxLaunches = 4;      // (param, grad) dtype pairs
 constexpr int64_t kMaxGrid = 1 << 24;  // workgroups per launch (grid-stride above)
@@ -137,7 +142,8 @@ WsLayout ws_layout(int32_t n, const int64_t *numel) {
     // passes load table entries in fours and may read up to 3 past the end
     w.partials = w.tiles + round_up((w.n_tiles + kMaxLaunches * kXcds + 4) * 4, kTableAlign);
     w.partials2 = w.partials + round_up(w.n_tiles * 8, kTableAlign);
-    w.total = n == 0 ? 0 : w.partials2 + round_up(kReduceBlocks * 8, kTableAlign);
+    w.consts = w.partials2 + round_up(kReduceBlocks * 8, kTableAlign);
+    w.total = n == 0 ? 0 : w.consts + round_up((int64_t)sizeof(kConsts), kTableAlign);
     return w;
 }
 
@@ -512,6 +518,7 @@ int apexw_create(int32_t n_tensors, const int64_t *numel, const int32_t *param_d
         std::memcpy(stage + wl.desc, h->desc.data(), (size_t)n_tensors * sizeof(TensorDesc));
     if (!tiles.empty())
         std::memcpy(stage + wl.tiles, tiles.data(), tiles.size() * 4);
+    if (static_bytes > 0) std::memcpy(stage + wl.consts, kConsts, sizeof(kConsts));
     if (static_bytes > 0)
         TRY(hipMemcpyAsync(h->ws, stage, (size_t)static_bytes, hipMemcpyHostToDevice, st));
     const int64_t words = need_state / 4;
@@ -602,8 +609,10 @@ int apexw_step_ex(apexw_t h, const apexw_group *groups, int32_t n_groups, void *
     a.tile_tensor = reinterpret_cast<const int32_t *>(h->ws + h->wl.tiles);
     a.records = reinterpret_cast<StepRecord *>(h->ws + h->wl.records);
     a.steps = reinterpret_cast<int32_t *>(h->state + h->steps_off);
-    a.found_inf = found_inf_dev;
-    a.inv_scale = inv_scale_dev;
+    const float *consts = reinterpret_cast<const float *>(h->ws + h->wl.consts);
+    a.found_inf = found_inf_dev != nullptr ? found_inf_dev : consts;        // 0: no skip
+    a.inv_scale = inv_scale_dev != nullptr ? inv_scale_dev : consts + 1;    // 1: unscaled
+    a.clip_coef = a.clip_coef != nullptr ? a.clip_coef : consts + 1;        // 1: unclipped
     a.n_tensors = h->n;
     hipLaunchKernelGGL(adamw_prepare_kernel, dim3((unsigned)ceil_div(h->n, kPrepThreads)),
                        dim3(kPrepThreads), 0, st, a);

@@ -533,12 +533,21 @@ __global__ __launch_bounds__(kPrepThreads) void adamw_prepare_kernel(KernelArgs 
     const int32_t i = blockIdx.x * kPrepThreads + threadIdx.x;
     if (i >= a.n_tensors) return;
     StepRecord r = {};
-    const bool skip = a.found_inf != nullptr && *a.found_inf != 0.0f;
-    const void *grad = skip ? nullptr : a.grads[i];
+    // every independent load first (flag, grad pointer, counter, group,
+    // scale factors): one memory round trip instead of a chain of four.
+    // found_inf, inv_scale and clip_coef are never NULL here: the host
+    // passes device constants 0 / 1 / 1 in place of absent ones.
+    const float fi = *a.found_inf;
+    const void *g_ptr = a.grads[i];
+    const int32_t t_old = a.steps[i];
+    const int32_t gi = a.desc[i].group;
+    const float inv_scale = *a.inv_scale;
+    const float clip_coef = *a.clip_coef;
+    asm volatile("" ::"v"(fi), "v"(g_ptr), "v"(t_old), "v"(gi), "v"(inv_scale), "v"(clip_coef));
+    const void *grad = fi != 0.0f ? nullptr : g_ptr;
     if (grad != nullptr) {
-        const int32_t t = a.steps[i] + 1;
+        const int32_t t = t_old + 1;
         a.steps[i] = t;
-        const int32_t gi = a.desc[i].group;
         const GroupScalars g = a.groups_dev != nullptr ? group_scalars(a.groups_dev[gi]) : a.groups[gi];
         r.grad = grad;
         r.beta1 = g.beta1;
@@ -550,8 +559,8 @@ __global__ __launch_bounds__(kPrepThreads) void adamw_prepare_kernel(KernelArgs 
         r.eps = g.eps;
         r.bc1 = (float)(1.0 - pow_uint(g.beta1_d, (uint32_t)t));
         r.bc2 = (float)(1.0 - pow_uint(g.beta2_d, (uint32_t)t));
-        r.inv_scale = a.inv_scale != nullptr ? *a.inv_scale : 1.0f;
-        r.clip_coef = a.clip_coef != nullptr ? *a.clip_coef : 1.0f;
+        r.inv_scale = inv_scale;
+        r.clip_coef = clip_coef;
     }
     a.records[i] = r;
 }
