@@ -57,6 +57,8 @@ extern "C" {
 #define APEXW_ENOSPC (-3)  /* state or workspace buffer smaller than needed */
 #define APEXW_EHIP (-4)    /* a HIP runtime call failed */
 #define APEXW_ENOMEM (-5)  /* host allocation failed */
+#define APEXW_ESPARSE (-6) /* a sparse gradient: not expressible through these
+                              dense pointers; returned by language bindings */
 
 /* ---- element types of parameters and grads (dense, contiguous) */
 #define APEXW_F32 0
@@ -161,10 +163,14 @@ int apexw_create(int32_t n_tensors, const int64_t *numel,
  *   groups[g]     hyperparameters of group g for this call, n_groups entries
  *                 (must equal the count given to apexw_create)
  *   params[i]     device pointer to tensor i's values (param_dtype[i]); may
- *                 be NULL only when numel[i] == 0
+ *                 be NULL only when numel[i] == 0.  params itself NULL: the
+ *                 array of the previous call (APEXW_EINVAL if there is none)
  *   grads[i]      device pointer to tensor i's grad (grad_dtype[i]), or NULL
  *                 when the tensor has no grad this call: then its values,
- *                 moments and step counter are not touched
+ *                 moments and step counter are not touched.  grads itself
+ *                 NULL: the array of the previous call on this handle (step,
+ *                 check or norm call; APEXW_EINVAL if there is none) -- for
+ *                 callers whose grad buffers persist across steps
  *   found_inf_dev device pointer to one float, read by the GPU when the step
  *                 runs; nonzero (or NaN) skips the whole step -- nothing is
  *                 written; NULL means never skip
@@ -298,6 +304,15 @@ int apexw_export_state(apexw_t h, const apexw_group *groups, int32_t n_groups,
                        void *dst_host, size_t dst_bytes, void *stream);
 int apexw_import_state(apexw_t h, const void *src_host, size_t src_bytes,
                        apexw_group *groups_out, int32_t n_groups, void *stream);
+
+/*
+ * Copy the int32 step counter of every tensor (n_tensors values, in tensor
+ * order) to host_out after the work queued on `stream`; synchronises that
+ * stream.  A tensor's counter is the number of steps that updated it
+ * (M041 sections 03 and 06: an absent grad or a skipped step does not count).
+ * Errors: APEXW_EINVAL for a NULL handle or host_out; APEXW_EHIP.
+ */
+int apexw_read_steps(apexw_t h, int32_t *host_out, void *stream);
 
 /*
  * Launch geometry of the handle: tile size in elements (256; one workgroup of

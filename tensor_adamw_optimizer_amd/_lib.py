@@ -21,6 +21,7 @@ APEXW_EDTYPE = -2
 APEXW_ENOSPC = -3
 APEXW_EHIP = -4
 APEXW_ENOMEM = -5
+APEXW_ESPARSE = -6
 
 APEXW_F32 = 0
 APEXW_BF16 = 1
@@ -38,7 +39,7 @@ ENTRY_POINTS = (
     "apexw_create", "apexw_step", "apexw_step_scaled", "apexw_unscale_check",
     "apexw_step_device", "apexw_step_ex", "apexw_clip_grad_norm",
     "apexw_export_bytes", "apexw_export_state", "apexw_import_state",
-    "apexw_launch_info", "apexw_set_workgroups",
+    "apexw_read_steps", "apexw_launch_info", "apexw_set_workgroups",
     "apexw_set_occupancy", "apexw_get_occupancy", "apexw_set_cache_policy",
     "apexw_destroy", "apexw_last_error",
 )
@@ -94,6 +95,7 @@ def lib() -> ctypes.CDLL:
         L.apexw_export_bytes.argtypes = [P, ctypes.POINTER(SZ)]
         L.apexw_export_state.argtypes = [P, P, I32, P, SZ, P]
         L.apexw_import_state.argtypes = [P, P, SZ, P, I32, P]
+        L.apexw_read_steps.argtypes = [P, P, P]
         L.apexw_launch_info.argtypes = [P, ctypes.POINTER(I32), ctypes.POINTER(I32),
                                         ctypes.POINTER(I32)]
         L.apexw_set_workgroups.argtypes = [P, I32]
@@ -244,6 +246,13 @@ def apexw_import_state(handle: int, blob: bytes, n_groups: int, stream: int = 0)
     _check(lib().apexw_import_state(handle, blob, len(blob), groups, n_groups, stream or None),
            "apexw_import_state")
     return list(groups[:n_groups])
+
+
+def apexw_read_steps(handle: int, n_tensors: int, stream: int = 0):
+    """The int32 step counter of every tensor, copied to the host (syncs)."""
+    out = (ctypes.c_int32 * max(1, n_tensors))()
+    _check(lib().apexw_read_steps(handle, out, stream or None), "apexw_read_steps")
+    return list(out)[:n_tensors]
 
 
 def apexw_launch_info(handle: int):

@@ -328,15 +328,27 @@ int upload_pointer_tables(apexw_opt *h, void *const *params, const void *const *
     return APEXW_OK;
 }
 
+// A NULL params or grads array on a step call means "the arrays of the
+// previous call" (persistent grad buffers need no new array each step).
+int reuse_last(apexw_opt *h, void *const **params, const void *const **grads) {
+    if (h->n == 0) return APEXW_OK;
+    if (params && !*params) {
+        if (!h->have_params) return fail(APEXW_EINVAL, "params is NULL and no earlier call gave them");
+        *params = h->last_params.data();
+    }
+    if (!*grads) {
+        if (!h->have_grads) return fail(APEXW_EINVAL, "grads is NULL and no earlier call gave them");
+        *grads = h->last_grads.data();
+    }
+    return APEXW_OK;
+}
+
 int launch_cap(const apexw_opt *h) { return h->wg_override > 0 ? h->wg_override : (int)kMaxGrid; }
 
-// Grid of the read-only passes over the grads (unscale check, grad norm):
-// there each wave walks about 8 tiles (measured on MI355X: 7.4 TB/s for the
-// check against 4.7 TB/s with one tile per wave), keeping a multiple of 8
-// workgroups (one set per XCD) and at least 2048 of them.  Results do not depend on it.
 // Workgroups of a read pass over a launch of `tiles` tiles: a workgroup takes
 // groups of kReadBatch tiles (read_groups() of them in all), about two groups
-// each, at least 2048 workgroups, a multiple of the XCD count.
+// each, at least 2048 workgroups, a multiple of the XCD count (one set per
+// XCD).  Results do not depend on it.
 int64_t read_pass_grid(const apexw_opt *h, int64_t tiles) {
     const int64_t groups = read_groups(ceil_div(tiles, kXcds));
     if (h->wg_override > 0) return std::min<int64_t>(groups, h->wg_override);
@@ -564,7 +576,7 @@ int apexw_step_ex(apexw_t h, const apexw_group *groups, int32_t n_groups, void *
         return fail(APEXW_EINVAL, "n_groups is %d, the handle was created with %d", n_groups,
                     h->n_groups);
     if (!groups && !o.groups_dev) return fail(APEXW_EINVAL, "groups is NULL");
-    if (h->n > 0 && (!params || !grads)) return fail(APEXW_EINVAL, "params and grads must not be NULL");
+    if (int rc = reuse_last(h, &params, &grads)) return rc;
     const float *inv_scale_dev = o.inv_scale;
     const float *found_inf_dev = o.found_inf;
     if (o.groups_dev) groups = nullptr;
@@ -644,7 +656,7 @@ int apexw_unscale_check(apexw_t h, const void *const *grads, const float *inv_sc
                         float *found_inf_dev, void *stream) {
     if (!h) return fail(APEXW_EINVAL, "handle is NULL");
     if (!found_inf_dev) return fail(APEXW_EINVAL, "found_inf_dev is NULL");
-    if (h->n > 0 && !grads) return fail(APEXW_EINVAL, "grads must not be NULL");
+    if (int rc = reuse_last(h, nullptr, &grads)) return rc;
     DeviceGuard guard(h->device);
     hipStream_t st = static_cast<hipStream_t>(stream);
     int rc = upload_pointer_tables(h, nullptr, grads, st);
@@ -684,7 +696,7 @@ int apexw_clip_grad_norm(apexw_t h, const void *const *grads, const float *inv_s
     if (!clip_coef_dev) return fail(APEXW_EINVAL, "clip_coef_dev is NULL");
     if (!(max_norm > 0.0) || !std::isfinite(max_norm))
         return fail(APEXW_EINVAL, "max_norm must be finite and > 0");
-    if (h->n > 0 && !grads) return fail(APEXW_EINVAL, "grads must not be NULL");
+    if (int rc = reuse_last(h, nullptr, &grads)) return rc;
     DeviceGuard guard(h->device);
     hipStream_t st = static_cast<hipStream_t>(stream);
     int rc = upload_pointer_tables(h, nullptr, grads, st);
@@ -832,6 +844,18 @@ int apexw_import_state(apexw_t h, const void *src_host, size_t src_bytes, apexw_
     DeviceGuard guard(h->device);
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (sb > 0) HIP_TRY(hipMemcpyAsync(h->state, p + off, (size_t)sb, hipMemcpyHostToDevice, st));
+    HIP_TRY(hipStreamSynchronize(st));
+    return APEXW_OK;
+}
+
+int apexw_read_steps(apexw_t h, int32_t *host_out, void *stream) {
+    if (!h) return fail(APEXW_EINVAL, "handle is NULL");
+    if (h->n > 0 && !host_out) return fail(APEXW_EINVAL, "host_out is NULL");
+    if (h->n == 0) return APEXW_OK;
+    DeviceGuard guard(h->device);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    HIP_TRY(hipMemcpyAsync(host_out, h->state + h->steps_off, (size_t)h->n * 4,
+                           hipMemcpyDeviceToHost, st));
     HIP_TRY(hipStreamSynchronize(st));
     return APEXW_OK;
 }

@@ -16,8 +16,9 @@ import torch
 from . import _lib as L
 
 _DT = {torch.float32: L.APEXW_F32, torch.bfloat16: L.APEXW_BF16}
-_FMT = {"f32": L.APEXW_STATE_F32, "bf16": L.APEXW_STATE_BF16, "q8": L.APEXW_STATE_Q8}
-_MOMENT_DTYPE = {"f32": (torch.float32, torch.float32),
+_FMT = {"f32": L.APEXW_STATE_F32, "fp32": L.APEXW_STATE_F32, "bf16": L.APEXW_STATE_BF16,
+        "q8": L.APEXW_STATE_Q8}
+_MOMENT_DTYPE = {"f32": (torch.float32, torch.float32), "fp32": (torch.float32, torch.float32),
                  "bf16": (torch.bfloat16, torch.bfloat16),
                  "q8": (torch.int8, torch.uint8)}
 
@@ -35,7 +36,7 @@ class _GroupView:
 class AdamW:
     """Fused multi-tensor AdamW (decoupled decay, scalar bias correction).
 
-    state: "f32", "bf16" (round-to-nearest-even moments) or "q8" (int8 m /
+    state: "f32" (or "fp32"), "bf16" (round-to-nearest-even moments) or "q8" (int8 m /
     uint8 v codes with one fp32 absmax scale per 256-element block).
     grad_dtype: dtype the grads will have (default: each parameter's dtype).
     """
@@ -97,7 +98,8 @@ class AdamW:
                 ptrs.append(0)
                 continue
             if g.is_sparse:
-                raise RuntimeError("sparse gradients are not supported")
+                raise L.ApexwError(L.APEXW_ESPARSE, "AdamW.step",
+                                   "sparse gradients are not supported")
             if g.dtype != gdt or g.shape != p.shape or not g.is_contiguous() \
                     or g.device != p.device:
                 raise ValueError("grad must be a contiguous %s tensor shaped like its "
@@ -211,6 +213,11 @@ class AdamW:
         """int32 step counter of every parameter (view)."""
         n = len(self._params)
         return self.state[self._steps_off:self._steps_off + 4 * n].view(torch.int32)
+
+    def read_steps(self):
+        """Step counters copied to the host (synchronises the current stream)."""
+        with torch.cuda.device(self.device):
+            return L.apexw_read_steps(self._h, len(self._params), self._stream())
 
     def launch_info(self):
         return L.apexw_launch_info(self._h)

@@ -355,6 +355,40 @@ def test_views_into_flat_buffers_against_oracle(fmt):
     opt.close()
 
 
+def test_null_arrays_reuse_the_previous_call_and_read_steps():
+    """params / grads passed as NULL arrays mean the previous call's arrays:
+    three calls with NULL arrays after one explicit call give the same bits
+    as four explicit calls; apexw_read_steps copies the counters."""
+    _need_gpu()
+    say("case: NULL arrays reuse the previous call")
+    w = W.tiny()
+    outs = []
+    for reuse in (False, True):
+        p_cpu = W.init_params(w, "cpu")
+        params = [p.to(DEV) for p in p_cpu]
+        grads = [torch.randn(s, generator=torch.Generator().manual_seed(3)).mul_(1e-3).to(DEV)
+                 for s in w.shapes]
+        opt = GpuOpt(w.numels, w.param_dtype, w.grad_dtype, w.group_of, 1, w.state_fmt)
+        pa = L.make_ptrs([p.data_ptr() for p in params])
+        ga = L.make_ptrs([g.data_ptr() for g in grads])
+        for k in range(4):
+            if reuse and k > 0:
+                L.apexw_step(opt.h, L.make_groups(w.groups), 1, None, None, 0, opt.stream)
+            else:
+                L.apexw_step(opt.h, L.make_groups(w.groups), 1, pa, ga, 0, opt.stream)
+        torch.cuda.synchronize()
+        outs.append((torch.cat([p.reshape(-1) for p in params]).cpu(), opt.state.cpu()))
+        assert L.apexw_read_steps(opt.h, len(w.numels), opt.stream) == [4] * len(w.numels)
+        opt.close()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    # a fresh handle has no previous arrays
+    opt = GpuOpt(w.numels, w.param_dtype, w.grad_dtype, w.group_of, 1, w.state_fmt)
+    with pytest.raises(L.ApexwError) as e:
+        L.apexw_step(opt.h, L.make_groups(w.groups), 1, None, None, 0, opt.stream)
+    assert e.value.code == L.APEXW_EINVAL
+    opt.close()
+
+
 def test_all_grads_absent_and_pointer_changes():
     """No grads at all: nothing changes.  Grads moved to new buffers between
     calls: the library follows the new pointers."""

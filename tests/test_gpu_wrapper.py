@@ -75,3 +75,24 @@ def test_wrapper_amp_clip_checkpoint(state):
         m, v = opt.moments(j)
         assert n_bit_mismatch(bits(m), ref.m[j]) == 0 and n_bit_mismatch(bits(v), ref.v[j]) == 0
     opt.close()
+
+
+def test_wrapper_rejects_sparse_grads_and_reads_steps():
+    """A sparse grad cannot go through the dense ABI: the wrapper raises
+    ApexwError(APEXW_ESPARSE) before queueing anything; read_steps and the
+    "fp32" state alias work."""
+    from tensor_adamw_optimizer_amd import _lib as L
+    say("case: wrapper sparse grad / read_steps")
+    p = torch.zeros(8, 4, device="cuda")
+    q = torch.zeros(16, device="cuda")
+    opt = AdamW([p, q], lr=1e-3, state="fp32")
+    p.grad = torch.ones(8, 4, device="cuda")
+    q.grad = torch.ones(16, device="cuda")
+    opt.step()
+    assert opt.read_steps() == [1, 1]
+    p.grad = torch.ones(8, 4, device="cuda").to_sparse()
+    with pytest.raises(L.ApexwError) as e:
+        opt.step()
+    assert e.value.code == L.APEXW_ESPARSE
+    assert opt.read_steps() == [1, 1]
+    opt.close()

@@ -134,3 +134,12 @@ def test_null_handle_rejected():
         L.apexw_destroy(0)
     with pytest.raises(L.ApexwError):
         L.apexw_launch_info(0)
+    with pytest.raises(L.ApexwError) as e:
+        L.apexw_read_steps(0, 3)
+    assert e.value.code == L.APEXW_EINVAL
+
+
+def test_error_codes_are_distinct_and_negative():
+    codes = [L.APEXW_EINVAL, L.APEXW_EDTYPE, L.APEXW_ENOSPC, L.APEXW_EHIP, L.APEXW_ENOMEM,
+             L.APEXW_ESPARSE]
+    assert len(set(codes)) == len(codes) and all(c < 0 for c in codes)
