@@ -472,11 +472,21 @@ __device__ __forceinline__ void tile_q8(const TensorDesc &d, const void *grad,
     }
     float am = 0.0f, av = 0.0f;
 #pragma unroll
-    for (int j = 0; j < kVec; ++j) {
-        adamw_update(th[j], g[j], m[j], v[j], s);
-        if (off + j < n) {                    // lanes past the end do not count
-            am = fmaxf(am, fabsf(m[j]));      // (a NaN moment is passed over)
-            av = fmaxf(av, fabsf(v[j]));      // v >= 0; fabs makes a -0 +0
+    for (int j = 0; j < kVec; ++j) adamw_update(th[j], g[j], m[j], v[j], s);
+    // block maxima (a NaN moment is passed over; v >= 0, fabs makes a -0 +0)
+    if (n == kTile) {                         // wave-uniform: a full block
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) {
+            am = fmaxf(am, fabsf(m[j]));
+            av = fmaxf(av, fabsf(v[j]));
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) {
+            if (off + j < n) {                // elements past the end do not count
+                am = fmaxf(am, fabsf(m[j]));
+                av = fmaxf(av, fabsf(v[j]));
+            }
         }
     }
     am = wave_max_nonneg(am);
