@@ -389,6 +389,49 @@ def test_null_arrays_reuse_the_previous_call_and_read_steps():
     opt.close()
 
 
+def test_thirty_two_groups_with_edge_hyperparameters_against_oracle():
+    """The maximum of 32 parameter groups, each with its own hyperparameters
+    -- among them lr = 0 (theta unchanged), beta2 = 0, a decay factor
+    1 - lr*wd below zero, a large eps -- over 64 tensors of mixed dtypes,
+    three calls, bit-exact against the oracle in every state format."""
+    _need_gpu()
+    say("case: 32 groups")
+    rng = np.random.default_rng(21)
+    groups = []
+    for gi in range(32):
+        groups.append(W.Group(lr=float(10 ** rng.uniform(-5, -1)), beta1=float(rng.uniform(0, 0.99)),
+                              beta2=float(rng.uniform(0.5, 0.9999)), eps=float(10 ** rng.uniform(-10, -4)),
+                              weight_decay=float(rng.uniform(0, 0.2))))
+    groups[0] = W.Group(lr=0.0, weight_decay=0.5)
+    groups[1] = W.Group(lr=1e-3, beta2=0.0)
+    groups[2] = W.Group(lr=0.5, weight_decay=3.0)          # 1 - lr*wd = -0.5
+    groups[3] = W.Group(lr=1e-2, eps=1.0)
+    sizes = [int(x) for x in rng.integers(1, 3000, 64)]
+    pdt = [(W.F32, W.BF16)[i % 2] for i in range(64)]
+    gdt = [(W.F32, W.BF16)[(i // 2) % 2] for i in range(64)]
+    group_of = [i % 32 for i in range(64)]
+    for fmt in (W.STATE_F32, W.STATE_BF16, W.STATE_Q8):
+        gen = torch.Generator().manual_seed(22)
+        p_cpu = [(torch.randn(n, generator=gen) * 0.02).to(W.TORCH_DTYPE[d]) for n, d in zip(sizes, pdt)]
+        params = [p.to(DEV) for p in p_cpu]
+        th_ref = [bits(p) for p in p_cpu]
+        opt = GpuOpt(sizes, pdt, gdt, group_of, 32, fmt)
+        ref = oracle.OracleAdamW(sizes, pdt, gdt, group_of, fmt)
+        for k in range(3):
+            g_cpu = [(torch.randn(n, generator=gen) * 1e-3).to(W.TORCH_DTYPE[d]) for n, d in zip(sizes, gdt)]
+            opt.step(groups, params, [g.to(DEV) for g in g_cpu])
+            ref.step(th_ref, [bits(g) for g in g_cpu], groups)
+        torch.cuda.synchronize()
+        for i in range(64):
+            assert n_bit_mismatch(bits(params[i]), th_ref[i]) == 0, (fmt, i)
+            m, v = (bits(t) for t in opt.moments(i))
+            assert n_bit_mismatch(m, ref.m[i]) == 0 and n_bit_mismatch(v, ref.v[i]) == 0, (fmt, i)
+        # lr = 0: theta of group 0's tensors is unchanged
+        for i in (0, 32):
+            assert n_bit_mismatch(bits(params[i]), bits(p_cpu[i])) == 0
+        opt.close()
+
+
 def test_all_grads_absent_and_pointer_changes():
     """No grads at all: nothing changes.  Grads moved to new buffers between
     calls: the library follows the new pointers."""
@@ -627,7 +670,7 @@ def test_lora_q8_full_size_sampled():
     opt.close()
 
 
-@pytest.mark.parametrize("fmt", [W.STATE_F32, W.STATE_Q8])
+@pytest.mark.parametrize("fmt", [W.STATE_F32, W.STATE_BF16, W.STATE_Q8])
 def test_maximum_size_tensor_past_int32(fmt):
     """One bf16 tensor of 2^31 + 4099 elements (64-bit element offsets, 8.4M
     tiles, a 3-element final 8-bit block), bf16 grads, 2 calls; whole
