@@ -47,11 +47,17 @@ def algorithmic_bytes(w) -> int:
 
 
 def kernel_source_hash() -> str:
+    """Hash of the library's code with comments and blank space removed, so
+    that a comment edit does not invalidate counters taken on the same code."""
+    import re
     h = hashlib.sha256()
     for rel in ("tensor_adamw_optimizer_amd/csrc/apexw.hip",
                 "tensor_adamw_optimizer_amd/csrc/apexw_kernels.hpp", "include/apexw.h"):
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

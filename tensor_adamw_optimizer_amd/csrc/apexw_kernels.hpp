@@ -1,6 +1,7 @@
 // apexw_kernels.hpp -- gfx950 device code of the fused multi-tensor AdamW step.
 //
-// Two kernels per step:
+// Two kernels per step (prepare, then one update launch per (param, grad)
+// dtype pair):
 //  * adamw_prepare_kernel -- one lane per tensor: unless found_inf is set,
 //    advances the step counter of every tensor that has a grad and writes
 //    that tensor's step record (grad pointer, fp32 group scalars and bias
@@ -16,9 +17,21 @@
 //    quantisation block.  Every element is read once and written once:
 //    theta, g, m, v in; theta, m, v out (28 B per fp32 element, the one-pass
 //    ledger of the M041 page, section 04).  Small one-tile workgroups keep
-//    many independent read and write streams in flight; the path is
-//    HBM-bandwidth bound, so there is no matrix-core work and the arithmetic
-//    is ordinary fp32 VALU code compiled without contraction.
+//    many independent read and write streams in flight.  With fp32 moments
+//    the path is HBM-bandwidth bound; with 8-bit moments the exact fp32
+//    arithmetic (three correctly rounded divisions per element, the block
+//    reductions, decode and encode) is the limit.  There is no contraction
+//    in the method, so no matrix-core work; the arithmetic is ordinary fp32
+//    VALU code compiled without contraction, with exact shortcuts where the
+//    hardware offers them (bf16 pair conversion, square root from
+//    v_sqrt_f32 plus a residual check, 8-bit codes from v_rcp_f32 plus a
+//    tie guard).
+//
+// Read-only passes for the mixed-precision recipe and clipping:
+//  * unscale_check_kernel -- any non-finite unscaled grad sets found_inf;
+//  * grad_norm_partials_kernel, grad_norm_reduce_kernel,
+//    grad_norm_final_kernel -- the global grad norm in a fixed summation
+//    order and the clip coefficient.
 //
 // Sources: "Fused optimizers and state precision" (ai-infra-kb M041),
 // sections 02 (update), 03 (groups, missing grads), 04 (scalar bias
