@@ -1,10 +1,10 @@
 """torch-facing wrapper of the HIP fused AdamW library.
 
-``AdamW`` takes CUDA (ROCm) tensors or torch-style parameter-group dicts,
-allocates the optimizer state and the library workspace as torch uint8
-buffers, and on ``step()`` hands the current grads, the group
-hyperparameters and the device ``found_inf`` flag to ``apexw_step`` on
-torch's current stream.  torch is only the allocator and the stream here;
+``AdamW`` is a torch.optim.Optimizer over CUDA (ROCm) tensors or
+parameter-group dicts.  It allocates the optimizer state and the library
+workspace as torch uint8 buffers, and on ``step()`` hands the current grads,
+the group hyperparameters and the device ``found_inf`` flag to the library
+on torch's current stream.  torch is only the allocator and the stream here;
 the whole update runs in the library's kernels.
 """
 from __future__ import annotations
@@ -33,33 +33,37 @@ class _GroupView:
         self.weight_decay = float(g["weight_decay"])
 
 
-class AdamW:
+class AdamW(torch.optim.Optimizer):
     """Fused multi-tensor AdamW (decoupled decay, scalar bias correction).
+
+    A torch.optim.Optimizer: parameter groups, learning-rate schedulers and
+    zero_grad work as usual, and torch.amp.GradScaler hands over its scale
+    and overflow flag (the update unscales the grads itself and skips the
+    step on the device, no host sync).  The tensor list is fixed at
+    construction (add_param_group afterwards is refused).
 
     state: "f32" (or "fp32"), "bf16" (round-to-nearest-even moments) or "q8" (int8 m /
     uint8 v codes with one fp32 absmax scale per 256-element block).
     grad_dtype: dtype the grads will have (default: each parameter's dtype).
     """
 
+    # torch.amp.GradScaler: set grad_scale / found_inf on the optimizer and
+    # call step() directly instead of unscaling the grads first
+    _step_supports_amp_scaling = True
+
     def __init__(self, params: Iterable, lr: float = 1e-3, betas=(0.9, 0.999),
                  eps: float = 1e-8, weight_decay: float = 0.0, state: str = "f32",
                  grad_dtype: Optional[torch.dtype] = None):
         if state not in _FMT:
             raise ValueError("state must be one of %s" % sorted(_FMT))
+        self._h = None
         defaults = dict(lr=lr, betas=tuple(betas), eps=eps, weight_decay=weight_decay)
-        params = list(params)
-        if params and isinstance(params[0], dict):
-            groups = [dict(defaults, **{k: v for k, v in g.items()}) for g in params]
-        else:
-            groups = [dict(defaults, params=params)]
-        self.param_groups: List[Dict] = []
+        super().__init__(params, defaults)
         self._params: List[torch.Tensor] = []
         group_of: List[int] = []
-        for gi, g in enumerate(groups):
-            g["params"] = list(g["params"])
-            self.param_groups.append(g)
+        for gi, g in enumerate(self.param_groups):
             for p in g["params"]:
-                if not isinstance(p, torch.Tensor) or p.device.type != "cuda":
+                if p.device.type != "cuda":
                     raise ValueError("parameters must be GPU tensors")
                 if p.dtype not in _DT:
                     raise TypeError("parameter dtype %s is not float32 or bfloat16" % p.dtype)
@@ -67,8 +71,6 @@ class AdamW:
                     raise ValueError("parameters must be contiguous")
                 self._params.append(p)
                 group_of.append(gi)
-        if not self._params:
-            raise ValueError("no parameters")
         self.device = self._params[0].device
         self.state_fmt = state
         self._numel = [p.numel() for p in self._params]
@@ -80,14 +82,21 @@ class AdamW:
         self._layout, self._steps_off = L.apexw_state_layout(self._numel, fmt)
         ws_bytes = L.apexw_workspace_bytes(self._numel)
         with torch.cuda.device(self.device):
-            self.state = torch.empty(self.state_bytes, dtype=torch.uint8, device=self.device)
+            self.state_buffer = torch.empty(self.state_bytes, dtype=torch.uint8, device=self.device)
             self.workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=self.device)
             stream = torch.cuda.current_stream(self.device).cuda_stream
             self._h = L.apexw_create(self._numel, self._pdt, self._gdt, group_of,
-                                     len(self.param_groups), fmt, self.state.data_ptr(),
+                                     len(self.param_groups), fmt, self.state_buffer.data_ptr(),
                                      self.state_bytes, self.workspace.data_ptr(), ws_bytes,
                                      stream)
         self._params_arr = L.make_ptrs([p.data_ptr() for p in self._params])
+
+    def add_param_group(self, param_group: Dict) -> None:
+        if getattr(self, "_h", None) is not None:
+            raise NotImplementedError(
+                "the tensor list of this optimizer is fixed at construction; build a new "
+                "one (state_dict / load_state_dict carry the state of the common tensors)")
+        super().add_param_group(param_group)
 
     # ------------------------------------------------------------ stepping
     def _grads_arr(self):
@@ -118,14 +127,27 @@ class AdamW:
     def _stream(self) -> int:
         return torch.cuda.current_stream(self.device).cuda_stream
 
-    def step(self, found_inf: Optional[torch.Tensor] = None,
+    @torch.no_grad()
+    def step(self, closure=None, found_inf: Optional[torch.Tensor] = None,
              inv_scale: Optional[torch.Tensor] = None,
-             clip_coef: Optional[torch.Tensor] = None) -> None:
+             clip_coef: Optional[torch.Tensor] = None):
         """One update; a parameter whose .grad is None is left untouched.
         found_inf: one-element float32 GPU tensor, nonzero skips the step on
         the device.  inv_scale: grads are unscaled by it first.  clip_coef:
-        then multiplied by it (see clip_grad_norm)."""
+        then multiplied by it (see clip_grad_norm).  Under a GradScaler the
+        scaler's grad_scale and found_inf are used when these are not given."""
+        loss = None
+        if closure is not None:
+            with torch.enable_grad():
+                loss = closure()
+        scaler_scale = getattr(self, "grad_scale", None)
+        scaler_inf = getattr(self, "found_inf", None)
+        if found_inf is None and scaler_inf is not None:
+            found_inf = scaler_inf.to(torch.float32).reshape(1)
+        if inv_scale is None and scaler_scale is not None:
+            inv_scale = torch.reciprocal(scaler_scale.to(torch.float32).reshape(1))
         self.step_pointers(self._grads_arr(), found_inf, inv_scale, clip_coef)
+        return loss
 
     def step_pointers(self, grads_arr, found_inf: Optional[torch.Tensor] = None,
                       inv_scale: Optional[torch.Tensor] = None,
@@ -158,15 +180,6 @@ class AdamW:
                                    norm.data_ptr(), coef.data_ptr(), self._stream())
         return norm, coef
 
-    def zero_grad(self, set_to_none: bool = True) -> None:
-        for p in self._params:
-            if p.grad is None:
-                continue
-            if set_to_none:
-                p.grad = None
-            else:
-                p.grad.zero_()
-
     # ------------------------------------------------------------ checkpoint
     def state_dict(self) -> Dict:
         """The optimizer checkpoint: the library's blob (format, tensor list,
@@ -196,8 +209,8 @@ class AdamW:
         m_off, v_off, _, _ = self._layout[i]
         dm, dv = _MOMENT_DTYPE[self.state_fmt]
         n = self._numel[i]
-        m = self.state[m_off:m_off + n * dm.itemsize].view(dm)
-        v = self.state[v_off:v_off + n * dv.itemsize].view(dv)
+        m = self.state_buffer[m_off:m_off + n * dm.itemsize].view(dm)
+        v = self.state_buffer[v_off:v_off + n * dv.itemsize].view(dv)
         return m, v
 
     def scales(self, i: int):
@@ -206,13 +219,13 @@ class AdamW:
         if ms < 0:
             raise ValueError("only the 8-bit state has block scales")
         nb = (self._numel[i] + L.APEXW_Q8_BLOCK - 1) // L.APEXW_Q8_BLOCK
-        return (self.state[ms:ms + 4 * nb].view(torch.float32),
-                self.state[vs:vs + 4 * nb].view(torch.float32))
+        return (self.state_buffer[ms:ms + 4 * nb].view(torch.float32),
+                self.state_buffer[vs:vs + 4 * nb].view(torch.float32))
 
     def steps(self) -> torch.Tensor:
         """int32 step counter of every parameter (view)."""
         n = len(self._params)
-        return self.state[self._steps_off:self._steps_off + 4 * n].view(torch.int32)
+        return self.state_buffer[self._steps_off:self._steps_off + 4 * n].view(torch.int32)
 
     def read_steps(self):
         """Step counters copied to the host (synchronises the current stream)."""

@@ -96,3 +96,51 @@ def test_wrapper_rejects_sparse_grads_and_reads_steps():
     assert e.value.code == L.APEXW_ESPARSE
     assert opt.read_steps() == [1, 1]
     opt.close()
+
+
+def test_wrapper_with_lr_scheduler_and_grad_scaler_against_oracle():
+    """The wrapper as a torch.optim.Optimizer: a StepLR schedule changes lr
+    between steps, and torch.amp.GradScaler drives the steps -- the scaler
+    hands over its scale and overflow flag, the update unscales in the
+    kernel, and a step whose grads hold an inf is skipped on the device
+    (the scaler then halves its scale).  Every step against the oracle."""
+    say("case: wrapper + StepLR + GradScaler")
+    gen = torch.Generator().manual_seed(61)
+    shapes = [(128, 9), (513,)]
+    p_cpu = [(torch.randn(s, generator=gen) * 0.02) for s in shapes]
+    params = [p.to(DEV) for p in p_cpu]
+    opt = AdamW(params, lr=1e-2, weight_decay=0.05)
+    assert isinstance(opt, torch.optim.Optimizer)
+    sched = torch.optim.lr_scheduler.StepLR(opt, step_size=2, gamma=0.5)
+    scaler = torch.amp.GradScaler("cuda", init_scale=2.0 ** 12, growth_interval=1000)
+    ref = oracle.OracleAdamW([p.numel() for p in p_cpu], ["f32"] * 2, ["f32"] * 2, [0, 0], "f32")
+    th_ref = [bits(p) for p in p_cpu]
+    lr = 1e-2
+    loss = torch.ones((), device=DEV)
+    for k in range(1, 8):
+        scaler.scale(loss)                           # as a training loop scales its loss
+        scale = scaler.get_scale()
+        g_cpu = [torch.randn(s, generator=gen) * 1e-3 for s in shapes]
+        for p, g in zip(params, g_cpu):
+            p.grad = (g * scale).to(DEV)             # as a scaled backward would leave them
+        overflow = k == 4
+        if overflow:
+            params[1].grad[7] = float("inf")
+        scaler.step(opt)
+        scaler.update()
+        grp = [W.Group(lr=lr, weight_decay=0.05)]
+        g_np = [bits(g * scale) for g in g_cpu]
+        if overflow:
+            g_np[1][7] = np.float32(np.inf)
+        ref.step(th_ref, g_np, grp, found_inf=overflow, inv_scale=float(np.float32(1.0 / scale)))
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert n_bit_mismatch(bits(params[i]), th_ref[i]) == 0, (k, i)
+        if overflow:
+            assert scaler.get_scale() == scale / 2
+        sched.step()
+        lr = opt.param_groups[0]["lr"]
+        opt.zero_grad()
+    assert list(bits(opt.steps())) == [6, 6]
+    assert lr == 1e-2 * 0.5 ** 3
+    opt.close()
