@@ -479,6 +479,39 @@ def test_results_do_not_depend_on_grid(wg, fmt):
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
 
 
+@pytest.mark.parametrize("fmt", [W.STATE_F32, W.STATE_Q8])
+def test_results_do_not_depend_on_tensor_order(fmt):
+    """The same tensors listed in a shuffled order (so their tiles, launch
+    positions and table stripes all change): every tensor's theta, moments,
+    scales and counter are bitwise the same."""
+    _need_gpu()
+    say("case: tensor order", fmt)
+    w = dataclasses.replace(W.many_small(n_tensors=120), state_fmt=fmt)
+    n = len(w.shapes)
+    perm = np.random.default_rng(31).permutation(n)
+    runs = []
+    for order in (np.arange(n), perm):
+        p_all = W.init_params(w, DEV)
+        params = [p_all[i] for i in order]
+        opt = GpuOpt([w.numels[i] for i in order], [w.param_dtype[i] for i in order],
+                     [w.grad_dtype[i] for i in order], [w.group_of[i] for i in order], 3, fmt)
+        for k in range(1, 4):
+            g_all = W.grads_for_call(w, k, DEV)
+            opt.step(w.groups, params, [g_all[i] for i in order])
+        torch.cuda.synchronize()
+        res = {}
+        for j, i in enumerate(order):
+            m, v = opt.moments(j)
+            res[int(i)] = [bits(params[j]), bits(m), bits(v)]
+            if fmt == W.STATE_Q8:
+                res[int(i)] += [bits(t) for t in opt.scales(j)]
+        runs.append(res)
+        opt.close()
+    for i in range(n):
+        for a, b in zip(runs[0][i], runs[1][i]):
+            assert n_bit_mismatch(a, b) == 0, i
+
+
 # =================================================================== configs
 
 def _sampled_run(w: W.Workload, sample_tensors, elems=None, seed=0, every=None,
