@@ -51,7 +51,11 @@ int fail(int code, const char *fmt, ...) {
                         hipGetErrorString(e_));                              \
     } while (0)
 
-constexpr int64_t kMomentAlign = 16;   // 128-bit loads of every moment array
+// Every moment array starts and ends on a 64-byte boundary: aligned vector
+// loads, and the update writes a tensor's last partial 64-byte chunk of m and
+// v whole (zeros past the end) -- a partly written chunk costs the memory a
+// read-modify-write.
+constexpr int64_t kMomentAlign = 64;
 constexpr int64_t kTableAlign = 256;
 
 int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
@@ -78,8 +82,8 @@ int check_list(int32_t n, const int64_t *numel) {
 }
 
 // State layout: every m array, every v array, (Q8) every m scale array and
-// every v scale array, then the int32 step counters.  Moment arrays start on
-// 16-byte boundaries.
+// every v scale array, then the int32 step counters.  Moment arrays start and
+// end on 64-byte boundaries.
 int compute_layout(int32_t n, const int64_t *numel, int32_t fmt,
                    apexw_tensor_state *per_tensor, int64_t *steps_off,
                    int64_t *total) {

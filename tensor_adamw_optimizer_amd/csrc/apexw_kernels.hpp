@@ -380,12 +380,19 @@ __device__ __forceinline__ void tile_dense(const TensorDesc &d, const void *grad
         }
 #pragma unroll
         for (int j = 0; j < kVec; ++j) adamw_update(th[j], g[j], m[j], v[j], s);
+        // m and v up to the end of their last 64-byte chunk (zeros past the
+        // tensor: the state arrays are padded for it), theta to its end
+        constexpr int kChunk = ST == APEXW_F32 ? 16 : 32;
+        const int n_pad = (n + kChunk - 1) / kChunk * kChunk;
 #pragma unroll
         for (int j = 0; j < kVec; ++j) {
             if (off + j < n) {
                 store1<PT>(d.param, e + j, th[j]);
                 store1<ST>(d.m, e + j, m[j]);
                 store1<ST>(d.v, e + j, v[j]);
+            } else if (off + j < n_pad) {
+                store1<ST>(d.m, e + j, 0.0f);
+                store1<ST>(d.v, e + j, 0.0f);
             }
         }
     }
@@ -515,12 +522,18 @@ __device__ __forceinline__ void tile_q8(const TensorDesc &d, const void *grad,
         store_u32<NT>(d.v, e, pack_codes_unsigned(v, bv));
         store4_any<PT, NT>(d.param, e, th, pv);
     } else {
+        // codes up to the end of their last 64-byte chunk (zero codes past
+        // the tensor: the state arrays are padded for it), theta to its end
+        const int n_pad = (n + 63) / 64 * 64;
 #pragma unroll
         for (int j = 0; j < kVec; ++j) {
             if (off + j < n) {
                 gptr<int8_t>(d.m)[e + j] = (int8_t)(int)code_value(m[j], bm, -127.0f, 127.0f);
                 gptr<uint8_t>(d.v)[e + j] = (uint8_t)(int)code_value(v[j], bv, 0.0f, 255.0f);
                 store1<PT>(d.param, e + j, th[j]);
+            } else if (off + j < n_pad) {
+                gptr<int8_t>(d.m)[e + j] = 0;
+                gptr<uint8_t>(d.v)[e + j] = 0;
             }
         }
     }
