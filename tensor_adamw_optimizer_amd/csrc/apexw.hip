@@ -145,7 +145,9 @@ WsLayout ws_layout(int32_t n, const int64_t *numel) {
     // each launch's table is padded to a multiple of kXcds entries; the read
     // passes load table entries in fours and may read up to 3 past the end
     w.partials = w.tiles + round_up((w.n_tiles + kMaxLaunches * kXcds + 4) * 4, kTableAlign);
-    w.partials2 = w.partials + round_up(w.n_tiles * 8, kTableAlign);
+    // grad-norm partials: one per tile-table entry (stored at the tile's
+    // table position; padding entries stay 0)
+    w.partials2 = w.partials + round_up((w.n_tiles + kMaxLaunches * kXcds) * 8, kTableAlign);
     w.consts = w.partials2 + round_up(kReduceBlocks * 8, kTableAlign);
     w.total = n == 0 ? 0 : w.consts + round_up((int64_t)sizeof(kConsts), kTableAlign);
     return w;
@@ -236,6 +238,7 @@ struct apexw_opt {
     bool ev_pending[kRing] = {};
     int next_slot = 0;
     int cu_count = 0;
+    int64_t table_entries = 0;          // tile-table length (all launches, with padding)
     int lds_per_cu = 0, lds_per_block = 0;
     int32_t wg_override = 0;
     int32_t occupancy = 0;              // override for every launch (0: defaults)
@@ -509,6 +512,7 @@ int apexw_create(int32_t n_tensors, const int64_t *numel, const int32_t *param_d
             logical += L.tile_count;
             h->launches.push_back(L);
         }
+        h->table_entries = (int64_t)tiles.size();
     } catch (const std::bad_alloc &) {
         return bail(fail(APEXW_ENOMEM, "host allocation failed"));
     }
@@ -717,7 +721,7 @@ int apexw_clip_grad_norm(apexw_t h, const void *const *grads, const float *inv_s
     a.norm_out = norm_out_dev;
     a.clip_out = clip_coef_dev;
     a.max_norm = max_norm;
-    a.n_tiles_total = h->wl.n_tiles;
+    a.n_tiles_total = h->table_entries;   // partials live at table positions
     const bool streaming = h->cache_policy == 0 ? h->streaming_auto : h->cache_policy == 1;
     // every tile writes its partial (0 without a grad), so no launch is skipped
     for (const Launch &L : h->launches) {

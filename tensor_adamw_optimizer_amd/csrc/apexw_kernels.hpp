@@ -129,7 +129,7 @@ struct KernelArgs {
     double *norm_out;                // grad-norm finalize: the norm (may be null)
     float *clip_out;                 // grad-norm finalize: the clip coefficient
     double max_norm;
-    int64_t n_tiles_total;           // logical tiles over all launches
+    int64_t n_tiles_total;           // tile-table entries over all launches (grad norm)
     int64_t tile_begin;              // this launch's tiles: [begin, begin+count)
     int64_t tile_count;
     int64_t table_begin;             // this launch's part of tile_tensor
@@ -681,12 +681,14 @@ __host__ __device__ __forceinline__ int64_t read_groups(int64_t stride) {
 }
 
 // A tile of a read group: grad (nullptr: absent), first element, valid
-// length (0 for a tile past the launch end), logical tile index.
+// length (0 for a tile past the launch end), logical tile index, position in
+// the tile table.
 struct ReadTile {
     const void *grad;
     int64_t base;
     int n;
     int64_t k;
+    int64_t pos;
 };
 
 // The tiles of group j; false if the group starts past the launch end.  The
@@ -697,14 +699,15 @@ __device__ __forceinline__ bool read_group(const KernelArgs &a, int64_t j,
     const int64_t x = j % kXcds, c = j / kXcds;
     const int64_t k0 = x + (int64_t)kXcds * kReadBatch * c;
     if (k0 >= a.tile_count) return false;
-    const APEXW_CONST int32_t *row =
-        cptr<int32_t>(a.tile_tensor) + a.table_begin + x * a.table_stride + kReadBatch * c;
+    const int64_t pos0 = a.table_begin + x * a.table_stride + kReadBatch * c;
+    const APEXW_CONST int32_t *row = cptr<int32_t>(a.tile_tensor) + pos0;
     int32_t ti[kReadBatch];
 #pragma unroll
     for (int u = 0; u < kReadBatch; ++u) ti[u] = row[u];
 #pragma unroll
     for (int u = 0; u < kReadBatch; ++u) {
         t[u].k = k0 + (int64_t)kXcds * u;
+        t[u].pos = pos0 + u;
         const bool live = t[u].k < a.tile_count;
         const int32_t i = live ? ti[u] : ti[0];
         const APEXW_CONST int64_t *dd = cptr<int64_t>(&a.desc[i].numel);   // numel, first_tile
@@ -758,10 +761,13 @@ __global__ __launch_bounds__(kThreads) void unscale_check_kernel(KernelArgs a) {
 // the norm of all present unscaled grads u = g * inv_scale (fp32, as the
 // update uses them), squares and sums in fp64, reduced in a fixed order so
 // the result does not depend on scheduling:
-//  1. grad_norm_partials_kernel: the squares of each tile are summed by one
-//     wave (lane order, then wave_sum's fixed order) into partials[tile]; tiles
-//     without a grad contribute 0; optionally sets found_inf_out like the
-//     unscale check;
+//  1. grad_norm_partials_kernel: the squares of each read group (four tiles
+//     fixed by the tile table alone, not by the grid) are summed by one wave
+//     -- per lane over the group's tiles in order, then wave_sum's fixed
+//     order -- into partials[p], p the table position of the group's first
+//     tile; every other entry stays 0 (set at create, never written), which
+//     adds nothing; tiles without a grad contribute 0; optionally sets
+//     found_inf_out like the unscale check;
 //  2. grad_norm_reduce_kernel: workgroup b sums partials[b*C .. (b+1)*C) with
 //     a strided loop and a tree in LDS into partials2[b];
 //  3. grad_norm_final_kernel: one workgroup sums partials2 the same way and
@@ -806,25 +812,20 @@ __global__ __launch_bounds__(kThreads) void grad_norm_partials_kernel(KernelArgs
         if (!read_group(a, jg, t)) continue;
 #pragma unroll
         for (int u = 0; u < kReadBatch; ++u) load_tile_grads<GT, NT>(t[u], g[u]);
-        double sq[kReadBatch];
+        double sq = 0.0;                  // the group's tiles in order, each lane's 4 values
 #pragma unroll
         for (int u = 0; u < kReadBatch; ++u) {
-            sq[u] = 0.0;
 #pragma unroll
             for (int j = 0; j < kVec; ++j) {
                 const float x = g[u][j] * inv;
                 if (t[u].grad != nullptr && off + j < t[u].n) {
                     bad |= !(fabsf(x) <= 3.40282347e38f);
-                    sq[u] = sq[u] + (double)x * (double)x;
+                    sq = sq + (double)x * (double)x;
                 }
             }
         }
-#pragma unroll
-        for (int u = 0; u < kReadBatch; ++u) sq[u] = wave_sum(sq[u]);
-#pragma unroll
-        for (int u = 0; u < kReadBatch; ++u)
-            if (threadIdx.x == 0 && t[u].k < a.tile_count)
-                gptr<double>(static_cast<void *>(a.partials))[a.tile_begin + t[u].k] = sq[u];
+        sq = wave_sum(sq);
+        if (threadIdx.x == 0) gptr<double>(static_cast<void *>(a.partials))[t[0].pos] = sq;
     }
     if (a.found_inf_out != nullptr && wave_any(bad) && threadIdx.x == 0)
         *gptr<float>(static_cast<void *>(a.found_inf_out)) = 1.0f;
