@@ -184,26 +184,29 @@ int default_occupancy(int32_t fmt, int pt, int gt) {
 
 typedef void (*kernel_fn)(KernelArgs);
 
-template <int ST, bool NT>
+template <int ST, bool NT, bool SC>
 kernel_fn pick_kernel(int pt, int gt) {
-    if (pt == APEXW_F32 && gt == APEXW_F32) return adamw_step_kernel<ST, APEXW_F32, APEXW_F32, NT>;
-    if (pt == APEXW_F32 && gt == APEXW_BF16) return adamw_step_kernel<ST, APEXW_F32, APEXW_BF16, NT>;
-    if (pt == APEXW_BF16 && gt == APEXW_F32) return adamw_step_kernel<ST, APEXW_BF16, APEXW_F32, NT>;
-    return adamw_step_kernel<ST, APEXW_BF16, APEXW_BF16, NT>;
+    if (pt == APEXW_F32 && gt == APEXW_F32) return adamw_step_kernel<ST, APEXW_F32, APEXW_F32, NT, SC>;
+    if (pt == APEXW_F32 && gt == APEXW_BF16) return adamw_step_kernel<ST, APEXW_F32, APEXW_BF16, NT, SC>;
+    if (pt == APEXW_BF16 && gt == APEXW_F32) return adamw_step_kernel<ST, APEXW_BF16, APEXW_F32, NT, SC>;
+    return adamw_step_kernel<ST, APEXW_BF16, APEXW_BF16, NT, SC>;
+}
+
+template <bool NT, bool SC>
+kernel_fn pick_format(int fmt, int pt, int gt) {
+    if (fmt == APEXW_STATE_F32) return pick_kernel<APEXW_STATE_F32, NT, SC>(pt, gt);
+    if (fmt == APEXW_STATE_BF16) return pick_kernel<APEXW_STATE_BF16, NT, SC>(pt, gt);
+    return pick_kernel<APEXW_STATE_Q8, NT, SC>(pt, gt);
 }
 
 // streaming = non-temporal loads and stores (the single-use streams of a
 // list far larger than the caches); a list whose parameters, grads and state
 // fit the 256 MB Infinity Cache many times over keeps them cached instead.
-kernel_fn kernel_for(int fmt, int pt, int gt, bool streaming) {
-    if (streaming) {
-        if (fmt == APEXW_STATE_F32) return pick_kernel<APEXW_STATE_F32, true>(pt, gt);
-        if (fmt == APEXW_STATE_BF16) return pick_kernel<APEXW_STATE_BF16, true>(pt, gt);
-        return pick_kernel<APEXW_STATE_Q8, true>(pt, gt);
-    }
-    if (fmt == APEXW_STATE_F32) return pick_kernel<APEXW_STATE_F32, false>(pt, gt);
-    if (fmt == APEXW_STATE_BF16) return pick_kernel<APEXW_STATE_BF16, false>(pt, gt);
-    return pick_kernel<APEXW_STATE_Q8, false>(pt, gt);
+// scaled = the step was given inv_scale or clip_coef.
+kernel_fn kernel_for(int fmt, int pt, int gt, bool streaming, bool scaled) {
+    if (streaming)
+        return scaled ? pick_format<true, true>(fmt, pt, gt) : pick_format<true, false>(fmt, pt, gt);
+    return scaled ? pick_format<false, true>(fmt, pt, gt) : pick_format<false, false>(fmt, pt, gt);
 }
 
 // Bytes an optimizer touches per step (parameters, grads, state): above this
@@ -629,6 +632,7 @@ int apexw_step_ex(apexw_t h, const apexw_group *groups, int32_t n_groups, void *
     a.tile_tensor = reinterpret_cast<const int32_t *>(h->ws + h->wl.tiles);
     a.records = reinterpret_cast<StepRecord *>(h->ws + h->wl.records);
     a.steps = reinterpret_cast<int32_t *>(h->state + h->steps_off);
+    const bool scaled = inv_scale_dev != nullptr || a.clip_coef != nullptr;
     const float *consts = reinterpret_cast<const float *>(h->ws + h->wl.consts);
     a.found_inf = found_inf_dev != nullptr ? found_inf_dev : consts;        // 0: no skip
     a.inv_scale = inv_scale_dev != nullptr ? inv_scale_dev : consts + 1;    // 1: unscaled
@@ -653,7 +657,7 @@ int apexw_step_ex(apexw_t h, const apexw_group *groups, int32_t n_groups, void *
         a.table_stride = L.table_stride;
         const int64_t wg = std::min(L.tile_count, cap);
         const bool streaming = h->cache_policy == 0 ? h->streaming_auto : h->cache_policy == 1;
-        hipLaunchKernelGGL(kernel_for(h->fmt, L.pt, L.gt, streaming), dim3((unsigned)wg), dim3(kThreads),
+        hipLaunchKernelGGL(kernel_for(h->fmt, L.pt, L.gt, streaming, scaled), dim3((unsigned)wg), dim3(kThreads),
                            lds, st, a);
         HIP_TRY(hipGetLastError());
     }

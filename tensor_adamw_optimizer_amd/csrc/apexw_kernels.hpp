@@ -204,9 +204,12 @@ __device__ __forceinline__ float sqrt_rn(float x) {
 // rounded, evaluated left to right as printed, on the unscaled and clipped
 // grad (the mixed-precision recipe of M041 section 06: unscale, check,
 // clip; multiplying by 1 is exact).
+// SC: the step may scale the grads (inv_scale, clip_coef given); a plain
+// step skips the two multiplies by 1, which change nothing.
+template <bool SC>
 __device__ __forceinline__ void adamw_update(float &theta, float g_scaled, float &m,
                                              float &v, const StepScalars &s) {
-    const float g = (g_scaled * s.inv_scale) * s.clip_coef;
+    const float g = SC ? (g_scaled * s.inv_scale) * s.clip_coef : g_scaled;
     m = s.beta1 * m + s.one_minus_beta1 * g;
     v = s.beta2 * v + (s.one_minus_beta2 * g) * g;
     const float m_hat = m / s.bc1;
@@ -352,7 +355,7 @@ __device__ __forceinline__ float wave_max_nonneg(float x) {
 // its valid elements one by one (zeros elsewhere), runs the update on all 4
 // values together -- one converged pass instead of one per element -- and
 // stores only the valid ones.
-template <int PT, int GT, int ST, bool NT>
+template <int PT, int GT, int ST, bool NT, bool SC>
 __device__ __forceinline__ void tile_dense(const TensorDesc &d, const void *grad,
                                            int64_t base, int n, const StepScalars &s) {
     const int off = threadIdx.x * kVec;
@@ -365,7 +368,7 @@ __device__ __forceinline__ void tile_dense(const TensorDesc &d, const void *grad
         load4_any<GT, NT>(grad, e, g, gv);
         load4_any<PT, NT>(d.param, e, th, pv);
 #pragma unroll
-        for (int j = 0; j < kVec; ++j) adamw_update(th[j], g[j], m[j], v[j], s);
+        for (int j = 0; j < kVec; ++j) adamw_update<SC>(th[j], g[j], m[j], v[j], s);
         store4_any<PT, NT>(d.param, e, th, pv);
         store4<ST, NT>(d.m, e, m);
         store4<ST, NT>(d.v, e, v);
@@ -379,7 +382,7 @@ __device__ __forceinline__ void tile_dense(const TensorDesc &d, const void *grad
             th[j] = ok ? load1<PT>(d.param, e + j) : 0.0f;
         }
 #pragma unroll
-        for (int j = 0; j < kVec; ++j) adamw_update(th[j], g[j], m[j], v[j], s);
+        for (int j = 0; j < kVec; ++j) adamw_update<SC>(th[j], g[j], m[j], v[j], s);
         // m and v up to the end of their last 64-byte chunk (zeros past the
         // tensor: the state arrays are padded for it), theta to its end
         constexpr int kChunk = ST == APEXW_F32 ? 16 : 32;
@@ -457,7 +460,7 @@ __device__ __forceinline__ uint32_t pack_codes_unsigned(const float (&x)[kVec], 
 // One tile = one 8-bit block (block index base/256 of the tensor): decode
 // with the stored scales, update in fp32, reduce the block maxima over the
 // wave, re-encode.  theta uses this step's fp32 moments.
-template <int PT, int GT, bool NT>
+template <int PT, int GT, bool NT, bool SC>
 __device__ __forceinline__ void tile_q8(const TensorDesc &d, const void *grad,
                                         int64_t base, int n, const StepScalars &s) {
     const int off = threadIdx.x * kVec;
@@ -492,7 +495,7 @@ __device__ __forceinline__ void tile_q8(const TensorDesc &d, const void *grad,
     }
     float am = 0.0f, av = 0.0f;
 #pragma unroll
-    for (int j = 0; j < kVec; ++j) adamw_update(th[j], g[j], m[j], v[j], s);
+    for (int j = 0; j < kVec; ++j) adamw_update<SC>(th[j], g[j], m[j], v[j], s);
     // block maxima (a NaN moment is passed over; v >= 0, fabs makes a -0 +0)
     if (n == kTile) {                         // wave-uniform: a full block
 #pragma unroll
@@ -627,7 +630,8 @@ __device__ __forceinline__ int64_t table_pos(const KernelArgs &a, int64_t k) {
 // The update: one 256-element tile per workgroup (the grid-stride loop only
 // runs more than once when the tile count exceeds the grid).
 // ST: APEXW_STATE_F32 / _BF16 / _Q8.  PT, GT: parameter and grad types.
-template <int ST, int PT, int GT, bool NT>
+// SC: the grads are scaled (inv_scale and / or clip_coef given).
+template <int ST, int PT, int GT, bool NT, bool SC>
 __global__ __launch_bounds__(kThreads) void adamw_step_kernel(KernelArgs a) {
     const APEXW_CONST int32_t *tile_tensor = cptr<int32_t>(a.tile_tensor);
     int64_t k = blockIdx.x;                    // < tile_count: grid <= tiles
@@ -648,11 +652,11 @@ __global__ __launch_bounds__(kThreads) void adamw_step_kernel(KernelArgs a) {
         if (r.grad != nullptr && n > 0) {
             const StepScalars s = step_scalars(r);
             if constexpr (ST == APEXW_STATE_F32)
-                tile_dense<PT, GT, APEXW_F32, NT>(d, r.grad, base, n, s);
+                tile_dense<PT, GT, APEXW_F32, NT, SC>(d, r.grad, base, n, s);
             else if constexpr (ST == APEXW_STATE_BF16)
-                tile_dense<PT, GT, APEXW_BF16, NT>(d, r.grad, base, n, s);
+                tile_dense<PT, GT, APEXW_BF16, NT, SC>(d, r.grad, base, n, s);
             else
-                tile_q8<PT, GT, NT>(d, r.grad, base, n, s);
+                tile_q8<PT, GT, NT, SC>(d, r.grad, base, n, s);
         }
         k += gridDim.x;
         if (k >= a.tile_count) break;
