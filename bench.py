@@ -200,6 +200,8 @@ def main() -> int:
                     help="update workgroups per CU (0: the format's default)")
     ap.add_argument("--cache-policy", type=int, default=0,
                     help="0 auto, 1 streaming (non-temporal), 2 cached")
+    ap.add_argument("--launch-mode", type=int, default=0,
+                    help="0 auto, 1 prepare + update kernels, 2 single launch (small lists)")
     ap.add_argument("--amp", action="store_true",
                     help="time the mixed-precision recipe: zero found_inf, unscale-and-check "
                          "pass, update on grads scaled by 2^16")
@@ -258,6 +260,9 @@ def main() -> int:
         L.apexw_set_occupancy(h, args.occupancy)
     if args.cache_policy:
         L.apexw_set_cache_policy(h, args.cache_policy)
+    if args.launch_mode:
+        L.apexw_set_launch_mode(h, args.launch_mode)
+    launch_mode = L.apexw_get_launch_mode(h)
     occupancy = L.apexw_get_occupancy(h)
     tile, n_tiles, wgs = L.apexw_launch_info(h)
     params_arr = L.make_ptrs([p.data_ptr() for p in params])
@@ -384,7 +389,8 @@ def main() -> int:
                                     if args.flush_mall else "")),
         "max_memory_allocated": max_mem,
         "launch": {"tile_elems": tile, "tiles": n_tiles, "workgroups": wgs,
-                   "workgroups_per_cu_cap": occupancy},
+                   "workgroups_per_cu_cap": occupancy,
+                   "mode": "single launch" if launch_mode == 2 else "prepare + update"},
         "state_bytes": state_bytes,
         "roofline": {
             "bound": "hbm",
@@ -394,7 +400,7 @@ def main() -> int:
             "frac": gbps / HBM_PEAK_GBPS,
             "traffic": traffic,
             "algorithmic_bytes_per_launch": ab,
-            "kernel": "adamw_step_kernel" + ((" + grad_norm kernels" if args.clip > 0 else " + unscale_check_kernel") if args.amp else ""),
+            "kernel": ("adamw_single_step_kernel" if launch_mode == 2 else "adamw_step_kernel") + ((" + grad_norm kernels" if args.clip > 0 else " + unscale_check_kernel") if args.amp else ""),
         },
     }
     out["context"] = {"device_copy_gbps": copy_gbps,

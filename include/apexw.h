@@ -351,6 +351,26 @@ int apexw_set_occupancy(apexw_t h, int32_t workgroups_per_cu);
  */
 int apexw_set_cache_policy(apexw_t h, int32_t policy);
 
+/*
+ * How a step is launched.  1: a prepare kernel (one lane per tensor: step
+ * counter, bias corrections, per-tensor record) and then one update kernel
+ * per (param, grad) dtype pair.  2: one kernel per dtype pair that does both:
+ * every workgroup forms its tensor's record from the counter, and the last
+ * workgroup to finish (found through a two-level tree of arrival counters in
+ * the workspace) advances the counters.  It saves a launch, most of the cost
+ * of a small list, but each workgroup's arrival costs a device-scope atomic:
+ * on MI355X it is faster up to about 8,000 tiles.  Mode 2 needs a list of at
+ * most 6144 tiles (1,572,864 elements) whose dtype pairs each hold a
+ * non-empty tensor; APEXW_EINVAL otherwise.  0 (default): mode 2 for such
+ * lists unless they stream (apexw_set_cache_policy), else mode 1.  Results
+ * do not depend on the mode; steps of one handle queued on two streams at
+ * once race in either mode.
+ */
+int apexw_set_launch_mode(apexw_t h, int32_t mode);
+
+/* The launch mode (1 or 2) the handle's next step uses. */
+int apexw_get_launch_mode(apexw_t h, int32_t *mode);
+
 /* The largest cap in force over the handle's update launches (0: none). */
 int apexw_get_occupancy(apexw_t h, int32_t *workgroups_per_cu);
 

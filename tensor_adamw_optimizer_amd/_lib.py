@@ -41,7 +41,7 @@ ENTRY_POINTS = (
     "apexw_export_bytes", "apexw_export_state", "apexw_import_state",
     "apexw_read_steps", "apexw_launch_info", "apexw_set_workgroups",
     "apexw_set_occupancy", "apexw_get_occupancy", "apexw_set_cache_policy",
-    "apexw_destroy", "apexw_last_error",
+    "apexw_set_launch_mode", "apexw_get_launch_mode", "apexw_destroy", "apexw_last_error",
 )
 
 
@@ -102,6 +102,8 @@ def lib() -> ctypes.CDLL:
         L.apexw_set_occupancy.argtypes = [P, I32]
         L.apexw_get_occupancy.argtypes = [P, ctypes.POINTER(I32)]
         L.apexw_set_cache_policy.argtypes = [P, I32]
+        L.apexw_set_launch_mode.argtypes = [P, I32]
+        L.apexw_get_launch_mode.argtypes = [P, ctypes.POINTER(I32)]
         L.apexw_destroy.argtypes = [P]
         L.apexw_last_error.argtypes = []
         L.apexw_last_error.restype = ctypes.c_char_p
@@ -278,6 +280,16 @@ def apexw_get_occupancy(handle: int) -> int:
 
 def apexw_set_cache_policy(handle: int, policy: int) -> None:
     _check(lib().apexw_set_cache_policy(handle, policy), "apexw_set_cache_policy")
+
+
+def apexw_set_launch_mode(handle: int, mode: int) -> None:
+    _check(lib().apexw_set_launch_mode(handle, mode), "apexw_set_launch_mode")
+
+
+def apexw_get_launch_mode(handle: int) -> int:
+    m = ctypes.c_int32(0)
+    _check(lib().apexw_get_launch_mode(handle, ctypes.byref(m)), "apexw_get_launch_mode")
+    return m.value
 
 
 def apexw_destroy(handle: int) -> None:

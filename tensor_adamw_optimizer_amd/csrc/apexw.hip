@@ -122,8 +122,9 @@ int compute_layout(int32_t n, const int64_t *numel, int32_t fmt,
 // grad-norm partial sums (one per tile, then one per reduce workgroup), each
 // on a 256-byte boundary.
 struct WsLayout {
-    int64_t desc, grads, records, tiles, partials, partials2, consts, total;
+    int64_t desc, grads, records, tiles, partials, partials2, consts, done, tensors, total;
     int64_t n_tiles;
+    bool single;                         // room for the single-launch step
 };
 
 // The constants region: 0.0f and 1.0f, passed to the prepare kernel in place
@@ -133,6 +134,11 @@ constexpr float kConsts[2] = {0.0f, 1.0f};
 
 constexpr int kMaxLaunches = 4;      // (param, grad) dtype pairs
 constexpr int64_t kMaxGrid = 1 << 24;  // workgroups per launch (grid-stride above)
+
+// Lists of at most this many tiles may take the single-launch step (one
+// kernel per dtype pair, no prepare launch); the workspace then holds its
+// arrival counters and the tensor list of every launch.
+constexpr int64_t kSingleLaunchTiles = 6144;
 
 WsLayout ws_layout(int32_t n, const int64_t *numel) {
     WsLayout w;
@@ -149,7 +155,10 @@ WsLayout ws_layout(int32_t n, const int64_t *numel) {
     // table position; padding entries stay 0)
     w.partials2 = w.partials + round_up((w.n_tiles + kMaxLaunches * kXcds) * 8, kTableAlign);
     w.consts = w.partials2 + round_up(kReduceBlocks * 8, kTableAlign);
-    w.total = n == 0 ? 0 : w.consts + round_up((int64_t)sizeof(kConsts), kTableAlign);
+    w.done = w.consts + round_up((int64_t)sizeof(kConsts), kTableAlign);
+    w.single = w.n_tiles <= kSingleLaunchTiles;
+    w.tensors = w.done + (w.single ? round_up((int64_t)kMaxLaunches * kDoneWords * 4, kTableAlign) : 0);
+    w.total = n == 0 ? 0 : w.tensors + (w.single ? round_up((int64_t)n * 4, kTableAlign) : 0);
     return w;
 }
 
@@ -209,6 +218,23 @@ kernel_fn kernel_for(int fmt, int pt, int gt, bool streaming, bool scaled) {
     return scaled ? pick_format<false, true>(fmt, pt, gt) : pick_format<false, false>(fmt, pt, gt);
 }
 
+template <int ST, bool SC>
+kernel_fn pick_single(int pt, int gt) {
+    if (pt == APEXW_F32 && gt == APEXW_F32) return adamw_single_step_kernel<ST, APEXW_F32, APEXW_F32, SC>;
+    if (pt == APEXW_F32 && gt == APEXW_BF16) return adamw_single_step_kernel<ST, APEXW_F32, APEXW_BF16, SC>;
+    if (pt == APEXW_BF16 && gt == APEXW_F32) return adamw_single_step_kernel<ST, APEXW_BF16, APEXW_F32, SC>;
+    return adamw_single_step_kernel<ST, APEXW_BF16, APEXW_BF16, SC>;
+}
+
+// The single-launch step kernel (cached accesses: such lists are small).
+kernel_fn single_kernel_for(int fmt, int pt, int gt, bool scaled) {
+    if (fmt == APEXW_STATE_F32)
+        return scaled ? pick_single<APEXW_STATE_F32, true>(pt, gt) : pick_single<APEXW_STATE_F32, false>(pt, gt);
+    if (fmt == APEXW_STATE_BF16)
+        return scaled ? pick_single<APEXW_STATE_BF16, true>(pt, gt) : pick_single<APEXW_STATE_BF16, false>(pt, gt);
+    return scaled ? pick_single<APEXW_STATE_Q8, true>(pt, gt) : pick_single<APEXW_STATE_Q8, false>(pt, gt);
+}
+
 // Bytes an optimizer touches per step (parameters, grads, state): above this
 // the update streams past the caches.
 constexpr int64_t kStreamingBytes = (int64_t)192 << 20;
@@ -247,6 +273,8 @@ struct apexw_opt {
     int32_t occupancy = 0;              // override for every launch (0: defaults)
     int cache_policy = 0;               // 0 auto, 1 streaming, 2 cached
     bool streaming_auto = true;
+    bool single_ok = false;             // the single-launch step is available
+    int launch_mode = 0;                // 0 auto, 1 prepare + update, 2 single launch
 };
 
 namespace {
@@ -351,6 +379,15 @@ int reuse_last(apexw_opt *h, void *const **params, const void *const **grads) {
         *grads = h->last_grads.data();
     }
     return APEXW_OK;
+}
+
+bool streams(const apexw_opt *h) {
+    return h->cache_policy == 0 ? h->streaming_auto : h->cache_policy == 1;
+}
+
+// The single launch: forced, or by default for the lists it is made for.
+bool single_launch(const apexw_opt *h) {
+    return h->launch_mode == 2 || (h->launch_mode == 0 && h->single_ok && !streams(h));
 }
 
 int launch_cap(const apexw_opt *h) { return h->wg_override > 0 ? h->wg_override : (int)kMaxGrid; }
@@ -516,6 +553,10 @@ int apexw_create(int32_t n_tensors, const int64_t *numel, const int32_t *param_d
             h->launches.push_back(L);
         }
         h->table_entries = (int64_t)tiles.size();
+        // the single launch needs a tile in every launch (a launch of empty
+        // tensors only advances counters, which the prepare kernel does)
+        h->single_ok = wl.single && n_tensors > 0;
+        for (const Launch &L : h->launches) h->single_ok = h->single_ok && L.tile_count > 0;
     } catch (const std::bad_alloc &) {
         return bail(fail(APEXW_ENOMEM, "host allocation failed"));
     }
@@ -541,6 +582,8 @@ int apexw_create(int32_t n_tensors, const int64_t *numel, const int32_t *param_d
         std::memcpy(stage + wl.desc, h->desc.data(), (size_t)n_tensors * sizeof(TensorDesc));
     if (!tiles.empty())
         std::memcpy(stage + wl.tiles, tiles.data(), tiles.size() * 4);
+    if (wl.single && n_tensors > 0)           // arrival counters stay zero
+        std::memcpy(stage + wl.tensors, h->tensor_list.data(), (size_t)n_tensors * 4);
     if (static_bytes > 0) std::memcpy(stage + wl.consts, kConsts, sizeof(kConsts));
     if (static_bytes > 0)
         TRY(hipMemcpyAsync(h->ws, stage, (size_t)static_bytes, hipMemcpyHostToDevice, st));
@@ -638,14 +681,22 @@ int apexw_step_ex(apexw_t h, const apexw_group *groups, int32_t n_groups, void *
     a.inv_scale = inv_scale_dev != nullptr ? inv_scale_dev : consts + 1;    // 1: unscaled
     a.clip_coef = a.clip_coef != nullptr ? a.clip_coef : consts + 1;        // 1: unclipped
     a.n_tensors = h->n;
-    hipLaunchKernelGGL(adamw_prepare_kernel, dim3((unsigned)ceil_div(h->n, kPrepThreads)),
-                       dim3(kPrepThreads), 0, st, a);
-    HIP_TRY(hipGetLastError());
+    const bool streaming = streams(h);
+    const bool single = single_launch(h);
+    if (single) {
+        a.tensor_list = reinterpret_cast<const int32_t *>(h->ws + h->wl.tensors);
+    } else {
+        hipLaunchKernelGGL(adamw_prepare_kernel, dim3((unsigned)ceil_div(h->n, kPrepThreads)),
+                           dim3(kPrepThreads), 0, st, a);
+        HIP_TRY(hipGetLastError());
+    }
     const int64_t cap = launch_cap(h);
+    int li = -1;
     for (const Launch &L : h->launches) {
         // residency cap: the dynamic LDS a workgroup reserves (it uses none)
         const int occ = h->occupancy > 0 ? h->occupancy : default_occupancy(h->fmt, L.pt, L.gt);
         const unsigned lds = occ > 0 ? (unsigned)std::min(h->lds_per_cu / occ, h->lds_per_block) : 0u;
+        ++li;
         if (L.tile_count == 0) continue;      // only empty tensors: t advanced above
         bool any = false;                     // no grads in this launch: skip it
         for (int32_t j = 0; j < L.tensor_count && !any; ++j)
@@ -656,9 +707,16 @@ int apexw_step_ex(apexw_t h, const apexw_group *groups, int32_t n_groups, void *
         a.table_begin = L.table_begin;
         a.table_stride = L.table_stride;
         const int64_t wg = std::min(L.tile_count, cap);
-        const bool streaming = h->cache_policy == 0 ? h->streaming_auto : h->cache_policy == 1;
-        hipLaunchKernelGGL(kernel_for(h->fmt, L.pt, L.gt, streaming, scaled), dim3((unsigned)wg), dim3(kThreads),
-                           lds, st, a);
+        if (single) {
+            a.tensor_begin = L.tensor_begin;
+            a.tensor_count = L.tensor_count;
+            a.done = reinterpret_cast<uint32_t *>(h->ws + h->wl.done) + (int64_t)li * kDoneWords;
+            hipLaunchKernelGGL(single_kernel_for(h->fmt, L.pt, L.gt, scaled), dim3((unsigned)wg),
+                               dim3(kThreads), lds, st, a);
+        } else {
+            hipLaunchKernelGGL(kernel_for(h->fmt, L.pt, L.gt, streaming, scaled), dim3((unsigned)wg),
+                               dim3(kThreads), lds, st, a);
+        }
         HIP_TRY(hipGetLastError());
     }
     return APEXW_OK;
@@ -680,7 +738,7 @@ int apexw_unscale_check(apexw_t h, const void *const *grads, const float *inv_sc
     a.tile_tensor = reinterpret_cast<const int32_t *>(h->ws + h->wl.tiles);
     a.inv_scale = inv_scale_dev;
     a.found_inf_out = found_inf_dev;
-    const bool streaming = h->cache_policy == 0 ? h->streaming_auto : h->cache_policy == 1;
+    const bool streaming = streams(h);
     for (const Launch &L : h->launches) {
         if (L.tile_count == 0) continue;
         bool any = false;
@@ -726,7 +784,7 @@ int apexw_clip_grad_norm(apexw_t h, const void *const *grads, const float *inv_s
     a.clip_out = clip_coef_dev;
     a.max_norm = max_norm;
     a.n_tiles_total = h->table_entries;   // partials live at table positions
-    const bool streaming = h->cache_policy == 0 ? h->streaming_auto : h->cache_policy == 1;
+    const bool streaming = streams(h);
     // every tile writes its partial (0 without a grad), so no launch is skipped
     for (const Launch &L : h->launches) {
         if (L.tile_count == 0) continue;
@@ -903,6 +961,23 @@ int apexw_set_cache_policy(apexw_t h, int32_t policy) {
     if (!h) return fail(APEXW_EINVAL, "handle is NULL");
     if (policy < 0 || policy > 2) return fail(APEXW_EINVAL, "policy must be 0, 1 or 2");
     h->cache_policy = policy;
+    return APEXW_OK;
+}
+
+int apexw_set_launch_mode(apexw_t h, int32_t mode) {
+    if (!h) return fail(APEXW_EINVAL, "handle is NULL");
+    if (mode < 0 || mode > 2) return fail(APEXW_EINVAL, "mode must be 0, 1 or 2");
+    if (mode == 2 && !h->single_ok)
+        return fail(APEXW_EINVAL, "the single-launch step needs a non-empty list of at most %lld "
+                                  "tiles with a tile in every dtype pair it uses",
+                    (long long)kSingleLaunchTiles);
+    h->launch_mode = mode;
+    return APEXW_OK;
+}
+
+int apexw_get_launch_mode(apexw_t h, int32_t *mode) {
+    if (!h || !mode) return fail(APEXW_EINVAL, "NULL argument");
+    *mode = single_launch(h) ? 2 : 1;
     return APEXW_OK;
 }
 

@@ -135,7 +135,11 @@ struct KernelArgs {
     int64_t table_begin;             // this launch's part of tile_tensor
     int64_t table_stride;            // ceil(tile_count / kXcds)
     int32_t n_tensors;
+    int32_t tensor_begin;            // single-launch step: this launch's tensors are
+    int32_t tensor_count;            //   tensor_list[begin, begin+count)
     int32_t pad_;
+    const int32_t *tensor_list;
+    uint32_t *done;                  // single-launch step: arrival counters
     GroupScalars groups[APEXW_MAX_GROUPS];
 };
 
@@ -355,9 +359,11 @@ __device__ __forceinline__ float wave_max_nonneg(float x) {
 // its valid elements one by one (zeros elsewhere), runs the update on all 4
 // values together -- one converged pass instead of one per element -- and
 // stores only the valid ones.
-template <int PT, int GT, int ST, bool NT, bool SC>
+// get() yields the step's scalars; it is called after the tile's loads are
+// issued, so any memory reads or arithmetic it needs overlap with them.
+template <int PT, int GT, int ST, bool NT, bool SC, typename Get>
 __device__ __forceinline__ void tile_dense(const TensorDesc &d, const void *grad,
-                                           int64_t base, int n, const StepScalars &s) {
+                                           int64_t base, int n, const Get &get) {
     const int off = threadIdx.x * kVec;
     const int64_t e = base + off;
     float th[kVec], g[kVec], m[kVec], v[kVec];
@@ -367,6 +373,7 @@ __device__ __forceinline__ void tile_dense(const TensorDesc &d, const void *grad
         load4<ST, NT>(d.v, e, v);
         load4_any<GT, NT>(grad, e, g, gv);
         load4_any<PT, NT>(d.param, e, th, pv);
+        const StepScalars s = get();
 #pragma unroll
         for (int j = 0; j < kVec; ++j) adamw_update<SC>(th[j], g[j], m[j], v[j], s);
         store4_any<PT, NT>(d.param, e, th, pv);
@@ -381,6 +388,7 @@ __device__ __forceinline__ void tile_dense(const TensorDesc &d, const void *grad
             g[j] = ok ? load1<GT>(grad, e + j) : 0.0f;
             th[j] = ok ? load1<PT>(d.param, e + j) : 0.0f;
         }
+        const StepScalars s = get();
 #pragma unroll
         for (int j = 0; j < kVec; ++j) adamw_update<SC>(th[j], g[j], m[j], v[j], s);
         // m and v up to the end of their last 64-byte chunk (zeros past the
@@ -460,9 +468,9 @@ __device__ __forceinline__ uint32_t pack_codes_unsigned(const float (&x)[kVec], 
 // One tile = one 8-bit block (block index base/256 of the tensor): decode
 // with the stored scales, update in fp32, reduce the block maxima over the
 // wave, re-encode.  theta uses this step's fp32 moments.
-template <int PT, int GT, bool NT, bool SC>
+template <int PT, int GT, bool NT, bool SC, typename Get>
 __device__ __forceinline__ void tile_q8(const TensorDesc &d, const void *grad,
-                                        int64_t base, int n, const StepScalars &s) {
+                                        int64_t base, int n, const Get &get) {
     const int off = threadIdx.x * kVec;
     const int64_t e = base + off;
     const int64_t blk = base / APEXW_Q8_BLOCK;
@@ -493,6 +501,7 @@ __device__ __forceinline__ void tile_q8(const TensorDesc &d, const void *grad,
             th[j] = ok ? load1<PT>(d.param, e + j) : 0.0f;
         }
     }
+    const StepScalars s = get();
     float am = 0.0f, av = 0.0f;
 #pragma unroll
     for (int j = 0; j < kVec; ++j) adamw_update<SC>(th[j], g[j], m[j], v[j], s);
@@ -562,6 +571,46 @@ __device__ __forceinline__ GroupScalars group_scalars(const apexw_group &G) {
     return S;
 }
 
+// Wave-uniform metadata reads through the constant space (scalar loads),
+// copied out word by word.
+template <typename T>
+__device__ __forceinline__ T load_uniform(const T *tab, int32_t i) {
+    static_assert(sizeof(T) % 8 == 0, "64-bit words");
+    const APEXW_CONST uint64_t *p = cptr<uint64_t>(tab + i);
+    uint64_t w[sizeof(T) / 8];
+#pragma unroll
+    for (int j = 0; j < (int)(sizeof(T) / 8); ++j) w[j] = p[j];
+    T out;
+    __builtin_memcpy(&out, w, sizeof out);
+    return out;
+}
+
+// The step record of a tensor of group gi with a grad, at its advanced step
+// count t: group scalars, bias corrections 1 - beta^t from fp64
+// square-and-multiply rounded once to fp32, the grad scale factors.
+__device__ __forceinline__ StepRecord step_record(const KernelArgs &a, int32_t gi, const void *grad,
+                                                  int32_t t, float inv_scale, float clip_coef) {
+    GroupScalars g;
+    if (a.groups_dev != nullptr)
+        g = group_scalars(load_uniform(a.groups_dev, gi));
+    else
+        g = a.groups[gi];
+    StepRecord r = {};
+    r.grad = grad;
+    r.beta1 = g.beta1;
+    r.one_minus_beta1 = g.one_minus_beta1;
+    r.beta2 = g.beta2;
+    r.one_minus_beta2 = g.one_minus_beta2;
+    r.lr = g.lr;
+    r.decay = g.decay;
+    r.eps = g.eps;
+    r.bc1 = (float)(1.0 - pow_uint(g.beta1_d, (uint32_t)t));
+    r.bc2 = (float)(1.0 - pow_uint(g.beta2_d, (uint32_t)t));
+    r.inv_scale = inv_scale;
+    r.clip_coef = clip_coef;
+    return r;
+}
+
 // Before the update, one lane per tensor: unless found_inf is set (M041
 // section 06, Apex guide 4.3), advance t of each tensor with a grad and write
 // its step record (grad pointer, group scalars, bias corrections from fp64
@@ -587,35 +636,9 @@ __global__ __launch_bounds__(kPrepThreads) void adamw_prepare_kernel(KernelArgs 
     if (grad != nullptr) {
         const int32_t t = t_old + 1;
         a.steps[i] = t;
-        const GroupScalars g = a.groups_dev != nullptr ? group_scalars(a.groups_dev[gi]) : a.groups[gi];
-        r.grad = grad;
-        r.beta1 = g.beta1;
-        r.one_minus_beta1 = g.one_minus_beta1;
-        r.beta2 = g.beta2;
-        r.one_minus_beta2 = g.one_minus_beta2;
-        r.lr = g.lr;
-        r.decay = g.decay;
-        r.eps = g.eps;
-        r.bc1 = (float)(1.0 - pow_uint(g.beta1_d, (uint32_t)t));
-        r.bc2 = (float)(1.0 - pow_uint(g.beta2_d, (uint32_t)t));
-        r.inv_scale = inv_scale;
-        r.clip_coef = clip_coef;
+        r = step_record(a, gi, grad, t, inv_scale, clip_coef);
     }
     a.records[i] = r;
-}
-
-// Wave-uniform metadata reads through the constant space (scalar loads),
-// copied out word by word.
-template <typename T>
-__device__ __forceinline__ T load_uniform(const T *tab, int32_t i) {
-    static_assert(sizeof(T) % 8 == 0, "64-bit words");
-    const APEXW_CONST uint64_t *p = cptr<uint64_t>(tab + i);
-    uint64_t w[sizeof(T) / 8];
-#pragma unroll
-    for (int j = 0; j < (int)(sizeof(T) / 8); ++j) w[j] = p[j];
-    T out;
-    __builtin_memcpy(&out, w, sizeof out);
-    return out;
 }
 
 // Position of tile k of a launch in its tile table.  The table is stored
@@ -650,7 +673,7 @@ __global__ __launch_bounds__(kThreads) void adamw_step_kernel(KernelArgs a) {
         if constexpr (ST == APEXW_STATE_Q8) asm volatile("" ::"s"(d.m_scale), "s"(d.v_scale));
         // no grad (absent, or the step is skipped): tensor untouched
         if (r.grad != nullptr && n > 0) {
-            const StepScalars s = step_scalars(r);
+            const auto s = [&] { return step_scalars(r); };
             if constexpr (ST == APEXW_STATE_F32)
                 tile_dense<PT, GT, APEXW_F32, NT, SC>(d, r.grad, base, n, s);
             else if constexpr (ST == APEXW_STATE_BF16)
@@ -661,6 +684,103 @@ __global__ __launch_bounds__(kThreads) void adamw_step_kernel(KernelArgs a) {
         k += gridDim.x;
         if (k >= a.tile_count) break;
         i = tile_tensor[table_pos(a, k)];
+    }
+}
+
+// Arrival counters of the single-launch step, per launch: kDoneFan
+// first-level counters and one top counter, each alone in a 128-byte line
+// (kDoneStride words apart).  Workgroup b arrives at counter b % kDoneFan;
+// the last to arrive there clears it and arrives at the top counter; the last
+// to arrive at the top has seen every workgroup arrive.  One counter for the
+// whole grid would serialise one atomic per workgroup on one address.
+constexpr int kDoneFan = 64;
+constexpr int kDoneStride = 32;
+constexpr int kDoneWords = (kDoneFan + 1) * kDoneStride;
+
+// An arrival at a counter that expects `expected` arrivals per launch: a
+// device-scope wrapping increment by lane 0 (the counter goes back to 0 on the
+// last arrival, ready for the next launch), returning the count before it
+// (0 in the other lanes).  Only a read-before-write order matters here (every
+// counter read, then the advance); no data written before the increment is
+// read after it in this launch, so no cache write-back is needed.
+__device__ __forceinline__ uint32_t arrive(uint32_t *ctr, uint32_t expected) {
+    uint32_t before = 0;
+    if (threadIdx.x == 0) before = __builtin_amdgcn_atomic_inc32(ctr, expected - 1u, __ATOMIC_RELAXED, "agent");
+    return before;
+}
+
+// True in every lane of the wave whose arrival was the last of `expected`.
+__device__ __forceinline__ bool arrived_last(uint32_t before, uint32_t expected) {
+    return __builtin_amdgcn_readfirstlane(before) == expected - 1u;
+}
+
+// The whole step in one launch per dtype pair, for lists of few tiles (where
+// the prepare launch costs about as much as the work): every workgroup forms
+// its tensor's step record itself from the counter as it stands (t + 1), and
+// the workgroup that arrives last -- after every workgroup has read the
+// counters -- advances the counters of the launch's tensors that had a grad.
+// A workgroup arrives at its first-level counter as soon as it has read its
+// last counter, so that add's latency hides under the tile's loads; the
+// first-level winners arrive at the top after their tiles.  Results are
+// bitwise those of the two-kernel step.
+template <int ST, int PT, int GT, bool SC>
+__global__ __launch_bounds__(kThreads) void adamw_single_step_kernel(KernelArgs a) {
+    const APEXW_CONST int32_t *tile_tensor = cptr<int32_t>(a.tile_tensor);
+    const float fi = *cptr<float>(a.found_inf);
+    const float inv_scale = *cptr<float>(a.inv_scale);
+    const float clip_coef = *cptr<float>(a.clip_coef);
+    const uint32_t grid = gridDim.x, c = blockIdx.x % kDoneFan;
+    const uint32_t first_level = (grid - 1u - c) / kDoneFan + 1u;      // workgroups b % kDoneFan == c
+    uint32_t before = 0;
+    bool checked = false, last1 = false;       // first-level result, once read
+    int64_t k = blockIdx.x;                    // < tile_count: grid <= tiles
+    for (;;) {
+        const int32_t i = tile_tensor[table_pos(a, k)];
+        const TensorDesc d = load_uniform(a.desc, i);
+        const void *grad = reinterpret_cast<const void *>(cptr<uint64_t>(a.grads)[i]);
+        const int32_t t_old = cptr<int32_t>(a.steps)[i];
+        const bool last_tile = k + grid >= a.tile_count;
+        if (last_tile) {
+            // the counter read has returned before the add is issued: the
+            // empty asm reads the loaded value
+            asm volatile("" ::"s"(t_old) : "memory");
+            before = arrive(a.done + c * kDoneStride, first_level);
+        }
+        const int64_t base = (a.tile_begin + k - d.first_tile) * kTile;
+        const int64_t left = d.numel - base;
+        const int n = left < kTile ? (int)left : kTile;
+        if (fi == 0.0f && grad != nullptr && n > 0) {
+            const auto s = [&] {
+                // read the add's result here, once the tile's loads are in
+                // flight (it was issued before them and returns first), not
+                // after the stores, which would wait for them too
+                if (last_tile) {
+                    last1 = arrived_last(before, first_level);
+                    checked = true;
+                }
+                return step_scalars(step_record(a, d.group, grad, t_old + 1, inv_scale, clip_coef));
+            };
+            if constexpr (ST == APEXW_STATE_F32)
+                tile_dense<PT, GT, APEXW_F32, false, SC>(d, grad, base, n, s);
+            else if constexpr (ST == APEXW_STATE_BF16)
+                tile_dense<PT, GT, APEXW_BF16, false, SC>(d, grad, base, n, s);
+            else
+                tile_q8<PT, GT, false, SC>(d, grad, base, n, s);
+        }
+        if (last_tile) break;
+        k += grid;
+    }
+    if (!checked) last1 = arrived_last(before, first_level);
+    if (!last1) return;
+    const uint32_t top = grid < (uint32_t)kDoneFan ? grid : (uint32_t)kDoneFan;
+    if (!arrived_last(arrive(a.done + kDoneFan * kDoneStride, top), top)) return;
+    if (fi != 0.0f) return;                    // a skipped step advances nothing
+    for (int32_t j = threadIdx.x; j < a.tensor_count; j += kThreads) {
+        const int32_t i = a.tensor_list[a.tensor_begin + j];
+        const int32_t t = a.steps[i];
+        const void *grad = a.grads[i];
+        asm volatile("" ::"v"(t), "v"(grad));   // both loads in one round trip
+        if (grad != nullptr) a.steps[i] = t + 1;
     }
 }
 

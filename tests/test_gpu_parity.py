@@ -39,16 +39,20 @@ def _oracle_for(w: W.Workload, idx=None, state_fmt=None):
 
 # =================================================================== tiny
 
-def test_tiny_every_call_against_oracle():
+@pytest.mark.parametrize("mode", [0, 1])
+def test_tiny_every_call_against_oracle(mode):
     """525,315 fp32 params, 20 calls, call 7 skipped, [3] has no grad on odd
-    calls: theta, m, v and t compared after every call."""
+    calls: theta, m, v and t compared after every call; the default launch
+    (one kernel for a list this small) and prepare + update."""
     _need_gpu()
     w = W.tiny()
-    say("case: tiny", w.describe())
+    say("case: tiny", w.describe(), "mode", mode)
     p_cpu = W.init_params(w, "cpu")
     params = [p.to(DEV) for p in p_cpu]
     grads = [torch.empty(s, dtype=torch.float32, device=DEV) for s in w.shapes]
     opt = GpuOpt(w.numels, w.param_dtype, w.grad_dtype, w.group_of, len(w.groups), w.state_fmt)
+    L.apexw_set_launch_mode(opt.h, mode)
+    assert L.apexw_get_launch_mode(opt.h) == (2 if mode == 0 else 1)
     ref = _oracle_for(w)
     th_ref = [bits(p) for p in p_cpu]
     fi = torch.zeros(1, dtype=torch.float32, device=DEV)
@@ -81,15 +85,21 @@ def test_tiny_every_call_against_oracle():
 EDGE_SIZES = [1, 3, 5, 255, 256, 257, 1023, 4095, 4096, 4097, 8191, 12289, 0, 100003]
 
 
-@pytest.mark.parametrize("policy", [0, 1])
+# (cache policy, launch mode): the small list's default (cached, single
+# launch), streaming (prepare + update), cached prepare + update, and the
+# single launch forced under a streaming policy
+MODES = [(0, 0), (1, 0), (0, 1), (1, 2)]
+
+
+@pytest.mark.parametrize("policy,mode", MODES)
 @pytest.mark.parametrize("fmt", [W.STATE_F32, W.STATE_BF16, W.STATE_Q8])
-def test_ragged_mixed_dtypes_groups_and_misalignment(fmt, policy):
+def test_ragged_mixed_dtypes_groups_and_misalignment(fmt, policy, mode):
     """Every (param, grad) dtype pair in one optimizer (one launch each), ragged
-    sizes, an empty tensor, three groups, a parameter and a grad that are not
+    sizes, empty tensors, three groups, a parameter and a grad that are not
     16-byte aligned, grads absent on some calls, one skipped call; cached
-    (the small list's default) and streaming accesses."""
+    and streaming accesses, both launch modes."""
     _need_gpu()
-    say("case: ragged", fmt, "policy", policy)
+    say("case: ragged", fmt, "policy", policy, "mode", mode)
     sizes = EDGE_SIZES * 2
     n = len(sizes)
     pdt = [(W.F32, W.BF16)[(i // 2) % 2] for i in range(n)]
@@ -112,6 +122,7 @@ def test_ragged_mixed_dtypes_groups_and_misalignment(fmt, policy):
             params.append(p.to(DEV))
     opt = GpuOpt(sizes, pdt, gdt, group_of, 3, fmt)
     L.apexw_set_cache_policy(opt.h, policy)
+    L.apexw_set_launch_mode(opt.h, mode)
     ref = oracle.OracleAdamW(sizes, pdt, gdt, group_of, fmt)
     th_ref = [bits(p) for p in p_cpu]
     fi = torch.zeros(1, device=DEV)
@@ -147,12 +158,14 @@ def test_ragged_mixed_dtypes_groups_and_misalignment(fmt, policy):
     opt.close()
 
 
+@pytest.mark.parametrize("mode", [0, 1])
 @pytest.mark.parametrize("fmt", [W.STATE_F32, W.STATE_BF16, W.STATE_Q8])
-def test_found_inf_leaves_everything_bitwise(fmt):
+def test_found_inf_leaves_everything_bitwise(fmt, mode):
     _need_gpu()
-    say("case: found_inf", fmt)
+    say("case: found_inf", fmt, "mode", mode)
     sizes = [5000, 4096, 77]
     opt = GpuOpt(sizes, [W.BF16, W.F32, W.F32], [W.F32, W.BF16, W.F32], [0, 0, 0], 1, fmt)
+    L.apexw_set_launch_mode(opt.h, mode)
     params = [torch.randn(sizes[0], device=DEV).to(torch.bfloat16), torch.randn(sizes[1], device=DEV),
               torch.randn(sizes[2], device=DEV)]
     grads = [torch.randn(sizes[0], device=DEV) * 1e-3,
@@ -461,16 +474,22 @@ def test_all_grads_absent_and_pointer_changes():
 
 
 @pytest.mark.parametrize("fmt", [W.STATE_F32, W.STATE_BF16, W.STATE_Q8])
-@pytest.mark.parametrize("wg", [1, 7, 300, 0])
-def test_results_do_not_depend_on_grid(wg, fmt):
+@pytest.mark.parametrize("wg,mode", [(1, 2), (7, 2), (63, 2), (64, 2), (65, 2), (300, 2), (0, 2),
+                                     (1, 1), (300, 1)])
+def test_results_do_not_depend_on_grid(wg, mode, fmt):
+    """Workgroup caps (a workgroup then walks several tiles) in both launch
+    modes -- for the single launch, caps below, at and above the 64 counters
+    of the arrival tree's first level -- against prepare + update at the
+    default grid, over three calls (the arrival counters must reset)."""
     _need_gpu()
-    say("case: grid", wg, "fmt", fmt)
-    w = dataclasses.replace(W.many_small(n_tensors=300), state_fmt=fmt)
+    say("case: grid", wg, "mode", mode, "fmt", fmt)
+    w = dataclasses.replace(W.many_small(n_tensors=120), state_fmt=fmt)   # 5,847 tiles
     outs = []
-    for setting in (wg, 0):
+    for setting, md in ((wg, mode), (0, 1)):
         params = W.init_params(w, DEV)
         opt = GpuOpt(w.numels, w.param_dtype, w.grad_dtype, w.group_of, 3, w.state_fmt)
         L.apexw_set_workgroups(opt.h, setting)
+        L.apexw_set_launch_mode(opt.h, md)
         for k in range(1, 4):
             opt.step(w.groups, params, W.grads_for_call(w, k, DEV))
         torch.cuda.synchronize()

@@ -137,6 +137,19 @@ def test_null_handle_rejected():
     with pytest.raises(L.ApexwError) as e:
         L.apexw_read_steps(0, 3)
     assert e.value.code == L.APEXW_EINVAL
+    with pytest.raises(L.ApexwError) as e:
+        L.apexw_set_launch_mode(0, 1)
+    assert e.value.code == L.APEXW_EINVAL
+
+
+def test_single_launch_room_only_for_small_lists():
+    """The single-launch step's counters and tensor list take workspace only
+    for lists of at most 6144 tiles."""
+    small = L.apexw_workspace_bytes([256 * 6144])
+    big = L.apexw_workspace_bytes([256 * 6144 + 1])
+    # one more tile adds 4 B of table and 8 B of partials (256-byte rounding),
+    # so the larger list's smaller workspace shows the dropped regions
+    assert big < small
 
 
 def test_error_codes_are_distinct_and_negative():
