@@ -109,7 +109,8 @@ struct StepRecord {
     float bc1, bc2;                  // 1 - beta1^t, 1 - beta2^t
     float inv_scale;                 // grads are unscaled by this first
     float clip_coef;                 // then multiplied by this (norm clipping)
-    float pad_[3];
+    float rbc1, rbc2;                // 1/bc1, 1/bc2 correctly rounded
+    float div_lo;                    // 2^-100 if bc1, bc2 >= 2^-60, else +inf (see div_uniform)
 };
 static_assert(sizeof(StepRecord) == 64, "step record is one 64-byte record");
 
@@ -148,6 +149,8 @@ struct StepScalars {
     float beta1, one_minus_beta1, beta2, one_minus_beta2;
     float lr, decay, eps;
     float bc1, bc2;                  // 1 - beta1^t, 1 - beta2^t (fp32)
+    float rbc1, rbc2;                // 1/bc1, 1/bc2 correctly rounded
+    float div_lo;                    // 2^-100 if bc1, bc2 >= 2^-60, else +inf
     float inv_scale;                 // 1 unless grads arrive scaled
     float clip_coef;                 // 1 unless the grad norm is clipped
 };
@@ -174,6 +177,9 @@ __device__ __forceinline__ StepScalars step_scalars(const StepRecord &r) {
     s.eps = r.eps;
     s.bc1 = r.bc1;
     s.bc2 = r.bc2;
+    s.rbc1 = r.rbc1;
+    s.rbc2 = r.rbc2;
+    s.div_lo = r.div_lo;
     s.inv_scale = r.inv_scale;
     s.clip_coef = r.clip_coef;
     return s;
@@ -204,6 +210,28 @@ __device__ __forceinline__ float sqrt_rn(float x) {
     return r;
 }
 
+// x / b correctly rounded, for a wave-uniform divisor b in [2^-60, 1] with
+// y = 1/b correctly rounded (lo = 2^-100): q = x*y, then one correction with
+// the exact residual r = fma(-q, b, x), q + r*y rounded once -- Markstein's
+// correction step.  Its result equals the correctly rounded quotient for
+// every pair of fp32 significands (all 2^46 pairs of x and b in [1, 2) were
+// checked against the hardware's correctly rounded division), and scaling x
+// and b by powers of two scales every step exactly as long as nothing leaves
+// the normal range: for 2^-100 <= |x| < 2^64 the residual's lowest bit stays
+// >= 2^-147 and x*y < 2^124.  Other x (zero -- whose sign the short form
+// loses --, subnormals, inf, NaN, huge) take the division, and so does every
+// x when b is outside that range (lo = +inf then).
+__device__ __forceinline__ float div_uniform(float x, float b, float y, float lo) {
+    float q = x * y;
+    const float r = fmaf(-q, b, x);
+    q = fmaf(r, y, q);
+    if (!(fabsf(x) >= lo && fabsf(x) < 0x1p64f)) {   // rare: skipped by the wave
+        asm volatile("");                                                // not speculated
+        q = x / b;
+    }
+    return q;
+}
+
 // The AdamW update of one element (M041 section 02), fp32, each operation
 // rounded, evaluated left to right as printed, on the unscaled and clipped
 // grad (the mixed-precision recipe of M041 section 06: unscale, check,
@@ -216,8 +244,8 @@ __device__ __forceinline__ void adamw_update(float &theta, float g_scaled, float
     const float g = SC ? (g_scaled * s.inv_scale) * s.clip_coef : g_scaled;
     m = s.beta1 * m + s.one_minus_beta1 * g;
     v = s.beta2 * v + (s.one_minus_beta2 * g) * g;
-    const float m_hat = m / s.bc1;
-    const float v_hat = v / s.bc2;
+    const float m_hat = div_uniform(m, s.bc1, s.rbc1, s.div_lo);
+    const float v_hat = div_uniform(v, s.bc2, s.rbc2, s.div_lo);
     const float denom = sqrt_rn(v_hat) + s.eps;
     theta = theta * s.decay - (s.lr * m_hat) / denom;
 }
@@ -606,6 +634,9 @@ __device__ __forceinline__ StepRecord step_record(const KernelArgs &a, int32_t g
     r.eps = g.eps;
     r.bc1 = (float)(1.0 - pow_uint(g.beta1_d, (uint32_t)t));
     r.bc2 = (float)(1.0 - pow_uint(g.beta2_d, (uint32_t)t));
+    r.rbc1 = 1.0f / r.bc1;
+    r.rbc2 = 1.0f / r.bc2;
+    r.div_lo = r.bc1 >= 0x1p-60f && r.bc2 >= 0x1p-60f ? 0x1p-100f : __builtin_inff();   // both are <= 1
     r.inv_scale = inv_scale;
     r.clip_coef = clip_coef;
     return r;

@@ -1,10 +1,14 @@
-"""CPU checks of the two rounding shortcuts the update kernel takes instead
-of a correctly rounded division or square root per element (code_value and
-sqrt_rn in csrc/apexw_kernels.hpp), written out with numpy's IEEE fp32
-arithmetic and checked against the definitions.  The hardware approximations
-they start from (v_rcp_f32, v_sqrt_f32: within one ulp) are modelled by
-trying the correctly rounded value and both of its neighbours.  (The GPU
-parity tests check the kernel itself bit for bit against the oracle.)"""
+"""CPU checks of the rounding shortcuts the update kernel takes instead of a
+correctly rounded division or square root per element (code_value, sqrt_rn
+and div_uniform in csrc/apexw_kernels.hpp), written out with IEEE fp32
+arithmetic (numpy, or C with libm's fmaf for the fused multiply-adds) and
+checked against the definitions.  The hardware approximations two of them
+start from (v_rcp_f32, v_sqrt_f32: within one ulp) are modelled by trying
+the correctly rounded value and both of its neighbours.  (The GPU parity
+tests check the kernel itself bit for bit against the oracle.)"""
+import os
+import subprocess
+
 import numpy as np
 
 F32 = np.float32
@@ -125,3 +129,23 @@ def test_sqrt_selection_over_the_range_it_is_used_on():
     for v in (F32(0.0), F32(np.inf)):
         s0 = np.array([v], F32)
         assert sqrt_rule(np.array([v], F32), s0)[0] == v
+
+
+def test_uniform_divisor_rule_against_ieee_division(tmp_path):
+    """m/bc1 and v/bc2: y = 1/b correctly rounded, q = x*y, one correction
+    with the exact residual; in range (2^-100 <= |x| < 2^64, b in
+    [2^-60, 1]) it equals IEEE division on every significand of x in a
+    binade (both signs) and on samples at the range ends, for bias
+    corrections of common betas and random divisors; outside the range the
+    short form differs for some x (zero's sign, subnormals, inf), which is
+    why the kernel tests the range."""
+    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "rules", "div_rule.c")
+    exe = str(tmp_path / "div_rule")
+    subprocess.run(["gcc", "-std=c99", "-O2", "-ffp-contract=off", "-Wall", "-o", exe, src, "-lm"],
+                   check=True)
+    out = subprocess.run([exe], stdout=subprocess.PIPE, text=True, timeout=300, check=True).stdout
+    lines = dict(line.split(" ", 1) for line in out.strip().splitlines())
+    checked, _, mismatches = lines["checked"].split()
+    assert int(checked) > 4e8 and int(mismatches) == 0, out
+    outside, _, differ = lines["outside"].split()
+    assert int(differ) > 0, out
