@@ -221,10 +221,14 @@ __device__ __forceinline__ float sqrt_rn(float x) {
 // >= 2^-147 and x*y < 2^124.  Other x (zero -- whose sign the short form
 // loses --, subnormals, inf, NaN, huge) take the division, and so does every
 // x when b is outside that range (lo = +inf then).
-__device__ __forceinline__ float div_uniform(float x, float b, float y, float lo) {
-    float q = x * y;
+__device__ __forceinline__ float div_short(float x, float b, float y) {
+    const float q = x * y;
     const float r = fmaf(-q, b, x);
-    q = fmaf(r, y, q);
+    return fmaf(r, y, q);
+}
+
+__device__ __forceinline__ float div_uniform(float x, float b, float y, float lo) {
+    float q = div_short(x, b, y);
     if (!(fabsf(x) >= lo && fabsf(x) < 0x1p64f)) {   // rare: skipped by the wave
         asm volatile("");                                                // not speculated
         q = x / b;
@@ -448,8 +452,18 @@ __device__ __forceinline__ void tile_dense(const TensorDesc &d, const void *grad
 // so both stay within 3e-5 of x/s and inside the code range.  When r is more
 // than 2.5e-4 away from every half-integer, r and RN(x/s) therefore round to
 // the same integer; otherwise (rare, or a NaN), or when s is zero, denormal
-// or infinite, the quotient itself is rounded and clamped.  r - rint(r) is
-// exact (Sterbenz), so the distance test is exact too.
+// or infinite, the quotient itself is rounded and clamped.  d = |r - rint(r)|
+// is exact (Sterbenz) and at most 1/2, so "|d - 1/2| > 2.5e-4" is exactly
+// "d < kTieBound", the float just above 1/2 - 2.5e-4: one comparison.
+//
+// The block scale amax/levels is the correctly rounded quotient, formed by
+// div_short with 1/levels (a compile-time constant) for amax in
+// [2^-100, FLT_MAX] -- the significand pairs of 127 and 255 are among those
+// checked, and no step leaves the normal range there -- else by the
+// division (zero, subnormal or infinite amax; wave-uniform, so no
+// divergence).
+constexpr float kTieBound = 0x1.ffbe78p-2f;   // RU(1/2 - 2.5e-4f) = 0.49975002
+
 struct BlockScale {
     float s, inv;
     bool fast;      // s normal and finite: inv is usable
@@ -457,7 +471,11 @@ struct BlockScale {
 
 __device__ __forceinline__ BlockScale block_scale(float amax, float levels) {
     BlockScale b;
-    b.s = amax / levels;
+    b.s = div_short(amax, levels, 1.0f / levels);
+    if (!(amax >= 0x1p-100f && amax <= 0x1.fffffep127f)) {   // uniform; rare
+        asm volatile("");
+        b.s = amax / levels;
+    }
     b.fast = b.s >= 0x1p-126f && b.s <= 0x1p126f;
     b.inv = __builtin_amdgcn_rcpf(b.s);
     return b;
@@ -467,7 +485,7 @@ __device__ __forceinline__ BlockScale block_scale(float amax, float levels) {
 __device__ __forceinline__ float code_value(float x, const BlockScale &b, float lo, float hi) {
     const float r = x * b.inv;
     float q = rintf(r);
-    if (!b.fast || !(fabsf(fabsf(r - q) - 0.5f) > 2.5e-4f)) {   // rare: skipped by the wave
+    if (!b.fast || !(fabsf(r - q) < kTieBound)) {   // rare: skipped by the wave
         asm volatile("");                                          // not speculated
         q = b.s == 0.0f ? 0.0f : fminf(fmaxf(rintf(x / b.s), lo), hi);
     }

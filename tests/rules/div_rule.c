@@ -2,8 +2,10 @@
  * (wave-uniform divisors b in [2^-60, 1]) without a full division per
  * element: with y = 1/b correctly rounded, q = RN(x*y), r = fma(-q, b, x)
  * (exact), the quotient is RN(q + r*y) = fma(r, y, q), taken when
- * 2^-100 <= |x| < 2^64; other x take the division.  This program checks the
- * rule against IEEE division on the host (gcc, no contraction, libm fmaf).
+ * 2^-100 <= |x| < 2^64; other x take the division.  The 8-bit block scales
+ * amax/127 and amax/255 use the same form for amax in [2^-100, FLT_MAX].
+ * This program checks the rule against IEEE division on the host (gcc, no
+ * contraction, libm fmaf).
  *
  * Output, one line each:
  *   checked <n> mismatches <k>          (in-range x: must be 0)
@@ -65,6 +67,27 @@ int main(void) {
                 bad += u_of(short_div(x, b, y)) != u_of(x / b);
                 ++checked;
             }
+    }
+    /* the 8-bit block scales amax/127 and amax/255: constant divisors, x in
+     * [2^-100, FLT_MAX] (every significand at exponent 0, samples at all
+     * exponents up to the largest) */
+    const float cs[2] = {127.0f, 255.0f};
+    for (int ic = 0; ic < 2; ++ic) {
+        const float b = cs[ic], y = 1.0f / b;
+        for (uint32_t m = 0; m < (1u << 23); ++m) {
+            const float x = f_of(0x3f800000u | m);
+            bad += u_of(short_div(x, b, y)) != u_of(x / b);
+            ++checked;
+        }
+        for (int e = -100; e <= 127; ++e)
+            for (int k = 0; k < 2048; ++k) {
+                const float x = ldexpf(f_of(0x3f800000u | (rnd32() & 0x7fffffu)), e);
+                bad += u_of(short_div(x, b, y)) != u_of(x / b);
+                ++checked;
+            }
+        const float top = 0x1.fffffep127f;
+        bad += u_of(short_div(top, b, y)) != u_of(top / b);
+        ++checked;
     }
     printf("checked %ld mismatches %ld\n", checked, bad);
     /* outside the range: zeros, subnormals and tiny values, inf, NaN, huge */

@@ -14,6 +14,19 @@ import numpy as np
 F32 = np.float32
 
 
+# the float just above 1/2 - 2.5e-4f (kTieBound in the kernel)
+TIE_BOUND = np.array([0x3EFFDF3C], np.uint32).view(F32)[0]
+
+
+def test_tie_bound_is_the_distance_test():
+    """|d - 1/2| > 2.5e-4f (d = |r - rint(r)| in [0, 1/2], computed in fp32)
+    holds exactly when d < TIE_BOUND, for every float d in [0, 1/2]."""
+    d = np.arange(0, 0x3F000001, 61, dtype=np.uint32).view(F32)      # [0, 1/2], every 61st
+    d = np.concatenate([d, np.array([0x3EFFDF3B, 0x3EFFDF3C, 0x3EFFDF3D, 0x3F000000],
+                                    np.uint32).view(F32)])
+    assert np.array_equal(np.abs(d - F32(0.5)) > F32(2.5e-4), d < TIE_BOUND)
+
+
 def _neighbours(a):
     return (np.nextafter(a, F32(-np.inf)), a, np.nextafter(a, F32(np.inf)))
 
@@ -22,13 +35,14 @@ def _neighbours(a):
 
 def code_rule(x, s, inv, lo, hi):
     """The kernel's rule: r = x*inv rounded to even, unless the block scale
-    is not a normal number or r is within 2.5e-4 of a half-integer (or NaN);
-    then the correctly rounded quotient, rounded and clamped."""
+    is not a normal number or r is within 2.5e-4 of a half-integer (or NaN),
+    tested as |r - rint(r)| < TIE_BOUND; then the correctly rounded
+    quotient, rounded and clamped."""
     with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
         fast = (s >= F32(2.0 ** -126)) & (s <= F32(2.0 ** 126))
         r = x * inv
         q = np.rint(r)
-        exact = ~fast | ~(np.abs(np.abs(r - q) - F32(0.5)) > F32(2.5e-4))
+        exact = ~fast | ~(np.abs(r - q) < TIE_BOUND)
         slow = np.where(s == 0, F32(0), np.clip(np.rint(x / s), lo, hi))
         return np.where(exact, slow, q), exact
 
