@@ -177,6 +177,8 @@ int apexw_create(int32_t n_tensors, const int64_t *numel,
  *                 written; NULL means never skip
  * Never synchronises with the host.  The pointer tables are re-uploaded (one
  * asynchronous copy) only when params or grads differ from the previous call.
+ * Launches: a prepare kernel and one update kernel per (param, grad) dtype
+ * pair present, or for small lists one kernel per pair (apexw_set_launch_mode).
  * All calls on one handle must be ordered on the GPU (one stream, or streams
  * the caller orders).  Non-finite grads with found_inf unset are not checked
  * and propagate into theta, m and v.

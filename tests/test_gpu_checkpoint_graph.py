@@ -121,17 +121,22 @@ def test_device_groups_equal_host_groups(fmt):
     b.close()
 
 
+@pytest.mark.parametrize("mode", [0, 1])
 @pytest.mark.parametrize("fmt", [W.STATE_F32, W.STATE_BF16, W.STATE_Q8])
-def test_graph_capture_replays_match_oracle(fmt):
+def test_graph_capture_replays_match_oracle(fmt, mode):
     """Capture [zero found_inf, unscale check, step with device hyperparameters]
     once; replay it 6 times with new grads, a new learning rate and (once) an
     overflow written in place between replays, with eager work and
-    synchronisations in between; every replay is checked against the oracle."""
-    say("case: graph capture", fmt)
+    synchronisations in between; every replay is checked against the oracle.
+    Both launch modes (the single launch's arrival counters must come back
+    to zero in every replay)."""
+    say("case: graph capture", fmt, "mode", mode)
     p_cpu, gs = _inputs(34, 7)
     params = [p.to(DEV) for p in p_cpu]
     grads = [g.to(DEV) for g in gs[0]]
     opt = GpuOpt(SIZES, PDT, GDT, GROUP_OF, 2, fmt)
+    L.apexw_set_launch_mode(opt.h, mode)
+    assert L.apexw_get_launch_mode(opt.h) == (2 if mode == 0 else 1)
     ref = oracle.OracleAdamW(SIZES, PDT, GDT, GROUP_OF, fmt)
     th_ref = [bits(p) for p in p_cpu]
     fi = torch.zeros(1, device=DEV)
