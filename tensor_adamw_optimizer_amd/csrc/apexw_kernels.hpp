@@ -387,10 +387,9 @@ __device__ __forceinline__ float wave_max_nonneg(float x) {
 
 // One 256-element tile of a tensor with fp32 or bf16 moments (ST = element
 // type of m and v).  n = valid elements in this tile (1..256).  A full tile
-// takes the vector path.  In a tensor's last, partial tile every lane loads
-// its valid elements one by one (zeros elsewhere), runs the update on all 4
-// values together -- one converged pass instead of one per element -- and
-// stores only the valid ones.
+// takes the vector path.  In a tensor's last, partial tile the update runs
+// on all 4 values of every lane together (one converged pass), and only the
+// valid elements of theta are stored.
 // get() yields the step's scalars; it is called after the tile's loads are
 // issued, so any memory reads or arithmetic it needs overlap with them.
 template <int PT, int GT, int ST, bool NT, bool SC, typename Get>
@@ -412,31 +411,48 @@ __device__ __forceinline__ void tile_dense(const TensorDesc &d, const void *grad
         store4<ST, NT>(d.m, e, m);
         store4<ST, NT>(d.v, e, v);
     } else {
+        // m and v are read and written as whole vectors up to the end of
+        // their last 64-byte chunk (the state arrays are padded for it, and
+        // the padding is always written as +0); theta and g as vectors in
+        // the lanes wholly inside the tensor, element by element in the one
+        // lane that straddles its end
+        constexpr int kChunk = ST == APEXW_F32 ? 16 : 32;
+        const int n_pad = (n + kChunk - 1) / kChunk * kChunk;
+        const bool pv = vec_aligned<PT>(d.param), gv = vec_aligned<GT>(grad);
+        const bool inside = off + kVec <= n, padded = off < n_pad;
 #pragma unroll
-        for (int j = 0; j < kVec; ++j) {
-            const bool ok = off + j < n;
-            m[j] = ok ? load1<ST>(d.m, e + j) : 0.0f;
-            v[j] = ok ? load1<ST>(d.v, e + j) : 0.0f;
-            g[j] = ok ? load1<GT>(grad, e + j) : 0.0f;
-            th[j] = ok ? load1<PT>(d.param, e + j) : 0.0f;
+        for (int j = 0; j < kVec; ++j) m[j] = v[j] = 0.0f;
+        if (padded) {
+            load4<ST, NT>(d.m, e, m);
+            load4<ST, NT>(d.v, e, v);
+        }
+        if (inside) {
+            load4_any<GT, NT>(grad, e, g, gv);
+            load4_any<PT, NT>(d.param, e, th, pv);
+        } else {
+#pragma unroll
+            for (int j = 0; j < kVec; ++j) {
+                const bool ok = off + j < n;
+                g[j] = ok ? load1<GT>(grad, e + j) : 0.0f;
+                th[j] = ok ? load1<PT>(d.param, e + j) : 0.0f;
+            }
         }
         const StepScalars s = get();
 #pragma unroll
-        for (int j = 0; j < kVec; ++j) adamw_update<SC>(th[j], g[j], m[j], v[j], s);
-        // m and v up to the end of their last 64-byte chunk (zeros past the
-        // tensor: the state arrays are padded for it), theta to its end
-        constexpr int kChunk = ST == APEXW_F32 ? 16 : 32;
-        const int n_pad = (n + kChunk - 1) / kChunk * kChunk;
-#pragma unroll
         for (int j = 0; j < kVec; ++j) {
-            if (off + j < n) {
-                store1<PT>(d.param, e + j, th[j]);
-                store1<ST>(d.m, e + j, m[j]);
-                store1<ST>(d.v, e + j, v[j]);
-            } else if (off + j < n_pad) {
-                store1<ST>(d.m, e + j, 0.0f);
-                store1<ST>(d.v, e + j, 0.0f);
-            }
+            adamw_update<SC>(th[j], g[j], m[j], v[j], s);
+            if (off + j >= n) m[j] = v[j] = 0.0f;      // padding: +0
+        }
+        if (padded) {
+            store4<ST, NT>(d.m, e, m);
+            store4<ST, NT>(d.v, e, v);
+        }
+        if (inside) {
+            store4_any<PT, NT>(d.param, e, th, pv);
+        } else {
+#pragma unroll
+            for (int j = 0; j < kVec; ++j)
+                if (off + j < n) store1<PT>(d.param, e + j, th[j]);
         }
     }
 }
