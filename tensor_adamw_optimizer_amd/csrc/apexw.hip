@@ -151,8 +151,9 @@ WsLayout ws_layout(int32_t n, const int64_t *numel) {
     // each launch's table is padded to a multiple of kXcds entries; the read
     // passes load table entries in fours and may read up to 3 past the end
     w.partials = w.tiles + round_up((w.n_tiles + kMaxLaunches * kXcds + 4) * 4, kTableAlign);
-    // grad-norm partials: one per tile-table entry (stored at the tile's
-    // table position; padding entries stay 0)
+    // grad-norm partials: one per read group of every launch, the launches
+    // one after another (a launch of t tiles has 8 * ceil(ceil(t/8)/4) <= t + 8
+    // groups); entries of groups past a launch's end stay 0
     w.partials2 = w.partials + round_up((w.n_tiles + kMaxLaunches * kXcds) * 8, kTableAlign);
     w.consts = w.partials2 + round_up(kReduceBlocks * 8, kTableAlign);
     w.done = w.consts + round_up((int64_t)sizeof(kConsts), kTableAlign);
@@ -783,10 +784,15 @@ int apexw_clip_grad_norm(apexw_t h, const void *const *grads, const float *inv_s
     a.norm_out = norm_out_dev;
     a.clip_out = clip_coef_dev;
     a.max_norm = max_norm;
-    a.n_tiles_total = h->table_entries;   // partials live at table positions
+    int64_t n_partials = 0;                // one per read group, launch after launch
+    for (const Launch &L : h->launches) n_partials += read_groups(L.table_stride);
+    a.n_partials = n_partials;
     const bool streaming = streams(h);
-    // every tile writes its partial (0 without a grad), so no launch is skipped
+    // every group writes its partial (0 without a grad), so no launch is skipped
+    int64_t group_begin = 0;
     for (const Launch &L : h->launches) {
+        a.group_begin = group_begin;
+        group_begin += read_groups(L.table_stride);
         if (L.tile_count == 0) continue;
         a.tile_begin = L.tile_begin;
         a.tile_count = L.tile_count;

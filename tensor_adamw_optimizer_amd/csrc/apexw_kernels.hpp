@@ -125,12 +125,13 @@ struct KernelArgs {
     float *found_inf_out;            // unscale check: set to 1 on a non-finite
     const apexw_group *groups_dev;   // non-null: hyperparameters read on the device
     const float *clip_coef;          // nullptr: 1 (no clipping)
-    double *partials;                // grad-norm pass: fp64 sum of squares per tile
+    double *partials;                // grad-norm pass: fp64 sum of squares per read group
     double *partials2;               // grad-norm finalize: one per first-stage workgroup
     double *norm_out;                // grad-norm finalize: the norm (may be null)
     float *clip_out;                 // grad-norm finalize: the clip coefficient
     double max_norm;
-    int64_t n_tiles_total;           // tile-table entries over all launches (grad norm)
+    int64_t n_partials;              // grad norm: read groups over all launches
+    int64_t group_begin;             // grad norm: this launch's first partial
     int64_t tile_begin;              // this launch's tiles: [begin, begin+count)
     int64_t tile_count;
     int64_t table_begin;             // this launch's part of tile_tensor
@@ -338,13 +339,30 @@ __device__ __forceinline__ bool vec_aligned(const void *p) {
     return ((uintptr_t)p & (DT == APEXW_F32 ? 15u : 7u)) == 0u;
 }
 
+// bf16 data is fetched as raw words in either branch and widened after the
+// branches join: widening inside a branch makes the compiler wait there for
+// the load, and for every load issued before it, ahead of the next load.
 template <int DT, bool NT>
 __device__ __forceinline__ void load4_any(const void *base, int64_t e, float (&x)[kVec], bool vec) {
-    if (vec) {
-        load4<DT, NT>(base, e, x);
-    } else {
+    if constexpr (DT == APEXW_F32) {
+        if (vec) {
+            load4<DT, NT>(base, e, x);
+        } else {
 #pragma unroll
-        for (int j = 0; j < kVec; ++j) x[j] = load1<DT>(base, e + j);
+            for (int j = 0; j < kVec; ++j) x[j] = load1<DT>(base, e + j);
+        }
+    } else {
+        u32x2 w;
+        if (vec) {
+            const APEXW_GLOBAL u32x2 *p = gptr<u32x2>(static_cast<const uint16_t *>(base) + e);
+            w = NT ? __builtin_nontemporal_load(p) : *p;
+        } else {
+            const APEXW_GLOBAL uint16_t *h = gptr<uint16_t>(base) + e;
+            w.x = (uint32_t)h[0] | (uint32_t)h[1] << 16;
+            w.y = (uint32_t)h[2] | (uint32_t)h[3] << 16;
+        }
+        x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x);
+        x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
     }
 }
 
@@ -921,6 +939,29 @@ __device__ __forceinline__ void load_tile_grads(const ReadTile &t, float (&g)[kV
     }
 }
 
+// The grads of a read group.  When all four tiles are full, present and
+// vector-aligned (the common case; a wave-uniform test) their four vector
+// loads are issued back to back in straight-line code; the general path
+// chooses per lane between vector and element loads, and there the compiler
+// waits for every load in flight before each tile's loads, which would
+// serialise the tiles of the group.
+template <int GT, bool NT>
+__device__ __forceinline__ void load_group_grads(const ReadTile (&t)[kReadBatch],
+                                                 float (&g)[kReadBatch][kVec]) {
+    bool full = true;
+#pragma unroll
+    for (int u = 0; u < kReadBatch; ++u)
+        full = full && t[u].grad != nullptr && t[u].n == kTile && vec_aligned<GT>(t[u].grad);
+    if (full) {
+#pragma unroll
+        for (int u = 0; u < kReadBatch; ++u)
+            load4<GT, NT>(t[u].grad, t[u].base + threadIdx.x * kVec, g[u]);
+    } else {
+#pragma unroll
+        for (int u = 0; u < kReadBatch; ++u) load_tile_grads<GT, NT>(t[u], g[u]);
+    }
+}
+
 template <int GT, bool NT>
 __global__ __launch_bounds__(kThreads) void unscale_check_kernel(KernelArgs a) {
     const float inv = a.inv_scale != nullptr ? *a.inv_scale : 1.0f;
@@ -931,8 +972,7 @@ __global__ __launch_bounds__(kThreads) void unscale_check_kernel(KernelArgs a) {
         ReadTile t[kReadBatch];
         float g[kReadBatch][kVec];
         if (!read_group(a, jg, t)) continue;
-#pragma unroll
-        for (int u = 0; u < kReadBatch; ++u) load_tile_grads<GT, NT>(t[u], g[u]);
+        load_group_grads<GT, NT>(t, g);
 #pragma unroll
         for (int u = 0; u < kReadBatch; ++u)
 #pragma unroll
@@ -953,10 +993,11 @@ __global__ __launch_bounds__(kThreads) void unscale_check_kernel(KernelArgs a) {
 //  1. grad_norm_partials_kernel: the squares of each read group (four tiles
 //     fixed by the tile table alone, not by the grid) are summed by one wave
 //     -- per lane over the group's tiles in order, then wave_sum's fixed
-//     order -- into partials[p], p the table position of the group's first
-//     tile; every other entry stays 0 (set at create, never written), which
-//     adds nothing; tiles without a grad contribute 0; optionally sets
-//     found_inf_out like the unscale check;
+//     order -- into partials[group_begin + j] for group j of the launch (the
+//     launches' groups one after another, so consecutive groups fill whole
+//     64-byte lines; a group that starts past its launch's end leaves its
+//     entry 0, as set at create); tiles without a grad contribute 0;
+//     optionally sets found_inf_out like the unscale check;
 //  2. grad_norm_reduce_kernel: workgroup b sums partials[b*C .. (b+1)*C) with
 //     a strided loop and a tree in LDS into partials2[b];
 //  3. grad_norm_final_kernel: one workgroup sums partials2 the same way and
@@ -999,8 +1040,7 @@ __global__ __launch_bounds__(kThreads) void grad_norm_partials_kernel(KernelArgs
         ReadTile t[kReadBatch];
         float g[kReadBatch][kVec];
         if (!read_group(a, jg, t)) continue;
-#pragma unroll
-        for (int u = 0; u < kReadBatch; ++u) load_tile_grads<GT, NT>(t[u], g[u]);
+        load_group_grads<GT, NT>(t, g);
         double sq = 0.0;                  // the group's tiles in order, each lane's 4 values
 #pragma unroll
         for (int u = 0; u < kReadBatch; ++u) {
@@ -1014,7 +1054,7 @@ __global__ __launch_bounds__(kThreads) void grad_norm_partials_kernel(KernelArgs
             }
         }
         sq = wave_sum(sq);
-        if (threadIdx.x == 0) gptr<double>(static_cast<void *>(a.partials))[t[0].pos] = sq;
+        if (threadIdx.x == 0) gptr<double>(static_cast<void *>(a.partials))[a.group_begin + jg] = sq;
     }
     if (a.found_inf_out != nullptr && wave_any(bad) && threadIdx.x == 0)
         *gptr<float>(static_cast<void *>(a.found_inf_out)) = 1.0f;
@@ -1040,9 +1080,9 @@ __device__ __forceinline__ double block_sum(const double *src, int64_t lo, int64
 }
 
 __global__ __launch_bounds__(kReduceThreads) void grad_norm_reduce_kernel(KernelArgs a) {
-    const int64_t chunk = (a.n_tiles_total + kReduceBlocks - 1) / kReduceBlocks;
+    const int64_t chunk = (a.n_partials + kReduceBlocks - 1) / kReduceBlocks;
     const int64_t lo = (int64_t)blockIdx.x * chunk;
-    const int64_t hi = lo + chunk < a.n_tiles_total ? lo + chunk : a.n_tiles_total;
+    const int64_t hi = lo + chunk < a.n_partials ? lo + chunk : a.n_partials;
     const double sum = block_sum(a.partials, lo, hi > lo ? hi : lo);
     if (threadIdx.x == 0) gptr<double>(static_cast<void *>(a.partials2))[blockIdx.x] = sum;
 }
