@@ -337,7 +337,7 @@ int apexw_set_workgroups(apexw_t h, int32_t workgroups);
  * Cap how many update workgroups may be resident on one compute unit at a
  * time, for every update launch (enforced through the dynamic LDS each
  * workgroup reserves; the kernel uses none).  0 restores the defaults, which
- * depend on the bytes each element moves (fp32 params and moments, 28 B: 12;
+ * depend on the bytes each element moves (fp32 params and moments, 28 B: 14;
  * bf16 params, fp32 grads and moments, 24 B: 16; bf16 or 8-bit moments: no
  * cap).  Fewer concurrent streams can keep the HBM read/write mix more
  * efficient; results do not depend on it.

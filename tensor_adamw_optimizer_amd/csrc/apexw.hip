@@ -175,7 +175,7 @@ struct Launch {
 // Default cap on update workgroups resident per compute unit for one launch
 // (0: no cap), from the bytes each element moves.  Measured on MI355X: the
 // heavier the per-tile traffic, the fewer one-wave streams per CU keep the
-// HBM read/write mix most efficient (28 B/elem: 12, 24 B/elem: 16); the lean
+// HBM read/write mix most efficient (28 B/elem: 14, 24 B/elem: 16); the lean
 // bf16 and 8-bit formats want every stream they can get.
 
 int element_bytes(int32_t fmt, int pt, int gt) {
@@ -185,7 +185,6 @@ int element_bytes(int32_t fmt, int pt, int gt) {
 
 int default_occupancy(int32_t fmt, int pt, int gt) {
     const int b = element_bytes(fmt, pt, gt);
-    if (b >= 27) return 12;
     if (b >= 25) return 14;
     if (b >= 23) return 16;
     if (b >= 21) return 20;
