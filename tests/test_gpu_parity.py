@@ -405,7 +405,8 @@ def test_null_arrays_reuse_the_previous_call_and_read_steps():
 def test_thirty_two_groups_with_edge_hyperparameters_against_oracle():
     """The maximum of 32 parameter groups, each with its own hyperparameters
     -- among them lr = 0 (theta unchanged), beta2 = 0, a decay factor
-    1 - lr*wd below zero, a large eps -- over 64 tensors of mixed dtypes,
+    1 - lr*wd below zero, a large eps, eps = 0, beta1 = 0, betas within
+    1e-7 of 1 (tiny bias corrections) -- over 64 tensors of mixed dtypes,
     three calls, bit-exact against the oracle in every state format."""
     _need_gpu()
     say("case: 32 groups")
@@ -419,6 +420,9 @@ def test_thirty_two_groups_with_edge_hyperparameters_against_oracle():
     groups[1] = W.Group(lr=1e-3, beta2=0.0)
     groups[2] = W.Group(lr=0.5, weight_decay=3.0)          # 1 - lr*wd = -0.5
     groups[3] = W.Group(lr=1e-2, eps=1.0)
+    groups[4] = W.Group(lr=1e-3, eps=0.0)
+    groups[5] = W.Group(lr=1e-3, beta1=0.0, beta2=0.999999)
+    groups[6] = W.Group(lr=1e-3, beta1=0.9999999, beta2=0.99999999)   # bias corrections ~1e-7, 1e-8
     sizes = [int(x) for x in rng.integers(1, 3000, 64)]
     pdt = [(W.F32, W.BF16)[i % 2] for i in range(64)]
     gdt = [(W.F32, W.BF16)[(i // 2) % 2] for i in range(64)]
@@ -442,6 +446,44 @@ def test_thirty_two_groups_with_edge_hyperparameters_against_oracle():
         # lr = 0: theta of group 0's tensors is unchanged
         for i in (0, 32):
             assert n_bit_mismatch(bits(params[i]), bits(p_cpu[i])) == 0
+        opt.close()
+
+
+@pytest.mark.parametrize("fmt", [W.STATE_F32, W.STATE_Q8])
+def test_large_step_counters_against_oracle(fmt):
+    """Step counters set far along (as a resumed run would have them, written
+    straight into the caller-owned state buffer, up to t = 2^31 - 2 so the
+    step reaches the largest int32): beta^t by square-and-multiply over all
+    31 bits, bias corrections that round to 1, bit-exact against the oracle
+    in both launch modes."""
+    _need_gpu()
+    say("case: large step counters", fmt)
+    sizes = [1000, 4096, 77]
+    t0 = [2 ** 31 - 2, 1_000_003, 12_345]
+    groups = [W.Group(lr=1e-3, weight_decay=0.1, beta1=0.9, beta2=0.999999)]
+    for mode in (1, 2):
+        gen = torch.Generator().manual_seed(91)
+        p_cpu = [torch.randn(n, generator=gen) * 0.02 for n in sizes]
+        params = [p.to(DEV) for p in p_cpu]
+        th_ref = [bits(p) for p in p_cpu]
+        opt = GpuOpt(sizes, [W.F32] * 3, [W.F32] * 3, [0, 0, 0], 1, fmt)
+        L.apexw_set_launch_mode(opt.h, mode)
+        ref = oracle.OracleAdamW(sizes, [W.F32] * 3, [W.F32] * 3, [0, 0, 0], fmt)
+        opt.steps().copy_(torch.tensor(t0, dtype=torch.int32))
+        ref.t[:3] = t0
+        for k in range(2 if mode == 1 else 1):
+            g_cpu = [torch.randn(n, generator=gen) * 1e-3 for n in sizes]
+            if k == 1:                              # t[0] is at the int32 maximum now
+                g_cpu[0] = None
+            opt.step(groups, params, [None if g is None else g.to(DEV) for g in g_cpu])
+            ref.step(th_ref, [None if g is None else bits(g) for g in g_cpu], groups)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(opt.steps()), ref.t[:3])
+        assert ref.t[0] == 2 ** 31 - 1
+        for i in range(3):
+            assert n_bit_mismatch(bits(params[i]), th_ref[i]) == 0, (mode, i)
+            m, v = (bits(t) for t in opt.moments(i))
+            assert n_bit_mismatch(m, ref.m[i]) == 0 and n_bit_mismatch(v, ref.v[i]) == 0, (mode, i)
         opt.close()
 
 
