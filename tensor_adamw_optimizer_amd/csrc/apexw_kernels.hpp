@@ -1,7 +1,9 @@
 // apexw_kernels.hpp -- gfx950 device code of the fused multi-tensor AdamW step.
 //
 // Two kernels per step (prepare, then one update launch per (param, grad)
-// dtype pair):
+// dtype pair), or for small lists one (adamw_single_step_kernel, which forms
+// the step records itself and advances the counters from its last
+// workgroup, found through a tree of arrival counters):
 //  * adamw_prepare_kernel -- one lane per tensor: unless found_inf is set,
 //    advances the step counter of every tensor that has a grad and writes
 //    that tensor's step record (grad pointer, fp32 group scalars and bias
@@ -24,8 +26,9 @@
 //    in the method, so no matrix-core work; the arithmetic is ordinary fp32
 //    VALU code compiled without contraction, with exact shortcuts where the
 //    hardware offers them (bf16 pair conversion, square root from
-//    v_sqrt_f32 plus a residual check, 8-bit codes from v_rcp_f32 plus a
-//    tie guard).
+//    v_sqrt_f32 plus a residual check, division by the per-tensor bias
+//    corrections from their reciprocals plus one residual correction, 8-bit
+//    codes from v_rcp_f32 plus a tie guard).
 //
 // Read-only passes for the mixed-precision recipe and clipping:
 //  * unscale_check_kernel -- any non-finite unscaled grad sets found_inf;
@@ -63,6 +66,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // table, descriptors, step records) is read-only for the whole
 // update launch, so it is read through the constant space, which lets the
 // compiler use scalar loads (scalar cache) for these wave-uniform values.
+// (The single-launch kernel also reads the step counters that way; its last
+// workgroup writes them only after every workgroup has read them, through a
+// generic pointer.)
 #define APEXW_GLOBAL __attribute__((address_space(1)))
 #define APEXW_CONST __attribute__((address_space(4)))
 
