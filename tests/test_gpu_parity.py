@@ -487,6 +487,53 @@ def test_large_step_counters_against_oracle(fmt):
         opt.close()
 
 
+def test_single_launch_counters_over_many_steps():
+    """The single-launch step's arrival counters must be back at zero after
+    every launch: 300 steps of a two-launch list (two dtype pairs) in the
+    single-launch mode, with the workgroup cap changed at random between
+    steps (below, at and above the 64 first-level counters; the expected
+    arrival counts change with it), random skipped steps and random absent
+    grads; step counters against their definition after every step, and
+    theta, m, v bit-exact against the oracle at the end."""
+    _need_gpu()
+    say("case: single launch, 300 steps")
+    sizes = [70_000, 513, 129_000, 1]
+    pdt = [W.F32, W.BF16, W.F32, W.BF16]
+    gdt = [W.F32, W.F32, W.F32, W.F32]
+    groups = [W.Group(lr=1e-3, weight_decay=0.05)]
+    rng = np.random.default_rng(123)
+    gen = torch.Generator().manual_seed(124)
+    p_cpu = [(torch.randn(n, generator=gen) * 0.02).to(W.TORCH_DTYPE[d]) for n, d in zip(sizes, pdt)]
+    params = [p.to(DEV) for p in p_cpu]
+    th_ref = [bits(p) for p in p_cpu]
+    opt = GpuOpt(sizes, pdt, gdt, [0] * 4, 1, W.STATE_F32)
+    L.apexw_set_launch_mode(opt.h, 2)
+    ref = oracle.OracleAdamW(sizes, pdt, gdt, [0] * 4, W.STATE_F32)
+    fi = torch.zeros(1, device=DEV)
+    want = np.zeros(4, np.int32)
+    caps = [0, 1, 5, 63, 64, 65, 200, 513]
+    for k in range(300):
+        L.apexw_set_workgroups(opt.h, int(rng.choice(caps)))
+        present = rng.random(4) < 0.8
+        skip = rng.random() < 0.1
+        g_cpu = [torch.randn(n, generator=gen) * 1e-3 for n in sizes]
+        fi.fill_(1.0 if skip else 0.0)
+        opt.step(groups, params, [g.to(DEV) if ok else None for g, ok in zip(g_cpu, present)],
+                 found_inf=fi)
+        ref.step(th_ref, [bits(g) if ok else None for g, ok in zip(g_cpu, present)], groups,
+                 found_inf=skip)
+        if not skip:
+            want += present.astype(np.int32)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(opt.steps()), want), (k, bits(opt.steps()), want)
+    assert np.array_equal(ref.t[:4], want)
+    for i in range(4):
+        assert n_bit_mismatch(bits(params[i]), th_ref[i]) == 0, i
+        m, v = opt.moments(i)
+        assert n_bit_mismatch(bits(m), ref.m[i]) == 0 and n_bit_mismatch(bits(v), ref.v[i]) == 0, i
+    opt.close()
+
+
 def test_all_grads_absent_and_pointer_changes():
     """No grads at all: nothing changes.  Grads moved to new buffers between
     calls: the library follows the new pointers."""
