@@ -179,6 +179,17 @@ def make_ptrs(ptrs: Sequence[int]) -> ctypes.Array:
     return (ctypes.c_void_p * max(1, len(ptrs)))(*[p or None for p in ptrs])
 
 
+class ptr_table:
+    """A void*[] over an array('Q') of addresses (0 = NULL), passed to the
+    library without a per-element conversion; keeps the array alive."""
+
+    def __init__(self, ptrs: "array"):
+        if ptrs.itemsize != 8:
+            raise TypeError("ptr_table needs 64-bit addresses")
+        self._a = ptrs if len(ptrs) else type(ptrs)("Q", [0])
+        self._as_parameter_ = ctypes.c_void_p(self._a.buffer_info()[0])
+
+
 def apexw_step(handle: int, groups_arr, n_groups: int, params_arr, grads_arr,
                found_inf_ptr: int = 0, stream: int = 0) -> None:
     """groups_arr / params_arr / grads_arr: arrays from make_groups / make_ptrs."""

@@ -9,6 +9,7 @@ the whole update runs in the library's kernels.
 """
 from __future__ import annotations
 
+from array import array
 from typing import Dict, Iterable, List, Optional
 
 import torch
@@ -100,22 +101,26 @@ class AdamW(torch.optim.Optimizer):
 
     # ------------------------------------------------------------ stepping
     def _grads_arr(self):
-        ptrs = []
-        for p, gdt in zip(self._params, self._gdtype):
-            g = p.grad
-            if g is None:
-                ptrs.append(0)
-                continue
-            if g.is_sparse:
+        """The grad-pointer table of this step (0: no grad).  One pass of
+        cheap per-tensor calls: torch itself guarantees that a .grad has its
+        parameter's shape and device (and its dtype unless the parameter's
+        grad_dtype says otherwise); sparse grads, which have no data pointer,
+        and non-contiguous grads are refused."""
+        gs = [p.grad for p in self._params]
+        try:
+            ptrs = array("Q", [0 if g is None else (g.data_ptr() or 16) for g in gs])
+        except RuntimeError:
+            if any(g is not None and g.layout is not torch.strided for g in gs):
                 raise L.ApexwError(L.APEXW_ESPARSE, "AdamW.step",
-                                   "sparse gradients are not supported")
-            if g.dtype != gdt or g.shape != p.shape or not g.is_contiguous() \
-                    or g.device != p.device:
-                raise ValueError("grad must be a contiguous %s tensor shaped like its "
-                                 "parameter on %s" % (gdt, p.device))
-            # an empty grad has no storage; any non-null pointer marks "present"
-            ptrs.append(g.data_ptr() or 16)
-        return L.make_ptrs(ptrs)
+                                   "sparse gradients are not supported") from None
+            raise
+        if not all(g is None or (g.is_contiguous() and g.dtype is d)
+                   for g, d in zip(gs, self._gdtype)):
+            bad = next(i for i, (g, d) in enumerate(zip(gs, self._gdtype))
+                       if g is not None and not (g.is_contiguous() and g.dtype is d))
+            raise ValueError("grad %d must be a contiguous %s tensor shaped like its parameter"
+                             % (bad, self._gdtype[bad]))
+        return L.ptr_table(ptrs)
 
     def _dev_ptr(self, t: Optional[torch.Tensor], name: str, dtype=torch.float32) -> int:
         if t is None:
@@ -152,7 +157,10 @@ class AdamW(torch.optim.Optimizer):
     def step_pointers(self, grads_arr, found_inf: Optional[torch.Tensor] = None,
                       inv_scale: Optional[torch.Tensor] = None,
                       clip_coef: Optional[torch.Tensor] = None) -> None:
-        """Step with a prepared void*[] of grad pointers (see _lib.make_ptrs)."""
+        """Step with a prepared void*[] of grad pointers (_lib.make_ptrs or
+        _lib.ptr_table), or with None: the grad table of the previous call on
+        this optimizer -- for grad buffers that persist across steps, with no
+        per-tensor work on the host."""
         groups = [_GroupView(g) for g in self.param_groups]
         with torch.cuda.device(self.device):
             L.apexw_step_ex(self._h, L.make_groups(groups), len(groups), self._params_arr,

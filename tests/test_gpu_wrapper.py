@@ -144,3 +144,38 @@ def test_wrapper_with_lr_scheduler_and_grad_scaler_against_oracle():
     assert list(bits(opt.steps())) == [6, 6]
     assert lr == 1e-2 * 0.5 ** 3
     opt.close()
+
+
+def test_wrapper_grad_table_checks_and_reuse():
+    """A non-contiguous grad is refused before anything is queued;
+    step_pointers(None) reuses the previous grad table (persistent grad
+    buffers), giving the same result as a step that reads .grad."""
+    say("case: wrapper grad table")
+    gen = torch.Generator().manual_seed(71)
+    p_cpu = [torch.randn(32, 16, generator=gen) * 0.02, torch.randn(300, generator=gen) * 0.02]
+    a = [p.to(DEV) for p in p_cpu]
+    b = [p.to(DEV) for p in p_cpu]
+    opt_a = AdamW(a, lr=1e-2, weight_decay=0.1)
+    opt_b = AdamW(b, lr=1e-2, weight_decay=0.1)
+    g = [torch.randn(32, 16, generator=gen).to(DEV) * 1e-3, torch.randn(300, generator=gen).to(DEV) * 1e-3]
+    a[0].grad = g[0].t().contiguous().t()          # same values, transposed strides
+    a[1].grad = g[1].clone()
+    with pytest.raises(ValueError):
+        opt_a.step()
+    assert opt_a.read_steps() == [0, 0]
+    for k in range(3):
+        for p, x in zip(a, g):
+            p.grad = x.clone()
+        opt_a.step()
+        if k == 0:
+            for p, x in zip(b, g):
+                p.grad = x                          # persistent buffers, read once
+            opt_b.step()
+        else:
+            opt_b.step_pointers(None)               # the same buffers as the last call
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert n_bit_mismatch(bits(x), bits(y)) == 0
+    assert opt_a.read_steps() == opt_b.read_steps() == [3, 3]
+    opt_a.close()
+    opt_b.close()
