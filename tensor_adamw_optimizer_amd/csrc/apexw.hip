@@ -5,7 +5,9 @@
 // optimizer state out in one caller-owned buffer, and on every step queues a
 // small prepare kernel (step counters, per-tensor step records) followed by
 // one update kernel per (parameter dtype, grad dtype) pair present, each with
-// one workgroup per tile.  Per call it only compares the param / grad pointer
+// one workgroup per tile -- or, for small lists, only the per-pair kernels,
+// which then form the step records themselves and advance the counters from
+// their last workgroup.  Per call it only compares the param / grad pointer
 // arrays with the previous call's (one asynchronous upload when they differ)
 // and forms the per-group fp32 scalars, which travel in the kernel arguments.
 // It never synchronises with the host inside a step and allocates no device
@@ -127,9 +129,9 @@ struct WsLayout {
     bool single;                         // room for the single-launch step
 };
 
-// The constants region: 0.0f and 1.0f, passed to the prepare kernel in place
-// of an absent found_inf flag, inv_scale or clip coefficient, so that it
-// loads all of them unconditionally.
+// The constants region: 0.0f and 1.0f, passed to the step kernels in place
+// of an absent found_inf flag, inv_scale or clip coefficient, so that they
+// load all of them unconditionally.
 constexpr float kConsts[2] = {0.0f, 1.0f};
 
 constexpr int kMaxLaunches = 4;      // (param, grad) dtype pairs
@@ -691,13 +693,14 @@ int apexw_step_ex(apexw_t h, const apexw_group *groups, int32_t n_groups, void *
         HIP_TRY(hipGetLastError());
     }
     const int64_t cap = launch_cap(h);
-    int li = -1;
-    for (const Launch &L : h->launches) {
+    for (size_t li = 0; li < h->launches.size(); ++li) {
+        const Launch &L = h->launches[li];
         // residency cap: the dynamic LDS a workgroup reserves (it uses none)
         const int occ = h->occupancy > 0 ? h->occupancy : default_occupancy(h->fmt, L.pt, L.gt);
         const unsigned lds = occ > 0 ? (unsigned)std::min(h->lds_per_cu / occ, h->lds_per_block) : 0u;
-        ++li;
-        if (L.tile_count == 0) continue;      // only empty tensors: t advanced above
+        // only empty tensors: their counters advanced in the prepare kernel
+        // (the single launch is not used for lists with such a launch)
+        if (L.tile_count == 0) continue;
         bool any = false;                     // no grads in this launch: skip it
         for (int32_t j = 0; j < L.tensor_count && !any; ++j)
             any = grads[h->tensor_list[L.tensor_begin + j]] != nullptr;
@@ -710,7 +713,7 @@ int apexw_step_ex(apexw_t h, const apexw_group *groups, int32_t n_groups, void *
         if (single) {
             a.tensor_begin = L.tensor_begin;
             a.tensor_count = L.tensor_count;
-            a.done = reinterpret_cast<uint32_t *>(h->ws + h->wl.done) + (int64_t)li * kDoneWords;
+            a.done = reinterpret_cast<uint32_t *>(h->ws + h->wl.done) + li * kDoneWords;
             hipLaunchKernelGGL(single_kernel_for(h->fmt, L.pt, L.gt, scaled), dim3((unsigned)wg),
                                dim3(kThreads), lds, st, a);
         } else {
