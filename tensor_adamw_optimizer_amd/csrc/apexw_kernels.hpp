@@ -820,7 +820,9 @@ __global__ __launch_bounds__(kThreads) void adamw_single_step_kernel(KernelArgs 
     const float clip_coef = *cptr<float>(a.clip_coef);
     const uint32_t grid = gridDim.x, c = blockIdx.x % kDoneFan;
     const uint32_t first_level = (grid - 1u - c) / kDoneFan + 1u;      // workgroups b % kDoneFan == c
-    uint32_t before = 0;
+    const uint32_t top_level = grid < (uint32_t)kDoneFan ? grid : (uint32_t)kDoneFan;
+    uint32_t *const top = a.done + kDoneFan * kDoneStride;
+    uint32_t before = 0, before_top = 0;
     bool checked = false, last1 = false;       // first-level result, once read
     int64_t k = blockIdx.x;                    // < tile_count: grid <= tiles
     for (;;) {
@@ -842,10 +844,13 @@ __global__ __launch_bounds__(kThreads) void adamw_single_step_kernel(KernelArgs 
             const auto s = [&] {
                 // read the add's result here, once the tile's loads are in
                 // flight (it was issued before them and returns first), not
-                // after the stores, which would wait for them too
+                // after the stores, which would wait for them too; a
+                // first-level winner arrives at the top right away, so that
+                // add too overlaps the tile's work
                 if (last_tile) {
                     last1 = arrived_last(before, first_level);
                     checked = true;
+                    if (last1) before_top = arrive(top, top_level);
                 }
                 return step_scalars(step_record(a, d.group, grad, t_old + 1, inv_scale, clip_coef));
             };
@@ -859,10 +864,11 @@ __global__ __launch_bounds__(kThreads) void adamw_single_step_kernel(KernelArgs 
         if (last_tile) break;
         k += grid;
     }
-    if (!checked) last1 = arrived_last(before, first_level);
-    if (!last1) return;
-    const uint32_t top = grid < (uint32_t)kDoneFan ? grid : (uint32_t)kDoneFan;
-    if (!arrived_last(arrive(a.done + kDoneFan * kDoneStride, top), top)) return;
+    if (!checked) {
+        last1 = arrived_last(before, first_level);
+        if (last1) before_top = arrive(top, top_level);
+    }
+    if (!last1 || !arrived_last(before_top, top_level)) return;
     if (fi != 0.0f) return;                    // a skipped step advances nothing
     for (int32_t j = threadIdx.x; j < a.tensor_count; j += kThreads) {
         const int32_t i = a.tensor_list[a.tensor_begin + j];
