@@ -218,8 +218,8 @@ def main() -> int:
                          "the dtypes torch supports for the workload (context only)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the optimizer step is benchmarked on a "
-              "single MI355X (--gpus 1); multi-GPU runs are not part of this build.",
+        print("bench.py measures one GPU only: it times the optimizer step on a single "
+              "MI355X (--gpus 1); a step sharded over several GPUs is not implemented.",
               file=sys.stderr)
         return 2
 
