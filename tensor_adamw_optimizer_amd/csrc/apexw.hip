@@ -809,12 +809,13 @@ int apexw_clip_grad_norm(apexw_t h, const void *const *grads, const float *inv_s
         hipLaunchKernelGGL(k, dim3((unsigned)wg), dim3(kThreads), 0, st, a);
         HIP_TRY(hipGetLastError());
     }
-    if (h->n > 0) {
+    if (h->n > 0 && n_partials > kDirectPartials) {
         hipLaunchKernelGGL(grad_norm_reduce_kernel, dim3(kReduceBlocks), dim3(kReduceThreads), 0,
                            st, a);
         HIP_TRY(hipGetLastError());
     } else {
-        a.partials2 = nullptr;                // no workspace: the norm is 0
+        a.partials2 = nullptr;                // the final kernel sums the partials
+        if (h->n == 0) a.partials = nullptr;  // no workspace: the norm is 0
     }
     hipLaunchKernelGGL(grad_norm_final_kernel, dim3(1), dim3(kReduceThreads), 0, st, a);
     HIP_TRY(hipGetLastError());

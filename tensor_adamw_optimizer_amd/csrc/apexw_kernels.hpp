@@ -1015,6 +1015,8 @@ __global__ __launch_bounds__(kThreads) void unscale_check_kernel(KernelArgs a) {
 //  3. grad_norm_final_kernel: one workgroup sums partials2 the same way and
 //     writes the norm (fp64 sqrt) and the clip coefficient max_norm / norm
 //     when norm > max_norm (fp64, rounded once to fp32), else 1.
+//  For a list of at most kDirectPartials partials (one launch less for a
+//  small list) step 2 is left out and step 3 sums the partials themselves.
 
 // DPP move of a double (both halves) within 16-lane rows.
 template <int CTRL>
@@ -1074,6 +1076,7 @@ __global__ __launch_bounds__(kThreads) void grad_norm_partials_kernel(KernelArgs
 
 constexpr int kReduceThreads = 256;
 constexpr int kReduceBlocks = 256;
+constexpr int64_t kDirectPartials = 8192;
 
 // Fixed-order sum of src[lo, hi) by one workgroup: strided per thread, then a
 // tree over the workgroup's threads in LDS.
@@ -1100,8 +1103,12 @@ __global__ __launch_bounds__(kReduceThreads) void grad_norm_reduce_kernel(Kernel
 }
 
 __global__ __launch_bounds__(kReduceThreads) void grad_norm_final_kernel(KernelArgs a) {
-    // no partials at all (an empty tensor list): the norm is 0
-    const double sum = a.partials2 != nullptr ? block_sum(a.partials2, 0, kReduceBlocks) : 0.0;
+    // after the reduce kernel: its kReduceBlocks sums; for few partials (no
+    // reduce launch) the partials themselves; none at all (an empty tensor
+    // list): the norm is 0
+    const double sum = a.partials2 != nullptr ? block_sum(a.partials2, 0, kReduceBlocks)
+                       : a.partials != nullptr ? block_sum(a.partials, 0, a.n_partials)
+                                               : 0.0;
     if (threadIdx.x == 0) {
         const double norm = sqrt(sum);
         const float coef = norm > a.max_norm ? (float)(a.max_norm / norm) : 1.0f;
