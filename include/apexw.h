@@ -346,10 +346,12 @@ int apexw_set_occupancy(apexw_t h, int32_t workgroups_per_cu);
 
 /*
  * Cache policy of the update kernel: 0 (default) chooses by size -- lists
- * whose parameters, grads and state together reach 192 MiB stream with
- * non-temporal loads and stores, smaller ones use ordinary (cached) accesses
- * so they can stay in the 256 MB Infinity Cache from step to step; 1 forces
- * streaming, 2 forces cached.  Results do not depend on it.
+ * whose parameters, grads and state together reach 64 MiB stream with
+ * non-temporal loads and stores (in a training loop the forward and backward
+ * passes evict the 256 MB Infinity Cache between steps, and streaming is then
+ * the faster), smaller ones use ordinary (cached) accesses; 1 forces
+ * streaming, 2 forces cached (fastest when steps run back to back with
+ * nothing in between).  Results do not depend on it.
  */
 int apexw_set_cache_policy(apexw_t h, int32_t policy);
 

@@ -238,8 +238,13 @@ kernel_fn single_kernel_for(int fmt, int pt, int gt, bool scaled) {
 }
 
 // Bytes an optimizer touches per step (parameters, grads, state): above this
-// the update streams past the caches.
-constexpr int64_t kStreamingBytes = (int64_t)192 << 20;
+// the update streams past the caches.  Measured on MI355X with the 8-bit
+// LoRA list (146 MB touched): streaming takes 65 us when the 256 MB Infinity
+// Cache was flushed before the step, as a training loop's forward and
+// backward passes do, against 71 us with cached accesses; only when steps
+// run back to back with nothing in between is caching faster (55 against
+// 57 us).  Small lists keep cached accesses (and the single launch).
+constexpr int64_t kStreamingBytes = (int64_t)64 << 20;
 
 }  // namespace
 
