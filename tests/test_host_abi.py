@@ -156,3 +156,44 @@ def test_error_codes_are_distinct_and_negative():
     codes = [L.APEXW_EINVAL, L.APEXW_EDTYPE, L.APEXW_ENOSPC, L.APEXW_EHIP, L.APEXW_ENOMEM,
              L.APEXW_ESPARSE]
     assert len(set(codes)) == len(codes) and all(c < 0 for c in codes)
+
+
+def _check_layout(numel, fmt):
+    per, steps = L.apexw_state_layout(numel, fmt)
+    total = L.apexw_state_bytes(numel, fmt)
+    eb = {L.APEXW_STATE_F32: 4, L.APEXW_STATE_BF16: 2, L.APEXW_STATE_Q8: 1}[fmt]
+    spans = []
+    for (m, v, ms, vs), n in zip(per, numel):
+        # moment arrays start and end on 64-byte boundaries (the padding the
+        # update writes whole), scales on 4-byte ones
+        assert m % 64 == 0 and v % 64 == 0
+        pad = -(-n * eb // 64) * 64
+        spans += [(m, m + pad), (v, v + pad)]
+        if fmt == L.APEXW_STATE_Q8:
+            nb = -(-n // 256)
+            assert ms % 4 == 0 and vs % 4 == 0
+            spans += [(ms, ms + 4 * nb), (vs, vs + 4 * nb)]
+    spans.append((steps, steps + 4 * len(numel)))
+    spans = sorted(s for s in spans if s[1] > s[0])
+    for (a0, a1), (b0, b1) in zip(spans, spans[1:]):
+        assert a1 <= b0
+    assert total == steps + 4 * len(numel) == spans[-1][1]
+
+
+def test_layout_property_random_lists():
+    """Random tensor lists (sizes 0 .. 2^21, up to 300 tensors, every
+    format): moment arrays padded to whole 64-byte chunks, every region
+    disjoint, the step counters last; the workspace never shrinks when a
+    tensor grows."""
+    import numpy as np
+    rng = np.random.default_rng(8)
+    for trial in range(60):
+        n = int(rng.integers(1, 300))
+        numel = [int(x) for x in (rng.integers(0, 2, n) * rng.integers(0, 1 << 21, n))]
+        for fmt in (L.APEXW_STATE_F32, L.APEXW_STATE_BF16, L.APEXW_STATE_Q8):
+            _check_layout(numel, fmt)
+        w0 = L.apexw_workspace_bytes(numel)
+        grown = list(numel)
+        grown[int(rng.integers(0, n))] += int(rng.integers(1, 1 << 16))
+        assert L.apexw_workspace_bytes(grown) >= w0 or sum(-(-x // 256) for x in grown) > 6144 >= \
+            sum(-(-x // 256) for x in numel)
