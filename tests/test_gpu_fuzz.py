@@ -1,0 +1,95 @@
+"""Randomised GPU parity: 48 seeded configurations, each a random tensor
+list (sizes 0 .. 50,000, every (param, grad) dtype pair, 1-4 groups with
+random hyperparameters including edge values), a random state format,
+launch mode, cache policy and workgroup cap, and 4 calls with random absent
+grads, a random skipped call and, on some calls, an inv_scale and a clip
+coefficient -- theta, moments, 8-bit scales and counters bit for bit against
+the oracle after the last call."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_helpers import GpuOpt, bits, n_bit_mismatch, say
+from tensor_adamw_optimizer_amd import _lib as L
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+FORMATS = [W.STATE_F32, W.STATE_BF16, W.STATE_Q8]
+
+
+def _random_group(rng):
+    pick = rng.integers(0, 6)
+    lr = float(10 ** rng.uniform(-5, -1))
+    beta1 = float(rng.choice([0.0, 0.5, 0.9, 0.99, 0.9999]))
+    beta2 = float(rng.choice([0.0, 0.9, 0.999, 0.99999]))
+    eps = float(rng.choice([0.0, 1e-12, 1e-8, 1e-3]))
+    wd = float(rng.choice([0.0, 0.01, 0.1, 2.0]))
+    if pick == 0:
+        lr = 0.0
+    return W.Group(lr=lr, beta1=beta1, beta2=beta2, eps=eps, weight_decay=wd)
+
+
+@pytest.mark.parametrize("seed", range(48))
+def test_random_configuration_against_oracle(seed):
+    rng = np.random.default_rng(1000 + seed)
+    n = int(rng.integers(1, 25))
+    sizes = [0 if rng.random() < 0.05 else int(np.exp(rng.uniform(0, np.log(50_000)))) for _ in range(n)]
+    pdt = [str(rng.choice([W.F32, W.BF16])) for _ in range(n)]
+    gdt = [str(rng.choice([W.F32, W.BF16])) for _ in range(n)]
+    n_groups = int(rng.integers(1, 5))
+    group_of = [int(rng.integers(0, n_groups)) for _ in range(n)]
+    groups = [_random_group(rng) for _ in range(n_groups)]
+    fmt = FORMATS[seed % 3]
+    say("case: fuzz", seed, "n", n, "fmt", fmt, "groups", n_groups)
+    gen = torch.Generator().manual_seed(2000 + seed)
+    p_cpu = [(torch.randn(s, generator=gen) * 0.02).to(W.TORCH_DTYPE[d]) for s, d in zip(sizes, pdt)]
+    params = [p.to(DEV) for p in p_cpu]
+    th_ref = [bits(p) for p in p_cpu]
+    opt = GpuOpt(sizes, pdt, gdt, group_of, n_groups, fmt)
+    try:
+        L.apexw_set_launch_mode(opt.h, int(rng.choice([0, 1, 2])))
+    except L.ApexwError:
+        L.apexw_set_launch_mode(opt.h, 1)             # the single launch is not available
+    L.apexw_set_cache_policy(opt.h, int(rng.choice([0, 1, 2])))
+    L.apexw_set_workgroups(opt.h, int(rng.choice([0, 0, 1, 7, 64, 100])))
+    ref = oracle.OracleAdamW(sizes, pdt, gdt, group_of, fmt)
+    fi = torch.zeros(1, device=DEV)
+    inv_t = torch.zeros(1, device=DEV)
+    clip_t = torch.zeros(1, device=DEV)
+    skip_call = int(rng.integers(0, 6))                 # 4 or 5: no skipped call
+    for k in range(4):
+        scaled = rng.random() < 0.5
+        inv = float(np.float32(2.0 ** -int(rng.integers(0, 12)) if rng.random() < 0.7
+                               else rng.uniform(0.1, 1.0))) if scaled else 1.0
+        clip = float(np.float32(rng.uniform(0.2, 1.0))) if scaled and rng.random() < 0.5 else None
+        g_cpu = [(torch.randn(s, generator=gen) * 1e-3 / inv).to(W.TORCH_DTYPE[d]) for s, d in zip(sizes, gdt)]
+        present = [rng.random() < 0.85 for _ in range(n)]
+        skip = k == skip_call
+        fi.fill_(1.0 if skip else 0.0)
+        pa = L.make_ptrs([p.data_ptr() for p in params])
+        g_dev = [g.to(DEV) if ok else None for g, ok in zip(g_cpu, present)]
+        ga = L.make_ptrs([0 if g is None else (g.data_ptr() or 16) for g in g_dev])
+        if scaled:
+            inv_t.fill_(inv)
+            if clip is not None:
+                clip_t.fill_(clip)
+        L.apexw_step_ex(opt.h, L.make_groups(groups), n_groups, pa, ga,
+                        inv_scale_ptr=inv_t.data_ptr() if scaled else 0,
+                        clip_coef_ptr=clip_t.data_ptr() if clip is not None else 0,
+                        found_inf_ptr=fi.data_ptr(), stream=opt.stream)
+        ref.step(th_ref, [bits(g) if ok else None for g, ok in zip(g_cpu, present)], groups,
+                 found_inf=skip, inv_scale=inv if scaled else None, clip_coef=clip)
+        torch.cuda.synchronize()
+    assert np.array_equal(bits(opt.steps()), ref.t[:n])
+    for i in range(n):
+        assert n_bit_mismatch(bits(params[i]), th_ref[i]) == 0, (seed, i)
+        m, v = opt.moments(i)
+        assert n_bit_mismatch(bits(m), ref.m[i]) == 0, (seed, i)
+        assert n_bit_mismatch(bits(v), ref.v[i]) == 0, (seed, i)
+        if fmt == W.STATE_Q8:
+            ms, vs = opt.scales(i)
+            assert n_bit_mismatch(bits(ms), ref.m_scale[i]) == 0, (seed, i)
+            assert n_bit_mismatch(bits(vs), ref.v_scale[i]) == 0, (seed, i)
+    opt.close()
