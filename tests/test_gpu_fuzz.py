@@ -3,8 +3,12 @@ list (sizes 0 .. 50,000, every (param, grad) dtype pair, 1-4 groups with
 random hyperparameters including edge values), a random state format,
 launch mode, cache policy and workgroup cap, and 4 calls with random absent
 grads, a random skipped call and, on some calls, an inv_scale and a clip
-coefficient -- theta, moments, 8-bit scales and counters bit for bit against
-the oracle after the last call."""
+coefficient; parameters and grads sometimes views at odd element offsets
+into larger buffers (no vector alignment), and the hyperparameters
+sometimes read from device memory -- theta, moments, 8-bit scales and
+counters bit for bit against the oracle after the last call."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -17,6 +21,23 @@ from tensor_adamw_optimizer_amd import _lib as L
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 FORMATS = [W.STATE_F32, W.STATE_BF16, W.STATE_Q8]
+
+
+def _view(src: torch.Tensor, rng) -> torch.Tensor:
+    """A device copy of src, at an odd element offset into a larger buffer
+    with probability 0.3 (misaligned for vector accesses), else plain."""
+    if src.numel() == 0 or rng.random() >= 0.3:
+        return src.to(DEV)
+    off = int(rng.integers(1, 4))
+    buf = torch.zeros(src.numel() + off, dtype=src.dtype, device=DEV)
+    buf[off:].copy_(src)
+    return buf[off:]
+
+
+def _device_groups(groups):
+    arr = L.make_groups(groups)
+    raw = bytes(ctypes.string_at(ctypes.addressof(arr), ctypes.sizeof(L.apexw_group) * len(groups)))
+    return torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(DEV)
 
 
 def _random_group(rng):
@@ -45,7 +66,8 @@ def test_random_configuration_against_oracle(seed):
     say("case: fuzz", seed, "n", n, "fmt", fmt, "groups", n_groups)
     gen = torch.Generator().manual_seed(2000 + seed)
     p_cpu = [(torch.randn(s, generator=gen) * 0.02).to(W.TORCH_DTYPE[d]) for s, d in zip(sizes, pdt)]
-    params = [p.to(DEV) for p in p_cpu]
+    params = [_view(p, rng) for p in p_cpu]
+    dev_groups = rng.random() < 0.3
     th_ref = [bits(p) for p in p_cpu]
     opt = GpuOpt(sizes, pdt, gdt, group_of, n_groups, fmt)
     try:
@@ -69,16 +91,18 @@ def test_random_configuration_against_oracle(seed):
         skip = k == skip_call
         fi.fill_(1.0 if skip else 0.0)
         pa = L.make_ptrs([p.data_ptr() for p in params])
-        g_dev = [g.to(DEV) if ok else None for g, ok in zip(g_cpu, present)]
+        g_dev = [_view(g, rng) if ok else None for g, ok in zip(g_cpu, present)]
         ga = L.make_ptrs([0 if g is None else (g.data_ptr() or 16) for g in g_dev])
         if scaled:
             inv_t.fill_(inv)
             if clip is not None:
                 clip_t.fill_(clip)
-        L.apexw_step_ex(opt.h, L.make_groups(groups), n_groups, pa, ga,
+        table = _device_groups(groups) if dev_groups else None
+        L.apexw_step_ex(opt.h, None if dev_groups else L.make_groups(groups), n_groups, pa, ga,
                         inv_scale_ptr=inv_t.data_ptr() if scaled else 0,
                         clip_coef_ptr=clip_t.data_ptr() if clip is not None else 0,
-                        found_inf_ptr=fi.data_ptr(), stream=opt.stream)
+                        found_inf_ptr=fi.data_ptr(),
+                        groups_dev_ptr=table.data_ptr() if dev_groups else 0, stream=opt.stream)
         ref.step(th_ref, [bits(g) if ok else None for g, ok in zip(g_cpu, present)], groups,
                  found_inf=skip, inv_scale=inv if scaled else None, clip_coef=clip)
         torch.cuda.synchronize()
