@@ -3,7 +3,8 @@ list (sizes 0 .. 50,000, every (param, grad) dtype pair, 1-4 groups with
 random hyperparameters including edge values), a random state format,
 launch mode, cache policy and workgroup cap, and 4 calls with random absent
 grads, a random skipped call and, on some calls, an inv_scale and a clip
-coefficient; parameters and grads sometimes views at odd element offsets
+coefficient (from the device norm pass on some calls); parameters and
+grads sometimes views at odd element offsets
 into larger buffers (no vector alignment), and the hyperparameters
 sometimes read from device memory -- theta, moments, 8-bit scales and
 counters bit for bit against the oracle after the last call."""
@@ -97,13 +98,26 @@ def test_random_configuration_against_oracle(seed):
             inv_t.fill_(inv)
             if clip is not None:
                 clip_t.fill_(clip)
+        g_np = [bits(g) if ok else None for g, ok in zip(g_cpu, present)]
+        if clip is not None and rng.random() < 0.5:
+            # the coefficient from the device norm pass instead (and its check)
+            max_norm = float(rng.uniform(1e-4, 1e-1))
+            norm_t = torch.zeros(1, dtype=torch.float64, device=DEV)
+            chk = torch.zeros(1, device=DEV)
+            L.apexw_clip_grad_norm(opt.h, ga, inv_t.data_ptr(), max_norm, chk.data_ptr(),
+                                   norm_t.data_ptr(), clip_t.data_ptr(), opt.stream)
+            torch.cuda.synchronize()
+            want = ref.grad_norm(g_np, inv)
+            assert abs(norm_t.item() - want) <= 1e-12 * max(want, 1e-300), (seed, k)
+            clip = ref.clip_coef(want, max_norm)
+            assert clip_t.item() == clip and chk.item() == 0.0, (seed, k)
         table = _device_groups(groups) if dev_groups else None
         L.apexw_step_ex(opt.h, None if dev_groups else L.make_groups(groups), n_groups, pa, ga,
                         inv_scale_ptr=inv_t.data_ptr() if scaled else 0,
                         clip_coef_ptr=clip_t.data_ptr() if clip is not None else 0,
                         found_inf_ptr=fi.data_ptr(),
                         groups_dev_ptr=table.data_ptr() if dev_groups else 0, stream=opt.stream)
-        ref.step(th_ref, [bits(g) if ok else None for g, ok in zip(g_cpu, present)], groups,
+        ref.step(th_ref, g_np, groups,
                  found_inf=skip, inv_scale=inv if scaled else None, clip_coef=clip)
         torch.cuda.synchronize()
     assert np.array_equal(bits(opt.steps()), ref.t[:n])
