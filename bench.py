@@ -24,6 +24,11 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+# launch modes of the step (apexw_get_launch_mode) and the update kernel each runs
+MODE_NAMES = {1: "prepare + update", 2: "single launch",
+              3: "carried (one launch, bias corrections from the previous step)"}
+MODE_KERNELS = {1: "adamw_step_kernel", 2: "adamw_single_step_kernel", 3: "adamw_carry_step_kernel"}
+
 METRIC = "params updated/sec + achieved HBM GB/s (% of peak) per AdamW step, 1 MI355X"
 HBM_PEAK_GBPS = 8000.0
 
@@ -201,7 +206,8 @@ def main() -> int:
     ap.add_argument("--cache-policy", type=int, default=0,
                     help="0 auto, 1 streaming (non-temporal), 2 cached")
     ap.add_argument("--launch-mode", type=int, default=0,
-                    help="0 auto, 1 prepare + update kernels, 2 single launch (small lists)")
+                    help="0 auto, 1 prepare + update kernels, 2 single launch (small lists), "
+                         "3 one launch with the bias corrections carried from the previous step")
     ap.add_argument("--amp", action="store_true",
                     help="time the mixed-precision recipe: zero found_inf, unscale-and-check "
                          "pass, update on grads scaled by 2^16")
@@ -390,7 +396,7 @@ def main() -> int:
         "max_memory_allocated": max_mem,
         "launch": {"tile_elems": tile, "tiles": n_tiles, "workgroups": wgs,
                    "workgroups_per_cu_cap": occupancy,
-                   "mode": "single launch" if launch_mode == 2 else "prepare + update"},
+                   "mode": MODE_NAMES[launch_mode]},
         "state_bytes": state_bytes,
         "roofline": {
             "bound": "hbm",
@@ -400,7 +406,7 @@ def main() -> int:
             "frac": gbps / HBM_PEAK_GBPS,
             "traffic": traffic,
             "algorithmic_bytes_per_launch": ab,
-            "kernel": ("adamw_single_step_kernel" if launch_mode == 2 else "adamw_step_kernel") + ((" + grad_norm kernels" if args.clip > 0 else " + unscale_check_kernel") if args.amp else ""),
+            "kernel": MODE_KERNELS[launch_mode] + ((" + grad_norm kernels" if args.clip > 0 else " + unscale_check_kernel") if args.amp else ""),
         },
     }
     out["context"] = {"device_copy_gbps": copy_gbps,

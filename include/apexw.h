@@ -127,7 +127,7 @@ int apexw_state_layout(int32_t n_tensors, const int64_t *numel, int32_t fmt,
 /*
  * Bytes of device workspace apexw_create needs for this tensor list (tensor
  * table, grad-pointer table, per-tensor step records, tile table, grad-norm
- * partial sums).  Same argument rules
+ * partial sums, two arrays of carried bias corrections).  Same argument rules
  * as apexw_state_bytes, minus fmt.
  */
 int apexw_workspace_bytes(int32_t n_tensors, const int64_t *numel,
@@ -177,11 +177,15 @@ int apexw_create(int32_t n_tensors, const int64_t *numel,
  *                 written; NULL means never skip
  * Never synchronises with the host.  The pointer tables are re-uploaded (one
  * asynchronous copy) only when params or grads differ from the previous call.
- * Launches: a prepare kernel and one update kernel per (param, grad) dtype
- * pair present, or for small lists one kernel per pair (apexw_set_launch_mode).
+ * Launches: by default one update kernel per (param, grad) dtype pair
+ * present, with the bias corrections carried from the previous step in the
+ * workspace; other modes and the cases that take them: apexw_set_launch_mode.
  * All calls on one handle must be ordered on the GPU (one stream, or streams
  * the caller orders).  Non-finite grads with found_inf unset are not checked
- * and propagate into theta, m and v.
+ * and propagate into theta, m and v.  The step counters in the state buffer
+ * are read by the step that follows; a caller that rewrites them there
+ * directly (not through apexw_import_state) calls apexw_set_launch_mode
+ * before the next step, which drops the carried corrections.
  */
 int apexw_step(apexw_t h, const apexw_group *groups, int32_t n_groups,
                void *const *params, const void *const *grads,
@@ -365,14 +369,30 @@ int apexw_set_cache_policy(apexw_t h, int32_t policy);
  * of a small list, but each workgroup's arrival costs a device-scope atomic:
  * on MI355X it is faster up to about 8,000 tiles.  Mode 2 needs a list of at
  * most 6144 tiles (1,572,864 elements) whose dtype pairs each hold a
- * non-empty tensor; APEXW_EINVAL otherwise.  0 (default): mode 2 for such
- * lists unless they stream (apexw_set_cache_policy), else mode 1.  Results
- * do not depend on the mode; steps of one handle queued on two streams at
- * once race in either mode.
+ * non-empty tensor; APEXW_EINVAL otherwise.  3: one kernel per dtype pair at
+ * any size, no atomics: every workgroup takes its tensor's bias corrections
+ * from an array the previous step wrote, and the first tile of each tensor
+ * advances its counter and writes the corrections for the following step
+ * into a second array (the two alternate).  The chain of carried corrections
+ * starts with a small kernel that forms them from the counters as they stand
+ * -- on the first step, after any step in another mode, after a change of
+ * beta1 or beta2, after apexw_import_state or apexw_set_launch_mode, and after
+ * a step in which a dtype pair had no grad at all.  A step whose
+ * hyperparameters live in device memory (apexw_step_device, groups_dev), or
+ * one queued while its stream is being captured into a graph (a replay would
+ * not move the chain on), takes mode 2 or 1 as mode 0 would without mode 3.
+ * Mode 3 needs a non-empty list without empty tensors; APEXW_EINVAL
+ * otherwise.  0 (default): mode 3 for such lists, else mode 2 for lists it
+ * takes unless they stream (apexw_set_cache_policy), else mode 1.  Results do
+ * not depend on the mode; steps of one handle queued on two streams at once
+ * race in every mode.  Every call drops the carried corrections (so a caller
+ * that wrote step counters into the state buffer calls it before the next
+ * step).
  */
 int apexw_set_launch_mode(apexw_t h, int32_t mode);
 
-/* The launch mode (1 or 2) the handle's next step uses. */
+/* The launch mode (1, 2 or 3) the handle's next step uses when its
+ * hyperparameters come from the host and its stream is not being captured. */
 int apexw_get_launch_mode(apexw_t h, int32_t *mode);
 
 /* The largest cap in force over the handle's update launches (0: none). */

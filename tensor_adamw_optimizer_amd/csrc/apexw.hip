@@ -124,7 +124,7 @@ int compute_layout(int32_t n, const int64_t *numel, int32_t fmt,
 // grad-norm partial sums (one per tile, then one per reduce workgroup), each
 // on a 256-byte boundary.
 struct WsLayout {
-    int64_t desc, grads, records, tiles, partials, partials2, consts, done, tensors, total;
+    int64_t desc, grads, records, tiles, partials, partials2, consts, bias, done, tensors, total;
     int64_t n_tiles;
     bool single;                         // room for the single-launch step
 };
@@ -158,7 +158,9 @@ WsLayout ws_layout(int32_t n, const int64_t *numel) {
     // groups); entries of groups past a launch's end stay 0
     w.partials2 = w.partials + round_up((w.n_tiles + kMaxLaunches * kXcds) * 8, kTableAlign);
     w.consts = w.partials2 + round_up(kReduceBlocks * 8, kTableAlign);
-    w.done = w.consts + round_up((int64_t)sizeof(kConsts), kTableAlign);
+    // the carried step's bias corrections: two arrays of one record per tensor
+    w.bias = w.consts + round_up((int64_t)sizeof(kConsts), kTableAlign);
+    w.done = w.bias + round_up(2 * (int64_t)n * (int64_t)sizeof(BiasRecord), kTableAlign);
     w.single = w.n_tiles <= kSingleLaunchTiles;
     w.tensors = w.done + (w.single ? round_up((int64_t)kMaxLaunches * kDoneWords * 4, kTableAlign) : 0);
     w.total = n == 0 ? 0 : w.tensors + (w.single ? round_up((int64_t)n * 4, kTableAlign) : 0);
@@ -228,6 +230,28 @@ kernel_fn pick_single(int pt, int gt) {
     return adamw_single_step_kernel<ST, APEXW_BF16, APEXW_BF16, SC>;
 }
 
+template <int ST, bool NT, bool SC>
+kernel_fn pick_carry(int pt, int gt) {
+    if (pt == APEXW_F32 && gt == APEXW_F32) return adamw_carry_step_kernel<ST, APEXW_F32, APEXW_F32, NT, SC>;
+    if (pt == APEXW_F32 && gt == APEXW_BF16) return adamw_carry_step_kernel<ST, APEXW_F32, APEXW_BF16, NT, SC>;
+    if (pt == APEXW_BF16 && gt == APEXW_F32) return adamw_carry_step_kernel<ST, APEXW_BF16, APEXW_F32, NT, SC>;
+    return adamw_carry_step_kernel<ST, APEXW_BF16, APEXW_BF16, NT, SC>;
+}
+
+template <bool NT, bool SC>
+kernel_fn pick_carry_format(int fmt, int pt, int gt) {
+    if (fmt == APEXW_STATE_F32) return pick_carry<APEXW_STATE_F32, NT, SC>(pt, gt);
+    if (fmt == APEXW_STATE_BF16) return pick_carry<APEXW_STATE_BF16, NT, SC>(pt, gt);
+    return pick_carry<APEXW_STATE_Q8, NT, SC>(pt, gt);
+}
+
+// The carried-step kernel (launch mode 3).
+kernel_fn carry_kernel_for(int fmt, int pt, int gt, bool streaming, bool scaled) {
+    if (streaming)
+        return scaled ? pick_carry_format<true, true>(fmt, pt, gt) : pick_carry_format<true, false>(fmt, pt, gt);
+    return scaled ? pick_carry_format<false, true>(fmt, pt, gt) : pick_carry_format<false, false>(fmt, pt, gt);
+}
+
 // The single-launch step kernel (cached accesses: such lists are small).
 kernel_fn single_kernel_for(int fmt, int pt, int gt, bool scaled) {
     if (fmt == APEXW_STATE_F32)
@@ -281,7 +305,15 @@ struct apexw_opt {
     int cache_policy = 0;               // 0 auto, 1 streaming, 2 cached
     bool streaming_auto = true;
     bool single_ok = false;             // the single-launch step is available
-    int launch_mode = 0;                // 0 auto, 1 prepare + update, 2 single launch
+    int launch_mode = 0;                // 0 auto, 1 prepare + update, 2 single launch, 3 carried
+    // the carried step (mode 3): bias corrections for the next step live in
+    // bias array carry_parity of the workspace when carry_valid, formed with
+    // the betas below; any other kind of step, an import or a mode change
+    // drops them
+    bool carry_ok = false;              // no empty tensor: every tensor has a first tile
+    bool carry_valid = false;
+    int carry_parity = 0;
+    std::vector<double> carry_beta1, carry_beta2;
 };
 
 namespace {
@@ -392,9 +424,18 @@ bool streams(const apexw_opt *h) {
     return h->cache_policy == 0 ? h->streaming_auto : h->cache_policy == 1;
 }
 
-// The single launch: forced, or by default for the lists it is made for.
+// The carried step: forced, or by default for every list without an empty
+// tensor (steps with hyperparameters in device memory and steps being
+// captured into a graph take another mode).
+bool carry_launch(const apexw_opt *h) {
+    return h->carry_ok && (h->launch_mode == 3 || h->launch_mode == 0);
+}
+
+// The single launch: forced, or by default for the lists it is made for
+// (also when mode 3 is asked for but a step cannot take it).
 bool single_launch(const apexw_opt *h) {
-    return h->launch_mode == 2 || (h->launch_mode == 0 && h->single_ok && !streams(h));
+    return h->launch_mode == 2 ||
+           ((h->launch_mode == 0 || h->launch_mode == 3) && h->single_ok && !streams(h));
 }
 
 int launch_cap(const apexw_opt *h) { return h->wg_override > 0 ? h->wg_override : (int)kMaxGrid; }
@@ -564,6 +605,10 @@ int apexw_create(int32_t n_tensors, const int64_t *numel, const int32_t *param_d
         // tensors only advances counters, which the prepare kernel does)
         h->single_ok = wl.single && n_tensors > 0;
         for (const Launch &L : h->launches) h->single_ok = h->single_ok && L.tile_count > 0;
+        h->carry_ok = n_tensors > 0;
+        for (int32_t i = 0; i < n_tensors; ++i) h->carry_ok = h->carry_ok && numel[i] > 0;
+        h->carry_beta1.assign((size_t)n_groups, 0.0);
+        h->carry_beta2.assign((size_t)n_groups, 0.0);
     } catch (const std::bad_alloc &) {
         return bail(fail(APEXW_ENOMEM, "host allocation failed"));
     }
@@ -689,8 +734,38 @@ int apexw_step_ex(apexw_t h, const apexw_group *groups, int32_t n_groups, void *
     a.clip_coef = a.clip_coef != nullptr ? a.clip_coef : consts + 1;        // 1: unclipped
     a.n_tensors = h->n;
     const bool streaming = streams(h);
-    const bool single = single_launch(h);
-    if (single) {
+    // the carried step needs the hyperparameters on the host (their betas
+    // form the carried corrections) and a step that runs now: a captured
+    // graph replays its launches without this host state moving on
+    bool carry = false;
+    if (groups && carry_launch(h)) {
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        HIP_TRY(hipStreamIsCapturing(st, &cap));
+        carry = cap == hipStreamCaptureStatusNone;
+    }
+    if (!carry) h->carry_valid = false;
+    const bool single = !carry && single_launch(h);
+    bool carry_broken = false;                // a launch left out: restart the chain
+    if (carry) {
+        BiasRecord *bias = reinterpret_cast<BiasRecord *>(h->ws + h->wl.bias);
+        bool same = h->carry_valid;
+        for (int32_t g = 0; same && g < n_groups; ++g)
+            same = groups[g].beta1 == h->carry_beta1[(size_t)g] &&
+                   groups[g].beta2 == h->carry_beta2[(size_t)g];
+        a.bias_cur = bias + (size_t)h->carry_parity * (size_t)h->n;
+        a.bias_next = bias + (size_t)(1 - h->carry_parity) * (size_t)h->n;
+        if (!same) {                          // (re)start from the counters as they stand
+            KernelArgs ai = a;
+            ai.bias_next = bias + (size_t)h->carry_parity * (size_t)h->n;
+            hipLaunchKernelGGL(carry_init_kernel, dim3((unsigned)ceil_div(h->n, kPrepThreads)),
+                               dim3(kPrepThreads), 0, st, ai);
+            HIP_TRY(hipGetLastError());
+            for (int32_t g = 0; g < n_groups; ++g) {
+                h->carry_beta1[(size_t)g] = groups[g].beta1;
+                h->carry_beta2[(size_t)g] = groups[g].beta2;
+            }
+        }
+    } else if (single) {
         a.tensor_list = reinterpret_cast<const int32_t *>(h->ws + h->wl.tensors);
     } else {
         hipLaunchKernelGGL(adamw_prepare_kernel, dim3((unsigned)ceil_div(h->n, kPrepThreads)),
@@ -709,13 +784,19 @@ int apexw_step_ex(apexw_t h, const apexw_group *groups, int32_t n_groups, void *
         bool any = false;                     // no grads in this launch: skip it
         for (int32_t j = 0; j < L.tensor_count && !any; ++j)
             any = grads[h->tensor_list[L.tensor_begin + j]] != nullptr;
-        if (!any) continue;
+        if (!any) {
+            carry_broken = true;              // its tensors carry nothing forward
+            continue;
+        }
         a.tile_begin = L.tile_begin;
         a.tile_count = L.tile_count;
         a.table_begin = L.table_begin;
         a.table_stride = L.table_stride;
         const int64_t wg = std::min(L.tile_count, cap);
-        if (single) {
+        if (carry) {
+            hipLaunchKernelGGL(carry_kernel_for(h->fmt, L.pt, L.gt, streaming, scaled),
+                               dim3((unsigned)wg), dim3(kThreads), lds, st, a);
+        } else if (single) {
             a.tensor_begin = L.tensor_begin;
             a.tensor_count = L.tensor_count;
             a.done = reinterpret_cast<uint32_t *>(h->ws + h->wl.done) + li * kDoneWords;
@@ -726,6 +807,10 @@ int apexw_step_ex(apexw_t h, const apexw_group *groups, int32_t n_groups, void *
                                dim3(kThreads), lds, st, a);
         }
         HIP_TRY(hipGetLastError());
+    }
+    if (carry) {
+        h->carry_valid = !carry_broken;
+        h->carry_parity ^= 1;
     }
     return APEXW_OK;
 }
@@ -929,6 +1014,7 @@ int apexw_import_state(apexw_t h, const void *src_host, size_t src_bytes, apexw_
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (sb > 0) HIP_TRY(hipMemcpyAsync(h->state, p + off, (size_t)sb, hipMemcpyHostToDevice, st));
     HIP_TRY(hipStreamSynchronize(st));
+    h->carry_valid = false;                  // new counters: the carried corrections are stale
     return APEXW_OK;
 }
 
@@ -980,18 +1066,21 @@ int apexw_set_cache_policy(apexw_t h, int32_t policy) {
 
 int apexw_set_launch_mode(apexw_t h, int32_t mode) {
     if (!h) return fail(APEXW_EINVAL, "handle is NULL");
-    if (mode < 0 || mode > 2) return fail(APEXW_EINVAL, "mode must be 0, 1 or 2");
+    if (mode < 0 || mode > 3) return fail(APEXW_EINVAL, "mode must be 0, 1, 2 or 3");
     if (mode == 2 && !h->single_ok)
         return fail(APEXW_EINVAL, "the single-launch step needs a non-empty list of at most %lld "
                                   "tiles with a tile in every dtype pair it uses",
                     (long long)kSingleLaunchTiles);
+    if (mode == 3 && !h->carry_ok)
+        return fail(APEXW_EINVAL, "the carried step needs a non-empty list without empty tensors");
     h->launch_mode = mode;
+    h->carry_valid = false;                  // also: counters written by the caller are re-read
     return APEXW_OK;
 }
 
 int apexw_get_launch_mode(apexw_t h, int32_t *mode) {
     if (!h || !mode) return fail(APEXW_EINVAL, "NULL argument");
-    *mode = single_launch(h) ? 2 : 1;
+    *mode = carry_launch(h) ? 3 : single_launch(h) ? 2 : 1;
     return APEXW_OK;
 }
 

@@ -120,6 +120,18 @@ struct StepRecord {
 };
 static_assert(sizeof(StepRecord) == 64, "step record is one 64-byte record");
 
+// Bias corrections of a tensor's next step, carried from one step to the
+// next (launch mode 3): 1 - beta^(t+1) for the counter t as it stands, their
+// reciprocals and the short-division bound.  Two arrays in the workspace; a
+// step reads one and the first tile of each tensor writes the other.
+struct BiasRecord {
+    float bc1, bc2;                  // 1 - beta1^(t+1), 1 - beta2^(t+1)
+    float rbc1, rbc2;                // 1/bc1, 1/bc2 correctly rounded
+    float div_lo;                    // as in StepRecord
+    int32_t pad_[3];
+};
+static_assert(sizeof(BiasRecord) == 32, "bias record is one 32-byte record");
+
 struct KernelArgs {
     const TensorDesc *desc;
     const void *const *grads;        // grads[i] == nullptr: no grad this call
@@ -148,6 +160,8 @@ struct KernelArgs {
     int32_t pad_;
     const int32_t *tensor_list;
     uint32_t *done;                  // single-launch step: arrival counters
+    const BiasRecord *bias_cur;      // carried step: this step's bias corrections
+    BiasRecord *bias_next;           //   and the next step's (written by first tiles)
     GroupScalars groups[APEXW_MAX_GROUPS];
 };
 
@@ -671,9 +685,21 @@ __device__ __forceinline__ T load_uniform(const T *tab, int32_t i) {
     return out;
 }
 
+// Bias corrections at step count t: 1 - beta^t from fp64 square-and-multiply
+// rounded once to fp32, their correctly rounded reciprocals, and the range
+// bound of the short division by them (div_uniform).
+__device__ __forceinline__ BiasRecord bias_record(double beta1_d, double beta2_d, int32_t t) {
+    BiasRecord b = {};
+    b.bc1 = (float)(1.0 - pow_uint(beta1_d, (uint32_t)t));
+    b.bc2 = (float)(1.0 - pow_uint(beta2_d, (uint32_t)t));
+    b.rbc1 = 1.0f / b.bc1;
+    b.rbc2 = 1.0f / b.bc2;
+    b.div_lo = b.bc1 >= 0x1p-60f && b.bc2 >= 0x1p-60f ? 0x1p-100f : __builtin_inff();   // both are <= 1
+    return b;
+}
+
 // The step record of a tensor of group gi with a grad, at its advanced step
-// count t: group scalars, bias corrections 1 - beta^t from fp64
-// square-and-multiply rounded once to fp32, the grad scale factors.
+// count t: group scalars, bias corrections, the grad scale factors.
 __device__ __forceinline__ StepRecord step_record(const KernelArgs &a, int32_t gi, const void *grad,
                                                   int32_t t, float inv_scale, float clip_coef) {
     GroupScalars g;
@@ -681,6 +707,7 @@ __device__ __forceinline__ StepRecord step_record(const KernelArgs &a, int32_t g
         g = group_scalars(load_uniform(a.groups_dev, gi));
     else
         g = a.groups[gi];
+    const BiasRecord b = bias_record(g.beta1_d, g.beta2_d, t);
     StepRecord r = {};
     r.grad = grad;
     r.beta1 = g.beta1;
@@ -690,11 +717,11 @@ __device__ __forceinline__ StepRecord step_record(const KernelArgs &a, int32_t g
     r.lr = g.lr;
     r.decay = g.decay;
     r.eps = g.eps;
-    r.bc1 = (float)(1.0 - pow_uint(g.beta1_d, (uint32_t)t));
-    r.bc2 = (float)(1.0 - pow_uint(g.beta2_d, (uint32_t)t));
-    r.rbc1 = 1.0f / r.bc1;
-    r.rbc2 = 1.0f / r.bc2;
-    r.div_lo = r.bc1 >= 0x1p-60f && r.bc2 >= 0x1p-60f ? 0x1p-100f : __builtin_inff();   // both are <= 1
+    r.bc1 = b.bc1;
+    r.bc2 = b.bc2;
+    r.rbc1 = b.rbc1;
+    r.rbc2 = b.rbc2;
+    r.div_lo = b.div_lo;
     r.inv_scale = inv_scale;
     r.clip_coef = clip_coef;
     return r;
@@ -774,6 +801,96 @@ __global__ __launch_bounds__(kThreads) void adamw_step_kernel(KernelArgs a) {
         if (k >= a.tile_count) break;
         i = tile_tensor[table_pos(a, k)];
     }
+}
+
+// The carried step (launch mode 3): the whole step in one launch per dtype
+// pair at any list size, with no prepare launch and no arrival counters.
+// Every workgroup takes its tensor's bias corrections from bias_cur (formed
+// for the counter as it stands, t + 1, by the previous step or by
+// carry_init_kernel), its group's scalars from the kernel arguments and the
+// flag and scale factors from device memory.  The first tile of each tensor
+// alone reads and advances the counter (only with a grad and without
+// found_inf) and writes the corrections for the following step, at t + 2 or
+// unchanged, into bias_next; no other workgroup reads the counter, so no
+// ordering between workgroups is needed.  Results are bitwise those of the
+// other modes: the same fp64 and fp32 operations form the same scalars.
+template <int ST, int PT, int GT, bool NT, bool SC>
+__global__ __launch_bounds__(kThreads) void adamw_carry_step_kernel(KernelArgs a) {
+    const APEXW_CONST int32_t *tile_tensor = cptr<int32_t>(a.tile_tensor);
+    const float fi = *cptr<float>(a.found_inf);
+    const float inv_scale = *cptr<float>(a.inv_scale);
+    const float clip_coef = *cptr<float>(a.clip_coef);
+    int64_t k = blockIdx.x;                    // < tile_count: grid <= tiles
+    int32_t i = tile_tensor[table_pos(a, k)];
+    for (;;) {
+        const TensorDesc d = load_uniform(a.desc, i);
+        const void *g_ptr = reinterpret_cast<const void *>(cptr<uint64_t>(a.grads)[i]);
+        const BiasRecord b = load_uniform(a.bias_cur, i);
+        const int64_t base = (a.tile_begin + k - d.first_tile) * kTile;
+        const int64_t left = d.numel - base;
+        const int n = left < kTile ? (int)left : kTile;
+        // the flag goes through the asm with the metadata: its test stays in
+        // the loop, so its load completes with theirs instead of delaying the
+        // first tile-table load
+        float fl = fi;
+        asm volatile("" : "+s"(fl) : "s"(g_ptr), "s"(d.param), "s"(d.m), "s"(d.v));
+        if constexpr (ST == APEXW_STATE_Q8) asm volatile("" ::"s"(d.m_scale), "s"(d.v_scale));
+        // no grad (absent, or the step is skipped): tensor untouched
+        const void *grad = fl != 0.0f ? nullptr : g_ptr;
+        if (grad != nullptr && n > 0) {
+            const auto s = [&] {
+                const GroupScalars &G = a.groups[d.group];
+                StepScalars r;
+                r.beta1 = G.beta1;
+                r.one_minus_beta1 = G.one_minus_beta1;
+                r.beta2 = G.beta2;
+                r.one_minus_beta2 = G.one_minus_beta2;
+                r.lr = G.lr;
+                r.decay = G.decay;
+                r.eps = G.eps;
+                r.bc1 = b.bc1;
+                r.bc2 = b.bc2;
+                r.rbc1 = b.rbc1;
+                r.rbc2 = b.rbc2;
+                r.div_lo = b.div_lo;
+                r.inv_scale = inv_scale;
+                r.clip_coef = clip_coef;
+                return r;
+            };
+            if constexpr (ST == APEXW_STATE_F32)
+                tile_dense<PT, GT, APEXW_F32, NT, SC>(d, grad, base, n, s);
+            else if constexpr (ST == APEXW_STATE_BF16)
+                tile_dense<PT, GT, APEXW_BF16, NT, SC>(d, grad, base, n, s);
+            else
+                tile_q8<PT, GT, NT, SC>(d, grad, base, n, s);
+        }
+        if (base == 0 && threadIdx.x == 0) {   // the tensor's first tile
+            BiasRecord nb = b;
+            if (grad != nullptr) {
+                // (counter arithmetic wraps, as 32-bit unsigned: the
+                // corrections for a step past the int32 maximum are formed
+                // ahead of time but only used if such a step comes)
+                const uint32_t t = (uint32_t)a.steps[i] + 1u;
+                a.steps[i] = (int32_t)t;
+                const GroupScalars &G = a.groups[d.group];
+                nb = bias_record(G.beta1_d, G.beta2_d, (int32_t)(t + 1u));
+            }
+            a.bias_next[i] = nb;
+        }
+        k += gridDim.x;
+        if (k >= a.tile_count) break;
+        i = tile_tensor[table_pos(a, k)];
+    }
+}
+
+// Starts (or restarts) the carried chain: one lane per tensor writes the
+// bias corrections for its counter as it stands, t + 1, into bias_next.
+__global__ __launch_bounds__(kPrepThreads) void carry_init_kernel(KernelArgs a) {
+    const int32_t i = blockIdx.x * kPrepThreads + threadIdx.x;
+    if (i >= a.n_tensors) return;
+    const uint32_t t = (uint32_t)a.steps[i];
+    const GroupScalars &G = a.groups[a.desc[i].group];
+    a.bias_next[i] = bias_record(G.beta1_d, G.beta2_d, (int32_t)(t + 1u));
 }
 
 // Arrival counters of the single-launch step, per launch: kDoneFan

@@ -72,9 +72,9 @@ def test_random_configuration_against_oracle(seed):
     th_ref = [bits(p) for p in p_cpu]
     opt = GpuOpt(sizes, pdt, gdt, group_of, n_groups, fmt)
     try:
-        L.apexw_set_launch_mode(opt.h, int(rng.choice([0, 1, 2])))
+        L.apexw_set_launch_mode(opt.h, int(rng.choice([0, 1, 2, 3])))
     except L.ApexwError:
-        L.apexw_set_launch_mode(opt.h, 1)             # the single launch is not available
+        L.apexw_set_launch_mode(opt.h, 1)             # the single launch or carried step is not available
     L.apexw_set_cache_policy(opt.h, int(rng.choice([0, 1, 2])))
     L.apexw_set_workgroups(opt.h, int(rng.choice([0, 0, 1, 7, 64, 100])))
     ref = oracle.OracleAdamW(sizes, pdt, gdt, group_of, fmt)

@@ -39,11 +39,11 @@ def _oracle_for(w: W.Workload, idx=None, state_fmt=None):
 
 # =================================================================== tiny
 
-@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("mode", [0, 1, 2, 3])
 def test_tiny_every_call_against_oracle(mode):
     """525,315 fp32 params, 20 calls, call 7 skipped, [3] has no grad on odd
-    calls: theta, m, v and t compared after every call; the default launch
-    (one kernel for a list this small) and prepare + update."""
+    calls: theta, m, v and t compared after every call; every launch mode
+    (the default is the carried step)."""
     _need_gpu()
     w = W.tiny()
     say("case: tiny", w.describe(), "mode", mode)
@@ -52,7 +52,7 @@ def test_tiny_every_call_against_oracle(mode):
     grads = [torch.empty(s, dtype=torch.float32, device=DEV) for s in w.shapes]
     opt = GpuOpt(w.numels, w.param_dtype, w.grad_dtype, w.group_of, len(w.groups), w.state_fmt)
     L.apexw_set_launch_mode(opt.h, mode)
-    assert L.apexw_get_launch_mode(opt.h) == (2 if mode == 0 else 1)
+    assert L.apexw_get_launch_mode(opt.h) == (3 if mode == 0 else mode)
     ref = _oracle_for(w)
     th_ref = [bits(p) for p in p_cpu]
     fi = torch.zeros(1, dtype=torch.float32, device=DEV)
@@ -86,9 +86,11 @@ EDGE_SIZES = [1, 3, 5, 255, 256, 257, 1023, 4095, 4096, 4097, 8191, 12289, 0, 10
 
 
 # (cache policy, launch mode): the small list's default (cached, single
-# launch), streaming (prepare + update), cached prepare + update, and the
-# single launch forced under a streaming policy
-MODES = [(0, 0), (1, 0), (0, 1), (1, 2)]
+# launch: the list has empty tensors, so not the carried step), streaming
+# (prepare + update), cached prepare + update, the single launch forced
+# under a streaming policy, and the carried step cached and streaming (on the
+# list without its empty tensors)
+MODES = [(0, 0), (1, 0), (0, 1), (1, 2), (0, 3), (1, 3)]
 
 
 @pytest.mark.parametrize("policy,mode", MODES)
@@ -101,6 +103,8 @@ def test_ragged_mixed_dtypes_groups_and_misalignment(fmt, policy, mode):
     _need_gpu()
     say("case: ragged", fmt, "policy", policy, "mode", mode)
     sizes = EDGE_SIZES * 2
+    if mode == 3:                            # the carried step needs no empty tensor
+        sizes = [s if s else 2 for s in sizes]
     n = len(sizes)
     pdt = [(W.F32, W.BF16)[(i // 2) % 2] for i in range(n)]
     gdt = [(W.F32, W.BF16)[i % 2] for i in range(n)]
@@ -158,7 +162,7 @@ def test_ragged_mixed_dtypes_groups_and_misalignment(fmt, policy, mode):
     opt.close()
 
 
-@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("mode", [0, 1, 2])
 @pytest.mark.parametrize("fmt", [W.STATE_F32, W.STATE_BF16, W.STATE_Q8])
 def test_found_inf_leaves_everything_bitwise(fmt, mode):
     _need_gpu()
@@ -461,7 +465,7 @@ def test_large_step_counters_against_oracle(fmt):
     sizes = [1000, 4096, 77]
     t0 = [2 ** 31 - 2, 1_000_003, 12_345]
     groups = [W.Group(lr=1e-3, weight_decay=0.1, beta1=0.9, beta2=0.999999)]
-    for mode in (1, 2):
+    for mode in (1, 2, 3):
         gen = torch.Generator().manual_seed(91)
         p_cpu = [torch.randn(n, generator=gen) * 0.02 for n in sizes]
         params = [p.to(DEV) for p in p_cpu]
@@ -471,7 +475,7 @@ def test_large_step_counters_against_oracle(fmt):
         ref = oracle.OracleAdamW(sizes, [W.F32] * 3, [W.F32] * 3, [0, 0, 0], fmt)
         opt.steps().copy_(torch.tensor(t0, dtype=torch.int32))
         ref.t[:3] = t0
-        for k in range(2 if mode == 1 else 1):
+        for k in range(1 if mode == 2 else 2):
             g_cpu = [torch.randn(n, generator=gen) * 1e-3 for n in sizes]
             if k == 1:                              # t[0] is at the int32 maximum now
                 g_cpu[0] = None
@@ -564,7 +568,7 @@ def test_all_grads_absent_and_pointer_changes():
 
 @pytest.mark.parametrize("fmt", [W.STATE_F32, W.STATE_BF16, W.STATE_Q8])
 @pytest.mark.parametrize("wg,mode", [(1, 2), (7, 2), (63, 2), (64, 2), (65, 2), (300, 2), (0, 2),
-                                     (1, 1), (300, 1)])
+                                     (1, 1), (300, 1), (1, 3), (7, 3), (300, 3), (0, 3)])
 def test_results_do_not_depend_on_grid(wg, mode, fmt):
     """Workgroup caps (a workgroup then walks several tiles) in both launch
     modes -- for the single launch, caps below, at and above the 64 counters
@@ -856,3 +860,75 @@ def test_maximum_size_tensor_past_int32(fmt):
     opt.close()
     del theta, grad
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("fmt", [W.STATE_F32, W.STATE_Q8])
+def test_carried_step_restarts(fmt):
+    """The carried step (the default launch mode) over 12 calls of a two-launch
+    list, checked against the oracle after every call, through every event
+    that starts its chain of bias corrections again or must leave it intact:
+    a skipped call, a changed beta2, a switch to prepare + update and back,
+    one dtype pair without any grad, step counters written by the caller
+    followed by apexw_set_launch_mode, a call with no grad at all, and an
+    import of a state exported five calls earlier."""
+    _need_gpu()
+    say("case: carried step restarts", fmt)
+    sizes = [3000, 257, 4096, 1000, 513]
+    pdt = [W.F32, W.F32, W.F32, W.BF16, W.BF16]
+    gdt = [W.F32, W.F32, W.F32, W.BF16, W.BF16]
+    group_of = [0, 1, 0, 1, 0]
+    gen = torch.Generator().manual_seed(57)
+    p_cpu = [(torch.randn(s, generator=gen) * 0.02).to(W.TORCH_DTYPE[d]) for s, d in zip(sizes, pdt)]
+    params = [p.to(DEV) for p in p_cpu]
+    th_ref = [bits(p) for p in p_cpu]
+    opt = GpuOpt(sizes, pdt, gdt, group_of, 2, fmt)
+    assert L.apexw_get_launch_mode(opt.h) == 3
+    ref = oracle.OracleAdamW(sizes, pdt, gdt, group_of, fmt)
+    fi = torch.zeros(1, device=DEV)
+    blob = snap = None
+    for k in range(1, 13):
+        beta2 = 0.99 if k < 4 else 0.995
+        groups = [W.Group(lr=1e-3, weight_decay=0.1), W.Group(lr=5e-4, beta1=0.8, beta2=beta2)]
+        g_cpu = [(torch.randn(s, generator=gen) * 1e-3).to(W.TORCH_DTYPE[d]) for s, d in zip(sizes, gdt)]
+        present = [True] * len(sizes)
+        if k == 8:
+            present[3] = present[4] = False          # the bf16 launch has nothing to do
+        if k == 10:
+            present = [False] * len(sizes)
+        if k == 6:
+            L.apexw_set_launch_mode(opt.h, 1)
+        if k == 7:
+            L.apexw_set_launch_mode(opt.h, 3)
+        if k == 9:                                   # counters rewritten by the caller
+            torch.cuda.synchronize()
+            opt.steps().add_(5)
+            ref.t[:len(sizes)] += 5
+            L.apexw_set_launch_mode(opt.h, 0)
+        if k == 11:
+            L.apexw_import_state(opt.h, blob, 2, opt.stream)
+            ref.t, ref.m, ref.v, ref.m_scale, ref.v_scale = snap
+            snap = None
+        skip = k == 3
+        fi.fill_(1.0 if skip else 0.0)
+        opt.step(groups, params, [g.to(DEV) if ok else None for g, ok in zip(g_cpu, present)],
+                 found_inf=fi)
+        ref.step(th_ref, [bits(g) if ok else None for g, ok in zip(g_cpu, present)], groups,
+                 found_inf=skip)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(opt.steps()), ref.t), (k, bits(opt.steps()), ref.t)
+        for i in range(len(sizes)):
+            assert n_bit_mismatch(bits(params[i]), th_ref[i]) == 0, (k, i)
+            m, v = opt.moments(i)
+            assert n_bit_mismatch(bits(m), ref.m[i]) == 0, (k, i)
+            assert n_bit_mismatch(bits(v), ref.v[i]) == 0, (k, i)
+            if fmt == W.STATE_Q8:
+                ms, vs = opt.scales(i)
+                assert n_bit_mismatch(bits(ms), ref.m_scale[i]) == 0, (k, i)
+                assert n_bit_mismatch(bits(vs), ref.v_scale[i]) == 0, (k, i)
+        if k == 5:
+            blob = L.apexw_export_state(opt.h, L.make_groups(groups), 2, opt.stream)
+            snap = (ref.t.copy(), [a.copy() for a in ref.m], [a.copy() for a in ref.v],
+                    [None if a is None else a.copy() for a in ref.m_scale],
+                    [None if a is None else a.copy() for a in ref.v_scale])
+    assert list(ref.t) == [6, 6, 6, 6, 6]      # call 5 left t = 4; calls 11 and 12 follow the import
+    opt.close()
