@@ -426,9 +426,15 @@ bool streams(const apexw_opt *h) {
 
 // The carried step: forced, or by default for every list without an empty
 // tensor (steps with hyperparameters in device memory and steps being
-// captured into a graph take another mode).
+// captured into a graph take another mode) -- except 8-bit lists that
+// stream: there the carried kernel runs about 7% longer than the plain
+// update kernel (measured on MI355X, the 392-tensor LoRA list: 52.8 against
+// 51.1 us per step), more than the prepare launch it saves, and the gap
+// grows with the list.
 bool carry_launch(const apexw_opt *h) {
-    return h->carry_ok && (h->launch_mode == 3 || h->launch_mode == 0);
+    return h->carry_ok &&
+           (h->launch_mode == 3 ||
+            (h->launch_mode == 0 && !(h->fmt == APEXW_STATE_Q8 && streams(h))));
 }
 
 // The single launch: forced, or by default for the lists it is made for

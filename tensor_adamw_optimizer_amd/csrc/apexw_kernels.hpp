@@ -809,11 +809,12 @@ __global__ __launch_bounds__(kThreads) void adamw_step_kernel(KernelArgs a) {
 // for the counter as it stands, t + 1, by the previous step or by
 // carry_init_kernel), its group's scalars from the kernel arguments and the
 // flag and scale factors from device memory.  The first tile of each tensor
-// alone reads and advances the counter (only with a grad and without
-// found_inf) and writes the corrections for the following step, at t + 2 or
-// unchanged, into bias_next; no other workgroup reads the counter, so no
-// ordering between workgroups is needed.  Results are bitwise those of the
-// other modes: the same fp64 and fp32 operations form the same scalars.
+// alone advances the counter (only with a grad and without found_inf) and
+// writes the corrections for the following step, at t + 2 or unchanged, into
+// bias_next; no other workgroup uses the counter (every workgroup loads it
+// with the metadata, only the first tile's value counts), so no ordering
+// between workgroups is needed.  Results are bitwise those of the other
+// modes: the same fp64 and fp32 operations form the same scalars.
 template <int ST, int PT, int GT, bool NT, bool SC>
 __global__ __launch_bounds__(kThreads) void adamw_carry_step_kernel(KernelArgs a) {
     const APEXW_CONST int32_t *tile_tensor = cptr<int32_t>(a.tile_tensor);
@@ -826,20 +827,36 @@ __global__ __launch_bounds__(kThreads) void adamw_carry_step_kernel(KernelArgs a
         const TensorDesc d = load_uniform(a.desc, i);
         const void *g_ptr = reinterpret_cast<const void *>(cptr<uint64_t>(a.grads)[i]);
         const BiasRecord b = load_uniform(a.bias_cur, i);
+        // the counter, read with the metadata (dense formats; only the first
+        // tile of the tensor uses it, and writes it below, alone)
+        const int32_t t_old = cptr<int32_t>(a.steps)[i];
         const int64_t base = (a.tile_begin + k - d.first_tile) * kTile;
         const int64_t left = d.numel - base;
         const int n = left < kTile ? (int)left : kTile;
+        const bool first = base == 0;
         // the flag goes through the asm with the metadata: its test stays in
         // the loop, so its load completes with theirs instead of delaying the
         // first tile-table load
         float fl = fi;
-        asm volatile("" : "+s"(fl) : "s"(g_ptr), "s"(d.param), "s"(d.m), "s"(d.v));
+        asm volatile("" : "+s"(fl) : "s"(g_ptr), "s"(d.param), "s"(d.m), "s"(d.v), "s"(d.group));
         if constexpr (ST == APEXW_STATE_Q8) asm volatile("" ::"s"(d.m_scale), "s"(d.v_scale));
+        else asm volatile("" ::"s"(t_old));
         // no grad (absent, or the step is skipped): tensor untouched
         const void *grad = fl != 0.0f ? nullptr : g_ptr;
+        BiasRecord nb = b;                     // a tensor that does not advance keeps them
+        // (counter arithmetic wraps, as 32-bit unsigned: the corrections for
+        // a step past the int32 maximum are formed ahead of time but only
+        // used if such a step comes)
+        const uint32_t t_new = (uint32_t)t_old + 1u;
         if (grad != nullptr && n > 0) {
             const auto s = [&] {
                 const GroupScalars &G = a.groups[d.group];
+                // dense formats: the first tile forms the next step's
+                // corrections here, while the tile's loads are in flight (the
+                // VALU-bound 8-bit update measured faster with them formed
+                // after the tile, below)
+                if constexpr (ST != APEXW_STATE_Q8)
+                    if (first) nb = bias_record(G.beta1_d, G.beta2_d, (int32_t)(t_new + 1u));
                 StepScalars r;
                 r.beta1 = G.beta1;
                 r.one_minus_beta1 = G.one_minus_beta1;
@@ -864,16 +881,16 @@ __global__ __launch_bounds__(kThreads) void adamw_carry_step_kernel(KernelArgs a
             else
                 tile_q8<PT, GT, NT, SC>(d, grad, base, n, s);
         }
-        if (base == 0 && threadIdx.x == 0) {   // the tensor's first tile
-            BiasRecord nb = b;
-            if (grad != nullptr) {
-                // (counter arithmetic wraps, as 32-bit unsigned: the
-                // corrections for a step past the int32 maximum are formed
-                // ahead of time but only used if such a step comes)
-                const uint32_t t = (uint32_t)a.steps[i] + 1u;
-                a.steps[i] = (int32_t)t;
-                const GroupScalars &G = a.groups[d.group];
-                nb = bias_record(G.beta1_d, G.beta2_d, (int32_t)(t + 1u));
+        if (first && threadIdx.x == 0) {       // the tensor's first tile
+            if constexpr (ST == APEXW_STATE_Q8) {
+                if (grad != nullptr) {
+                    const uint32_t t1 = (uint32_t)a.steps[i] + 1u;
+                    a.steps[i] = (int32_t)t1;
+                    const GroupScalars &G = a.groups[d.group];
+                    nb = bias_record(G.beta1_d, G.beta2_d, (int32_t)(t1 + 1u));
+                }
+            } else if (grad != nullptr) {
+                a.steps[i] = (int32_t)t_new;
             }
             a.bias_next[i] = nb;
         }
