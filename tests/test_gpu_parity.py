@@ -932,3 +932,36 @@ def test_carried_step_restarts(fmt):
                     [None if a is None else a.copy() for a in ref.v_scale])
     assert list(ref.t) == [6, 6, 6, 6, 6]      # call 5 left t = 4; calls 11 and 12 follow the import
     opt.close()
+
+
+def test_launch_mode_choice():
+    """Which mode a step takes: the carried step needs a list without empty
+    tensors (APEXW_EINVAL when forced otherwise, and the default falls back
+    to the single launch); an 8-bit list that streams defaults to prepare +
+    update, a small 8-bit list to the carried step; every call of
+    apexw_set_launch_mode keeps the mode it was given."""
+    _need_gpu()
+    say("case: launch mode choice")
+    opt = GpuOpt([1000, 0, 77], [W.F32] * 3, [W.F32] * 3, [0, 0, 0], 1, W.STATE_F32)
+    assert L.apexw_get_launch_mode(opt.h) == 2
+    with pytest.raises(L.ApexwError) as e:
+        L.apexw_set_launch_mode(opt.h, 3)
+    assert e.value.code == L.APEXW_EINVAL
+    assert L.apexw_get_launch_mode(opt.h) == 2
+    opt.close()
+    small = GpuOpt([4096, 300], [W.BF16] * 2, [W.BF16] * 2, [0, 0], 1, W.STATE_Q8)
+    assert L.apexw_get_launch_mode(small.h) == 3
+    L.apexw_set_cache_policy(small.h, 1)             # streaming: as a large 8-bit list
+    assert L.apexw_get_launch_mode(small.h) == 1
+    L.apexw_set_launch_mode(small.h, 3)
+    assert L.apexw_get_launch_mode(small.h) == 3
+    L.apexw_set_launch_mode(small.h, 2)
+    assert L.apexw_get_launch_mode(small.h) == 2
+    small.close()
+    w = W.lora_q8()
+    big = GpuOpt(w.numels, w.param_dtype, w.grad_dtype, w.group_of, len(w.groups), w.state_fmt)
+    assert L.apexw_get_launch_mode(big.h) == 1       # 146 MB per step: streams
+    big.close()
+    fl = GpuOpt([1 << 22] * 4, [W.BF16] * 4, [W.F32] * 4, [0] * 4, 1, W.STATE_F32)
+    assert L.apexw_get_launch_mode(fl.h) == 3        # streams too, dense moments
+    fl.close()
