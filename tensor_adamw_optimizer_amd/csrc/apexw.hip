@@ -771,6 +771,7 @@ int apexw_step_ex(apexw_t h, const apexw_group *groups, int32_t n_groups, void *
                 h->carry_beta2[(size_t)g] = groups[g].beta2;
             }
         }
+        h->carry_valid = false;               // until every launch of the step is queued
     } else if (single) {
         a.tensor_list = reinterpret_cast<const int32_t *>(h->ws + h->wl.tensors);
     } else {

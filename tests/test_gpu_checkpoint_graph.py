@@ -199,3 +199,62 @@ def test_graph_capture_replays_match_oracle(fmt, mode):
                                     torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     opt.close()
+
+
+@pytest.mark.parametrize("fmt", [W.STATE_F32, W.STATE_Q8])
+def test_capture_between_carried_steps(fmt):
+    """Eager steps in the default (carried) mode, then a plain apexw_step
+    (hyperparameters from the host) captured into a graph -- the capture takes
+    the single launch, not the carried step -- replayed 3 times, which
+    advances the counters with no host call, then eager carried steps again:
+    they must restart their chain from the counters as the replays left
+    them.  Every call is checked against the oracle."""
+    say("case: capture between carried steps", fmt)
+    p_cpu, gs = _inputs(41, 10)
+    params = [p.to(DEV) for p in p_cpu]
+    grads = [g.to(DEV) for g in gs[0]]
+    opt = GpuOpt(SIZES, PDT, GDT, GROUP_OF, 2, fmt)
+    assert L.apexw_get_launch_mode(opt.h) == 3
+    ref = oracle.OracleAdamW(SIZES, PDT, GDT, GROUP_OF, fmt)
+    th_ref = [bits(p) for p in p_cpu]
+    pa = L.make_ptrs([p.data_ptr() for p in params])
+    ga = L.make_ptrs([g.data_ptr() for g in grads])
+    groups = L.make_groups(GROUPS)
+
+    def check(k):
+        assert np.array_equal(bits(opt.steps()), ref.t), k
+        for i in range(len(SIZES)):
+            assert n_bit_mismatch(bits(params[i]), th_ref[i]) == 0, (k, i)
+            m, v = opt.moments(i)
+            assert n_bit_mismatch(bits(m), ref.m[i]) == 0 and n_bit_mismatch(bits(v), ref.v[i]) == 0, (k, i)
+
+    def eager(k):
+        for g, x in zip(grads, gs[k]):
+            g.copy_(x.to(DEV))
+        L.apexw_step(opt.h, groups, 2, pa, ga, 0, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        ref.step(th_ref, [bits(x) for x in gs[k]], GROUPS)
+        check(k)
+
+    for k in range(3):
+        eager(k)
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            L.apexw_step(opt.h, groups, 2, pa, ga, 0, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    check("after capture")                            # capture ran nothing
+    for k in range(3, 6):
+        for g, x in zip(grads, gs[k]):
+            g.copy_(x.to(DEV))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref.step(th_ref, [bits(x) for x in gs[k]], GROUPS)
+        check(k)
+    for k in range(6, 10):
+        eager(k)
+    assert list(ref.t) == [10] * len(SIZES)
+    opt.close()
