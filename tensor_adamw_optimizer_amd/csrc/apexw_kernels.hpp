@@ -68,7 +68,11 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // compiler use scalar loads (scalar cache) for these wave-uniform values.
 // (The single-launch kernel also reads the step counters that way; its last
 // workgroup writes them only after every workgroup has read them, through a
-// generic pointer.)
+// generic pointer.  In the carried step every workgroup loads its tensor's
+// counter that way too, but only the tensor's first tile uses the value, and
+// that tile writes the counter after its own read, which the written value
+// depends on; the carried bias corrections are read from one array and
+// written to the other, so no workgroup reads what this launch writes.)
 #define APEXW_GLOBAL __attribute__((address_space(1)))
 #define APEXW_CONST __attribute__((address_space(4)))
 
