@@ -258,3 +258,40 @@ def test_capture_between_carried_steps(fmt):
         eager(k)
     assert list(ref.t) == [10] * len(SIZES)
     opt.close()
+
+
+@pytest.mark.parametrize("fmt", [W.STATE_F32, W.STATE_BF16, W.STATE_Q8])
+def test_carried_step_with_device_hyperparameters_in_between(fmt):
+    """The carried step forced (mode 3), with steps whose hyperparameters live
+    in device memory mixed in (they take another mode and drop the carried
+    corrections; the next host step starts them again), betas changing on
+    the device-side calls: 10 calls, each checked against the oracle."""
+    say("case: carried step and device hyperparameters", fmt)
+    p_cpu, gs = _inputs(43, 10)
+    params = [p.to(DEV) for p in p_cpu]
+    opt = GpuOpt(SIZES, PDT, GDT, GROUP_OF, 2, fmt)
+    L.apexw_set_launch_mode(opt.h, 3)
+    ref = oracle.OracleAdamW(SIZES, PDT, GDT, GROUP_OF, fmt)
+    th_ref = [bits(p) for p in p_cpu]
+    pa = L.make_ptrs([p.data_ptr() for p in params])
+    st = torch.cuda.current_stream().cuda_stream
+    for k in range(10):
+        device_call = k in (2, 3, 6)
+        groups = GROUPS if not device_call else \
+            [W.Group(lr=2e-3, weight_decay=0.1, beta2=0.99), W.Group(lr=4e-4, beta1=0.85, eps=1e-6)]
+        g_dev = [g.to(DEV) for g in gs[k]]
+        ga = L.make_ptrs([g.data_ptr() for g in g_dev])
+        if device_call:
+            table = _group_table(groups)
+            L.apexw_step_device(opt.h, table.data_ptr(), 2, pa, ga, 0, 0, st)
+        else:
+            L.apexw_step(opt.h, L.make_groups(groups), 2, pa, ga, 0, st)
+        torch.cuda.synchronize()
+        ref.step(th_ref, [bits(g) for g in gs[k]], groups)
+        assert np.array_equal(bits(opt.steps()), ref.t), k
+        for i in range(len(SIZES)):
+            assert n_bit_mismatch(bits(params[i]), th_ref[i]) == 0, (k, i)
+            m, v = opt.moments(i)
+            assert n_bit_mismatch(bits(m), ref.m[i]) == 0 and n_bit_mismatch(bits(v), ref.v[i]) == 0, (k, i)
+    assert L.apexw_get_launch_mode(opt.h) == 3
+    opt.close()
