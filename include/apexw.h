@@ -382,10 +382,8 @@ int apexw_set_cache_policy(apexw_t h, int32_t policy);
  * one queued while its stream is being captured into a graph (a replay would
  * not move the chain on), takes mode 2 or 1 as mode 0 would without mode 3.
  * Mode 3 needs a non-empty list without empty tensors; APEXW_EINVAL
- * otherwise.  0 (default): mode 3 for such lists (but not for APEXW_STATE_Q8
- * lists that stream, whose carried kernel runs longer than the prepare
- * launch it saves), else mode 2 for lists it takes unless they stream
- * (apexw_set_cache_policy), else mode 1.  Results do
+ * otherwise.  0 (default): mode 3 for such lists, else mode 2 for lists it
+ * takes unless they stream (apexw_set_cache_policy), else mode 1.  Results do
  * not depend on the mode; steps of one handle queued on two streams at once
  * race in every mode.  Every call drops the carried corrections (so a caller
  * that wrote step counters into the state buffer calls it before the next

@@ -239,10 +239,18 @@ kernel_fn pick_carry(int pt, int gt) {
 }
 
 template <bool NT, bool SC>
+kernel_fn pick_carry_q8(int pt, int gt) {
+    if (pt == APEXW_F32 && gt == APEXW_F32) return adamw_carry_step_q8_kernel<APEXW_F32, APEXW_F32, NT, SC>;
+    if (pt == APEXW_F32 && gt == APEXW_BF16) return adamw_carry_step_q8_kernel<APEXW_F32, APEXW_BF16, NT, SC>;
+    if (pt == APEXW_BF16 && gt == APEXW_F32) return adamw_carry_step_q8_kernel<APEXW_BF16, APEXW_F32, NT, SC>;
+    return adamw_carry_step_q8_kernel<APEXW_BF16, APEXW_BF16, NT, SC>;
+}
+
+template <bool NT, bool SC>
 kernel_fn pick_carry_format(int fmt, int pt, int gt) {
     if (fmt == APEXW_STATE_F32) return pick_carry<APEXW_STATE_F32, NT, SC>(pt, gt);
     if (fmt == APEXW_STATE_BF16) return pick_carry<APEXW_STATE_BF16, NT, SC>(pt, gt);
-    return pick_carry<APEXW_STATE_Q8, NT, SC>(pt, gt);
+    return pick_carry_q8<NT, SC>(pt, gt);
 }
 
 // The carried-step kernel (launch mode 3).
@@ -426,15 +434,9 @@ bool streams(const apexw_opt *h) {
 
 // The carried step: forced, or by default for every list without an empty
 // tensor (steps with hyperparameters in device memory and steps being
-// captured into a graph take another mode) -- except 8-bit lists that
-// stream: there the carried kernel runs about 7% longer than the plain
-// update kernel (measured on MI355X, the 392-tensor LoRA list: 52.8 against
-// 51.1 us per step), more than the prepare launch it saves, and the gap
-// grows with the list.
+// captured into a graph take another mode).
 bool carry_launch(const apexw_opt *h) {
-    return h->carry_ok &&
-           (h->launch_mode == 3 ||
-            (h->launch_mode == 0 && !(h->fmt == APEXW_STATE_Q8 && streams(h))));
+    return h->carry_ok && (h->launch_mode == 3 || h->launch_mode == 0);
 }
 
 // The single launch: forced, or by default for the lists it is made for

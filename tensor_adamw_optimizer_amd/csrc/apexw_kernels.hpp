@@ -820,7 +820,7 @@ __global__ __launch_bounds__(kThreads) void adamw_step_kernel(KernelArgs a) {
 // between workgroups is needed.  Results are bitwise those of the other
 // modes: the same fp64 and fp32 operations form the same scalars.
 template <int ST, int PT, int GT, bool NT, bool SC>
-__global__ __launch_bounds__(kThreads) void adamw_carry_step_kernel(KernelArgs a) {
+__device__ __forceinline__ void carry_step(const KernelArgs &a) {
     const APEXW_CONST int32_t *tile_tensor = cptr<int32_t>(a.tile_tensor);
     const float fi = *cptr<float>(a.found_inf);
     const float inv_scale = *cptr<float>(a.inv_scale);
@@ -902,6 +902,25 @@ __global__ __launch_bounds__(kThreads) void adamw_carry_step_kernel(KernelArgs a
         if (k >= a.tile_count) break;
         i = tile_tensor[table_pos(a, k)];
     }
+}
+
+template <int ST, int PT, int GT, bool NT, bool SC>
+__global__ __launch_bounds__(kThreads) void adamw_carry_step_kernel(KernelArgs a) {
+    carry_step<ST, PT, GT, NT, SC>(a);
+}
+
+// The 8-bit carried step under a budget of 80 scalar registers (the
+// compiler otherwise takes 93).  The 8-bit update is VALU-bound and wants
+// every wave the SIMDs can hold; at 93 SGPRs it measured 11% fewer waves
+// in flight on MI355X, although the compiler counts 8 waves per SIMD either
+// way, and ran 4-5% slower than at 78 (LoRA list, 53.7-54.5 against
+// 51.3-51.8 us per step).  The dense formats keep their allocation (their
+// residency is capped lower, and the budget's register moves cost bf16
+// moments 1%).
+template <int PT, int GT, bool NT, bool SC>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_num_sgpr(80)))
+void adamw_carry_step_q8_kernel(KernelArgs a) {
+    carry_step<APEXW_STATE_Q8, PT, GT, NT, SC>(a);
 }
 
 // Starts (or restarts) the carried chain: one lane per tensor writes the

@@ -937,9 +937,8 @@ def test_carried_step_restarts(fmt):
 def test_launch_mode_choice():
     """Which mode a step takes: the carried step needs a list without empty
     tensors (APEXW_EINVAL when forced otherwise, and the default falls back
-    to the single launch); an 8-bit list that streams defaults to prepare +
-    update, a small 8-bit list to the carried step; every call of
-    apexw_set_launch_mode keeps the mode it was given."""
+    to the single launch); every list without one defaults to it, 8-bit or
+    dense, small or streamed; forced modes are kept."""
     _need_gpu()
     say("case: launch mode choice")
     opt = GpuOpt([1000, 0, 77], [W.F32] * 3, [W.F32] * 3, [0, 0, 0], 1, W.STATE_F32)
@@ -951,16 +950,16 @@ def test_launch_mode_choice():
     opt.close()
     small = GpuOpt([4096, 300], [W.BF16] * 2, [W.BF16] * 2, [0, 0], 1, W.STATE_Q8)
     assert L.apexw_get_launch_mode(small.h) == 3
-    L.apexw_set_cache_policy(small.h, 1)             # streaming: as a large 8-bit list
-    assert L.apexw_get_launch_mode(small.h) == 1
-    L.apexw_set_launch_mode(small.h, 3)
+    L.apexw_set_cache_policy(small.h, 1)             # streaming
     assert L.apexw_get_launch_mode(small.h) == 3
+    L.apexw_set_launch_mode(small.h, 1)
+    assert L.apexw_get_launch_mode(small.h) == 1
     L.apexw_set_launch_mode(small.h, 2)
     assert L.apexw_get_launch_mode(small.h) == 2
     small.close()
     w = W.lora_q8()
     big = GpuOpt(w.numels, w.param_dtype, w.grad_dtype, w.group_of, len(w.groups), w.state_fmt)
-    assert L.apexw_get_launch_mode(big.h) == 1       # 146 MB per step: streams
+    assert L.apexw_get_launch_mode(big.h) == 3       # 146 MB per step: streams
     big.close()
     fl = GpuOpt([1 << 22] * 4, [W.BF16] * 4, [W.F32] * 4, [0] * 4, 1, W.STATE_F32)
     assert L.apexw_get_launch_mode(fl.h) == 3        # streams too, dense moments
