@@ -52,50 +52,55 @@ def build(force: bool = False) -> str:
 _lib = None
 
 
+def load(path: str) -> ctypes.CDLL:
+    """Open a build of the oracle at ``path`` and declare its signatures."""
+    L = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    L.oracle_bf16_to_f32.restype = ctypes.c_float
+    L.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
+    L.oracle_f32_to_bf16.restype = ctypes.c_uint16
+    L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
+    L.oracle_f32_to_bf16_array.restype = None
+    L.oracle_f32_to_bf16_array.argtypes = [ctypes.c_int64, P, P]
+    L.oracle_pow_int.restype = ctypes.c_double
+    L.oracle_pow_int.argtypes = [ctypes.c_double, ctypes.c_int32]
+    for name in ("oracle_quantize_signed", "oracle_quantize_unsigned"):
+        getattr(L, name).restype = None
+        getattr(L, name).argtypes = [ctypes.c_int64, P, P, P]
+    for name in ("oracle_dequantize_signed", "oracle_dequantize_unsigned"):
+        getattr(L, name).restype = None
+        getattr(L, name).argtypes = [ctypes.c_int64, P, ctypes.c_float, P]
+    L.oracle_adamw_step.restype = ctypes.c_int32
+    L.oracle_adamw_step.argtypes = [
+        ctypes.c_int32, P, P, P, P, P, P, P, ctypes.c_int32, ctypes.c_int32,
+        P, P, P, P, P, ctypes.c_int32]
+    L.oracle_adamw_step_scaled.restype = ctypes.c_int32
+    L.oracle_adamw_step_scaled.argtypes = [
+        ctypes.c_int32, P, P, P, P, P, P, P, ctypes.c_int32, ctypes.c_int32,
+        P, P, P, P, P, ctypes.c_float, ctypes.c_int32]
+    L.oracle_adamw_step_clipped.restype = ctypes.c_int32
+    L.oracle_adamw_step_clipped.argtypes = [
+        ctypes.c_int32, P, P, P, P, P, P, P, ctypes.c_int32, ctypes.c_int32,
+        P, P, P, P, P, ctypes.c_float, ctypes.c_float, ctypes.c_int32]
+    L.oracle_grad_norm.restype = ctypes.c_double
+    L.oracle_grad_norm.argtypes = [ctypes.c_int32, P, P, P, ctypes.c_float]
+    L.oracle_clip_coef.restype = ctypes.c_float
+    L.oracle_clip_coef.argtypes = [ctypes.c_double, ctypes.c_double]
+    L.oracle_unscale_check.restype = ctypes.c_int32
+    L.oracle_unscale_check.argtypes = [ctypes.c_int32, P, P, P, ctypes.c_float]
+    L.oracle_adamw_step_three_loops.restype = ctypes.c_int32
+    L.oracle_adamw_step_three_loops.argtypes = [
+        ctypes.c_int32, P, P, P, P, P, ctypes.c_int32, P, P, P,
+        ctypes.c_int32]
+    return L
+
+
 def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             build()
-        L = ctypes.CDLL(LIB_PATH)
-        P = ctypes.c_void_p
-        L.oracle_bf16_to_f32.restype = ctypes.c_float
-        L.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
-        L.oracle_f32_to_bf16.restype = ctypes.c_uint16
-        L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
-        L.oracle_f32_to_bf16_array.restype = None
-        L.oracle_f32_to_bf16_array.argtypes = [ctypes.c_int64, P, P]
-        L.oracle_pow_int.restype = ctypes.c_double
-        L.oracle_pow_int.argtypes = [ctypes.c_double, ctypes.c_int32]
-        for name in ("oracle_quantize_signed", "oracle_quantize_unsigned"):
-            getattr(L, name).restype = None
-            getattr(L, name).argtypes = [ctypes.c_int64, P, P, P]
-        for name in ("oracle_dequantize_signed", "oracle_dequantize_unsigned"):
-            getattr(L, name).restype = None
-            getattr(L, name).argtypes = [ctypes.c_int64, P, ctypes.c_float, P]
-        L.oracle_adamw_step.restype = ctypes.c_int32
-        L.oracle_adamw_step.argtypes = [
-            ctypes.c_int32, P, P, P, P, P, P, P, ctypes.c_int32, ctypes.c_int32,
-            P, P, P, P, P, ctypes.c_int32]
-        L.oracle_adamw_step_scaled.restype = ctypes.c_int32
-        L.oracle_adamw_step_scaled.argtypes = [
-            ctypes.c_int32, P, P, P, P, P, P, P, ctypes.c_int32, ctypes.c_int32,
-            P, P, P, P, P, ctypes.c_float, ctypes.c_int32]
-        L.oracle_adamw_step_clipped.restype = ctypes.c_int32
-        L.oracle_adamw_step_clipped.argtypes = [
-            ctypes.c_int32, P, P, P, P, P, P, P, ctypes.c_int32, ctypes.c_int32,
-            P, P, P, P, P, ctypes.c_float, ctypes.c_float, ctypes.c_int32]
-        L.oracle_grad_norm.restype = ctypes.c_double
-        L.oracle_grad_norm.argtypes = [ctypes.c_int32, P, P, P, ctypes.c_float]
-        L.oracle_clip_coef.restype = ctypes.c_float
-        L.oracle_clip_coef.argtypes = [ctypes.c_double, ctypes.c_double]
-        L.oracle_unscale_check.restype = ctypes.c_int32
-        L.oracle_unscale_check.argtypes = [ctypes.c_int32, P, P, P, ctypes.c_float]
-        L.oracle_adamw_step_three_loops.restype = ctypes.c_int32
-        L.oracle_adamw_step_three_loops.argtypes = [
-            ctypes.c_int32, P, P, P, P, P, ctypes.c_int32, P, P, P,
-            ctypes.c_int32]
-        _lib = L
+        _lib = load(LIB_PATH)
     return _lib
 
 

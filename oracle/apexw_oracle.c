@@ -21,12 +21,13 @@
  *
  * Readings of points the pages leave open (each is listed in the design
  * notes of the repository):
- *   R1  Arithmetic is fp32 with every operation rounded, in the order the
- *       update box of [M041 §02] prints it, left to right:
- *         m = beta1*m + (1-beta1)*g
- *         v = beta2*v + ((1-beta2)*g)*g
- *         m_hat = m / (1-beta1^t);  v_hat = v / (1-beta2^t)
- *         theta = theta*(1-lr*wd) - (lr*m_hat) / (sqrt(v_hat) + eps)
+ *   R1  Arithmetic is fp32 with every operation separately rounded.  The
+ *       update box of [M041 §02] is written in Python, and its own operator
+ *       rules fix the order: equal-precedence operators group from the left
+ *       and products and quotients bind tighter than sums.  So the new v adds
+ *       beta2*v to ((1-beta2)*g)*g, and the step of theta is the product
+ *       lr*m_hat divided by (sqrt(v_hat)+eps), subtracted from
+ *       theta*(1-lr*wd).  No multiply-add is contracted.
  *   R2  Scalar coefficients (1-beta1), (1-beta2), (1-lr*wd), lr, eps, beta1,
  *       beta2 are formed in fp64 from the fp64 hyperparameters and rounded
  *       once to fp32.  beta^t is fp64 square-and-multiply over the bits of t
@@ -106,9 +107,11 @@ double oracle_pow_int(double base, int32_t e)
 
 /* ------------------------------------------------------------ quantizer */
 
-/* [M041 §05] teaching signed block quantizer:
- *   scale = max(abs(x)) / 127;  q = round(x / scale);  x ~ q * scale
- * with the all-zero block handled on its own (scale 0, codes 0). */
+/* [M041 §05] block quantizer for a signed moment: the block's scale is its
+ * largest magnitude over 127, each code is the value over the scale rounded
+ * half to even (clamped to +-127), and decoding multiplies code by scale.  A
+ * block whose values are all zero gets scale 0 and codes 0, the case the
+ * section says is handled on its own. */
 void oracle_quantize_signed(int64_t n, const float *x, int8_t *q, float *scale)
 {
     float amax = 0.0f;

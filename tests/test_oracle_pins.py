@@ -302,6 +302,31 @@ def test_bf16_rounding_matches_torch():
     assert np.array_equal(back.view(np.uint32), ref_back.view(np.uint32))
 
 
+def test_bf16_rounding_of_nans():
+    """A NaN stays a NaN (torch agrees on the class; a signalling NaN whose
+    payload sits in the low 16 bits must not round up into an infinity), comes
+    out quiet (IEEE 754, section 6.2: an operation on a signalling NaN delivers
+    a quiet one), and keeps its sign and the top 7 bits of its payload."""
+    rng = np.random.default_rng(14)
+    sign = rng.integers(0, 2, 4000).astype(np.uint32) << 31
+    payload = rng.integers(1, 1 << 23, 4000).astype(np.uint32)
+    payload[:500] &= 0xFFFF                                    # low payload only
+    payload[:500] |= 1
+    payload[500:1000] |= 0x400000                              # already quiet
+    bits = sign | 0x7F800000 | payload
+    x = bits.view(np.float32)
+    assert np.isnan(x).all()
+    ours = oracle.f32_to_bf16(x)
+    theirs = torch.from_numpy(x.copy()).to(torch.bfloat16).float().numpy()
+    assert np.isnan(theirs).all()
+    wide = oracle.bf16_to_f32(ours)
+    assert np.isnan(wide).all()
+    assert np.all((ours & 0x7F80) == 0x7F80)                   # exponent all ones
+    assert np.all(ours & 0x0040)                               # quiet bit
+    assert np.array_equal(ours >> 15, (bits >> 31).astype(np.uint16))
+    assert np.array_equal(ours & 0x3F, ((bits >> 16) & 0x3F).astype(np.uint16))
+
+
 # ------------------------------------------------------------ quantizer
 
 def test_quantizer_all_zero_block():
