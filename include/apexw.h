@@ -1,29 +1,35 @@
 /*
  * apexw.h -- C ABI of a fused multi-tensor AdamW step for AMD MI355X (gfx950).
  *
- * One call of apexw_step updates every parameter of an optimizer -- a small
- * per-tensor prepare launch, then one streaming launch per (parameter dtype,
- * grad dtype) pair present -- with the AdamW rule
- * of "Fused optimizers and state precision" (ai-infra-kb M041), section 02:
+ * One call of apexw_step updates every parameter of an optimizer with the
+ * decoupled-decay AdamW rule of "Fused optimizers and state precision"
+ * (ai-infra-kb M041), section 02: with the tensor's step count t advanced by
+ * one,
  *
- *     t += 1
- *     m  = beta1*m + (1-beta1)*g
- *     v  = beta2*v + (1-beta2)*g*g
- *     m_hat = m / (1-beta1^t),   v_hat = v / (1-beta2^t)
- *     theta = theta*(1-lr*weight_decay) - lr*m_hat / (sqrt(v_hat) + eps)
+ *     m     <- beta1*m + (1-beta1)*g
+ *     v     <- beta2*v + (1-beta2)*g*g
+ *     theta <- theta*(1-lr*weight_decay) - lr*m_hat/(sqrt(v_hat)+eps),
+ *              m_hat = m/(1-beta1^t),  v_hat = v/(1-beta2^t)
  *
- * with decoupled weight decay, no AMSGrad, and the bias corrections applied as
- * per-tensor scalars (section 04: m_hat and v_hat are never stored).  Moments
- * are kept in one of three formats (section 05): fp32, bf16, or 8-bit codes
- * with one fp32 absmax scale per 256-element block.  Per parameter group lr,
- * betas, eps and weight decay are honoured (section 03); a parameter whose
- * grad is absent is left completely alone (section 03), and a step for which
- * the device flag found_inf is set changes nothing (section 06; the Apex
- * fused-optimizer guide, section 4.3, capturable mode) -- decided on the
- * device, without a host synchronisation.
+ * (no AMSGrad; section 04: the bias corrections are per-tensor scalars and
+ * m_hat, v_hat are never stored).  By default a step is one launch per
+ * (parameter dtype, grad dtype) pair present: every workgroup takes its
+ * tensor's bias corrections from an array the previous step wrote, and the
+ * first tile of each tensor advances the tensor's step counter and writes
+ * the corrections for the step after (apexw_set_launch_mode lists the other
+ * launch modes and when they are taken).  Moments are kept in one of three
+ * formats (section 05): fp32, bf16, or 8-bit codes with one fp32 absmax scale
+ * per 256-element block.  Per parameter group lr, betas, eps and weight decay
+ * are honoured (section 03); a parameter whose grad is absent is left
+ * completely alone (section 03), and a step for which the device flag
+ * found_inf is set changes nothing (section 06; the Apex fused-optimizer
+ * guide, section 4.3, capturable mode) -- decided on the device, without a
+ * host synchronisation.
  *
- * Arithmetic: fp32, every operation separately rounded in the order printed
- * above (left to right), correctly rounded division and square root; the
+ * Arithmetic: fp32, every operation separately rounded in the order the
+ * section 02 box fixes when read with its own (Python) operator rules --
+ * ((1-beta2)*g)*g, and (lr*m_hat)/(sqrt(v_hat)+eps) subtracted from
+ * theta*(1-lr*weight_decay) -- correctly rounded division and square root; the
  * scalars (1-beta1), (1-beta2), (1-lr*wd), lr, eps are formed in fp64 and
  * rounded once to fp32; beta^t is fp64 square-and-multiply over the bits of t
  * from the least significant end and 1-beta^t is rounded once to fp32.  bf16
@@ -226,8 +232,9 @@ int apexw_step_ex(apexw_t h, const apexw_group *groups, int32_t n_groups,
  * One pass reads every present grad: u = g * (*inv_scale_dev) in fp32 (NULL:
  * 1); if found_inf_dev is not NULL, sets it to 1.0f when any u is an
  * infinity or a NaN, exactly as apexw_unscale_check; sums u*u in fp64 into
- * one partial per 256-element tile; then a fixed-order reduction (so the
- * result does not depend on scheduling) writes the norm sqrt(sum) (fp64) to
+ * one partial per read group (four 256-element tiles fixed by the tile table,
+ * not by the grid); then a fixed-order reduction (so the result does not
+ * depend on scheduling) writes the norm sqrt(sum) (fp64) to
  * *norm_out_dev (may be NULL) and to *clip_coef_dev the factor
  * max_norm / norm if norm > max_norm (fp64, rounded once to fp32), else 1.
  * Pass clip_coef_dev (and the same inv_scale) in apexw_step_options.
@@ -270,6 +277,19 @@ int apexw_step_scaled(apexw_t h, const apexw_group *groups, int32_t n_groups,
 int apexw_unscale_check(apexw_t h, const void *const *grads,
                         const float *inv_scale_dev, float *found_inf_dev,
                         void *stream);
+
+/*
+ * The unscaling factor for grads multiplied by a loss scale, formed as the
+ * Apex fused-optimizer guide (section 4.3) forms the inv_scale it passes to
+ * its kernel: the fp64 reciprocal of the scale rounded once to fp32,
+ * *inv_scale_dev = (float)(1.0 / (double)*scale_dev).  For a power-of-two
+ * scale this is the exact reciprocal; for other scales it can differ in the
+ * last bit from a reciprocal taken in fp32.  One lane of one workgroup,
+ * queued on `stream` (hipStream_t; NULL: the default stream), no host sync;
+ * the two pointers are device pointers to one float each and may be equal.
+ * Errors: APEXW_EINVAL for a NULL pointer; APEXW_EHIP if the launch fails.
+ */
+int apexw_inv_scale(const float *scale_dev, float *inv_scale_dev, void *stream);
 
 /*
  * apexw_step_scaled with the group hyperparameters in device memory:
@@ -385,9 +405,13 @@ int apexw_set_cache_policy(apexw_t h, int32_t policy);
  * otherwise.  0 (default): mode 3 for such lists, else mode 2 for lists it
  * takes unless they stream (apexw_set_cache_policy), else mode 1.  Results do
  * not depend on the mode; steps of one handle queued on two streams at once
- * race in every mode.  Every call drops the carried corrections (so a caller
- * that wrote step counters into the state buffer calls it before the next
- * step).
+ * race in every mode.  Once a step of the handle has been queued under stream
+ * capture, its eager steps no longer take mode 3 either: a replay of that
+ * graph advances the counters with no host call, after which carried
+ * corrections would be stale.  Every call of this function drops the carried
+ * corrections (so a caller that wrote step counters into the state buffer
+ * calls it before the next step) and re-admits mode 3 after a capture: call
+ * it only once no graph holding a step of this handle will be replayed.
  */
 int apexw_set_launch_mode(apexw_t h, int32_t mode);
 
@@ -398,7 +422,10 @@ int apexw_get_launch_mode(apexw_t h, int32_t *mode);
 /* The largest cap in force over the handle's update launches (0: none). */
 int apexw_get_occupancy(apexw_t h, int32_t *workgroups_per_cu);
 
-/* Release the handle (host memory only; waits for nothing). */
+/* Release the handle: waits until the handle's pending table uploads (host
+ * to device copies out of its pinned staging area) have completed, then frees
+ * its host memory.  Device buffers -- state, workspace -- stay the caller's;
+ * work already queued that uses them must finish before they are freed. */
 int apexw_destroy(apexw_t h);
 
 /* Message of the last failed call on this thread ("" if none). */

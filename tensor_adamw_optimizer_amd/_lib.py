@@ -36,7 +36,7 @@ APEXW_MAX_GROUPS = 32
 # the entry points include/apexw.h declares
 ENTRY_POINTS = (
     "apexw_state_bytes", "apexw_state_layout", "apexw_workspace_bytes",
-    "apexw_create", "apexw_step", "apexw_step_scaled", "apexw_unscale_check",
+    "apexw_create", "apexw_step", "apexw_step_scaled", "apexw_inv_scale", "apexw_unscale_check",
     "apexw_step_device", "apexw_step_ex", "apexw_clip_grad_norm",
     "apexw_export_bytes", "apexw_export_state", "apexw_import_state",
     "apexw_read_steps", "apexw_launch_info", "apexw_set_workgroups",
@@ -88,6 +88,7 @@ def lib() -> ctypes.CDLL:
                                    ctypes.POINTER(P)]
         L.apexw_step.argtypes = [P, P, I32, P, P, P, P]
         L.apexw_step_scaled.argtypes = [P, P, I32, P, P, P, P, P]
+        L.apexw_inv_scale.argtypes = [P, P, P]
         L.apexw_unscale_check.argtypes = [P, P, P, P, P]
         L.apexw_step_device.argtypes = [P, P, I32, P, P, P, P, P]
         L.apexw_step_ex.argtypes = [P, P, I32, P, P, P, P]
@@ -202,6 +203,12 @@ def apexw_step_scaled(handle: int, groups_arr, n_groups: int, params_arr, grads_
     _check(lib().apexw_step_scaled(handle, groups_arr, n_groups, params_arr, grads_arr,
                                    inv_scale_ptr or None, found_inf_ptr or None, stream or None),
            "apexw_step_scaled")
+
+
+def apexw_inv_scale(scale_ptr: int, inv_scale_ptr: int, stream: int = 0) -> None:
+    """Device float at inv_scale_ptr = fp64 reciprocal of the one at scale_ptr."""
+    _check(lib().apexw_inv_scale(scale_ptr or None, inv_scale_ptr or None, stream or None),
+           "apexw_inv_scale")
 
 
 def apexw_unscale_check(handle: int, grads_arr, inv_scale_ptr: int, found_inf_ptr: int,

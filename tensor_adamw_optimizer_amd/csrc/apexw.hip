@@ -320,6 +320,11 @@ struct apexw_opt {
     // drops them
     bool carry_ok = false;              // no empty tensor: every tensor has a first tile
     bool carry_valid = false;
+    // a step of this handle was queued under stream capture: a replay of
+    // that graph moves the counters with no host call, so eager steps stop
+    // carrying corrections (any carried record could be stale) until
+    // apexw_set_launch_mode re-admits the carried step
+    bool graph_steps = false;
     int carry_parity = 0;
     std::vector<double> carry_beta1, carry_beta2;
 };
@@ -436,7 +441,7 @@ bool streams(const apexw_opt *h) {
 // tensor (steps with hyperparameters in device memory and steps being
 // captured into a graph take another mode).
 bool carry_launch(const apexw_opt *h) {
-    return h->carry_ok && (h->launch_mode == 3 || h->launch_mode == 0);
+    return h->carry_ok && (h->launch_mode == 3 || h->launch_mode == 0) && !h->graph_steps;
 }
 
 // The single launch: forced, or by default for the lists it is made for
@@ -457,6 +462,74 @@ int64_t read_pass_grid(const apexw_opt *h, int64_t tiles) {
     if (h->wg_override > 0) return std::min<int64_t>(groups, h->wg_override);
     const int64_t g = round_up(std::max<int64_t>(ceil_div(groups, 2), 2048), kXcds);
     return std::min(groups, g);
+}
+
+// One fp64 partial per read group, launch after launch, for the norm pass.
+int64_t norm_partials(const apexw_opt *h) {
+    int64_t n = 0;
+    for (const Launch &L : h->launches) n += read_groups(L.table_stride);
+    return n;
+}
+
+// The grad-norm pass of a handle with its fp64 partial sums in `partials`
+// (one per read group of every launch) and `partials2` (kReduceBlocks); every
+// entry the reduction reads is written by this call first.
+int clip_grad_norm_with(apexw_t h, const void *const *grads, const float *inv_scale_dev,
+                        double max_norm, float *found_inf_dev, double *norm_out_dev,
+                        float *clip_coef_dev, void *stream, double *partials, double *partials2) {
+    if (!clip_coef_dev) return fail(APEXW_EINVAL, "clip_coef_dev is NULL");
+    if (!(max_norm > 0.0) || !std::isfinite(max_norm))
+        return fail(APEXW_EINVAL, "max_norm must be finite and > 0");
+    if (int rc = reuse_last(h, nullptr, &grads)) return rc;
+    DeviceGuard guard(h->device);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int rc = upload_pointer_tables(h, nullptr, grads, st);
+    if (rc) return rc;
+    KernelArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.desc = reinterpret_cast<const TensorDesc *>(h->ws + h->wl.desc);
+    a.grads = reinterpret_cast<const void *const *>(h->ws + h->wl.grads);
+    a.tile_tensor = reinterpret_cast<const int32_t *>(h->ws + h->wl.tiles);
+    a.inv_scale = inv_scale_dev;
+    a.found_inf_out = found_inf_dev;
+    a.partials = partials;
+    a.partials2 = partials2;
+    a.norm_out = norm_out_dev;
+    a.clip_out = clip_coef_dev;
+    a.max_norm = max_norm;
+    const int64_t n_partials = norm_partials(h);
+    a.n_partials = n_partials;
+    const bool streaming = streams(h);
+    // every group writes its partial (0 without a grad), so no launch is skipped
+    int64_t group_begin = 0;
+    for (const Launch &L : h->launches) {
+        a.group_begin = group_begin;
+        group_begin += read_groups(L.table_stride);
+        if (L.tile_count == 0) continue;
+        a.tile_begin = L.tile_begin;
+        a.tile_count = L.tile_count;
+        a.table_begin = L.table_begin;
+        a.table_stride = L.table_stride;
+        const int64_t wg = read_pass_grid(h, L.tile_count);
+        kernel_fn k = L.gt == APEXW_F32
+                          ? (streaming ? grad_norm_partials_kernel<APEXW_F32, true>
+                                       : grad_norm_partials_kernel<APEXW_F32, false>)
+                          : (streaming ? grad_norm_partials_kernel<APEXW_BF16, true>
+                                       : grad_norm_partials_kernel<APEXW_BF16, false>);
+        hipLaunchKernelGGL(k, dim3((unsigned)wg), dim3(kThreads), 0, st, a);
+        HIP_TRY(hipGetLastError());
+    }
+    if (h->n > 0 && n_partials > kDirectPartials) {
+        hipLaunchKernelGGL(grad_norm_reduce_kernel, dim3(kReduceBlocks), dim3(kReduceThreads), 0,
+                           st, a);
+        HIP_TRY(hipGetLastError());
+    } else {
+        a.partials2 = nullptr;                // the final kernel sums the partials
+        if (h->n == 0) a.partials = nullptr;  // no workspace: the norm is 0
+    }
+    hipLaunchKernelGGL(grad_norm_final_kernel, dim3(1), dim3(kReduceThreads), 0, st, a);
+    HIP_TRY(hipGetLastError());
+    return APEXW_OK;
 }
 
 }  // namespace
@@ -723,6 +796,10 @@ int apexw_step_ex(apexw_t h, const apexw_group *groups, int32_t n_groups, void *
 
     DeviceGuard guard(h->device);
     hipStream_t st = static_cast<hipStream_t>(stream);
+    hipStreamCaptureStatus cap_status = hipStreamCaptureStatusNone;
+    HIP_TRY(hipStreamIsCapturing(st, &cap_status));
+    const bool capturing = cap_status != hipStreamCaptureStatusNone;
+    if (capturing) h->graph_steps = true;
     int rc = upload_pointer_tables(h, params, grads, st);
     if (rc) return rc;
 
@@ -744,13 +821,9 @@ int apexw_step_ex(apexw_t h, const apexw_group *groups, int32_t n_groups, void *
     const bool streaming = streams(h);
     // the carried step needs the hyperparameters on the host (their betas
     // form the carried corrections) and a step that runs now: a captured
-    // graph replays its launches without this host state moving on
-    bool carry = false;
-    if (groups && carry_launch(h)) {
-        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-        HIP_TRY(hipStreamIsCapturing(st, &cap));
-        carry = cap == hipStreamCaptureStatusNone;
-    }
+    // graph replays its launches without this host state moving on (and once
+    // one has been captured, carry_launch refuses every later step)
+    const bool carry = groups && carry_launch(h) && !capturing;
     if (!carry) h->carry_valid = false;
     const bool single = !carry && single_launch(h);
     bool carry_broken = false;                // a launch left out: restart the chain
@@ -824,6 +897,14 @@ int apexw_step_ex(apexw_t h, const apexw_group *groups, int32_t n_groups, void *
     return APEXW_OK;
 }
 
+int apexw_inv_scale(const float *scale_dev, float *inv_scale_dev, void *stream) {
+    if (!scale_dev || !inv_scale_dev) return fail(APEXW_EINVAL, "scale_dev and inv_scale_dev must not be NULL");
+    hipLaunchKernelGGL(inv_scale_kernel, dim3(1), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+                       scale_dev, inv_scale_dev);
+    HIP_TRY(hipGetLastError());
+    return APEXW_OK;
+}
+
 int apexw_unscale_check(apexw_t h, const void *const *grads, const float *inv_scale_dev,
                         float *found_inf_dev, void *stream) {
     if (!h) return fail(APEXW_EINVAL, "handle is NULL");
@@ -865,60 +946,10 @@ int apexw_clip_grad_norm(apexw_t h, const void *const *grads, const float *inv_s
                          double max_norm, float *found_inf_dev, double *norm_out_dev,
                          float *clip_coef_dev, void *stream) {
     if (!h) return fail(APEXW_EINVAL, "handle is NULL");
-    if (!clip_coef_dev) return fail(APEXW_EINVAL, "clip_coef_dev is NULL");
-    if (!(max_norm > 0.0) || !std::isfinite(max_norm))
-        return fail(APEXW_EINVAL, "max_norm must be finite and > 0");
-    if (int rc = reuse_last(h, nullptr, &grads)) return rc;
-    DeviceGuard guard(h->device);
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    int rc = upload_pointer_tables(h, nullptr, grads, st);
-    if (rc) return rc;
-    KernelArgs a;
-    std::memset(&a, 0, sizeof a);
-    a.desc = reinterpret_cast<const TensorDesc *>(h->ws + h->wl.desc);
-    a.grads = reinterpret_cast<const void *const *>(h->ws + h->wl.grads);
-    a.tile_tensor = reinterpret_cast<const int32_t *>(h->ws + h->wl.tiles);
-    a.inv_scale = inv_scale_dev;
-    a.found_inf_out = found_inf_dev;
-    a.partials = reinterpret_cast<double *>(h->ws + h->wl.partials);
-    a.partials2 = reinterpret_cast<double *>(h->ws + h->wl.partials2);
-    a.norm_out = norm_out_dev;
-    a.clip_out = clip_coef_dev;
-    a.max_norm = max_norm;
-    int64_t n_partials = 0;                // one per read group, launch after launch
-    for (const Launch &L : h->launches) n_partials += read_groups(L.table_stride);
-    a.n_partials = n_partials;
-    const bool streaming = streams(h);
-    // every group writes its partial (0 without a grad), so no launch is skipped
-    int64_t group_begin = 0;
-    for (const Launch &L : h->launches) {
-        a.group_begin = group_begin;
-        group_begin += read_groups(L.table_stride);
-        if (L.tile_count == 0) continue;
-        a.tile_begin = L.tile_begin;
-        a.tile_count = L.tile_count;
-        a.table_begin = L.table_begin;
-        a.table_stride = L.table_stride;
-        const int64_t wg = read_pass_grid(h, L.tile_count);
-        kernel_fn k = L.gt == APEXW_F32
-                          ? (streaming ? grad_norm_partials_kernel<APEXW_F32, true>
-                                       : grad_norm_partials_kernel<APEXW_F32, false>)
-                          : (streaming ? grad_norm_partials_kernel<APEXW_BF16, true>
-                                       : grad_norm_partials_kernel<APEXW_BF16, false>);
-        hipLaunchKernelGGL(k, dim3((unsigned)wg), dim3(kThreads), 0, st, a);
-        HIP_TRY(hipGetLastError());
-    }
-    if (h->n > 0 && n_partials > kDirectPartials) {
-        hipLaunchKernelGGL(grad_norm_reduce_kernel, dim3(kReduceBlocks), dim3(kReduceThreads), 0,
-                           st, a);
-        HIP_TRY(hipGetLastError());
-    } else {
-        a.partials2 = nullptr;                // the final kernel sums the partials
-        if (h->n == 0) a.partials = nullptr;  // no workspace: the norm is 0
-    }
-    hipLaunchKernelGGL(grad_norm_final_kernel, dim3(1), dim3(kReduceThreads), 0, st, a);
-    HIP_TRY(hipGetLastError());
-    return APEXW_OK;
+    return clip_grad_norm_with(h, grads, inv_scale_dev, max_norm, found_inf_dev, norm_out_dev,
+                               clip_coef_dev, stream,
+                               reinterpret_cast<double *>(h->ws + h->wl.partials),
+                               reinterpret_cast<double *>(h->ws + h->wl.partials2));
 }
 
 // ---------------------------------------------------------------- checkpoint
@@ -1084,6 +1115,7 @@ int apexw_set_launch_mode(apexw_t h, int32_t mode) {
         return fail(APEXW_EINVAL, "the carried step needs a non-empty list without empty tensors");
     h->launch_mode = mode;
     h->carry_valid = false;                  // also: counters written by the caller are re-read
+    h->graph_steps = false;                  // the caller replays no captured step any more
     return APEXW_OK;
 }
 

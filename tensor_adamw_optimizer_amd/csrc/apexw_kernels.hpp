@@ -1164,8 +1164,8 @@ __global__ __launch_bounds__(kThreads) void unscale_check_kernel(KernelArgs a) {
 //     -- per lane over the group's tiles in order, then wave_sum's fixed
 //     order -- into partials[group_begin + j] for group j of the launch (the
 //     launches' groups one after another, so consecutive groups fill whole
-//     64-byte lines; a group that starts past its launch's end leaves its
-//     entry 0, as set at create); tiles without a grad contribute 0;
+//     64-byte lines; a group that starts past its launch's end writes 0, so
+//     every entry is written on every call); tiles without a grad contribute 0;
 //     optionally sets found_inf_out like the unscale check;
 //  2. grad_norm_reduce_kernel: workgroup b sums partials[b*C .. (b+1)*C) with
 //     a strided loop and a tree in LDS into partials2[b];
@@ -1210,7 +1210,10 @@ __global__ __launch_bounds__(kThreads) void grad_norm_partials_kernel(KernelArgs
     for (int64_t jg = blockIdx.x; jg < groups; jg += gridDim.x) {
         ReadTile t[kReadBatch];
         float g[kReadBatch][kVec];
-        if (!read_group(a, jg, t)) continue;
+        if (!read_group(a, jg, t)) {      // starts past the launch end: contributes 0
+            if (threadIdx.x == 0) gptr<double>(static_cast<void *>(a.partials))[a.group_begin + jg] = 0.0;
+            continue;
+        }
         load_group_grads<GT, NT>(t, g);
         double sq = 0.0;                  // the group's tiles in order, each lane's 4 values
 #pragma unroll
@@ -1271,6 +1274,16 @@ __global__ __launch_bounds__(kReduceThreads) void grad_norm_final_kernel(KernelA
         const float coef = norm > a.max_norm ? (float)(a.max_norm / norm) : 1.0f;
         if (a.norm_out != nullptr) *gptr<double>(static_cast<void *>(a.norm_out)) = norm;
         *gptr<float>(static_cast<void *>(a.clip_out)) = coef;
+    }
+}
+
+// The inverse of a loss scale, formed the way the Apex fused-optimizer guide
+// (section 4.3) forms the factor it hands to its kernel: the fp64 reciprocal
+// of the scale, rounded once to fp32.
+__global__ __launch_bounds__(kThreads) void inv_scale_kernel(const float *scale, float *inv) {
+    if (threadIdx.x == 0) {
+        const double s = (double)*gptr<float>(static_cast<const void *>(scale));
+        *gptr<float>(static_cast<void *>(inv)) = (float)(1.0 / s);
     }
 }
 

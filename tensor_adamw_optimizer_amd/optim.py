@@ -46,6 +46,17 @@ class AdamW(torch.optim.Optimizer):
     state: "f32" (or "fp32"), "bf16" (round-to-nearest-even moments) or "q8" (int8 m /
     uint8 v codes with one fp32 absmax scale per 256-element block).
     grad_dtype: dtype the grads will have (default: each parameter's dtype).
+    flat_grads: give every parameter a .grad that is a view into one flat
+    buffer per grad dtype (each view 64-byte aligned), made here, zero-filled.
+    Autograd then accumulates into these views in place, and step() hands the
+    library the same pointer table every time instead of reading 'p.grad' of
+    every parameter: O(1) host work per step besides one pass over the
+    parameter pointers.  The contract: the .grad attributes stay these views
+    (do not assign or delete them; zero_grad() of this optimizer zeroes the
+    buffers in place whatever set_to_none says), so every parameter has a
+    grad on every step -- a parameter that received none gets a zero grad,
+    which decays it and counts a step, as torch does with set_to_none=False.
+    flat_grads_intact() tells whether the contract still holds.
     """
 
     # torch.amp.GradScaler: set grad_scale / found_inf on the optimizer and
@@ -54,7 +65,7 @@ class AdamW(torch.optim.Optimizer):
 
     def __init__(self, params: Iterable, lr: float = 1e-3, betas=(0.9, 0.999),
                  eps: float = 1e-8, weight_decay: float = 0.0, state: str = "f32",
-                 grad_dtype: Optional[torch.dtype] = None):
+                 grad_dtype: Optional[torch.dtype] = None, flat_grads: bool = False):
         if state not in _FMT:
             raise ValueError("state must be one of %s" % sorted(_FMT))
         self._h = None
@@ -90,7 +101,56 @@ class AdamW(torch.optim.Optimizer):
                                      len(self.param_groups), fmt, self.state_buffer.data_ptr(),
                                      self.state_bytes, self.workspace.data_ptr(), ws_bytes,
                                      stream)
-        self._params_arr = L.make_ptrs([p.data_ptr() for p in self._params])
+        self._param_ptrs = list(map(torch.Tensor.data_ptr, self._params))
+        self._params_arr = L.make_ptrs(self._param_ptrs)
+        self._inv_buf: Optional[torch.Tensor] = None
+        self._flat_bufs: List[torch.Tensor] = []
+        self._flat_views: List[torch.Tensor] = []
+        self._flat_arr = None
+        if flat_grads:
+            self._make_flat_grads()
+
+    def _make_flat_grads(self) -> None:
+        align = 64
+        offsets, total = [], {}
+        for n, d in zip(self._numel, self._gdtype):
+            off = total.get(d, 0)
+            offsets.append(off)
+            total[d] = off + (n * d.itemsize + align - 1) // align * align
+        bufs = {d: torch.zeros(max(b, align), dtype=torch.uint8, device=self.device)
+                for d, b in total.items()}
+        for p, n, d, off in zip(self._params, self._numel, self._gdtype, offsets):
+            p.grad = bufs[d][off:off + n * d.itemsize].view(d).view(p.shape)
+            self._flat_views.append(p.grad)
+        self._flat_bufs = list(bufs.values())
+        self._flat_arr = L.make_ptrs([g.data_ptr() or 16 for g in self._flat_views])
+
+    def flat_grads_intact(self) -> bool:
+        """True while every .grad is still the view flat_grads made."""
+        return bool(self._flat_views) and all(
+            p.grad is g for p, g in zip(self._params, self._flat_views))
+
+    def zero_grad(self, set_to_none: bool = True) -> None:
+        if self._flat_bufs:
+            for b in self._flat_bufs:       # the views stay in place
+                b.zero_()
+            return
+        super().zero_grad(set_to_none=set_to_none)
+
+    def _check_params(self) -> None:
+        """Re-read the parameter pointers (one pass of cheap calls); a storage
+        that moved -- 'p.data = ...', a re-materialised parameter -- gets a new
+        pointer table, and a change of size, dtype, device or layout is refused."""
+        ptrs = list(map(torch.Tensor.data_ptr, self._params))
+        if ptrs == self._param_ptrs:
+            return
+        for i, p in enumerate(self._params):
+            if (p.numel() != self._numel[i] or _DT.get(p.dtype) != self._pdt[i]
+                    or p.device != self.device or not p.is_contiguous()):
+                raise ValueError("parameter %d changed size, dtype, device or layout since the "
+                                 "optimizer was built" % i)
+        self._param_ptrs = ptrs
+        self._params_arr = L.make_ptrs(ptrs)
 
     def add_param_group(self, param_group: Dict) -> None:
         if getattr(self, "_h", None) is not None:
@@ -150,9 +210,22 @@ class AdamW(torch.optim.Optimizer):
         if found_inf is None and scaler_inf is not None:
             found_inf = scaler_inf.to(torch.float32).reshape(1)
         if inv_scale is None and scaler_scale is not None:
-            inv_scale = torch.reciprocal(scaler_scale.to(torch.float32).reshape(1))
-        self.step_pointers(self._grads_arr(), found_inf, inv_scale, clip_coef)
+            inv_scale = self.inv_scale_of(scaler_scale)
+        self.step_pointers(self._flat_arr if self._flat_arr is not None else self._grads_arr(),
+                           found_inf, inv_scale, clip_coef)
         return loss
+
+    def inv_scale_of(self, scale: torch.Tensor) -> torch.Tensor:
+        """The unscaling factor for a loss scale held on the device, formed by
+        the library as the fp64 reciprocal of the scale rounded once to fp32
+        (a one-element float32 tensor this optimizer reuses)."""
+        scale = scale.to(torch.float32).reshape(1)
+        if self._inv_buf is None:
+            self._inv_buf = torch.empty(1, dtype=torch.float32, device=self.device)
+        with torch.cuda.device(self.device):
+            L.apexw_inv_scale(self._dev_ptr(scale, "grad_scale"), self._inv_buf.data_ptr(),
+                              self._stream())
+        return self._inv_buf
 
     def step_pointers(self, grads_arr, found_inf: Optional[torch.Tensor] = None,
                       inv_scale: Optional[torch.Tensor] = None,
@@ -162,6 +235,7 @@ class AdamW(torch.optim.Optimizer):
         this optimizer -- for grad buffers that persist across steps, with no
         per-tensor work on the host."""
         groups = [_GroupView(g) for g in self.param_groups]
+        self._check_params()
         with torch.cuda.device(self.device):
             L.apexw_step_ex(self._h, L.make_groups(groups), len(groups), self._params_arr,
                             grads_arr, self._dev_ptr(inv_scale, "inv_scale"),

@@ -188,15 +188,18 @@ def test_graph_capture_replays_match_oracle(fmt, mode):
             assert n_bit_mismatch(bits(m), ref.m[i]) == 0 and n_bit_mismatch(bits(v), ref.v[i]) == 0
         del junk
     assert list(ref.t) == [6] * len(SIZES)
-    # a pointer change under capture is refused
+    # (the replays above moved every counter, so `graph` is not empty)
+    # a pointer change under capture is refused: nothing is captured, and
+    # torch says so when the capture ends
     other = [g.clone() for g in grads]
     g2 = torch.cuda.CUDAGraph()
     with torch.cuda.stream(s):
-        with pytest.raises(L.ApexwError):
-            with torch.cuda.graph(g2, stream=s):
-                L.apexw_step_device(opt.h, table.data_ptr(), 2, pa,
-                                    L.make_ptrs([g.data_ptr() for g in other]), 0, 0,
-                                    torch.cuda.current_stream().cuda_stream)
+        with pytest.warns(UserWarning, match="empty"):
+            with pytest.raises(L.ApexwError):
+                with torch.cuda.graph(g2, stream=s):
+                    L.apexw_step_device(opt.h, table.data_ptr(), 2, pa,
+                                        L.make_ptrs([g.data_ptr() for g in other]), 0, 0,
+                                        torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     opt.close()
 
@@ -257,6 +260,73 @@ def test_capture_between_carried_steps(fmt):
     for k in range(6, 10):
         eager(k)
     assert list(ref.t) == [10] * len(SIZES)
+    opt.close()
+
+
+@pytest.mark.parametrize("fmt", [W.STATE_F32, W.STATE_Q8])
+def test_replays_between_eager_steps(fmt):
+    """A step captured into a graph, then eager steps and replays taking
+    turns: capture, eager, replay, eager, replay, eager.  Each replay moves
+    the counters with no host call, so after the capture the eager steps must
+    not take the carried step (its corrections would be those of the counter
+    before the replay); apexw_set_launch_mode re-admits it once no replay is
+    coming.  Every call is checked against the oracle."""
+    say("case: replays between eager steps", fmt)
+    p_cpu, gs = _inputs(47, 12)
+    params = [p.to(DEV) for p in p_cpu]
+    grads = [g.to(DEV) for g in gs[0]]
+    opt = GpuOpt(SIZES, PDT, GDT, GROUP_OF, 2, fmt)
+    ref = oracle.OracleAdamW(SIZES, PDT, GDT, GROUP_OF, fmt)
+    th_ref = [bits(p) for p in p_cpu]
+    pa = L.make_ptrs([p.data_ptr() for p in params])
+    ga = L.make_ptrs([g.data_ptr() for g in grads])
+    groups = L.make_groups(GROUPS)
+    st = torch.cuda.current_stream().cuda_stream
+
+    def check(k):
+        assert np.array_equal(bits(opt.steps()), ref.t), k
+        for i in range(len(SIZES)):
+            assert n_bit_mismatch(bits(params[i]), th_ref[i]) == 0, (k, i)
+            m, v = opt.moments(i)
+            assert n_bit_mismatch(bits(m), ref.m[i]) == 0 and n_bit_mismatch(bits(v), ref.v[i]) == 0, (k, i)
+
+    def load(k):
+        for g, x in zip(grads, gs[k]):
+            g.copy_(x.to(DEV))
+        torch.cuda.synchronize()
+        ref.step(th_ref, [bits(x) for x in gs[k]], GROUPS)
+
+    def eager(k):
+        load(k)
+        L.apexw_step(opt.h, groups, 2, pa, ga, 0, st)
+        torch.cuda.synchronize()
+        check(k)
+
+    eager(0)
+    eager(1)
+    assert L.apexw_get_launch_mode(opt.h) == 3
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            L.apexw_step(opt.h, groups, 2, pa, ga, 0, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    check("after capture")
+    assert L.apexw_get_launch_mode(opt.h) != 3
+    for k in range(2, 8):
+        if k % 2 == 0:
+            eager(k)
+        else:
+            load(k)
+            graph.replay()
+            torch.cuda.synchronize()
+            check(k)
+    L.apexw_set_launch_mode(opt.h, 0)                # no replay follows
+    assert L.apexw_get_launch_mode(opt.h) == 3
+    for k in range(8, 12):
+        eager(k)
+    assert list(ref.t) == [12] * len(SIZES)
     opt.close()
 
 

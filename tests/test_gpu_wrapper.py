@@ -98,13 +98,46 @@ def test_wrapper_rejects_sparse_grads_and_reads_steps():
     opt.close()
 
 
-def test_wrapper_with_lr_scheduler_and_grad_scaler_against_oracle():
+def _inv_scale_apex(scale: float) -> float:
+    """inv_scale as the Apex guide, section 4.3, forms it: fp64 reciprocal of
+    the scale, rounded once to fp32."""
+    return float(np.float32(1.0 / np.float64(np.float32(scale))))
+
+
+def test_inv_scale_is_the_fp64_reciprocal_rounded_once():
+    say("case: apexw_inv_scale")
+    from tensor_adamw_optimizer_amd import _lib as L
+    rng = np.random.default_rng(62)
+    scales = np.concatenate([
+        np.float32(2.0) ** np.arange(-20, 25, dtype=np.float32),
+        np.float32(np.exp(rng.uniform(-80, 80, 400))),
+        np.array([3000.0, 65535.0, 1e-30, 3.0e38, 1.5e-45, 0.0, np.inf, np.nan], np.float32)])
+    s_dev = torch.from_numpy(scales.astype(np.float32)).to(DEV)
+    out = torch.full_like(s_dev, 7.0)
+    st = torch.cuda.current_stream().cuda_stream
+    for i in range(scales.size):
+        L.apexw_inv_scale(s_dev[i:].data_ptr(), out[i:].data_ptr(), st)
+    got = out.cpu().numpy()
+    with np.errstate(divide="ignore", over="ignore"):
+        want = np.float32(1.0 / scales.astype(np.float64))
+    assert np.array_equal(got.view(np.uint32)[~np.isnan(want)], want.view(np.uint32)[~np.isnan(want)])
+    assert np.isnan(got[np.isnan(want)]).all()
+    # in place (scale and result in one float)
+    x = torch.tensor([3000.0], device=DEV)
+    L.apexw_inv_scale(x.data_ptr(), x.data_ptr(), st)
+    assert x.item() == _inv_scale_apex(3000.0)
+
+
+@pytest.mark.parametrize("init_scale", [2.0 ** 12, 3000.0])
+def test_wrapper_with_lr_scheduler_and_grad_scaler_against_oracle(init_scale):
     """The wrapper as a torch.optim.Optimizer: a StepLR schedule changes lr
     between steps, and torch.amp.GradScaler drives the steps -- the scaler
     hands over its scale and overflow flag, the update unscales in the
-    kernel, and a step whose grads hold an inf is skipped on the device
-    (the scaler then halves its scale).  Every step against the oracle."""
-    say("case: wrapper + StepLR + GradScaler")
+    kernel by the library-formed fp64 reciprocal of the scale, and a step
+    whose grads hold an inf is skipped on the device (the scaler then halves
+    its scale).  A power-of-two scale and one that is not; every step
+    against the oracle."""
+    say("case: wrapper + StepLR + GradScaler", init_scale)
     gen = torch.Generator().manual_seed(61)
     shapes = [(128, 9), (513,)]
     p_cpu = [(torch.randn(s, generator=gen) * 0.02) for s in shapes]
@@ -112,7 +145,7 @@ def test_wrapper_with_lr_scheduler_and_grad_scaler_against_oracle():
     opt = AdamW(params, lr=1e-2, weight_decay=0.05)
     assert isinstance(opt, torch.optim.Optimizer)
     sched = torch.optim.lr_scheduler.StepLR(opt, step_size=2, gamma=0.5)
-    scaler = torch.amp.GradScaler("cuda", init_scale=2.0 ** 12, growth_interval=1000)
+    scaler = torch.amp.GradScaler("cuda", init_scale=init_scale, growth_interval=1000)
     ref = oracle.OracleAdamW([p.numel() for p in p_cpu], ["f32"] * 2, ["f32"] * 2, [0, 0], "f32")
     th_ref = [bits(p) for p in p_cpu]
     lr = 1e-2
@@ -132,8 +165,9 @@ def test_wrapper_with_lr_scheduler_and_grad_scaler_against_oracle():
         g_np = [bits(g * scale) for g in g_cpu]
         if overflow:
             g_np[1][7] = np.float32(np.inf)
-        ref.step(th_ref, g_np, grp, found_inf=overflow, inv_scale=float(np.float32(1.0 / scale)))
+        ref.step(th_ref, g_np, grp, found_inf=overflow, inv_scale=_inv_scale_apex(scale))
         torch.cuda.synchronize()
+        assert opt._inv_buf.item() == _inv_scale_apex(scale)
         for i in range(2):
             assert n_bit_mismatch(bits(params[i]), th_ref[i]) == 0, (k, i)
         if overflow:
@@ -177,5 +211,62 @@ def test_wrapper_grad_table_checks_and_reuse():
     for x, y in zip(a, b):
         assert n_bit_mismatch(bits(x), bits(y)) == 0
     assert opt_a.read_steps() == opt_b.read_steps() == [3, 3]
+    opt_a.close()
+    opt_b.close()
+
+
+def test_flat_grads_match_the_default_path_and_backward_fills_them():
+    """flat_grads: every .grad is a view of one buffer per dtype, filled in
+    place by backward, zeroed in place by zero_grad; the steps equal those of
+    an optimizer that reads .grad every step, and a parameter whose storage
+    moved ('p.data = ...') is followed.  Checked against the oracle too."""
+    say("case: wrapper flat grads")
+    gen = torch.Generator().manual_seed(72)
+    shapes = [(37, 11), (1000,), (5,), (64, 64)]
+    p_cpu = [torch.randn(s, generator=gen) * 0.02 for s in shapes]
+    a = [torch.nn.Parameter(p.to(DEV)) for p in p_cpu]
+    b = [torch.nn.Parameter(p.to(DEV)) for p in p_cpu]
+    opt_a = AdamW(a, lr=1e-2, weight_decay=0.1)
+    opt_b = AdamW(b, lr=1e-2, weight_decay=0.1, flat_grads=True)
+    views = [p.grad for p in b]
+    assert opt_b.flat_grads_intact()
+    assert all(v is not None and v.is_contiguous() and v.data_ptr() % 64 == 0 for v in views)
+    ref = oracle.OracleAdamW([p.numel() for p in p_cpu], ["f32"] * 4, ["f32"] * 4, [0] * 4, "f32")
+    th_ref = [bits(p) for p in p_cpu]
+    xs = [torch.randn(8, 37, generator=gen) for _ in range(5)]
+    for k in range(5):
+        x = xs[k].to(DEV)
+
+        def loss_of(ps):
+            h = (x @ ps[0]).sum(1)                       # [8]
+            return (h * ps[1][:8]).sum() + ps[2].square().sum() + (ps[3] * 1e-3).sum()
+
+        opt_a.zero_grad()
+        opt_b.zero_grad()
+        assert all(p.grad is v for p, v in zip(b, views))
+        loss_of(a).backward()
+        loss_of(b).backward()
+        assert opt_b.flat_grads_intact()
+        for p, q in zip(a, b):
+            assert n_bit_mismatch(bits(p.grad), bits(q.grad)) == 0
+        if k == 3:                                       # storage moves under the optimizer
+            for p in (a[1], b[1]):
+                p.data = p.data.clone()
+            th_dev = [bits(p.detach()) for p in a]
+            assert all(n_bit_mismatch(t, r) == 0 for t, r in zip(th_dev, th_ref))
+        g_np = [bits(p.grad) for p in a]
+        opt_a.step()
+        opt_b.step()
+        ref.step(th_ref, g_np, [W.Group(lr=1e-2, weight_decay=0.1)])
+        torch.cuda.synchronize()
+        for i in range(4):
+            assert n_bit_mismatch(bits(a[i].detach()), th_ref[i]) == 0, (k, i)
+            assert n_bit_mismatch(bits(b[i].detach()), th_ref[i]) == 0, (k, i)
+    assert opt_a.read_steps() == opt_b.read_steps() == [5] * 4
+    b[2].grad = None
+    assert not opt_b.flat_grads_intact()
+    with pytest.raises(ValueError):                       # a parameter that changed size
+        b[0].data = torch.zeros(3, device=DEV)
+        opt_b.step()
     opt_a.close()
     opt_b.close()
