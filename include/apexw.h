@@ -248,6 +248,25 @@ int apexw_clip_grad_norm(apexw_t h, const void *const *grads,
                          float *clip_coef_dev, void *stream);
 
 /*
+ * apexw_clip_grad_norm for callers that cannot allocate device memory (code
+ * under graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same pass with the same results, bit for bit, but its fp64
+ * partial sums live in a static device array of the library (8 MiB, one copy
+ * per GPU, held until the process ends) instead of the handle's workspace.
+ * The array holds one partial per read group of four tiles plus 256
+ * second-stage sums, room for lists of up to about 1.07e9 elements; a larger
+ * list gets APEXW_ENOSPC before anything is queued.  Every call on a GPU
+ * shares that array and writes every entry it reads, so calls that overlap
+ * on one GPU (other streams, other threads, other handles) race: order them.
+ * The first call on a device looks up the array's address there.  Other
+ * arguments and errors as apexw_clip_grad_norm.
+ */
+int apexw_clip_grad_norm_noalloc(apexw_t h, const void *const *grads,
+                                 const float *inv_scale_dev, double max_norm,
+                                 float *found_inf_dev, double *norm_out_dev,
+                                 float *clip_coef_dev, void *stream);
+
+/*
  * apexw_step on grads that arrive multiplied by a loss scale: every grad
  * value is first unscaled, g * (*inv_scale_dev) as one rounded fp32
  * multiply, then updated exactly as by apexw_step (the mixed-precision

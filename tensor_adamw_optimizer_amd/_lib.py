@@ -37,7 +37,7 @@ APEXW_MAX_GROUPS = 32
 ENTRY_POINTS = (
     "apexw_state_bytes", "apexw_state_layout", "apexw_workspace_bytes",
     "apexw_create", "apexw_step", "apexw_step_scaled", "apexw_inv_scale", "apexw_unscale_check",
-    "apexw_step_device", "apexw_step_ex", "apexw_clip_grad_norm",
+    "apexw_step_device", "apexw_step_ex", "apexw_clip_grad_norm", "apexw_clip_grad_norm_noalloc",
     "apexw_export_bytes", "apexw_export_state", "apexw_import_state",
     "apexw_read_steps", "apexw_launch_info", "apexw_set_workgroups",
     "apexw_set_occupancy", "apexw_get_occupancy", "apexw_set_cache_policy",
@@ -93,6 +93,7 @@ def lib() -> ctypes.CDLL:
         L.apexw_step_device.argtypes = [P, P, I32, P, P, P, P, P]
         L.apexw_step_ex.argtypes = [P, P, I32, P, P, P, P]
         L.apexw_clip_grad_norm.argtypes = [P, P, P, ctypes.c_double, P, P, P, P]
+        L.apexw_clip_grad_norm_noalloc.argtypes = [P, P, P, ctypes.c_double, P, P, P, P]
         L.apexw_export_bytes.argtypes = [P, ctypes.POINTER(SZ)]
         L.apexw_export_state.argtypes = [P, P, I32, P, SZ, P]
         L.apexw_import_state.argtypes = [P, P, SZ, P, I32, P]
@@ -243,6 +244,15 @@ def apexw_clip_grad_norm(handle: int, grads_arr, inv_scale_ptr: int, max_norm: f
                                       found_inf_ptr or None, norm_out_ptr or None,
                                       clip_coef_ptr or None, stream or None),
            "apexw_clip_grad_norm")
+
+
+def apexw_clip_grad_norm_noalloc(handle: int, grads_arr, inv_scale_ptr: int, max_norm: float,
+                                 found_inf_ptr: int, norm_out_ptr: int, clip_coef_ptr: int,
+                                 stream: int = 0) -> None:
+    _check(lib().apexw_clip_grad_norm_noalloc(handle, grads_arr, inv_scale_ptr or None, max_norm,
+                                              found_inf_ptr or None, norm_out_ptr or None,
+                                              clip_coef_ptr or None, stream or None),
+           "apexw_clip_grad_norm_noalloc")
 
 
 def apexw_export_bytes(handle: int) -> int:

@@ -25,6 +25,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -469,6 +470,39 @@ int64_t norm_partials(const apexw_opt *h) {
     int64_t n = 0;
     for (const Launch &L : h->launches) n += read_groups(L.table_stride);
     return n;
+}
+
+// Scratch of the norm pass that allocates nothing: a file-scope device array
+// of kScratchBytes that every call on a GPU shares (each GPU has its own
+// copy).  Layout: the per-group partials from offset 0, the kReduceBlocks
+// second-stage sums at kScratchPartials2 -- 8 MiB is room for 1,048,320
+// read groups, lists of up to about 1.07e9 elements.
+constexpr int64_t kScratchBytes = (int64_t)8 << 20;
+constexpr int64_t kScratchPartials2 = kScratchBytes - kReduceBlocks * 8;
+
+int64_t norm_scratch_bytes(const apexw_opt *h) {
+    return norm_partials(h) * 8 + kReduceBlocks * 8;
+}
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// The device address of `scratch` on `device` (current), looked up once per
+// device: in host code the array's name is only a stand-in for the symbol.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+char *g_scratch[kMaxDevices] = {};
+
+int scratch_address(int device, char **out) {
+    if (device < 0 || device >= kMaxDevices)
+        return fail(APEXW_EINVAL, "device %d outside 0..%d", device, kMaxDevices - 1);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch[device]) {
+        void *p = nullptr;
+        HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+        g_scratch[device] = static_cast<char *>(p);
+    }
+    *out = g_scratch[device];
+    return APEXW_OK;
 }
 
 // The grad-norm pass of a handle with its fp64 partial sums in `partials`
@@ -950,6 +984,28 @@ int apexw_clip_grad_norm(apexw_t h, const void *const *grads, const float *inv_s
                                clip_coef_dev, stream,
                                reinterpret_cast<double *>(h->ws + h->wl.partials),
                                reinterpret_cast<double *>(h->ws + h->wl.partials2));
+}
+
+int apexw_clip_grad_norm_noalloc(apexw_t h, const void *const *grads, const float *inv_scale_dev,
+                                 double max_norm, float *found_inf_dev, double *norm_out_dev,
+                                 float *clip_coef_dev, void *stream) {
+    if (!h) return fail(APEXW_EINVAL, "handle is NULL");
+    const int64_t need = norm_scratch_bytes(h);
+    if (need > kScratchBytes)
+        return fail(APEXW_ENOSPC, "the grad-norm partial sums of this list need %lld bytes; the "
+                    "library's static scratch holds %lld (use apexw_clip_grad_norm)",
+                    (long long)need, (long long)kScratchBytes);
+    DeviceGuard guard(h->device);
+    char *base = nullptr;
+    if (int rc = scratch_address(h->device, &base)) return rc;
+    // the per-group partials from the start, the second-stage sums at the end
+    double *partials = reinterpret_cast<double *>(base);
+    double *partials2 = reinterpret_cast<double *>(base + kScratchPartials2);
+    if (reinterpret_cast<char *>(partials + norm_partials(h)) > reinterpret_cast<char *>(partials2) ||
+        reinterpret_cast<char *>(partials2 + kReduceBlocks) > base + kScratchBytes)
+        return fail(APEXW_ENOSPC, "grad-norm scratch layout exceeds the static array");
+    return clip_grad_norm_with(h, grads, inv_scale_dev, max_norm, found_inf_dev, norm_out_dev,
+                               clip_coef_dev, stream, partials, partials2);
 }
 
 // ---------------------------------------------------------------- checkpoint
