@@ -79,9 +79,23 @@ def measured_traffic(workload: str):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, budget_s: float = 12.0):
-    """The oracle (scalar C, one thread) on a bounded sample of the workload:
-    a prefix of the first tensor, as many calls as fit in about budget_s."""
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, budget_s: float = 7.0):
+    """The oracle on a bounded sample of the workload, timed on the host
+    cores: a prefix of the first tensor (at most 2^24 elements), as many
+    calls as fit in about budget_s, once with the single-threaded parity
+    build and once with the OpenMP timing build of the same source (bitwise
+    the same results).  value = the all-core figure."""
     import numpy as np
     import torch
 
@@ -91,28 +105,51 @@ def cpu_baseline(w, budget_s: float = 12.0):
     n_full = w.numels[0]
     n = min(n_full, 1 << 24)
     gen = torch.Generator().manual_seed(123)
-    th = (torch.randn(n, generator=gen) * w.theta_std).to(W.TORCH_DTYPE[w.param_dtype[0]])
-    th = W.to_numpy_bits(th)
-    g = (torch.randn(n, generator=gen) * w.grad_std).to(W.TORCH_DTYPE[w.grad_dtype[0]])
-    g = W.to_numpy_bits(g)
-    ref = oracle.OracleAdamW([n], w.param_dtype[:1], w.grad_dtype[:1], [0], w.state_fmt)
+    th0 = W.to_numpy_bits((torch.randn(n, generator=gen) * w.theta_std)
+                          .to(W.TORCH_DTYPE[w.param_dtype[0]]))
+    g = W.to_numpy_bits((torch.randn(n, generator=gen) * w.grad_std)
+                        .to(W.TORCH_DTYPE[w.grad_dtype[0]]))
     grp = [w.groups[w.group_of[0]]]
-    ref.step([th], [g], grp)                                  # warm-up call
-    calls, t0 = 0, time.perf_counter()
-    while True:
-        ref.step([th], [g], grp)
-        calls += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or calls >= 400:
-            break
+    per_elem = (2 * ELEM[w.param_dtype[0]] + ELEM[w.grad_dtype[0]] + 4 * MOMENT[w.state_fmt]
+                + (16.0 / 256 if w.state_fmt == "q8" else 0.0))
+
+    def rate(threaded: bool):
+        ref = oracle.OracleAdamW([n], w.param_dtype[:1], w.grad_dtype[:1], [0], w.state_fmt,
+                                 threaded=threaded)
+        th = th0.copy()
+        ref.step([th], [g], grp)                              # warm-up call
+        calls, t0 = 0, time.perf_counter()
+        while True:
+            ref.step([th], [g], grp)
+            calls += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or calls >= 4000:
+                break
+        return n * calls / el, calls, el
+
+    one, calls1, el1 = rate(False)
+    threads = int(oracle.omp_lib().oracle_threads())
+    many, calls_n, el_n = rate(True)
     return {
-        "value": n * calls / el,
+        "value": many,
         "unit": "params/s",
-        "cores": 1,
+        "cores": threads,
         "kind": "oracle",
-        "sample": "%d of the %d params (prefix of tensor 0, %s params / %s grads / %s state), "
-                  "%d calls in %.1f s, single-threaded scalar C oracle (gcc -O2, no contraction)"
-                  % (n, w.n_params, w.param_dtype[0], w.grad_dtype[0], w.state_fmt, calls, el),
+        "sample": "%d of the %d params (prefix of tensor 0, %s params / %s grads / %s state); "
+                  "all-core: OpenMP timing build of the scalar C oracle, %d threads, %d calls in "
+                  "%.1f s; single-thread: the parity build, %d calls in %.1f s (gcc -O2, no "
+                  "contraction; both builds give the same bits)"
+                  % (n, w.n_params, w.param_dtype[0], w.grad_dtype[0], w.state_fmt, threads,
+                     calls_n, el_n, calls1, el1),
+        "single_thread_params_per_s": one,
+        "all_core_params_per_s": many,
+        "host_gbps_single_thread": one * per_elem / 1e9,
+        "host_gbps_all_core": many * per_elem / 1e9,
+        "algorithmic_bytes_per_param": per_elem,
+        "nproc": os.cpu_count(),
+        "cpus_available": len(os.sched_getaffinity(0)),
+        "omp_num_threads_env": os.environ.get("OMP_NUM_THREADS"),
+        "cpu_model": _cpu_model(),
     }
 
 
@@ -145,16 +182,22 @@ def torch_compare(torch, w, dev, steps, warmup):
     grads = [torch.randn(p.shape, device=dev).mul_(w.grad_std).to(p.dtype) for p in params]
     stream = torch.cuda.current_stream(dev)
 
-    def timed(fn):
+    def timed(fn, host=None, key=None):
+        """Average time per call between two events around `steps` calls; with
+        `host`, also the host time per call (the calls only queue GPU work)."""
         for _ in range(warmup):
             fn()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         a.record(stream)
+        t0 = time.perf_counter()
         for _ in range(steps):
             fn()
+        t1 = time.perf_counter()
         b.record(stream)
         torch.cuda.synchronize()
+        if host is not None:
+            host[key] = (t1 - t0) / steps * 1e3
         return a.elapsed_time(b) / steps
 
     groups = []
@@ -164,12 +207,34 @@ def torch_compare(torch, w, dev, steps, warmup):
                        "weight_decay": g.weight_decay})
     for p, g in zip(params, grads):
         p.grad = g
+    host = {}
     for mode in ("fused", "foreach"):
         opt = torch.optim.AdamW(groups, **{mode: True})
-        ms = timed(opt.step)
+        ms = timed(opt.step, host, "torch_%s_adamw" % mode)
         res["torch_%s_adamw_ms" % mode] = ms
         del opt
         torch.cuda.empty_cache()
+    # this library's torch wrapper, its own step(): reading .grad of every
+    # parameter each step, and with flat_grads (one pointer table)
+    from tensor_adamw_optimizer_amd import AdamW as ApexwAdamW
+    state_name = {W.F32: "f32", W.BF16: "bf16"}[w.param_dtype[0]]
+    if len(set(w.param_dtype)) == 1:
+        opt = ApexwAdamW(groups, state=state_name)
+        res["apexw_wrapper_step_ms"] = timed(opt.step, host, "apexw_wrapper")
+        opt.close()
+        del opt
+        for p in params:
+            p.grad = None
+        opt = ApexwAdamW(groups, state=state_name, flat_grads=True)
+        for p, g in zip(params, grads):
+            p.grad.copy_(g)
+        res["apexw_wrapper_flat_grads_step_ms"] = timed(opt.step, host, "apexw_wrapper_flat_grads")
+        opt.close()
+        del opt
+        for p, g in zip(params, grads):
+            p.grad = g
+        torch.cuda.empty_cache()
+    res["host_ms_per_call"] = host
     # this library on the same dtypes (moments in the parameter dtype)
     same_fmt = {W.F32: L.APEXW_STATE_F32, W.BF16: L.APEXW_STATE_BF16}[w.param_dtype[0]]
     dts = {W.F32: L.APEXW_F32, W.BF16: L.APEXW_BF16}

@@ -22,6 +22,8 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "apexw_oracle.c")
 LIB_PATH = os.path.join(HERE, "liboracle.so")
+# the same source built with OpenMP: a timing build for the host baseline
+OMP_LIB_PATH = os.path.join(HERE, "liboracle_omp.so")
 
 F32, BF16 = 0, 1
 STATE_F32, STATE_BF16, STATE_Q8 = 0, 1, 2
@@ -37,16 +39,22 @@ class Group(ctypes.Structure):
                 ("weight_decay", ctypes.c_double)]
 
 
-def build(force: bool = False) -> str:
-    """Compile the oracle with gcc (no contraction, no fast-math)."""
-    if force or not os.path.exists(LIB_PATH) or \
-            os.path.getmtime(LIB_PATH) < os.path.getmtime(SRC):
-        tmp = LIB_PATH + ".tmp%d" % os.getpid()
+def _compile(path: str, extra, force: bool) -> str:
+    if force or not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(SRC):
+        tmp = path + ".tmp%d" % os.getpid()
         subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off",
                                "-fno-fast-math", "-fPIC", "-shared", "-Wall",
-                               "-o", tmp, SRC, "-lm"])
-        os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+                               *extra, "-o", tmp, SRC, "-lm"])
+        os.replace(tmp, path)
+    return path
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (no contraction, no fast-math): the
+    single-threaded parity build, and the OpenMP timing build of the same
+    source."""
+    _compile(OMP_LIB_PATH, ["-fopenmp"], force)
+    return _compile(LIB_PATH, ["-Wno-unknown-pragmas"], force)
 
 
 _lib = None
@@ -88,6 +96,8 @@ def load(path: str) -> ctypes.CDLL:
     L.oracle_clip_coef.argtypes = [ctypes.c_double, ctypes.c_double]
     L.oracle_unscale_check.restype = ctypes.c_int32
     L.oracle_unscale_check.argtypes = [ctypes.c_int32, P, P, P, ctypes.c_float]
+    L.oracle_threads.restype = ctypes.c_int32
+    L.oracle_threads.argtypes = []
     L.oracle_adamw_step_three_loops.restype = ctypes.c_int32
     L.oracle_adamw_step_three_loops.argtypes = [
         ctypes.c_int32, P, P, P, P, P, ctypes.c_int32, P, P, P,
@@ -102,6 +112,19 @@ def lib():
             build()
         _lib = load(LIB_PATH)
     return _lib
+
+
+_omp_lib = None
+
+
+def omp_lib():
+    """The OpenMP timing build (same source, same results)."""
+    global _omp_lib
+    if _omp_lib is None:
+        if not os.path.exists(OMP_LIB_PATH):
+            build()
+        _omp_lib = load(OMP_LIB_PATH)
+    return _omp_lib
 
 
 def _ptr(a: Optional[np.ndarray]) -> int:
@@ -182,7 +205,9 @@ class OracleAdamW:
 
     def __init__(self, numels: Sequence[int], param_dtype: Sequence[str],
                  grad_dtype: Sequence[str], group_of: Sequence[int],
-                 state_fmt: str):
+                 state_fmt: str, threaded: bool = False):
+        # threaded: step with the OpenMP timing build (bitwise the same)
+        self._threaded = threaded
         self.numels = [int(n) for n in numels]
         self.n = len(self.numels)
         self.param_dtype = list(param_dtype)
@@ -272,12 +297,13 @@ class OracleAdamW:
                 _groups(groups), len(groups), STATE_CODE[self.state_fmt],
                 _ptr_array(self.m), _ptr_array(self.v), _ptr_array(self.m_scale),
                 _ptr_array(self.v_scale), _ptr(self.t))
+        L = omp_lib() if self._threaded else lib()
         if inv_scale is None and clip_coef is None:
-            rc = lib().oracle_adamw_step(*args, int(bool(found_inf)))
+            rc = L.oracle_adamw_step(*args, int(bool(found_inf)))
         elif clip_coef is None:
-            rc = lib().oracle_adamw_step_scaled(*args, inv_scale, int(bool(found_inf)))
+            rc = L.oracle_adamw_step_scaled(*args, inv_scale, int(bool(found_inf)))
         else:
-            rc = lib().oracle_adamw_step_clipped(
+            rc = L.oracle_adamw_step_clipped(
                 *args, 1.0 if inv_scale is None else inv_scale, clip_coef, int(bool(found_inf)))
         if rc != 0:
             raise ValueError("oracle_adamw_step rejected its arguments")

@@ -10,6 +10,12 @@
  *
  * Build: gcc -O2 -ffp-contract=off -fno-fast-math -shared -fPIC (every fp32
  * operation below is a separately rounded IEEE operation; no FMA contraction).
+ * That single-threaded build is the one the parity tests use.  The same
+ * source built with -fopenmp in addition is a timing build for the host
+ * baseline: the two "omp parallel for" loops below then split a tensor's
+ * elements (or 8-bit blocks) over threads.  Every element and every block is
+ * computed by the same operations either way, so the results are the same
+ * bit for bit (a test checks it).
  *
  * Sources (cited by page title and section):
  *   [M041 §NN]  "Fused optimizers and state precision: optimize the reads and
@@ -61,6 +67,15 @@
 typedef struct {
     double lr, beta1, beta2, eps, weight_decay;
 } oracle_group;
+
+/* Threads the element loops use: 1 in the parity build, the OpenMP team
+ * size in the timing build. */
+#ifdef _OPENMP
+#include <omp.h>
+int32_t oracle_threads(void) { return (int32_t)omp_get_max_threads(); }
+#else
+int32_t oracle_threads(void) { return 1; }
+#endif
 
 /* ------------------------------------------------------------ conversions */
 
@@ -228,6 +243,7 @@ static void update_tensor_dense(int64_t n, int32_t pdt, void *theta,
                                 void *m, void *v, const step_scalars *s,
                                 float inv_scale, float clip_coef)
 {
+#pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i) {
         float th = load_value(pdt, theta, i);
         float g = (load_value(gdt, grad, i) * inv_scale) * clip_coef;
@@ -246,9 +262,10 @@ static void update_tensor_q8(int64_t n, int32_t pdt, void *theta, int32_t gdt,
                              float *ms, float *vs, const step_scalars *s,
                              float inv_scale, float clip_coef)
 {
-    float mf[ORACLE_BLOCK], vf[ORACLE_BLOCK];
     int64_t nblocks = (n + ORACLE_BLOCK - 1) / ORACLE_BLOCK;
+#pragma omp parallel for schedule(static)
     for (int64_t b = 0; b < nblocks; ++b) {
+        float mf[ORACLE_BLOCK], vf[ORACLE_BLOCK];
         int64_t lo = b * ORACLE_BLOCK;
         int64_t len = n - lo < ORACLE_BLOCK ? n - lo : ORACLE_BLOCK;
         oracle_dequantize_signed(len, mq + lo, ms[b], mf);

@@ -622,3 +622,41 @@ def test_clipped_amp_loop_against_fp64():
                                    grp.eps, grp.weight_decay))
     assert 0 < clipped < 12
     assert np.max(np.abs(th - st[0])) / np.max(np.abs(st[0])) <= 1e-5
+
+
+# ------------------------------------------------------------ timing build
+
+@pytest.mark.parametrize("fmt", ["f32", "bf16", "q8"])
+def test_threaded_timing_build_is_bitwise_the_parity_build(fmt):
+    """The OpenMP build of the same oracle source (the host baseline's timing
+    build) splits each tensor's elements or 8-bit blocks over threads; every
+    value must come out exactly as in the single-threaded parity build."""
+    assert oracle.omp_lib().oracle_threads() >= 1
+    rng = np.random.default_rng(15)
+    sizes = [200_003, 65_536, 1000, 3]
+    pdt = ["bf16", "f32", "bf16", "f32"]
+    gdt = ["f32", "f32", "bf16", "f32"]
+    groups = [Group(lr=1e-3, weight_decay=0.1), Group(lr=5e-4, beta1=0.8, eps=1e-6)]
+    gof = [0, 1, 0, 1]
+    runs = []
+    for threaded in (False, True):
+        r = np.random.default_rng(16)
+        o = OracleAdamW(sizes, pdt, gdt, gof, fmt, threaded=threaded)
+        th = [oracle.f32_to_bf16(f32(r.normal(0, 0.02, n))) if d == "bf16" else f32(r.normal(0, 0.02, n))
+              for n, d in zip(sizes, pdt)]
+        for k in range(1, 6):
+            gs = [oracle.f32_to_bf16(f32(r.normal(0, 1e-3, n))) if d == "bf16" else f32(r.normal(0, 1e-3, n))
+                  for n, d in zip(sizes, gdt)]
+            if k == 3:
+                gs[2] = None
+            o.step(th, gs, groups, found_inf=(k == 4), inv_scale=0.5 if k == 5 else None)
+        runs.append((th, o))
+    (th_a, a), (th_b, b) = runs
+    assert np.array_equal(a.t, b.t)
+    for i in range(len(sizes)):
+        assert np.array_equal(th_a[i].view(np.uint8), th_b[i].view(np.uint8)), i
+        assert np.array_equal(a.m[i].view(np.uint8), b.m[i].view(np.uint8)), i
+        assert np.array_equal(a.v[i].view(np.uint8), b.v[i].view(np.uint8)), i
+        if fmt == "q8":
+            assert np.array_equal(a.m_scale[i].view(np.uint32), b.m_scale[i].view(np.uint32)), i
+            assert np.array_equal(a.v_scale[i].view(np.uint32), b.v_scale[i].view(np.uint32)), i
