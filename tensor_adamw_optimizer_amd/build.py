@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "apexw.hip")
 DEPS = [SRC, os.path.join(HERE, "csrc", "apexw_kernels.hpp"),
-        os.path.join(ROOT, "include", "apexw.h")]
+        os.path.join(HERE, "csrc", "apexw_plan.hpp"), os.path.join(ROOT, "include", "apexw.h")]
 LIB = os.path.join(HERE, "libapexw.so")
 ARCH = os.environ.get("APEXW_OFFLOAD_ARCH", "gfx950")
 

@@ -135,7 +135,6 @@ struct WsLayout {
 // load all of them unconditionally.
 constexpr float kConsts[2] = {0.0f, 1.0f};
 
-constexpr int kMaxLaunches = 4;      // (param, grad) dtype pairs
 constexpr int64_t kMaxGrid = 1 << 24;  // workgroups per launch (grid-stride above)
 
 // Lists of at most this many tiles may take the single-launch step (one
@@ -153,7 +152,7 @@ WsLayout ws_layout(int32_t n, const int64_t *numel) {
     w.tiles = w.records + round_up((int64_t)n * (int64_t)sizeof(StepRecord), kTableAlign);
     // each launch's table is padded to a multiple of kXcds entries; the read
     // passes load table entries in fours and may read up to 3 past the end
-    w.partials = w.tiles + round_up((w.n_tiles + kMaxLaunches * kXcds + 4) * 4, kTableAlign);
+    w.partials = w.tiles + round_up(table_entries_reserved(w.n_tiles) * 4, kTableAlign);
     // grad-norm partials: one per read group of every launch, the launches
     // one after another (a launch of t tiles has 8 * ceil(ceil(t/8)/4) <= t + 8
     // groups); entries of groups past a launch's end stay 0
@@ -170,12 +169,7 @@ WsLayout ws_layout(int32_t n, const int64_t *numel) {
 
 bool finite_nonneg(double x) { return std::isfinite(x) && x >= 0.0; }
 
-struct Launch {
-    int pt, gt;
-    int64_t tile_begin, tile_count;     // logical tiles [begin, begin+count)
-    int64_t table_begin, table_stride;  // XCD-major table slice
-    int32_t tensor_begin, tensor_count;
-};
+using Launch = PlanLaunch;
 
 // Default cap on update workgroups resident per compute unit for one launch
 // (0: no cap), from the bytes each element moves.  Measured on MI355X: the
@@ -677,7 +671,7 @@ int apexw_create(int32_t n_tensors, const int64_t *numel, const int32_t *param_d
                               h->device));
 
     // static tables: the tensor of every tile, tiles grouped by dtype pair;
-    // logical tile k of a launch is stored at (k % kXcds) * stride + k / kXcds
+    // (build_plan: logical tile k of a launch at table_position(begin, stride, k))
     {
         int64_t touched = need_state;
         for (int32_t i = 0; i < n_tensors; ++i)
@@ -685,36 +679,14 @@ int apexw_create(int32_t n_tensors, const int64_t *numel, const int32_t *param_d
                                    (grad_dtype[i] == APEXW_F32 ? 4 : 2));
         h->streaming_auto = touched >= kStreamingBytes;
     }
-    std::vector<int32_t> tiles;
+    Plan plan;
+    if (!build_plan(n_tensors, numel, param_dtype, grad_dtype, &plan))
+        return bail(fail(APEXW_ENOMEM, "host allocation failed"));
+    const std::vector<int32_t> &tiles = plan.tiles;
     try {
-        tiles.reserve((size_t)(wl.n_tiles + kMaxLaunches * kXcds));
-        h->tensor_list.reserve(n_tensors);
-        h->first_tile.assign(n_tensors, 0);
-        const int pairs[kMaxLaunches][2] = {{APEXW_F32, APEXW_F32}, {APEXW_F32, APEXW_BF16},
-                                           {APEXW_BF16, APEXW_F32}, {APEXW_BF16, APEXW_BF16}};
-        int64_t logical = 0;
-        std::vector<int32_t> order;
-        for (int p = 0; p < kMaxLaunches; ++p) {
-            Launch L{pairs[p][0], pairs[p][1], logical, 0, (int64_t)tiles.size(), 0,
-                     (int32_t)h->tensor_list.size(), 0};
-            order.clear();
-            for (int32_t i = 0; i < n_tensors; ++i) {
-                if (param_dtype[i] != L.pt || grad_dtype[i] != L.gt) continue;
-                h->tensor_list.push_back(i);
-                h->first_tile[i] = logical + (int64_t)order.size();
-                order.insert(order.end(), (size_t)ceil_div(numel[i], kTile), i);
-            }
-            L.tile_count = (int64_t)order.size();
-            L.tensor_count = (int32_t)h->tensor_list.size() - L.tensor_begin;
-            if (L.tensor_count == 0) continue;
-            L.table_stride = ceil_div(L.tile_count, kXcds);
-            tiles.resize(tiles.size() + (size_t)(L.table_stride * kXcds), 0);
-            for (int64_t k = 0; k < L.tile_count; ++k)
-                tiles[(size_t)(L.table_begin + (k % kXcds) * L.table_stride + k / kXcds)] =
-                    order[(size_t)k];
-            logical += L.tile_count;
-            h->launches.push_back(L);
-        }
+        h->launches = plan.launches;
+        h->tensor_list = plan.tensor_list;
+        h->first_tile = plan.first_tile;
         h->table_entries = (int64_t)tiles.size();
         // the single launch needs a tile in every launch (a launch of empty
         // tensors only advances counters, which the prepare kernel does)

@@ -47,15 +47,13 @@
 #include <stdint.h>
 
 #include "apexw.h"
+#include "apexw_plan.hpp"
 
 namespace apexw {
 
-constexpr int kThreads = 64;                  // one wave64 per workgroup
-constexpr int kVec = 4;                       // contiguous elements per lane
-constexpr int kTile = kThreads * kVec;        // 256 elements per tile
 constexpr int kPrepThreads = 256;             // lanes per prepare workgroup
-constexpr int kXcds = 8;                      // gfx950: 8 XCDs, workgroups dealt round-robin
 static_assert(kTile == APEXW_Q8_BLOCK, "a tile is one 8-bit block");
+static_assert(kF32 == APEXW_F32 && kBF16 == APEXW_BF16, "plan dtype codes are the ABI's");
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -761,13 +759,10 @@ __global__ __launch_bounds__(kPrepThreads) void adamw_prepare_kernel(KernelArgs 
     a.records[i] = r;
 }
 
-// Position of tile k of a launch in its tile table.  The table is stored
-// XCD-major: the dispatcher deals workgroups to the XCDs round-robin, so the
-// workgroups one XCD runs (k, k+8, k+16, ...) read consecutive entries and
-// share the XCD's L2 lines.
+// Position of tile k of a launch in its XCD-major tile table (the plan's
+// table_position).
 __device__ __forceinline__ int64_t table_pos(const KernelArgs &a, int64_t k) {
-    const uint64_t uk = (uint64_t)k;                  // k >= 0: shifts, not divisions
-    return a.table_begin + (int64_t)(uk % kXcds) * a.table_stride + (int64_t)(uk / kXcds);
+    return table_position(a.table_begin, a.table_stride, k);
 }
 
 // The update: one 256-element tile per workgroup (the grid-stride loop only
@@ -1042,19 +1037,13 @@ __global__ __launch_bounds__(kThreads) void adamw_single_step_kernel(KernelArgs 
 // (the caller clears it), by plain stores of the same value; grads are not
 // rewritten -- the update applies inv_scale itself.  One wave per tile, the
 // tiles of one (param, grad) dtype launch.
-// The read passes below take their tiles in groups of kReadBatch: group j
-// is XCD stripe x = j % 8 of the launch's tile table, entries 4c .. 4c+3 with
-// c = j / 8, i.e. the logical tiles x + 8(4c + u), u = 0..3.  Its four table
-// entries are one 16-byte load, then the four grad pointers and descriptor
-// fields are fetched together, then every grad load of the group is issued
-// before any is used, so one wave keeps four tiles in flight.  What each
-// tile contributes does not depend on the grouping.
-constexpr int kReadBatch = 4;
-
-// Number of groups of a launch whose table stripes hold `stride` entries.
-__host__ __device__ __forceinline__ int64_t read_groups(int64_t stride) {
-    return kXcds * ((stride + kReadBatch - 1) / kReadBatch);
-}
+// The read passes below take their tiles in groups of kReadBatch (the plan's
+// read_window): group j is XCD stripe x = j % 8 of the launch's tile table,
+// entries 4c .. 4c+3 with c = j / 8, i.e. the logical tiles x + 8(4c + u),
+// u = 0..3.  Its four table entries are one 16-byte load, then the four grad
+// pointers and descriptor fields are fetched together, then every grad load
+// of the group is issued before any is used, so one wave keeps four tiles in
+// flight.  What each tile contributes does not depend on the grouping.
 
 // A tile of a read group: grad (nullptr: absent), first element, valid
 // length (0 for a tile past the launch end), logical tile index, position in
@@ -1072,10 +1061,10 @@ struct ReadTile {
 // allocation is padded for it); such entries are never used.
 __device__ __forceinline__ bool read_group(const KernelArgs &a, int64_t j,
                                            ReadTile (&t)[kReadBatch]) {
-    const int64_t x = j % kXcds, c = j / kXcds;
-    const int64_t k0 = x + (int64_t)kXcds * kReadBatch * c;
+    const ReadWindow w = read_window(a.table_begin, a.table_stride, j);
+    const int64_t k0 = w.k0;
     if (k0 >= a.tile_count) return false;
-    const int64_t pos0 = a.table_begin + x * a.table_stride + kReadBatch * c;
+    const int64_t pos0 = w.pos0;
     const APEXW_CONST int32_t *row = cptr<int32_t>(a.tile_tensor) + pos0;
     int32_t ti[kReadBatch];
 #pragma unroll
