@@ -233,26 +233,30 @@ kernel_fn pick_carry(int pt, int gt) {
     return adamw_carry_step_kernel<ST, APEXW_BF16, APEXW_BF16, NT, SC>;
 }
 
-template <bool NT, bool SC>
+template <bool NT, bool SC, bool ONE>
 kernel_fn pick_carry_q8(int pt, int gt) {
-    if (pt == APEXW_F32 && gt == APEXW_F32) return adamw_carry_step_q8_kernel<APEXW_F32, APEXW_F32, NT, SC>;
-    if (pt == APEXW_F32 && gt == APEXW_BF16) return adamw_carry_step_q8_kernel<APEXW_F32, APEXW_BF16, NT, SC>;
-    if (pt == APEXW_BF16 && gt == APEXW_F32) return adamw_carry_step_q8_kernel<APEXW_BF16, APEXW_F32, NT, SC>;
-    return adamw_carry_step_q8_kernel<APEXW_BF16, APEXW_BF16, NT, SC>;
+    if (pt == APEXW_F32 && gt == APEXW_F32) return adamw_carry_step_q8_kernel<APEXW_F32, APEXW_F32, NT, SC, ONE>;
+    if (pt == APEXW_F32 && gt == APEXW_BF16) return adamw_carry_step_q8_kernel<APEXW_F32, APEXW_BF16, NT, SC, ONE>;
+    if (pt == APEXW_BF16 && gt == APEXW_F32) return adamw_carry_step_q8_kernel<APEXW_BF16, APEXW_F32, NT, SC, ONE>;
+    return adamw_carry_step_q8_kernel<APEXW_BF16, APEXW_BF16, NT, SC, ONE>;
 }
 
+// one_tile: every workgroup takes exactly one tile (the grid is not capped);
+// the 8-bit kernel then runs its loop-free form
 template <bool NT, bool SC>
-kernel_fn pick_carry_format(int fmt, int pt, int gt) {
+kernel_fn pick_carry_format(int fmt, int pt, int gt, bool one_tile) {
     if (fmt == APEXW_STATE_F32) return pick_carry<APEXW_STATE_F32, NT, SC>(pt, gt);
     if (fmt == APEXW_STATE_BF16) return pick_carry<APEXW_STATE_BF16, NT, SC>(pt, gt);
-    return pick_carry_q8<NT, SC>(pt, gt);
+    return one_tile ? pick_carry_q8<NT, SC, true>(pt, gt) : pick_carry_q8<NT, SC, false>(pt, gt);
 }
 
 // The carried-step kernel (launch mode 3).
-kernel_fn carry_kernel_for(int fmt, int pt, int gt, bool streaming, bool scaled) {
+kernel_fn carry_kernel_for(int fmt, int pt, int gt, bool streaming, bool scaled, bool one_tile) {
     if (streaming)
-        return scaled ? pick_carry_format<true, true>(fmt, pt, gt) : pick_carry_format<true, false>(fmt, pt, gt);
-    return scaled ? pick_carry_format<false, true>(fmt, pt, gt) : pick_carry_format<false, false>(fmt, pt, gt);
+        return scaled ? pick_carry_format<true, true>(fmt, pt, gt, one_tile)
+                      : pick_carry_format<true, false>(fmt, pt, gt, one_tile);
+    return scaled ? pick_carry_format<false, true>(fmt, pt, gt, one_tile)
+                  : pick_carry_format<false, false>(fmt, pt, gt, one_tile);
 }
 
 // The single-launch step kernel (cached accesses: such lists are small).
@@ -882,7 +886,7 @@ int apexw_step_ex(apexw_t h, const apexw_group *groups, int32_t n_groups, void *
         a.table_stride = L.table_stride;
         const int64_t wg = std::min(L.tile_count, cap);
         if (carry) {
-            hipLaunchKernelGGL(carry_kernel_for(h->fmt, L.pt, L.gt, streaming, scaled),
+            hipLaunchKernelGGL(carry_kernel_for(h->fmt, L.pt, L.gt, streaming, scaled, wg == L.tile_count),
                                dim3((unsigned)wg), dim3(kThreads), lds, st, a);
         } else if (single) {
             a.tensor_begin = L.tensor_begin;

@@ -118,7 +118,7 @@ struct StepRecord {
     float inv_scale;                 // grads are unscaled by this first
     float clip_coef;                 // then multiplied by this (norm clipping)
     float rbc1, rbc2;                // 1/bc1, 1/bc2 correctly rounded
-    float div_lo;                    // 2^-100 if bc1, bc2 >= 2^-60, else +inf (see div_uniform)
+    float div_lo;                    // 2^-96 if bc1, bc2 >= 2^-60, else +inf (see div_uniform)
 };
 static_assert(sizeof(StepRecord) == 64, "step record is one 64-byte record");
 
@@ -173,10 +173,11 @@ struct StepScalars {
     float lr, decay, eps;
     float bc1, bc2;                  // 1 - beta1^t, 1 - beta2^t (fp32)
     float rbc1, rbc2;                // 1/bc1, 1/bc2 correctly rounded
-    float div_lo;                    // 2^-100 if bc1, bc2 >= 2^-60, else +inf
+    float div_lo;                    // 2^-96 if bc1, bc2 >= 2^-60, else +inf
     float inv_scale;                 // 1 unless grads arrive scaled
     float clip_coef;                 // 1 unless the grad norm is clipped
 };
+
 
 // beta^n in fp64: square-and-multiply from the least significant bit.
 __device__ __forceinline__ double pow_uint(double b, uint32_t n) {
@@ -212,38 +213,36 @@ __device__ __forceinline__ StepScalars step_scalars(const StepRecord &r) {
 // as a scalar: no per-lane materialisation of p).
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
-// Square root rounded to nearest.  v_sqrt_f32 is within one ulp, so the
-// answer is it or a neighbour: the lower neighbour lo if x <= lo*s, the upper
-// hi if x > hi*s (the squares of the two midpoints lie strictly beyond those
-// products and no float falls in between), decided by the sign of one exact
-// fma residual each.  For x >= 2^-96 those residuals cannot underflow; 0,
-// +inf and NaN come out of the same steps unchanged.  A positive x below
-// 2^-96 takes the compiler's scaled sequence instead (rare).
-__device__ __forceinline__ float sqrt_rn(float x) {
+// Square root rounded to nearest for x >= 2^-96 (or +inf).  v_sqrt_f32 is
+// within one ulp, so the answer is it or a neighbour: the lower neighbour lo
+// if x <= lo*s, the upper hi if x > hi*s (the squares of the two midpoints lie
+// strictly beyond those products and no float falls in between), decided by
+// the sign of one exact fma residual each.  For x >= 2^-96 those residuals
+// cannot underflow; +inf comes out of the same steps unchanged.
+__device__ __forceinline__ float sqrt_normal(float x) {
     const float s = __builtin_amdgcn_sqrtf(x);
     const float lo = __uint_as_float(__float_as_uint(s) - 1u);
     const float hi = __uint_as_float(__float_as_uint(s) + 1u);
     float r = s;
     if (fmaf(-lo, s, x) <= 0.0f) r = lo;
     if (fmaf(-hi, s, x) > 0.0f) r = hi;
-    if (x < 0x1p-96f && x > 0.0f) { // skipped by the whole wave unless a lane needs it
-        asm volatile("");           // (keeps the compiler from speculating it)
-        r = sqrtf(x);
-    }
     return r;
 }
 
 // x / b correctly rounded, for a wave-uniform divisor b in [2^-60, 1] with
-// y = 1/b correctly rounded (lo = 2^-100): q = x*y, then one correction with
+// y = 1/b correctly rounded (lo = 2^-96): q = x*y, then one correction with
 // the exact residual r = fma(-q, b, x), q + r*y rounded once -- Markstein's
-// correction step.  Its result equals the correctly rounded quotient for
-// every pair of fp32 significands (all 2^46 pairs of x and b in [1, 2) were
-// checked against the hardware's correctly rounded division), and scaling x
-// and b by powers of two scales every step exactly as long as nothing leaves
-// the normal range: for 2^-100 <= |x| < 2^64 the residual's lowest bit stays
-// >= 2^-147 and x*y < 2^124.  Other x (zero -- whose sign the short form
-// loses --, subnormals, inf, NaN, huge) take the division, and so does every
-// x when b is outside that range (lo = +inf then).
+// correction step (P. Markstein, "Computation of elementary functions on the
+// IBM RISC System/6000 processor", 1990: with y the correctly rounded
+// reciprocal and q within an ulp of x/b, q + r*y rounds to the correctly
+// rounded quotient).  tests/rules/div_exhaustive.c checks it bit for bit
+// against IEEE division for every pair of fp32 significands of x and b in
+// [1, 2) (2^46 pairs, no mismatch), and scaling x and b by powers of two
+// scales every step exactly as long as nothing leaves the normal range: for
+// 2^-96 <= |x| < 2^64 the residual's lowest bit stays >= 2^-143 and x*y <
+// 2^124.  Other x (zero -- whose sign the short form loses --, subnormals,
+// inf, NaN, huge) take the division, and so does every x when b is outside
+// that range (lo = +inf then).
 __device__ __forceinline__ float div_short(float x, float b, float y) {
     const float q = x * y;
     const float r = fmaf(-q, b, x);
@@ -265,15 +264,32 @@ __device__ __forceinline__ float div_uniform(float x, float b, float y, float lo
 // clip; multiplying by 1 is exact).
 // SC: the step may scale the grads (inv_scale, clip_coef given); a plain
 // step skips the two multiplies by 1, which change nothing.
+//
+// Exact shortcuts, none of which changes a bit of the result:
+//  * m_hat = m when bc1 == 1 (1 - beta1^t rounds to 1 in fp32 once beta1^t <
+//    2^-25, after about 160 steps for beta1 = 0.9): x / 1 == x; a
+//    wave-uniform branch;
+//  * v_hat and its root share one range test: for v in [div_lo, 2^64) with
+//    div_lo = 2^-96 the short division gives v_hat >= v >= 2^-96 (bc2 <= 1 and
+//    rounding is monotone) and at most 2^124, where sqrt_normal is exact; any
+//    other v (0, tiny, huge, inf, NaN) takes the division and the compiler's
+//    correctly rounded square root.
 template <bool SC>
 __device__ __forceinline__ void adamw_update(float &theta, float g_scaled, float &m,
                                              float &v, const StepScalars &s) {
     const float g = SC ? (g_scaled * s.inv_scale) * s.clip_coef : g_scaled;
     m = s.beta1 * m + s.one_minus_beta1 * g;
     v = s.beta2 * v + (s.one_minus_beta2 * g) * g;
-    const float m_hat = div_uniform(m, s.bc1, s.rbc1, s.div_lo);
-    const float v_hat = div_uniform(v, s.bc2, s.rbc2, s.div_lo);
-    const float denom = sqrt_rn(v_hat) + s.eps;
+    float m_hat = m;
+    if (s.bc1 != 1.0f) m_hat = div_uniform(m, s.bc1, s.rbc1, s.div_lo);
+    float v_hat = div_short(v, s.bc2, s.rbc2);
+    float root = sqrt_normal(v_hat);
+    if (!(v >= s.div_lo && v < 0x1p64f)) {           // rare: skipped by the wave
+        asm volatile("");                            // not speculated
+        v_hat = v / s.bc2;
+        root = sqrtf(v_hat);
+    }
+    const float denom = root + s.eps;
     theta = theta * s.decay - (s.lr * m_hat) / denom;
 }
 
@@ -402,25 +418,28 @@ __device__ __forceinline__ void store4_any(void *base, int64_t e, const float (&
 
 // Maximum over the 64 lanes of a wave of non-negative, NaN-free floats,
 // returned wave-uniform.  For such values the order of the bit patterns as
-// unsigned integers is the order of the numbers, so the reduction is integer:
-// quad swaps and the two row mirrors bring each 16-lane row's maximum to all
-// of its lanes (DPP), then the four row maxima are read by lane.
-template <int CTRL>
+// unsigned integers is the order of the numbers, so the reduction is integer
+// (DPP moves): quad swaps and the two row mirrors bring each 16-lane row's
+// maximum to all of its lanes; then row_bcast:15 carries row 0 into row 1 and
+// row 2 into row 3, and row_bcast:31 carries row 1 into rows 2 and 3, so lane
+// 63 ends with the maximum of all four rows.  Lanes of the rows a broadcast
+// does not write receive 0 (the old operand), the identity of the maximum,
+// which lets each move fuse with its maximum into one DPP instruction.
+template <int CTRL, int ROWS>
 __device__ __forceinline__ uint32_t max_dpp(uint32_t u) {
-    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, CTRL, 0xF, 0xF, false);
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, CTRL, ROWS, 0xF, false);
     return u > o ? u : o;
 }
 
 __device__ __forceinline__ float wave_max_nonneg(float x) {
     uint32_t u = __float_as_uint(x);
-    u = max_dpp<0xB1>(u);       // quad_perm [1,0,3,2]
-    u = max_dpp<0x4E>(u);       // quad_perm [2,3,0,1]
-    u = max_dpp<0x141>(u);      // row_half_mirror
-    u = max_dpp<0x140>(u);      // row_mirror
-    const uint32_t r0 = __builtin_amdgcn_readlane(u, 0), r1 = __builtin_amdgcn_readlane(u, 16);
-    const uint32_t r2 = __builtin_amdgcn_readlane(u, 32), r3 = __builtin_amdgcn_readlane(u, 48);
-    const uint32_t a = r0 > r1 ? r0 : r1, b = r2 > r3 ? r2 : r3;
-    return __uint_as_float(a > b ? a : b);
+    u = max_dpp<0xB1, 0xF>(u);       // quad_perm [1,0,3,2]
+    u = max_dpp<0x4E, 0xF>(u);       // quad_perm [2,3,0,1]
+    u = max_dpp<0x141, 0xF>(u);      // row_half_mirror
+    u = max_dpp<0x140, 0xF>(u);      // row_mirror
+    u = max_dpp<0x142, 0xA>(u);      // row_bcast:15, rows 1 and 3
+    u = max_dpp<0x143, 0xC>(u);      // row_bcast:31, rows 2 and 3
+    return __uint_as_float(__builtin_amdgcn_readlane(u, 63));
 }
 
 // ---------------------------------------------------------------- tiles
@@ -528,11 +547,14 @@ struct BlockScale {
 __device__ __forceinline__ BlockScale block_scale(float amax, float levels) {
     BlockScale b;
     b.s = div_short(amax, levels, 1.0f / levels);
+    // amax in [2^-100, FLT_MAX] puts s = amax/levels (levels 127 or 255) in
+    // [2^-108, 2^121]: normal, and its reciprocal normal too
+    b.fast = true;
     if (!(amax >= 0x1p-100f && amax <= 0x1.fffffep127f)) {   // uniform; rare
         asm volatile("");
         b.s = amax / levels;
+        b.fast = b.s >= 0x1p-126f && b.s <= 0x1p126f;
     }
-    b.fast = b.s >= 0x1p-126f && b.s <= 0x1p126f;
     b.inv = __builtin_amdgcn_rcpf(b.s);
     return b;
 }
@@ -696,7 +718,7 @@ __device__ __forceinline__ BiasRecord bias_record(double beta1_d, double beta2_d
     b.bc2 = (float)(1.0 - pow_uint(beta2_d, (uint32_t)t));
     b.rbc1 = 1.0f / b.bc1;
     b.rbc2 = 1.0f / b.bc2;
-    b.div_lo = b.bc1 >= 0x1p-60f && b.bc2 >= 0x1p-60f ? 0x1p-100f : __builtin_inff();   // both are <= 1
+    b.div_lo = b.bc1 >= 0x1p-60f && b.bc2 >= 0x1p-60f ? 0x1p-96f : __builtin_inff();   // both are <= 1
     return b;
 }
 
@@ -814,7 +836,10 @@ __global__ __launch_bounds__(kThreads) void adamw_step_kernel(KernelArgs a) {
 // with the metadata, only the first tile's value counts), so no ordering
 // between workgroups is needed.  Results are bitwise those of the other
 // modes: the same fp64 and fp32 operations form the same scalars.
-template <int ST, int PT, int GT, bool NT, bool SC>
+// ONE: the grid has a workgroup per tile, so each takes exactly one tile and
+// the body is straight-line code (no loop, so nothing is hoisted into a
+// preheader that every wave would run for its one tile).
+template <int ST, int PT, int GT, bool NT, bool SC, bool ONE = false>
 __device__ __forceinline__ void carry_step(const KernelArgs &a) {
     const APEXW_CONST int32_t *tile_tensor = cptr<int32_t>(a.tile_tensor);
     const float fi = *cptr<float>(a.found_inf);
@@ -893,6 +918,7 @@ __device__ __forceinline__ void carry_step(const KernelArgs &a) {
             }
             a.bias_next[i] = nb;
         }
+        if constexpr (ONE) break;
         k += gridDim.x;
         if (k >= a.tile_count) break;
         i = tile_tensor[table_pos(a, k)];
@@ -912,10 +938,10 @@ __global__ __launch_bounds__(kThreads) void adamw_carry_step_kernel(KernelArgs a
 // 51.3-51.8 us per step).  The dense formats keep their allocation (their
 // residency is capped lower, and the budget's register moves cost bf16
 // moments 1%).
-template <int PT, int GT, bool NT, bool SC>
+template <int PT, int GT, bool NT, bool SC, bool ONE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_num_sgpr(80)))
 void adamw_carry_step_q8_kernel(KernelArgs a) {
-    carry_step<APEXW_STATE_Q8, PT, GT, NT, SC>(a);
+    carry_step<APEXW_STATE_Q8, PT, GT, NT, SC, ONE>(a);
 }
 
 // Starts (or restarts) the carried chain: one lane per tensor writes the
