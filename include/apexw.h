@@ -109,8 +109,8 @@ typedef struct {
  * format fmt: the moment payload (8, 4 or 2 bytes per element), for Q8 two
  * fp32 scales per 256-element block (blocks never span tensors), and one
  * int32 step counter per tensor, plus padding that puts each tensor's moment
- * arrays on 64-byte boundaries (none when numel times the moment size is a
- * multiple of 64 for every tensor).  The library writes the padding (zeros).
+ * arrays on 128-byte boundaries (none when numel times the moment size is a
+ * multiple of 128 for every tensor).  The library writes the padding (zeros).
  * For the 392-tensor LoRA set of the "ApexW measured in Unsloth" page this is
  * 185.5015 / 92.7515 / 47.1011 MiB for F32 / BF16 / Q8, the page's
  * 185.501 / 92.751 / 47.101 MB optimizer-state figures.

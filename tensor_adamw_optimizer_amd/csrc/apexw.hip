@@ -1,17 +1,20 @@
 // apexw.hip -- host engine and C ABI of the fused multi-tensor AdamW step.
 //
 // The engine turns a parameter list into device tables once (tensor
-// descriptors, a table giving the tensor of every 256-element tile), lays the
-// optimizer state out in one caller-owned buffer, and on every step queues a
-// small prepare kernel (step counters, per-tensor step records) followed by
-// one update kernel per (parameter dtype, grad dtype) pair present, each with
-// one workgroup per tile -- or, for small lists, only the per-pair kernels,
-// which then form the step records themselves and advance the counters from
-// their last workgroup.  Per call it only compares the param / grad pointer
-// arrays with the previous call's (one asynchronous upload when they differ)
-// and forms the per-group fp32 scalars, which travel in the kernel arguments.
-// It never synchronises with the host inside a step and allocates no device
-// memory.
+// descriptors, the XCD-major table giving the tensor of every 256-element
+// tile, built by apexw_plan.hpp), lays the optimizer state out in one
+// caller-owned buffer, and on every step queues, by default, one carried-step
+// launch per (parameter dtype, grad dtype) pair present, each with one
+// workgroup per tile: the bias corrections come from the previous step, and
+// each tensor's first tile advances its counter and writes the next ones.
+// Steps whose hyperparameters live in device memory, steps queued under
+// stream capture (and every step after one), and lists with an empty tensor
+// take a prepare launch plus the update launches, or for small lists a single
+// launch per pair (apexw_set_launch_mode).  Per call the engine only compares
+// the param / grad pointer arrays with the previous call's (one asynchronous
+// upload when they differ) and forms the per-group fp32 scalars, which travel
+// in the kernel arguments.  It never synchronises with the host inside a step
+// and allocates no device memory.
 //
 // Sources: "Fused optimizers and state precision" (ai-infra-kb M041),
 // sections 02-06; "Apex fused optimizers" guide (qwbw.cn), sections 二/三
@@ -54,11 +57,13 @@ int fail(int code, const char *fmt, ...) {
                         hipGetErrorString(e_));                              \
     } while (0)
 
-// Every moment array starts and ends on a 64-byte boundary: aligned vector
-// loads, and the update writes a tensor's last partial 64-byte chunk of m and
-// v whole (zeros past the end) -- a partly written chunk costs the memory a
-// read-modify-write.
-constexpr int64_t kMomentAlign = 64;
+// Every moment array starts and ends on a 128-byte boundary, the cache line:
+// a tile's moments (1 KiB fp32, 512 B bf16, 256 B of 8-bit codes) then fill
+// whole lines, so no line is shared by two tiles -- which run on different
+// XCDs, whose separate L2s would each fetch it -- and the update writes a
+// tensor's last partial line of m and v whole (zeros past the end), since a
+// partly written line costs the memory a read-modify-write.
+constexpr int64_t kMomentAlign = 128;
 constexpr int64_t kTableAlign = 256;
 
 int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
@@ -86,7 +91,7 @@ int check_list(int32_t n, const int64_t *numel) {
 
 // State layout: every m array, every v array, (Q8) every m scale array and
 // every v scale array, then the int32 step counters.  Moment arrays start and
-// end on 64-byte boundaries.
+// end on 128-byte boundaries.
 int compute_layout(int32_t n, const int64_t *numel, int32_t fmt,
                    apexw_tensor_state *per_tensor, int64_t *steps_off,
                    int64_t *total) {
@@ -225,12 +230,12 @@ kernel_fn pick_single(int pt, int gt) {
     return adamw_single_step_kernel<ST, APEXW_BF16, APEXW_BF16, SC>;
 }
 
-template <int ST, bool NT, bool SC>
+template <int ST, bool NT, bool SC, bool ONE>
 kernel_fn pick_carry(int pt, int gt) {
-    if (pt == APEXW_F32 && gt == APEXW_F32) return adamw_carry_step_kernel<ST, APEXW_F32, APEXW_F32, NT, SC>;
-    if (pt == APEXW_F32 && gt == APEXW_BF16) return adamw_carry_step_kernel<ST, APEXW_F32, APEXW_BF16, NT, SC>;
-    if (pt == APEXW_BF16 && gt == APEXW_F32) return adamw_carry_step_kernel<ST, APEXW_BF16, APEXW_F32, NT, SC>;
-    return adamw_carry_step_kernel<ST, APEXW_BF16, APEXW_BF16, NT, SC>;
+    if (pt == APEXW_F32 && gt == APEXW_F32) return adamw_carry_step_kernel<ST, APEXW_F32, APEXW_F32, NT, SC, ONE>;
+    if (pt == APEXW_F32 && gt == APEXW_BF16) return adamw_carry_step_kernel<ST, APEXW_F32, APEXW_BF16, NT, SC, ONE>;
+    if (pt == APEXW_BF16 && gt == APEXW_F32) return adamw_carry_step_kernel<ST, APEXW_BF16, APEXW_F32, NT, SC, ONE>;
+    return adamw_carry_step_kernel<ST, APEXW_BF16, APEXW_BF16, NT, SC, ONE>;
 }
 
 template <bool NT, bool SC, bool ONE>
@@ -242,11 +247,15 @@ kernel_fn pick_carry_q8(int pt, int gt) {
 }
 
 // one_tile: every workgroup takes exactly one tile (the grid is not capped);
-// the 8-bit kernel then runs its loop-free form
+// the kernels then run their loop-free form
 template <bool NT, bool SC>
 kernel_fn pick_carry_format(int fmt, int pt, int gt, bool one_tile) {
-    if (fmt == APEXW_STATE_F32) return pick_carry<APEXW_STATE_F32, NT, SC>(pt, gt);
-    if (fmt == APEXW_STATE_BF16) return pick_carry<APEXW_STATE_BF16, NT, SC>(pt, gt);
+    if (fmt == APEXW_STATE_F32)
+        return one_tile ? pick_carry<APEXW_STATE_F32, NT, SC, true>(pt, gt)
+                        : pick_carry<APEXW_STATE_F32, NT, SC, false>(pt, gt);
+    if (fmt == APEXW_STATE_BF16)
+        return one_tile ? pick_carry<APEXW_STATE_BF16, NT, SC, true>(pt, gt)
+                        : pick_carry<APEXW_STATE_BF16, NT, SC, false>(pt, gt);
     return one_tile ? pick_carry_q8<NT, SC, true>(pt, gt) : pick_carry_q8<NT, SC, false>(pt, gt);
 }
 
@@ -885,6 +894,15 @@ int apexw_step_ex(apexw_t h, const apexw_group *groups, int32_t n_groups, void *
         a.table_begin = L.table_begin;
         a.table_stride = L.table_stride;
         const int64_t wg = std::min(L.tile_count, cap);
+        a.few = 0;
+        if (carry && wg == L.tile_count && L.tensor_count <= kFewTensors) {   // carry_ok: none empty
+            a.few = L.tensor_count;
+            for (int32_t j = 0; j < kFewTensors; ++j) {
+                const int32_t t = h->tensor_list[(size_t)(L.tensor_begin + std::min(j, L.tensor_count - 1))];
+                a.few_tensor[j] = t;
+                a.few_first[j] = (int32_t)(h->first_tile[(size_t)t] - L.tile_begin);
+            }
+        }
         if (carry) {
             hipLaunchKernelGGL(carry_kernel_for(h->fmt, L.pt, L.gt, streaming, scaled, wg == L.tile_count),
                                dim3((unsigned)wg), dim3(kThreads), lds, st, a);

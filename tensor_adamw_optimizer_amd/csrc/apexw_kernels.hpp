@@ -1,34 +1,38 @@
 // apexw_kernels.hpp -- gfx950 device code of the fused multi-tensor AdamW step.
 //
-// Two kernels per step (prepare, then one update launch per (param, grad)
-// dtype pair), or for small lists one (adamw_single_step_kernel, which forms
-// the step records itself and advances the counters from its last
-// workgroup, found through a tree of arrival counters):
-//  * adamw_prepare_kernel -- one lane per tensor: unless found_inf is set,
-//    advances the step counter of every tensor that has a grad and writes
-//    that tensor's step record (grad pointer, fp32 group scalars and bias
-//    corrections 1-beta1^t, 1-beta2^t from fp64 square-and-multiply) to the
-//    workspace; a tensor without a grad, or every tensor when found_inf is
-//    set, gets a record without a grad and no counter moves;
-//  * adamw_step_kernel -- the streaming update.  The parameter list is cut
-//    into 256-element tiles (a tile never spans two tensors) and each tile is
-//    one workgroup of one wave64: lane l owns the 4 contiguous elements
-//    4l..4l+3, so every load instruction of the wave covers one contiguous
-//    256-element run (fp32: 1 KiB as dwordx4, bf16: 512 B as dwordx2, 8-bit
-//    codes: 256 B as dword), and in the 8-bit format the tile is exactly one
-//    quantisation block.  Every element is read once and written once:
-//    theta, g, m, v in; theta, m, v out (28 B per fp32 element, the one-pass
-//    ledger of the M041 page, section 04).  Small one-tile workgroups keep
-//    many independent read and write streams in flight.  With fp32 moments
-//    the path is HBM-bandwidth bound; with 8-bit moments the exact fp32
-//    arithmetic (three correctly rounded divisions per element, the block
-//    reductions, decode and encode) is the limit.  There is no contraction
-//    in the method, so no matrix-core work; the arithmetic is ordinary fp32
-//    VALU code compiled without contraction, with exact shortcuts where the
-//    hardware offers them (bf16 pair conversion, square root from
-//    v_sqrt_f32 plus a residual check, division by the per-tensor bias
-//    corrections from their reciprocals plus one residual correction, 8-bit
-//    codes from v_rcp_f32 plus a tie guard).
+// The parameter list is cut into 256-element tiles (a tile never spans two
+// tensors) and each tile is one workgroup of one wave64: lane l owns the 4
+// contiguous elements 4l..4l+3, so every load instruction of the wave covers
+// one contiguous 256-element run (fp32: 1 KiB as dwordx4, bf16: 512 B as
+// dwordx2, 8-bit codes: 256 B as dword), and in the 8-bit format the tile is
+// exactly one quantisation block.  Every element is read once and written
+// once: theta, g, m, v in; theta, m, v out (28 B per fp32 element, the
+// one-pass ledger of the M041 page, section 04).  Small one-tile workgroups
+// keep many independent read and write streams in flight.  A step is one of:
+//  * adamw_carry_step_kernel (and its 8-bit form adamw_carry_step_q8_kernel)
+//    -- the default: one launch per (param, grad) dtype pair.  Every
+//    workgroup takes its tensor's bias corrections 1-beta1^t, 1-beta2^t from
+//    an array the previous step wrote; the first tile of each tensor
+//    advances the tensor's step counter (only with a grad and without
+//    found_inf) and writes the corrections for the step after into a second
+//    array; carry_init_kernel starts the chain from the counters;
+//  * adamw_prepare_kernel, then adamw_step_kernel -- one lane per tensor
+//    writes each tensor's step record (grad pointer, fp32 group scalars,
+//    bias corrections from fp64 square-and-multiply) and advances its
+//    counter, then the update launches read the records (steps whose
+//    hyperparameters live in device memory, and lists with an empty tensor);
+//  * adamw_single_step_kernel -- small lists: every workgroup forms its
+//    tensor's record itself and the last to finish, found through a tree of
+//    arrival counters, advances the counters.
+// With fp32 moments the path is HBM-bandwidth bound; with 8-bit moments the
+// exact fp32 arithmetic (the correctly rounded division and square root per
+// element, the block reductions, decode and encode) is the limit.  There is
+// no contraction in the method, so no matrix-core work; the arithmetic is
+// ordinary fp32 VALU code compiled without contraction, with exact shortcuts
+// where the hardware offers them (bf16 pair conversion, square root from
+// v_sqrt_f32 plus a residual check, division by the per-tensor bias
+// corrections from their reciprocals plus one residual correction, 8-bit
+// codes from v_rcp_f32 plus a tie guard).
 //
 // Read-only passes for the mixed-precision recipe and clipping:
 //  * unscale_check_kernel -- any non-finite unscaled grad sets found_inf;
@@ -52,6 +56,7 @@
 namespace apexw {
 
 constexpr int kPrepThreads = 256;             // lanes per prepare workgroup
+constexpr int kFewTensors = 8;                // launches this small skip the tile table
 static_assert(kTile == APEXW_Q8_BLOCK, "a tile is one 8-bit block");
 static_assert(kF32 == APEXW_F32 && kBF16 == APEXW_BF16, "plan dtype codes are the ABI's");
 
@@ -164,6 +169,11 @@ struct KernelArgs {
     uint32_t *done;                  // single-launch step: arrival counters
     const BiasRecord *bias_cur;      // carried step: this step's bias corrections
     BiasRecord *bias_next;           //   and the next step's (written by first tiles)
+    // carried step over a launch of at most kFewTensors tensors, none empty
+    // (0 otherwise): the tile's tensor is found from these, not the tile table
+    int32_t few;                     // tensors of the launch
+    int32_t few_first[kFewTensors];  // launch-relative first tile of each
+    int32_t few_tensor[kFewTensors]; // their tensor indices
     GroupScalars groups[APEXW_MAX_GROUPS];
 };
 
@@ -471,11 +481,11 @@ __device__ __forceinline__ void tile_dense(const TensorDesc &d, const void *grad
         store4<ST, NT>(d.v, e, v);
     } else {
         // m and v are read and written as whole vectors up to the end of
-        // their last 64-byte chunk (the state arrays are padded for it, and
+        // their last 128-byte line (the state arrays are padded for it, and
         // the padding is always written as +0); theta and g as vectors in
         // the lanes wholly inside the tensor, element by element in the one
         // lane that straddles its end
-        constexpr int kChunk = ST == APEXW_F32 ? 16 : 32;
+        constexpr int kChunk = ST == APEXW_F32 ? 32 : 64;
         const int n_pad = (n + kChunk - 1) / kChunk * kChunk;
         const bool pv = vec_aligned<PT>(d.param), gv = vec_aligned<GT>(grad);
         const bool inside = off + kVec <= n, padded = off < n_pad;
@@ -658,9 +668,9 @@ __device__ __forceinline__ void tile_q8(const TensorDesc &d, const void *grad,
         store_u32<NT>(d.v, e, pack_codes_unsigned(v, bv));
         store4_any<PT, NT>(d.param, e, th, pv);
     } else {
-        // codes up to the end of their last 64-byte chunk (zero codes past
+        // codes up to the end of their last 128-byte line (zero codes past
         // the tensor: the state arrays are padded for it), theta to its end
-        const int n_pad = (n + 63) / 64 * 64;
+        const int n_pad = (n + 127) / 128 * 128;
 #pragma unroll
         for (int j = 0; j < kVec; ++j) {
             if (off + j < n) {
@@ -836,6 +846,26 @@ __global__ __launch_bounds__(kThreads) void adamw_step_kernel(KernelArgs a) {
 // with the metadata, only the first tile's value counts), so no ordering
 // between workgroups is needed.  Results are bitwise those of the other
 // modes: the same fp64 and fp32 operations form the same scalars.
+// The tensor of launch-relative tile k: for a launch of a few non-empty
+// tensors, the number of tensors whose first tile is at or before k (scalar
+// compares on kernel arguments, no memory round trip before the tile's
+// metadata loads); otherwise the tile table.  Compiled in (FEW) only for
+// the loop-free kernels: across a grid-stride loop the eight bounds would
+// stay live in scalar registers.
+template <bool FEW>
+__device__ __forceinline__ int32_t tile_owner(const KernelArgs &a, const APEXW_CONST int32_t *tile_tensor,
+                                              int64_t k) {
+    if (FEW && a.few > 0) {                    // wave-uniform
+        // launch-relative tile indices fit 32 bits (lists have < 2^31 tiles)
+        const int32_t k32 = (int32_t)k;
+        int32_t j = 0;
+#pragma unroll
+        for (int u = 1; u < kFewTensors; ++u) j += (u < a.few && k32 >= a.few_first[u]) ? 1 : 0;
+        return a.few_tensor[j];
+    }
+    return tile_tensor[table_pos(a, k)];
+}
+
 // ONE: the grid has a workgroup per tile, so each takes exactly one tile and
 // the body is straight-line code (no loop, so nothing is hoisted into a
 // preheader that every wave would run for its one tile).
@@ -846,7 +876,7 @@ __device__ __forceinline__ void carry_step(const KernelArgs &a) {
     const float inv_scale = *cptr<float>(a.inv_scale);
     const float clip_coef = *cptr<float>(a.clip_coef);
     int64_t k = blockIdx.x;                    // < tile_count: grid <= tiles
-    int32_t i = tile_tensor[table_pos(a, k)];
+    int32_t i = tile_owner<ONE>(a, tile_tensor, k);
     for (;;) {
         const TensorDesc d = load_uniform(a.desc, i);
         const void *g_ptr = reinterpret_cast<const void *>(cptr<uint64_t>(a.grads)[i]);
@@ -921,13 +951,13 @@ __device__ __forceinline__ void carry_step(const KernelArgs &a) {
         if constexpr (ONE) break;
         k += gridDim.x;
         if (k >= a.tile_count) break;
-        i = tile_tensor[table_pos(a, k)];
+        i = tile_owner<ONE>(a, tile_tensor, k);
     }
 }
 
-template <int ST, int PT, int GT, bool NT, bool SC>
+template <int ST, int PT, int GT, bool NT, bool SC, bool ONE>
 __global__ __launch_bounds__(kThreads) void adamw_carry_step_kernel(KernelArgs a) {
-    carry_step<ST, PT, GT, NT, SC>(a);
+    carry_step<ST, PT, GT, NT, SC, ONE>(a);
 }
 
 // The 8-bit carried step under a budget of 80 scalar registers (the

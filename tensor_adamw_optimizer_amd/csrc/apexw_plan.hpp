@@ -13,8 +13,10 @@
 // never spans two tensors.
 #pragma once
 
+#include <stddef.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <new>
 #include <vector>
 
@@ -79,17 +81,22 @@ struct PlanLaunch {
 struct Plan {
     std::vector<PlanLaunch> launches;   // only dtype pairs that hold a tensor
     std::vector<int32_t> tiles;         // the tile table: tensor of each entry
-    std::vector<int32_t> tensor_list;   // tensors launch by launch, list order within
+    std::vector<int32_t> tensor_list;   // tensors launch by launch, the largest last
     std::vector<int64_t> first_tile;    // per tensor: its first logical tile
     int64_t n_tiles = 0;
 };
 
 // The plan of a list of n tensors: launches in the fixed pair order (fp32,
 // fp32), (fp32, bf16), (bf16, fp32), (bf16, bf16); within a launch, tensors in
-// list order and each tensor's ceil(numel/256) tiles in order; logical tile k
-// of a launch is stored at table_position(table_begin, stride, k), and the
-// padding entries of the last column hold 0.  An empty tensor joins its
-// launch's tensor list with no tile.  Returns false if memory runs out.
+// list order except that the one with the most tiles (the first such) goes
+// last, and each tensor's ceil(numel/256) tiles in order; logical tile k of a
+// launch is stored at table_position(table_begin, stride, k), and the padding
+// entries of the last column hold 0.  Workgroups are dispatched in logical
+// tile order, so the launch ends on full tiles of its largest tensor rather
+// than on a small tensor's tile -- which is its first tile (it also forms the
+// next step's bias corrections) and often partial, both longer paths.  An
+// empty tensor joins its launch's tensor list with no tile.  Returns false if
+// memory runs out.
 inline bool build_plan(int32_t n, const int64_t *numel, const int32_t *pdt, const int32_t *gdt,
                        Plan *out) {
     try {
@@ -100,13 +107,22 @@ inline bool build_plan(int32_t n, const int64_t *numel, const int32_t *pdt, cons
         p.tiles.reserve((size_t)(p.n_tiles + kMaxLaunches * kXcds));
         const int pairs[kMaxLaunches][2] = {{kF32, kF32}, {kF32, kBF16}, {kBF16, kF32}, {kBF16, kBF16}};
         int64_t logical = 0;
-        std::vector<int32_t> order;
+        std::vector<int32_t> order, members;
         for (int q = 0; q < kMaxLaunches; ++q) {
             PlanLaunch L{pairs[q][0], pairs[q][1], logical, 0, (int64_t)p.tiles.size(), 0,
                          (int32_t)p.tensor_list.size(), 0};
             order.clear();
-            for (int32_t i = 0; i < n; ++i) {
-                if (pdt[i] != L.pt || gdt[i] != L.gt) continue;
+            members.clear();
+            for (int32_t i = 0; i < n; ++i)
+                if (pdt[i] == L.pt && gdt[i] == L.gt) members.push_back(i);
+            if (!members.empty()) {
+                size_t big = 0;
+                for (size_t u = 1; u < members.size(); ++u)
+                    if (numel[members[u]] > numel[members[big]]) big = u;
+                std::rotate(members.begin() + (ptrdiff_t)big, members.begin() + (ptrdiff_t)big + 1,
+                            members.end());
+            }
+            for (const int32_t i : members) {
                 p.tensor_list.push_back(i);
                 p.first_tile[(size_t)i] = logical + (int64_t)order.size();
                 order.insert(order.end(), (size_t)plan_ceil_div(numel[i], kTile), i);

@@ -164,10 +164,10 @@ def _check_layout(numel, fmt):
     eb = {L.APEXW_STATE_F32: 4, L.APEXW_STATE_BF16: 2, L.APEXW_STATE_Q8: 1}[fmt]
     spans = []
     for (m, v, ms, vs), n in zip(per, numel):
-        # moment arrays start and end on 64-byte boundaries (the padding the
-        # update writes whole), scales on 4-byte ones
-        assert m % 64 == 0 and v % 64 == 0
-        pad = -(-n * eb // 64) * 64
+        # moment arrays start and end on 128-byte boundaries (whole cache
+        # lines; the padding the update writes whole), scales on 4-byte ones
+        assert m % 128 == 0 and v % 128 == 0
+        pad = -(-n * eb // 128) * 128
         spans += [(m, m + pad), (v, v + pad)]
         if fmt == L.APEXW_STATE_Q8:
             nb = -(-n // 256)
@@ -182,7 +182,7 @@ def _check_layout(numel, fmt):
 
 def test_layout_property_random_lists():
     """Random tensor lists (sizes 0 .. 2^21, up to 300 tensors, every
-    format): moment arrays padded to whole 64-byte chunks, every region
+    format): moment arrays padded to whole 128-byte lines, every region
     disjoint, the step counters last; the workspace never shrinks when a
     tensor grows."""
     import numpy as np
