@@ -46,6 +46,24 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+CHECK_SRC = os.path.join(ROOT, "tests", "rules", "bf16_all.hip")
+CHECK_LIB = os.path.join(ROOT, "tests", "rules", "libbf16_all.so")
+
+
+def build_checks(verbose: bool = False) -> str:
+    """The test-only device check of the bf16 conversion (tests/rules)."""
+    tmp = CHECK_LIB + ".tmp%d" % os.getpid()
+    cmd = ["hipcc", *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
+           "-o", tmp, CHECK_SRC]
+    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if res.returncode != 0:
+        if os.path.exists(tmp):
+            os.remove(tmp)
+        raise RuntimeError("hipcc failed:\n" + res.stdout)
+    os.replace(tmp, CHECK_LIB)
+    return CHECK_LIB
+
+
 def is_stale() -> bool:
     if not os.path.exists(LIB):
         return True
