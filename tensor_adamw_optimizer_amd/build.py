@@ -46,22 +46,32 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
-CHECK_SRC = os.path.join(ROOT, "tests", "rules", "bf16_all.hip")
-CHECK_LIB = os.path.join(ROOT, "tests", "rules", "libbf16_all.so")
+RULES = os.path.join(ROOT, "tests", "rules")
+CHECKS = [(os.path.join(RULES, src), os.path.join(RULES, lib))
+          for src, lib in (("bf16_all.hip", "libbf16_all.so"),
+                           ("rcp_sqrt_all.hip", "librcp_sqrt_all.so"))]
 
 
-def build_checks(verbose: bool = False) -> str:
-    """The test-only device check of the bf16 conversion (tests/rules)."""
-    tmp = CHECK_LIB + ".tmp%d" % os.getpid()
-    cmd = ["hipcc", *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
-           "-o", tmp, CHECK_SRC]
-    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    if res.returncode != 0:
-        if os.path.exists(tmp):
-            os.remove(tmp)
-        raise RuntimeError("hipcc failed:\n" + res.stdout)
-    os.replace(tmp, CHECK_LIB)
-    return CHECK_LIB
+def build_checks(verbose: bool = False) -> list:
+    """The test-only device checks of the kernel header's conversion,
+    square root, reciprocal and short division (tests/rules), each its own
+    library (each includes the kernel header), built with the library's
+    flags."""
+    built = []
+    for src, lib in CHECKS:
+        tmp = lib + ".tmp%d" % os.getpid()
+        cmd = ["hipcc", *FLAGS, "-I", os.path.join(ROOT, "include"), "-I",
+               os.path.join(HERE, "csrc"), "-o", tmp, src]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+        if res.returncode != 0:
+            if os.path.exists(tmp):
+                os.remove(tmp)
+            raise RuntimeError("hipcc failed:\n" + res.stdout)
+        os.replace(tmp, lib)
+        built.append(lib)
+    return built
 
 
 def is_stale() -> bool:

@@ -30,8 +30,9 @@
 // no contraction in the method, so no matrix-core work; the arithmetic is
 // ordinary fp32 VALU code compiled without contraction, with exact shortcuts
 // where the hardware offers them (bf16 pair conversion, square root from
-// v_sqrt_f32 plus a residual check, division by the per-tensor bias
-// corrections from their reciprocals plus one residual correction, 8-bit
+// v_sqrt_f32 and v_rsq_f32 plus one residual correction, every division --
+// by the per-tensor bias corrections and by the per-element denominator --
+// from a correctly rounded reciprocal plus one residual correction, 8-bit
 // codes from v_rcp_f32 plus a tie guard).
 //
 // Read-only passes for the mixed-precision recipe and clipping:
@@ -184,9 +185,19 @@ struct StepScalars {
     float bc1, bc2;                  // 1 - beta1^t, 1 - beta2^t (fp32)
     float rbc1, rbc2;                // 1/bc1, 1/bc2 correctly rounded
     float div_lo;                    // 2^-96 if bc1, bc2 >= 2^-60, else +inf
+    float x_lo;                      // 2^-96 if 0 <= eps <= 2^28, else +inf
     float inv_scale;                 // 1 unless grads arrive scaled
     float clip_coef;                 // 1 unless the grad norm is clipped
 };
+
+// The lower bound of |lr * m_hat| for the short form of the update's last
+// division (adamw_update): 2^-96 when eps lies in [0, 2^28], else +inf (every
+// element then takes the division).  An integer test on the bit pattern
+// (+0 .. 2^28 are the patterns 0 .. 0x4d800000; -0, negatives and NaNs lie
+// above), so it needs no vector instruction.
+__device__ __forceinline__ float step_x_lo(float eps) {
+    return __float_as_uint(eps) <= 0x4d800000u ? 0x1p-96f : __builtin_inff();
+}
 
 
 // beta^n in fp64: square-and-multiply from the least significant bit.
@@ -214,6 +225,7 @@ __device__ __forceinline__ StepScalars step_scalars(const StepRecord &r) {
     s.rbc1 = r.rbc1;
     s.rbc2 = r.rbc2;
     s.div_lo = r.div_lo;
+    s.x_lo = step_x_lo(r.eps);
     s.inv_scale = r.inv_scale;
     s.clip_coef = r.clip_coef;
     return s;
@@ -223,24 +235,31 @@ __device__ __forceinline__ StepScalars step_scalars(const StepRecord &r) {
 // as a scalar: no per-lane materialisation of p).
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
-// Square root rounded to nearest for x >= 2^-96 (or +inf).  v_sqrt_f32 is
-// within one ulp, so the answer is it or a neighbour: the lower neighbour lo
-// if x <= lo*s, the upper hi if x > hi*s (the squares of the two midpoints lie
-// strictly beyond those products and no float falls in between), decided by
-// the sign of one exact fma residual each.  For x >= 2^-96 those residuals
-// cannot underflow; +inf comes out of the same steps unchanged.
-__device__ __forceinline__ float sqrt_normal(float x) {
+// Square root rounded to nearest for x in [2^-96, 2^64): s = v_sqrt_f32(x)
+// (within one ulp, not always the nearest), then one correction with the
+// exact residual x - s*s (an fma) times half the reciprocal square root
+// (v_rsq_f32), rounded once.  tests/rules/rcp_sqrt_all.hip checks the result
+// on the device against the nearest square root for every fp32 x in that
+// range (an exact fp64 test of the two midpoints; no mismatch).
+__device__ __forceinline__ float sqrt_rn(float x) {
     const float s = __builtin_amdgcn_sqrtf(x);
-    const float lo = __uint_as_float(__float_as_uint(s) - 1u);
-    const float hi = __uint_as_float(__float_as_uint(s) + 1u);
-    float r = s;
-    if (fmaf(-lo, s, x) <= 0.0f) r = lo;
-    if (fmaf(-hi, s, x) > 0.0f) r = hi;
-    return r;
+    const float h = 0.5f * __builtin_amdgcn_rsqf(x);
+    return fmaf(fmaf(-s, s, x), h, s);
+}
+
+// 1/b rounded to nearest for b in [2^-126, 2^126]: v_rcp_f32 (within one
+// ulp) and one Newton step y + y*(1 - b*y), both products in fmas.
+// tests/rules/rcp_sqrt_all.hip checks it on the device for every fp32 b in
+// that range (no mismatch).
+__device__ __forceinline__ float rcp_rn(float b) {
+    const float y = __builtin_amdgcn_rcpf(b);
+    return fmaf(fmaf(-b, y, 1.0f), y, y);
 }
 
 // x / b correctly rounded, for a wave-uniform divisor b in [2^-60, 1] with
-// y = 1/b correctly rounded (lo = 2^-96): q = x*y, then one correction with
+// y = 1/b correctly rounded (lo = 2^-96) -- and for the per-element divisor
+// of the update's last division, whose range adamw_update states: q = x*y,
+// then one correction with
 // the exact residual r = fma(-q, b, x), q + r*y rounded once -- Markstein's
 // correction step (P. Markstein, "Computation of elementary functions on the
 // IBM RISC System/6000 processor", 1990: with y the correctly rounded
@@ -268,10 +287,10 @@ __device__ __forceinline__ float div_uniform(float x, float b, float y, float lo
     return q;
 }
 
-// The AdamW update of one element (M041 section 02), fp32, each operation
-// rounded, evaluated left to right as printed, on the unscaled and clipped
-// grad (the mixed-precision recipe of M041 section 06: unscale, check,
-// clip; multiplying by 1 is exact).
+// The AdamW update (M041 section 02), fp32, each operation rounded,
+// evaluated left to right as printed, on the unscaled and clipped grad (the
+// mixed-precision recipe of M041 section 06: unscale, check, clip;
+// multiplying by 1 is exact).
 // SC: the step may scale the grads (inv_scale, clip_coef given); a plain
 // step skips the two multiplies by 1, which change nothing.
 //
@@ -279,28 +298,55 @@ __device__ __forceinline__ float div_uniform(float x, float b, float y, float lo
 //  * m_hat = m when bc1 == 1 (1 - beta1^t rounds to 1 in fp32 once beta1^t <
 //    2^-25, after about 160 steps for beta1 = 0.9): x / 1 == x; a
 //    wave-uniform branch;
-//  * v_hat and its root share one range test: for v in [div_lo, 2^64) with
-//    div_lo = 2^-96 the short division gives v_hat >= v >= 2^-96 (bc2 <= 1 and
-//    rounding is monotone) and at most 2^124, where sqrt_normal is exact; any
-//    other v (0, tiny, huge, inf, NaN) takes the division and the compiler's
-//    correctly rounded square root.
+//  * v_hat, its root and the last division take short forms under one range
+//    test.  For v >= div_lo = 2^-96 whose short quotient v_hat is below 2^56,
+//    v < 2^64 (v_hat >= v: bc2 <= 1), so v_hat is the correctly rounded v /
+//    bc2, in [2^-96, 2^56), where sqrt_rn is exact; with eps in [0, 2^28]
+//    (x_lo finite) the divisor denom = root + eps lies in [2^-48, 2^29], where
+//    rcp_rn is exact; and for 2^-96 <= |lr * m_hat| < 2^64 the quotient lies
+//    in [2^-125, 2^112), so every step of the short division stays normal and
+//    its residual exact (lowest bit >= 2^-143), and it returns the correctly
+//    rounded quotient.  If any element of the wave fails the test (a zero --
+//    whose sign the short form would lose --, a tiny, huge, infinite or NaN
+//    value), the wave recomputes the last division of all its elements with
+//    the IEEE division and the compiler's correctly rounded square root,
+//    which agree with the short forms wherever those apply.
+//
+// adamw_update_fast: one element; theta gets the short-form result, and the
+// return value says whether the short forms apply.  td = theta * decay and
+// x = lr * m_hat are kept for the exact recomputation.
 template <bool SC>
-__device__ __forceinline__ void adamw_update(float &theta, float g_scaled, float &m,
-                                             float &v, const StepScalars &s) {
+__device__ __forceinline__ bool adamw_update_fast(float &theta, float g_scaled, float &m, float &v,
+                                                  const StepScalars &s, float &td, float &x) {
     const float g = SC ? (g_scaled * s.inv_scale) * s.clip_coef : g_scaled;
     m = s.beta1 * m + s.one_minus_beta1 * g;
     v = s.beta2 * v + (s.one_minus_beta2 * g) * g;
     float m_hat = m;
     if (s.bc1 != 1.0f) m_hat = div_uniform(m, s.bc1, s.rbc1, s.div_lo);
-    float v_hat = div_short(v, s.bc2, s.rbc2);
-    float root = sqrt_normal(v_hat);
-    if (!(v >= s.div_lo && v < 0x1p64f)) {           // rare: skipped by the wave
+    x = s.lr * m_hat;
+    td = theta * s.decay;
+    const float v_hat = div_short(v, s.bc2, s.rbc2);
+    const float denom = sqrt_rn(v_hat) + s.eps;
+    theta = td - div_short(x, denom, rcp_rn(denom));
+    return (v >= s.div_lo) & (v_hat < 0x1p56f) & (fabsf(x) >= s.x_lo) & (fabsf(x) < 0x1p64f);
+}
+
+// The update of a lane's kVec elements: short forms for all, and in the rare
+// wave where any element needs it, the exact last division for all (a
+// wave-uniform branch: no per-element exec-mask regions on the common path).
+template <bool SC>
+__device__ __forceinline__ void adamw_update4(float (&th)[kVec], const float (&g)[kVec],
+                                              float (&m)[kVec], float (&v)[kVec],
+                                              const StepScalars &s) {
+    float td[kVec], x[kVec];
+    bool ok = true;
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) ok &= adamw_update_fast<SC>(th[j], g[j], m[j], v[j], s, td[j], x[j]);
+    if (wave_any(!ok)) {
         asm volatile("");                            // not speculated
-        v_hat = v / s.bc2;
-        root = sqrtf(v_hat);
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) th[j] = td[j] - x[j] / (sqrtf(v[j] / s.bc2) + s.eps);
     }
-    const float denom = root + s.eps;
-    theta = theta * s.decay - (s.lr * m_hat) / denom;
 }
 
 // ---------------------------------------------------------------- bf16
@@ -474,8 +520,7 @@ __device__ __forceinline__ void tile_dense(const TensorDesc &d, const void *grad
         load4_any<GT, NT>(grad, e, g, gv);
         load4_any<PT, NT>(d.param, e, th, pv);
         const StepScalars s = get();
-#pragma unroll
-        for (int j = 0; j < kVec; ++j) adamw_update<SC>(th[j], g[j], m[j], v[j], s);
+        adamw_update4<SC>(th, g, m, v, s);
         store4_any<PT, NT>(d.param, e, th, pv);
         store4<ST, NT>(d.m, e, m);
         store4<ST, NT>(d.v, e, v);
@@ -507,11 +552,10 @@ __device__ __forceinline__ void tile_dense(const TensorDesc &d, const void *grad
             }
         }
         const StepScalars s = get();
+        adamw_update4<SC>(th, g, m, v, s);
 #pragma unroll
-        for (int j = 0; j < kVec; ++j) {
-            adamw_update<SC>(th[j], g[j], m[j], v[j], s);
+        for (int j = 0; j < kVec; ++j)
             if (off + j >= n) m[j] = v[j] = 0.0f;      // padding: +0
-        }
         if (padded) {
             store4<ST, NT>(d.m, e, m);
             store4<ST, NT>(d.v, e, v);
@@ -601,10 +645,118 @@ __device__ __forceinline__ uint32_t pack_codes_unsigned(const float (&x)[kVec], 
 
 // One tile = one 8-bit block (block index base/256 of the tensor): decode
 // with the stored scales, update in fp32, reduce the block maxima over the
-// wave, re-encode.  theta uses this step's fp32 moments.
-template <int PT, int GT, bool NT, bool SC, typename Get>
-__device__ __forceinline__ void tile_q8(const TensorDesc &d, const void *grad,
-                                        int64_t base, int n, const Get &get) {
+// wave, re-encode.  theta uses this step's fp32 moments.  A full tile is read
+// in two phases: q8_load_full issues every load and only keeps the raw words,
+// q8_finish_full decodes, updates, encodes and stores.
+
+// Four values of an fp32 or bf16 array as loaded: one 16-byte or 8-byte
+// vector, or element loads assembled into the same words.
+template <int DT> struct Raw4;
+template <> struct Raw4<APEXW_F32> { f32x4 w; };
+template <> struct Raw4<APEXW_BF16> { u32x2 w; };
+
+template <int DT, bool NT>
+__device__ __forceinline__ Raw4<DT> load_raw4(const void *base, int64_t e, bool vec) {
+    Raw4<DT> r;
+    if constexpr (DT == APEXW_F32) {
+        if (vec) {
+            const APEXW_GLOBAL f32x4 *p = gptr<f32x4>(static_cast<const float *>(base) + e);
+            r.w = NT ? __builtin_nontemporal_load(p) : *p;
+        } else {
+            const APEXW_GLOBAL float *h = gptr<float>(base) + e;
+            r.w = f32x4{h[0], h[1], h[2], h[3]};
+        }
+    } else {
+        if (vec) {
+            const APEXW_GLOBAL u32x2 *p = gptr<u32x2>(static_cast<const uint16_t *>(base) + e);
+            r.w = NT ? __builtin_nontemporal_load(p) : *p;
+        } else {
+            const APEXW_GLOBAL uint16_t *h = gptr<uint16_t>(base) + e;
+            r.w.x = (uint32_t)h[0] | (uint32_t)h[1] << 16;
+            r.w.y = (uint32_t)h[2] | (uint32_t)h[3] << 16;
+        }
+    }
+    return r;
+}
+
+template <int DT>
+__device__ __forceinline__ void widen4(const Raw4<DT> &r, float (&x)[kVec]) {
+    if constexpr (DT == APEXW_F32) {
+        x[0] = r.w.x; x[1] = r.w.y; x[2] = r.w.z; x[3] = r.w.w;
+    } else {
+        x[0] = bf16_lo(r.w.x); x[1] = bf16_hi(r.w.x);
+        x[2] = bf16_lo(r.w.y); x[3] = bf16_hi(r.w.y);
+    }
+}
+
+template <int PT, int GT>
+struct Q8Raw {
+    uint32_t cm, cv;                 // 4 codes of m and of v
+    Raw4<GT> g;
+    Raw4<PT> th;
+    float sm, sv;                    // the block's stored scales
+};
+
+template <int PT, int GT, bool NT>
+__device__ __forceinline__ Q8Raw<PT, GT> q8_load_full(const TensorDesc &d, const void *grad,
+                                                      int64_t base) {
+    const int64_t e = base + threadIdx.x * kVec;
+    const int64_t blk = base / APEXW_Q8_BLOCK;
+    Q8Raw<PT, GT> r;
+    r.sm = gptr<float>(static_cast<const void *>(d.m_scale))[blk];
+    r.sv = gptr<float>(static_cast<const void *>(d.v_scale))[blk];
+    r.cm = load_u32<NT>(d.m, e);
+    r.cv = load_u32<NT>(d.v, e);
+    r.g = load_raw4<GT, NT>(grad, e, vec_aligned<GT>(grad));
+    r.th = load_raw4<PT, NT>(d.param, e, vec_aligned<PT>(d.param));
+    return r;
+}
+
+// The block's new scales (lane 0 stores them) from its maxima.
+__device__ __forceinline__ void q8_block_scales(const TensorDesc &d, int64_t blk, float am,
+                                                float av, BlockScale &bm, BlockScale &bv) {
+    am = wave_max_nonneg(am);
+    av = wave_max_nonneg(av);
+    bm = block_scale(am, 127.0f);
+    bv = block_scale(av, 255.0f);
+    if (threadIdx.x == 0) {
+        gptr<float>(static_cast<void *>(d.m_scale))[blk] = bm.s;
+        gptr<float>(static_cast<void *>(d.v_scale))[blk] = bv.s;
+    }
+}
+
+template <int PT, int GT, bool NT, bool SC>
+__device__ __forceinline__ void q8_finish_full(const TensorDesc &d, int64_t base,
+                                               const Q8Raw<PT, GT> &r, const StepScalars &s) {
+    const int64_t e = base + threadIdx.x * kVec;
+    float th[kVec], g[kVec], m[kVec], v[kVec];
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) {
+        m[j] = (float)(int8_t)(r.cm >> (8 * j)) * r.sm;
+        v[j] = (float)(uint8_t)(r.cv >> (8 * j)) * r.sv;
+    }
+    widen4<GT>(r.g, g);
+    widen4<PT>(r.th, th);
+    adamw_update4<SC>(th, g, m, v, s);
+    // block maxima (a NaN moment is passed over; v >= 0, fabs makes a -0 +0)
+    float am = 0.0f, av = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) {
+        am = fmaxf(am, fabsf(m[j]));
+        av = fmaxf(av, fabsf(v[j]));
+    }
+    BlockScale bm, bv;
+    q8_block_scales(d, base / APEXW_Q8_BLOCK, am, av, bm, bv);
+    store_u32<NT>(d.m, e, pack_codes_signed(m, bm));
+    store_u32<NT>(d.v, e, pack_codes_unsigned(v, bv));
+    store4_any<PT, NT>(d.param, e, th, vec_aligned<PT>(d.param));
+}
+
+// A tensor's last tile when it holds n < 256 elements: element accesses in
+// the lane that straddles the end, elements past it left out of the maxima.
+template <int PT, int GT, bool NT, bool SC>
+__device__ __forceinline__ void q8_tile_partial(const TensorDesc &d, const void *grad,
+                                                int64_t base, int n, const StepScalars &s) {
     const int off = threadIdx.x * kVec;
     const int64_t e = base + off;
     const int64_t blk = base / APEXW_Q8_BLOCK;
@@ -635,34 +787,17 @@ __device__ __forceinline__ void tile_q8(const TensorDesc &d, const void *grad,
             th[j] = ok ? load1<PT>(d.param, e + j) : 0.0f;
         }
     }
-    const StepScalars s = get();
+    adamw_update4<SC>(th, g, m, v, s);
     float am = 0.0f, av = 0.0f;
 #pragma unroll
-    for (int j = 0; j < kVec; ++j) adamw_update<SC>(th[j], g[j], m[j], v[j], s);
-    // block maxima (a NaN moment is passed over; v >= 0, fabs makes a -0 +0)
-    if (n == kTile) {                         // wave-uniform: a full block
-#pragma unroll
-        for (int j = 0; j < kVec; ++j) {
+    for (int j = 0; j < kVec; ++j) {
+        if (off + j < n) {                    // elements past the end do not count
             am = fmaxf(am, fabsf(m[j]));
             av = fmaxf(av, fabsf(v[j]));
         }
-    } else {
-#pragma unroll
-        for (int j = 0; j < kVec; ++j) {
-            if (off + j < n) {                // elements past the end do not count
-                am = fmaxf(am, fabsf(m[j]));
-                av = fmaxf(av, fabsf(v[j]));
-            }
-        }
     }
-    am = wave_max_nonneg(am);
-    av = wave_max_nonneg(av);
-    const BlockScale bm = block_scale(am, 127.0f);
-    const BlockScale bv = block_scale(av, 255.0f);
-    if (threadIdx.x == 0) {
-        gptr<float>(static_cast<void *>(d.m_scale))[blk] = bm.s;
-        gptr<float>(static_cast<void *>(d.v_scale))[blk] = bv.s;
-    }
+    BlockScale bm, bv;
+    q8_block_scales(d, blk, am, av, bm, bv);
     if (full) {
         store_u32<NT>(d.m, e, pack_codes_signed(m, bm));
         store_u32<NT>(d.v, e, pack_codes_unsigned(v, bv));
@@ -682,6 +817,19 @@ __device__ __forceinline__ void tile_q8(const TensorDesc &d, const void *grad,
                 gptr<uint8_t>(d.v)[e + j] = 0;
             }
         }
+    }
+}
+
+// One 8-bit tile in a single phase; get() yields the step's scalars after
+// the tile's loads are issued.
+template <int PT, int GT, bool NT, bool SC, typename Get>
+__device__ __forceinline__ void tile_q8(const TensorDesc &d, const void *grad,
+                                        int64_t base, int n, const Get &get) {
+    if (n == kTile) {                          // wave-uniform
+        const Q8Raw<PT, GT> r = q8_load_full<PT, GT, NT>(d, grad, base);
+        q8_finish_full<PT, GT, NT, SC>(d, base, r, get());
+    } else {
+        q8_tile_partial<PT, GT, NT, SC>(d, grad, base, n, get());
     }
 }
 
@@ -924,6 +1072,7 @@ __device__ __forceinline__ void carry_step(const KernelArgs &a) {
                 r.rbc1 = b.rbc1;
                 r.rbc2 = b.rbc2;
                 r.div_lo = b.div_lo;
+                r.x_lo = step_x_lo(G.eps);
                 r.inv_scale = inv_scale;
                 r.clip_coef = clip_coef;
                 return r;
