@@ -806,6 +806,7 @@ int apexw_step_ex(apexw_t h, const apexw_group *groups, int32_t n_groups, void *
         S.lr = (float)G.lr;
         S.decay = (float)(1.0 - G.lr * G.weight_decay);
         S.eps = (float)G.eps;
+        S.x_lo = S.eps <= 0x1p28f ? 0x1p-96f : INFINITY;    // as step_x_lo (eps >= 0 here)
         S.beta1_d = G.beta1;
         S.beta2_d = G.beta2;
     }

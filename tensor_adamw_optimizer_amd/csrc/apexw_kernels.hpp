@@ -94,7 +94,8 @@ __device__ __forceinline__ const APEXW_CONST T *cptr(const void *p) {
 // Per-group scalars, formed on the host once per call.
 struct GroupScalars {
     float beta1, one_minus_beta1, beta2, one_minus_beta2;
-    float lr, decay, eps, pad_;
+    float lr, decay, eps;
+    float x_lo;                               // step_x_lo(eps)
     double beta1_d, beta2_d;                  // for beta^t in fp64
 };
 
@@ -322,7 +323,8 @@ __device__ __forceinline__ bool adamw_update_fast(float &theta, float g_scaled, 
     m = s.beta1 * m + s.one_minus_beta1 * g;
     v = s.beta2 * v + (s.one_minus_beta2 * g) * g;
     float m_hat = m;
-    if (s.bc1 != 1.0f) m_hat = div_uniform(m, s.bc1, s.rbc1, s.div_lo);
+    if (__float_as_uint(s.bc1) != 0x3f800000u)       // bc1 != 1, tested on the scalar unit
+        m_hat = div_uniform(m, s.bc1, s.rbc1, s.div_lo);
     x = s.lr * m_hat;
     td = theta * s.decay;
     const float v_hat = div_short(v, s.bc2, s.rbc2);
@@ -576,7 +578,8 @@ __device__ __forceinline__ void tile_dense(const TensorDesc &d, const void *grad
 // The code is round-half-even of the correctly rounded quotient x/s, clamped
 // to the code range.  The quotient is not formed per element.  When s is a
 // normal number (the usual case), inv = v_rcp_f32(s) is within one ulp of
-// 1/s, so r = RN(x*inv) is within |x/s|*3*2^-24 of x/s, and RN(x/s) within
+// 1/s (tests/rules/rcp_sqrt_all.hip checks it for every normal s whose
+// reciprocal is normal), so r = RN(x*inv) is within |x/s|*3*2^-24 of x/s, and RN(x/s) within
 // |x/s|*2^-24; every |x| <= amax has |x/s| <= 127/(1 - 2^-24) (resp. 255/..),
 // so both stay within 3e-5 of x/s and inside the code range.  When r is more
 // than 2.5e-4 away from every half-integer, r and RN(x/s) therefore round to
@@ -598,13 +601,16 @@ struct BlockScale {
     bool fast;      // s normal and finite: inv is usable
 };
 
+// amax: a block maximum, >= +0 and never a NaN (fmaxf passes NaNs over).
 __device__ __forceinline__ BlockScale block_scale(float amax, float levels) {
     BlockScale b;
     b.s = div_short(amax, levels, 1.0f / levels);
     // amax in [2^-100, FLT_MAX] puts s = amax/levels (levels 127 or 255) in
-    // [2^-108, 2^121]: normal, and its reciprocal normal too
+    // [2^-108, 2^121]: normal, and its reciprocal normal too.  For amax >= +0
+    // that range is the bit patterns 0x0d800000 .. 0x7f7fffff: one unsigned
+    // compare of the pattern, on the scalar unit (amax is wave-uniform).
     b.fast = true;
-    if (!(amax >= 0x1p-100f && amax <= 0x1.fffffep127f)) {   // uniform; rare
+    if (__float_as_uint(amax) - 0x0d800000u > 0x7f7fffffu - 0x0d800000u) {   // rare
         asm volatile("");
         b.s = amax / levels;
         b.fast = b.s >= 0x1p-126f && b.s <= 0x1p126f;
@@ -624,6 +630,24 @@ __device__ __forceinline__ float code_value(float x, const BlockScale &b, float 
     return q;
 }
 
+// The signed code of x plus 128, an integer-valued float in [1, 255], with
+// the offset inside the product: r = fma(x, inv, 128) rounds x*inv + 128
+// once.  |x*inv - x/s| <= 127*2^-23 and the rounding at most 2^-17 (half an
+// ulp below 256), so r is within 2.3e-5 of x/s + 128, and RN(x/s) + 128
+// within 2.7e-5 of r (|x/s| <= 127/(1 - 2^-24)); when r is more than 2.5e-4
+// from every half-integer the two round to the same integer, which is then
+// in [1, 255].  r >= 0.99997, so r - rint(r) is exact (Sterbenz).  Otherwise
+// (rare), or when s is not normal, the code_value rule gives the same code.
+__device__ __forceinline__ float code_value_signed_128(float x, const BlockScale &b) {
+    const float r = fmaf(x, b.inv, 128.0f);
+    float q = rintf(r);
+    if (!b.fast || !(fabsf(r - q) < kTieBound)) {   // rare: skipped by the wave
+        asm volatile("");                                          // not speculated
+        q = (b.s == 0.0f ? 0.0f : fminf(fmaxf(rintf(x / b.s), -127.0f), 127.0f)) + 128.0f;
+    }
+    return q;
+}
+
 // Four codes packed little-endian into one word (v_cvt_pk_u8_f32 writes an
 // integer-valued float in [0, 255] into one byte); signed codes are packed
 // offset by 128 and flipped back, which is two's complement per byte.
@@ -631,7 +655,7 @@ __device__ __forceinline__ uint32_t pack_codes_signed(const float (&x)[kVec], co
     uint32_t w = 0;
 #pragma unroll
     for (int j = 0; j < kVec; ++j)
-        w = __builtin_amdgcn_cvt_pk_u8_f32(code_value(x[j], b, -127.0f, 127.0f) + 128.0f, j, w);
+        w = __builtin_amdgcn_cvt_pk_u8_f32(code_value_signed_128(x[j], b), j, w);
     return w ^ 0x80808080u;
 }
 
@@ -847,7 +871,7 @@ __device__ __forceinline__ GroupScalars group_scalars(const apexw_group &G) {
     S.lr = (float)G.lr;
     S.decay = (float)(1.0 - G.lr * G.weight_decay);
     S.eps = (float)G.eps;
-    S.pad_ = 0.0f;
+    S.x_lo = step_x_lo(S.eps);
     S.beta1_d = G.beta1;
     S.beta2_d = G.beta2;
     return S;
@@ -1072,7 +1096,7 @@ __device__ __forceinline__ void carry_step(const KernelArgs &a) {
                 r.rbc1 = b.rbc1;
                 r.rbc2 = b.rbc2;
                 r.div_lo = b.div_lo;
-                r.x_lo = step_x_lo(G.eps);
+                r.x_lo = G.x_lo;
                 r.inv_scale = inv_scale;
                 r.clip_coef = clip_coef;
                 return r;

@@ -8,6 +8,8 @@
 //     reciprocal: y is the nearest iff (y - u-/2)*b < 1 < (y + u+/2)*b.
 //     Both tests are exact in fp64: the midpoints have 25 significant bits,
 //     their squares and their products with b at most 50.
+//     The same loop checks that v_rcp_f32 alone is within one ulp of 1/b
+//     (y - u- < 1/b < y + u+), which the 8-bit encoding's tie guard assumes.
 //  3. div_short(x, b, rcp_rn(b)) against IEEE division x / b on 2^32 pairs
 //     drawn by a counter-based hash: |x| in [2^-96, 2^64) with either sign, b
 //     in [2^-48, 2^29], uniform in exponent and significand -- the operand
@@ -22,8 +24,8 @@
 
 namespace {
 
-enum { kSqrtBad, kSqrtSeen, kRcpBad, kRcpSeen, kDivBad, kDivSeen, kSqrtFirst, kRcpFirst, kDivFirst,
-       kWords };
+enum { kSqrtBad, kSqrtSeen, kRcpBad, kRcpSeen, kDivBad, kDivSeen, kRawBad, kSqrtFirst, kRcpFirst,
+       kDivFirst, kRawFirst, kWords };
 
 __device__ __forceinline__ double gap_above(float s) {
     return (double)__uint_as_float(__float_as_uint(s) + 1u) - (double)s;
@@ -36,6 +38,12 @@ __device__ __forceinline__ bool is_nearest_sqrt(float x, float s) {
     if (!(s > 0.0f) || !(s < 0x1p127f)) return false;
     const double lo = (double)s - 0.5 * gap_below(s), hi = (double)s + 0.5 * gap_above(s);
     return lo * lo < (double)x && (double)x < hi * hi;
+}
+
+__device__ __forceinline__ bool within_one_ulp_rcp(float b, float y) {
+    if (!(y > 0.0f) || !(y < 0x1p127f)) return false;
+    const double lo = (double)y - gap_below(y), hi = (double)y + gap_above(y);
+    return lo * (double)b < 1.0 && 1.0 < hi * (double)b;
 }
 
 __device__ __forceinline__ bool is_nearest_rcp(float b, float y) {
@@ -61,8 +69,8 @@ __device__ __forceinline__ float draw(uint64_t h, int e_lo, int e_hi) {
 __global__ __launch_bounds__(256) void rcp_sqrt_all_kernel(unsigned long long *out) {
     const uint64_t tid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
-    unsigned long long c[6] = {0, 0, 0, 0, 0, 0};
-    unsigned long long f[3] = {~0ull, ~0ull, ~0ull};
+    unsigned long long c[7] = {0, 0, 0, 0, 0, 0, 0};
+    unsigned long long f[4] = {~0ull, ~0ull, ~0ull, ~0ull};
     // 1. square root: bit patterns of [2^-96, 2^64)
     for (uint64_t u = 0x0f800000u + tid; u < 0x5f800000u; u += stride) {
         const float x = __uint_as_float((uint32_t)u);
@@ -80,6 +88,10 @@ __global__ __launch_bounds__(256) void rcp_sqrt_all_kernel(unsigned long long *o
             ++c[kRcpBad];
             f[1] = f[1] < u ? f[1] : u;
         }
+        if (!within_one_ulp_rcp(b, __builtin_amdgcn_rcpf(b))) {
+            ++c[kRawBad];
+            f[3] = f[3] < u ? f[3] : u;
+        }
     }
     // 3. short division on hashed pairs
     for (uint64_t i = tid; i < (1ull << 32); i += stride) {
@@ -93,24 +105,24 @@ __global__ __launch_bounds__(256) void rcp_sqrt_all_kernel(unsigned long long *o
             f[2] = f[2] < i ? f[2] : i;
         }
     }
-    for (int j = 0; j < 6; ++j)
+    for (int j = 0; j < 7; ++j)
         if (c[j]) atomicAdd(&out[j], c[j]);
-    for (int j = 0; j < 3; ++j)
+    for (int j = 0; j < 4; ++j)
         if (f[j] != ~0ull) atomicMin(&out[kSqrtFirst + j], f[j]);
 }
 
 }  // namespace
 
-// Runs the three checks on the current device.  out[0..5]: square-root
-// mismatches and inputs checked, reciprocal mismatches and inputs checked,
-// division mismatches and pairs checked; out[6..8]: the first mismatching
-// input (bit pattern, or pair index) of each, 2^64-1 if none.  Returns 0 or a
-// nonzero HIP error code.
+// Runs the checks on the current device.  out[0..6]: square-root mismatches
+// and inputs checked, reciprocal mismatches and inputs checked, division
+// mismatches and pairs checked, raw reciprocals off by an ulp or more;
+// out[7..10]: the first failing input (bit pattern, or pair index) of each
+// check, 2^64-1 if none.  Returns 0 or a nonzero HIP error code.
 extern "C" int rcp_sqrt_check_all(unsigned long long *out) {
     unsigned long long *d = nullptr;
     hipError_t e = hipMalloc((void **)&d, kWords * sizeof(unsigned long long));
     if (e != hipSuccess) return (int)e;
-    unsigned long long init[kWords] = {0, 0, 0, 0, 0, 0, ~0ull, ~0ull, ~0ull};
+    unsigned long long init[kWords] = {0, 0, 0, 0, 0, 0, 0, ~0ull, ~0ull, ~0ull, ~0ull};
     e = hipMemcpy(d, init, sizeof init, hipMemcpyHostToDevice);
     if (e == hipSuccess) {
         hipLaunchKernelGGL(rcp_sqrt_all_kernel, dim3(65536), dim3(256), 0, 0, d);

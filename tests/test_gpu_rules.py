@@ -11,7 +11,8 @@ tests/rules/rcp_sqrt_all.hip: the update's square root (sqrt_rn: v_sqrt_f32
 plus one residual correction with v_rsq_f32) on every fp32 input in [2^-96,
 2^64) and its reciprocal (rcp_rn: v_rcp_f32 plus one Newton step) on every
 fp32 input in [2^-126, 2^126], each against an exact fp64 test of the
-nearest result; and the short division by that reciprocal against IEEE
+nearest result, and v_rcp_f32 alone within one ulp on that range (the 8-bit
+encoding's tie guard assumes it); and the short division by that reciprocal against IEEE
 division on 2^32 hashed operand pairs of the ranges the update admits.
 """
 import ctypes
@@ -53,13 +54,14 @@ def test_sqrt_reciprocal_and_short_division_are_correctly_rounded():
     lib.rcp_sqrt_check_all.argtypes = [ctypes.POINTER(ctypes.c_ulonglong)]
     print("case: sqrt_rn on [2^-96, 2^64), rcp_rn on [2^-126, 2^126], 2^32 short divisions",
           flush=True)
-    out = (ctypes.c_ulonglong * 9)()
+    out = (ctypes.c_ulonglong * 11)()
     rc = lib.rcp_sqrt_check_all(out)
     assert rc == 0, "HIP error %d" % rc
-    sqrt_bad, sqrt_seen, rcp_bad, rcp_seen, div_bad, div_seen = list(out)[:6]
+    sqrt_bad, sqrt_seen, rcp_bad, rcp_seen, div_bad, div_seen, raw_bad = list(out)[:7]
     assert sqrt_seen == 0x5F800000 - 0x0F800000          # every input of [2^-96, 2^64)
     assert rcp_seen == 0x7E800000 - 0x00800000 + 1       # every input of [2^-126, 2^126]
     assert div_seen == 1 << 32
-    assert sqrt_bad == 0, "sqrt_rn: %d inputs differ, the first 0x%08x" % (sqrt_bad, out[6])
-    assert rcp_bad == 0, "rcp_rn: %d inputs differ, the first 0x%08x" % (rcp_bad, out[7])
-    assert div_bad == 0, "short division: %d pairs differ, the first pair %d" % (div_bad, out[8])
+    assert sqrt_bad == 0, "sqrt_rn: %d inputs differ, the first 0x%08x" % (sqrt_bad, out[7])
+    assert rcp_bad == 0, "rcp_rn: %d inputs differ, the first 0x%08x" % (rcp_bad, out[8])
+    assert div_bad == 0, "short division: %d pairs differ, the first pair %d" % (div_bad, out[9])
+    assert raw_bad == 0, "v_rcp_f32: %d inputs an ulp or more off, the first 0x%08x" % (raw_bad, out[10])
