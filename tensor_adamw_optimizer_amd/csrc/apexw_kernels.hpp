@@ -76,7 +76,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // counter that way too, but only the tensor's first tile uses the value, and
 // that tile writes the counter after its own read, which the written value
 // depends on; the carried bias corrections are read from one array and
-// written to the other, so no workgroup reads what this launch writes.)
+// written to the other, so no workgroup reads what this launch writes.  The
+// 8-bit block scales are read that way too: each is read, then rewritten,
+// by the one wave that owns its block, and read by no other.)
 #define APEXW_GLOBAL __attribute__((address_space(1)))
 #define APEXW_CONST __attribute__((address_space(4)))
 
@@ -313,37 +315,39 @@ __device__ __forceinline__ float div_uniform(float x, float b, float y, float lo
 //    the IEEE division and the compiler's correctly rounded square root,
 //    which agree with the short forms wherever those apply.
 //
-// adamw_update_fast: one element; theta gets the short-form result, and the
-// return value says whether the short forms apply.  td = theta * decay and
-// x = lr * m_hat are kept for the exact recomputation.
+// The update of a lane's kVec elements, stage by stage over the elements (so
+// that the bc1 test is one branch for all of them and writes x = lr * m_hat
+// directly): short forms for all, and in the rare wave where any element
+// needs it, the exact last division for all (a wave-uniform branch: no
+// per-element exec-mask regions on the common path).
 template <bool SC>
-__device__ __forceinline__ bool adamw_update_fast(float &theta, float g_scaled, float &m, float &v,
-                                                  const StepScalars &s, float &td, float &x) {
-    const float g = SC ? (g_scaled * s.inv_scale) * s.clip_coef : g_scaled;
-    m = s.beta1 * m + s.one_minus_beta1 * g;
-    v = s.beta2 * v + (s.one_minus_beta2 * g) * g;
-    float m_hat = m;
-    if (__float_as_uint(s.bc1) != 0x3f800000u)       // bc1 != 1, tested on the scalar unit
-        m_hat = div_uniform(m, s.bc1, s.rbc1, s.div_lo);
-    x = s.lr * m_hat;
-    td = theta * s.decay;
-    const float v_hat = div_short(v, s.bc2, s.rbc2);
-    const float denom = sqrt_rn(v_hat) + s.eps;
-    theta = td - div_short(x, denom, rcp_rn(denom));
-    return (v >= s.div_lo) & (v_hat < 0x1p56f) & (fabsf(x) >= s.x_lo) & (fabsf(x) < 0x1p64f);
-}
-
-// The update of a lane's kVec elements: short forms for all, and in the rare
-// wave where any element needs it, the exact last division for all (a
-// wave-uniform branch: no per-element exec-mask regions on the common path).
-template <bool SC>
-__device__ __forceinline__ void adamw_update4(float (&th)[kVec], const float (&g)[kVec],
+__device__ __forceinline__ void adamw_update4(float (&th)[kVec], const float (&g_in)[kVec],
                                               float (&m)[kVec], float (&v)[kVec],
                                               const StepScalars &s) {
-    float td[kVec], x[kVec];
+    float x[kVec], td[kVec];
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) {
+        const float g = SC ? (g_in[j] * s.inv_scale) * s.clip_coef : g_in[j];
+        m[j] = s.beta1 * m[j] + s.one_minus_beta1 * g;
+        v[j] = s.beta2 * v[j] + (s.one_minus_beta2 * g) * g;
+    }
+    if (__float_as_uint(s.bc1) == 0x3f800000u) {     // bc1 == 1: m_hat = m (scalar test)
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) x[j] = s.lr * m[j];
+    } else {
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) x[j] = s.lr * div_uniform(m[j], s.bc1, s.rbc1, s.div_lo);
+    }
     bool ok = true;
 #pragma unroll
-    for (int j = 0; j < kVec; ++j) ok &= adamw_update_fast<SC>(th[j], g[j], m[j], v[j], s, td[j], x[j]);
+    for (int j = 0; j < kVec; ++j) {
+        td[j] = th[j] * s.decay;
+        const float v_hat = div_short(v[j], s.bc2, s.rbc2);
+        const float denom = sqrt_rn(v_hat) + s.eps;
+        th[j] = td[j] - div_short(x[j], denom, rcp_rn(denom));
+        ok &= (v[j] >= s.div_lo) & (v_hat < 0x1p56f) & (fabsf(x[j]) >= s.x_lo) &
+              (fabsf(x[j]) < 0x1p64f);
+    }
     if (wave_any(!ok)) {
         asm volatile("");                            // not speculated
 #pragma unroll
@@ -727,8 +731,10 @@ __device__ __forceinline__ Q8Raw<PT, GT> q8_load_full(const TensorDesc &d, const
     const int64_t e = base + threadIdx.x * kVec;
     const int64_t blk = base / APEXW_Q8_BLOCK;
     Q8Raw<PT, GT> r;
-    r.sm = gptr<float>(static_cast<const void *>(d.m_scale))[blk];
-    r.sv = gptr<float>(static_cast<const void *>(d.v_scale))[blk];
+    // the stored scales: wave-uniform, read through the constant space (scalar
+    // loads; this wave alone writes them, after this read)
+    r.sm = cptr<float>(d.m_scale)[blk];
+    r.sv = cptr<float>(d.v_scale)[blk];
     r.cm = load_u32<NT>(d.m, e);
     r.cv = load_u32<NT>(d.v, e);
     r.g = load_raw4<GT, NT>(grad, e, vec_aligned<GT>(grad));
@@ -787,8 +793,8 @@ __device__ __forceinline__ void q8_tile_partial(const TensorDesc &d, const void 
     const bool pv = vec_aligned<PT>(d.param), gv = vec_aligned<GT>(grad);
     const APEXW_GLOBAL int8_t *mq = gptr<int8_t>(static_cast<const void *>(d.m));
     const APEXW_GLOBAL uint8_t *vq = gptr<uint8_t>(static_cast<const void *>(d.v));
-    const float sm_old = gptr<float>(static_cast<const void *>(d.m_scale))[blk];
-    const float sv_old = gptr<float>(static_cast<const void *>(d.v_scale))[blk];
+    const float sm_old = cptr<float>(d.m_scale)[blk];
+    const float sv_old = cptr<float>(d.v_scale)[blk];
     float th[kVec], g[kVec], m[kVec], v[kVec];
     const bool full = off + kVec <= n;
     if (full) {
