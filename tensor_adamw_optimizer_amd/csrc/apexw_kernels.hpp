@@ -319,11 +319,13 @@ __device__ __forceinline__ float div_uniform(float x, float b, float y, float lo
 // that the bc1 test is one branch for all of them and writes x = lr * m_hat
 // directly): short forms for all, and in the rare wave where any element
 // needs it, the exact last division for all (a wave-uniform branch: no
-// per-element exec-mask regions on the common path).
+// per-element exec-mask regions on the common path).  valid: the lane's
+// elements inside the tensor (a tensor's last tile); the others are padding
+// whose results are discarded, so they do not call for the exact path.
 template <bool SC>
 __device__ __forceinline__ void adamw_update4(float (&th)[kVec], const float (&g_in)[kVec],
                                               float (&m)[kVec], float (&v)[kVec],
-                                              const StepScalars &s) {
+                                              const StepScalars &s, int valid = kVec) {
     float x[kVec], td[kVec];
 #pragma unroll
     for (int j = 0; j < kVec; ++j) {
@@ -345,8 +347,8 @@ __device__ __forceinline__ void adamw_update4(float (&th)[kVec], const float (&g
         const float v_hat = div_short(v[j], s.bc2, s.rbc2);
         const float denom = sqrt_rn(v_hat) + s.eps;
         th[j] = td[j] - div_short(x[j], denom, rcp_rn(denom));
-        ok &= (v[j] >= s.div_lo) & (v_hat < 0x1p56f) & (fabsf(x[j]) >= s.x_lo) &
-              (fabsf(x[j]) < 0x1p64f);
+        ok &= ((v[j] >= s.div_lo) & (v_hat < 0x1p56f) & (fabsf(x[j]) >= s.x_lo) &
+               (fabsf(x[j]) < 0x1p64f)) | (j >= valid);
     }
     if (wave_any(!ok)) {
         asm volatile("");                            // not speculated
@@ -558,7 +560,7 @@ __device__ __forceinline__ void tile_dense(const TensorDesc &d, const void *grad
             }
         }
         const StepScalars s = get();
-        adamw_update4<SC>(th, g, m, v, s);
+        adamw_update4<SC>(th, g, m, v, s, n - off);
 #pragma unroll
         for (int j = 0; j < kVec; ++j)
             if (off + j >= n) m[j] = v[j] = 0.0f;      // padding: +0
@@ -817,7 +819,7 @@ __device__ __forceinline__ void q8_tile_partial(const TensorDesc &d, const void 
             th[j] = ok ? load1<PT>(d.param, e + j) : 0.0f;
         }
     }
-    adamw_update4<SC>(th, g, m, v, s);
+    adamw_update4<SC>(th, g, m, v, s, n - off);
     float am = 0.0f, av = 0.0f;
 #pragma unroll
     for (int j = 0; j < kVec; ++j) {
