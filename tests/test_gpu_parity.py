@@ -964,3 +964,129 @@ def test_launch_mode_choice():
     fl = GpuOpt([1 << 22] * 4, [W.BF16] * 4, [W.F32] * 4, [0] * 4, 1, W.STATE_F32)
     assert L.apexw_get_launch_mode(fl.h) == 3        # streams too, dense moments
     fl.close()
+
+
+
+# Tile kinds of the short-form boundary test: which quantity sits near which
+# edge, and on which side (+1 inside the short forms' range, -1 outside).
+_EDGE_KINDS = [("v_lo", +1), ("v_lo", -1), ("vhat_hi", +1), ("vhat_hi", -1),
+               ("x_lo", +1), ("x_lo", -1), ("x_hi", +1), ("x_hi", -1), ("plain", 0)]
+
+
+def _edge_state(n, rng, group, t0, beta1, beta2):
+    """Moments (fp32, m signed) and grads for one tensor whose 256-element
+    tiles each put one quantity of the first update just inside or just
+    outside an edge of the short forms' range: v >= 2^-96, v / bc2 < 2^56,
+    |lr * m_hat| >= 2^-96, |lr * m_hat| < 2^64 (within a factor 2^0.1 .. 2^3
+    of the edge; boundary tiles get zero grads, so the moments only decay),
+    or ordinary values.  Returns m, v, g and the kind of every tile."""
+    bc1 = 1.0 - beta1 ** (t0 + 1)
+    bc2 = 1.0 - beta2 ** (t0 + 1)
+    m = (rng.standard_normal(n) * 1e-4).astype(np.float64)
+    v = np.abs(rng.standard_normal(n) * 1e-8)
+    g = rng.standard_normal(n) * 1e-3
+    kinds = []
+    for t in range((n + 255) // 256):
+        sl = slice(256 * t, min(n, 256 * t + 256))
+        k = int(rng.integers(0, len(_EDGE_KINDS)))
+        kinds.append(k)
+        what, side = _EDGE_KINDS[k]
+        if what == "plain":
+            continue
+        cnt = sl.stop - sl.start
+        f = np.exp2(rng.uniform(0.1, 3.0, cnt))          # how far from the edge
+        sign = np.where(rng.integers(0, 2, cnt) == 1, -1.0, 1.0)
+        g[sl] = 0.0
+        if what == "v_lo":           # v after the update = beta2 * v_old
+            v[sl] = 2.0 ** -96 * f ** side / beta2
+        elif what == "vhat_hi":      # v_hat = beta2 * v_old / bc2
+            v[sl] = 2.0 ** 56 * f ** -side * bc2 / beta2
+        elif what == "x_lo":         # x = lr * beta1 * m_old / bc1
+            m[sl] = sign * 2.0 ** -96 * f ** side * bc1 / (group.lr * beta1)
+        else:
+            m[sl] = sign * 2.0 ** 64 * f ** -side * bc1 / (group.lr * beta1)
+    return m.astype(np.float32), v.astype(np.float32), g.astype(np.float32), kinds
+
+
+@pytest.mark.parametrize("fmt", [W.STATE_F32, W.STATE_BF16, W.STATE_Q8])
+def test_short_form_range_boundaries_against_oracle(fmt):
+    """The update takes short forms of v / bc2, its square root and the last
+    division only inside a range (v >= 2^-96, v / bc2 < 2^56, 2^-96 <=
+    |lr * m_hat| < 2^64, 0 <= eps <= 2^28), and a wave with any element
+    outside it takes the IEEE operations.  Tiles whose moments lie just
+    inside (the short forms at their edges) or just outside (the IEEE path)
+    each edge, groups with eps = 2^28 and one ulp above it, eps = 0, lr = 1
+    and 2^-30, step counters at 0 (bc1 < 1) and far along (bc1 rounded to
+    1), three calls in every launch mode: every value bit-exact against the
+    oracle."""
+    _need_gpu()
+    sizes = [256 * 40, 256 * 40 - 77, 256 * 30, 256 * 30 + 5]
+    pdt = [W.F32, W.BF16, W.F32, W.F32]
+    gdt = [W.F32, W.F32, W.BF16, W.F32]
+    group_of = [0, 1, 2, 3]
+    groups = [W.Group(lr=1e-3, weight_decay=0.1),
+              W.Group(lr=1.0, eps=2.0 ** 28),
+              W.Group(lr=1e-3, eps=float(np.nextafter(np.float32(2.0 ** 28), np.float32(np.inf)))),
+              W.Group(lr=2.0 ** -30, eps=0.0, weight_decay=0.01)]
+    to_dev = lambda h, d: (torch.from_numpy(h.view(np.int32) if d == W.F32 else h.view(np.int16))
+                           .to(DEV).view(torch.float32 if d == W.F32 else torch.bfloat16))
+    for t0 in (0, 10_000):
+        for mode in (1, 2, 3):
+            say("case: short-form boundaries", fmt, "t0", t0, "mode", mode)
+            rng = np.random.default_rng(1234 + t0 + mode)
+            th0 = [(rng.standard_normal(n) * 0.02).astype(np.float32) for n in sizes]
+            th_ref = [x.copy() if d == W.F32 else oracle.f32_to_bf16(x) for x, d in zip(th0, pdt)]
+            params = [to_dev(h, d) for h, d in zip(th_ref, pdt)]
+            opt = GpuOpt(sizes, pdt, gdt, group_of, len(groups), fmt)
+            L.apexw_set_launch_mode(opt.h, mode)
+            ref = oracle.OracleAdamW(sizes, pdt, gdt, group_of, fmt)
+            grads = []
+            for i, n in enumerate(sizes):
+                G = groups[group_of[i]]
+                m, v, g, _ = _edge_state(n, rng, G, t0, G.beta1, G.beta2)
+                grads.append(g)
+                if fmt == W.STATE_F32:
+                    ref.m[i][:], ref.v[i][:] = m, v
+                elif fmt == W.STATE_BF16:
+                    ref.m[i][:], ref.v[i][:] = oracle.f32_to_bf16(m), oracle.f32_to_bf16(v)
+                else:
+                    # codes near the top of the range, scales from the block maxima
+                    nb = (n + 255) // 256
+                    pad = nb * 256 - n
+                    am = np.abs(np.pad(m, (0, pad))).reshape(nb, 256).max(1)
+                    av = np.pad(v, (0, pad)).reshape(nb, 256).max(1)
+                    ref.m_scale[i][:] = (am / 127).astype(np.float32)
+                    ref.v_scale[i][:] = (av / 255).astype(np.float32)
+                    ref.m[i][:] = (np.sign(m) * rng.integers(64, 128, n)).astype(np.int8)
+                    ref.v[i][:] = rng.integers(128, 256, n).astype(np.uint8)
+                    ms, vs = opt.scales(i)
+                    ms.copy_(torch.from_numpy(ref.m_scale[i].copy()))
+                    vs.copy_(torch.from_numpy(ref.v_scale[i].copy()))
+                dm, dv = opt.moments(i)
+                dm.copy_(torch.from_numpy(ref.m[i].copy()).view(dm.dtype))
+                dv.copy_(torch.from_numpy(ref.v[i].copy()).view(dv.dtype))
+            if t0:
+                opt.steps().copy_(torch.full((len(sizes),), t0, dtype=torch.int32))
+                ref.t[:len(sizes)] = t0
+            g_host = [g if d == W.F32 else oracle.f32_to_bf16(g) for g, d in zip(grads, gdt)]
+            g_dev = [to_dev(h, d) for h, d in zip(g_host, gdt)]
+            for k in range(3):
+                opt.step(groups, params, g_dev)
+                ref.step(th_ref, g_host, groups)
+            torch.cuda.synchronize()
+            f32 = lambda a: a.view(np.float32)
+            for i in range(len(sizes)):
+                as_p = f32 if pdt[i] == W.F32 else oracle.bf16_to_f32
+                _same_bits_or_both_nan("theta%d" % i, bits(params[i]), th_ref[i], as_p)
+                m, v = (bits(t) for t in opt.moments(i))
+                if fmt == W.STATE_Q8:
+                    assert np.array_equal(m, ref.m[i]) and np.array_equal(v, ref.v[i]), i
+                    ms, vs = (bits(t) for t in opt.scales(i))
+                    assert np.array_equal(ms.view(np.uint32), ref.m_scale[i].view(np.uint32)), i
+                    assert np.array_equal(vs.view(np.uint32), ref.v_scale[i].view(np.uint32)), i
+                else:
+                    as_s = f32 if fmt == W.STATE_F32 else oracle.bf16_to_f32
+                    _same_bits_or_both_nan("m%d" % i, m, ref.m[i], as_s)
+                    _same_bits_or_both_nan("v%d" % i, v, ref.v[i], as_s)
+            assert np.array_equal(bits(opt.steps()), ref.t[:len(sizes)])
+            opt.close()
