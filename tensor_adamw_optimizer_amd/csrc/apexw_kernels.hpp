@@ -480,30 +480,36 @@ __device__ __forceinline__ void store4_any(void *base, int64_t e, const float (&
 
 // ---------------------------------------------------------------- wave max
 
-// Maximum over the 64 lanes of a wave of non-negative, NaN-free floats,
-// returned wave-uniform.  For such values the order of the bit patterns as
-// unsigned integers is the order of the numbers, so the reduction is integer
-// (DPP moves): quad swaps and the two row mirrors bring each 16-lane row's
-// maximum to all of its lanes; then row_bcast:15 carries row 0 into row 1 and
-// row 2 into row 3, and row_bcast:31 carries row 1 into rows 2 and 3, so lane
-// 63 ends with the maximum of all four rows.  Lanes of the rows a broadcast
-// does not write receive 0 (the old operand), the identity of the maximum,
-// which lets each move fuse with its maximum into one DPP instruction.
+// Wave reductions of non-negative, NaN-free floats: for such values the
+// order of the bit patterns as unsigned integers is the order of the
+// numbers, so the reduction is integer (DPP moves).  max_dpp: one fused move
+// and maximum; lanes of the rows a broadcast does not write receive 0 (the
+// old operand), the identity of the maximum.
 template <int CTRL, int ROWS>
 __device__ __forceinline__ uint32_t max_dpp(uint32_t u) {
     const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, CTRL, ROWS, 0xF, false);
     return u > o ? u : o;
 }
 
-__device__ __forceinline__ float wave_max_nonneg(float x) {
-    uint32_t u = __float_as_uint(x);
+// Maxima over the 64 lanes of the wave of two sets of such values, returned
+// wave-uniform: one
+// v_permlane32_swap exchanges the upper half of a's lanes with the lower half
+// of b's, so one maximum leaves a's pairwise maxima in lanes 0-31 and b's in
+// lanes 32-63; the quad swaps and row mirrors give every 16-lane row its
+// maximum, and row_bcast:15 carries row 0 into row 1 and row 2 into row 3,
+// so lane 31 ends with a's maximum and lane 63 with b's -- nine instructions
+// where two separate reductions take fourteen.
+__device__ __forceinline__ void wave_max_nonneg2(float a, float b, float &max_a, float &max_b) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b),
+                                                     false, false);
+    uint32_t u = sw[0] > sw[1] ? sw[0] : sw[1];
     u = max_dpp<0xB1, 0xF>(u);       // quad_perm [1,0,3,2]
     u = max_dpp<0x4E, 0xF>(u);       // quad_perm [2,3,0,1]
     u = max_dpp<0x141, 0xF>(u);      // row_half_mirror
     u = max_dpp<0x140, 0xF>(u);      // row_mirror
     u = max_dpp<0x142, 0xA>(u);      // row_bcast:15, rows 1 and 3
-    u = max_dpp<0x143, 0xC>(u);      // row_bcast:31, rows 2 and 3
-    return __uint_as_float(__builtin_amdgcn_readlane(u, 63));
+    max_a = __uint_as_float(__builtin_amdgcn_readlane(u, 31));
+    max_b = __uint_as_float(__builtin_amdgcn_readlane(u, 63));
 }
 
 // ---------------------------------------------------------------- tiles
@@ -747,8 +753,7 @@ __device__ __forceinline__ Q8Raw<PT, GT> q8_load_full(const TensorDesc &d, const
 // The block's new scales (lane 0 stores them) from its maxima.
 __device__ __forceinline__ void q8_block_scales(const TensorDesc &d, int64_t blk, float am,
                                                 float av, BlockScale &bm, BlockScale &bv) {
-    am = wave_max_nonneg(am);
-    av = wave_max_nonneg(av);
+    wave_max_nonneg2(am, av, am, av);
     bm = block_scale(am, 127.0f);
     bv = block_scale(av, 255.0f);
     if (threadIdx.x == 0) {
