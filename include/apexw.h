@@ -363,7 +363,8 @@ int apexw_read_steps(apexw_t h, int32_t *host_out, void *stream);
 /*
  * Launch geometry of the handle: tile size in elements (256; one workgroup of
  * one wave64 per tile), number of tiles, and the largest workgroup count of
- * its update launches.  Any pointer may be NULL.
+ * its update launches (the uncapped 8-bit carried step runs half as many,
+ * two tiles each).  Any pointer may be NULL.
  */
 int apexw_launch_info(apexw_t h, int32_t *tile_elems, int32_t *n_tiles,
                       int32_t *workgroups);

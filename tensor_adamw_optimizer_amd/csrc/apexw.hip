@@ -238,12 +238,30 @@ kernel_fn pick_carry(int pt, int gt) {
     return adamw_carry_step_kernel<ST, APEXW_BF16, APEXW_BF16, NT, SC, ONE>;
 }
 
-template <bool NT, bool SC, bool ONE>
+// The 8-bit carried step: under a workgroup cap the grid-stride kernel;
+// otherwise (PAIR) the kernel that takes two tiles per workgroup, whose grid
+// is half the tiles (carry_grid).
+template <bool NT, bool SC, bool PAIR>
 kernel_fn pick_carry_q8(int pt, int gt) {
-    if (pt == APEXW_F32 && gt == APEXW_F32) return adamw_carry_step_q8_kernel<APEXW_F32, APEXW_F32, NT, SC, ONE>;
-    if (pt == APEXW_F32 && gt == APEXW_BF16) return adamw_carry_step_q8_kernel<APEXW_F32, APEXW_BF16, NT, SC, ONE>;
-    if (pt == APEXW_BF16 && gt == APEXW_F32) return adamw_carry_step_q8_kernel<APEXW_BF16, APEXW_F32, NT, SC, ONE>;
-    return adamw_carry_step_q8_kernel<APEXW_BF16, APEXW_BF16, NT, SC, ONE>;
+    if constexpr (PAIR) {
+        if (pt == APEXW_F32 && gt == APEXW_F32) return adamw_carry_pair_q8_kernel<APEXW_F32, APEXW_F32, NT, SC>;
+        if (pt == APEXW_F32 && gt == APEXW_BF16) return adamw_carry_pair_q8_kernel<APEXW_F32, APEXW_BF16, NT, SC>;
+        if (pt == APEXW_BF16 && gt == APEXW_F32) return adamw_carry_pair_q8_kernel<APEXW_BF16, APEXW_F32, NT, SC>;
+        return adamw_carry_pair_q8_kernel<APEXW_BF16, APEXW_BF16, NT, SC>;
+    } else {
+        if (pt == APEXW_F32 && gt == APEXW_F32) return adamw_carry_step_q8_kernel<APEXW_F32, APEXW_F32, NT, SC>;
+        if (pt == APEXW_F32 && gt == APEXW_BF16) return adamw_carry_step_q8_kernel<APEXW_F32, APEXW_BF16, NT, SC>;
+        if (pt == APEXW_BF16 && gt == APEXW_F32) return adamw_carry_step_q8_kernel<APEXW_BF16, APEXW_F32, NT, SC>;
+        return adamw_carry_step_q8_kernel<APEXW_BF16, APEXW_BF16, NT, SC>;
+    }
+}
+
+// Workgroups of a carried launch of `tiles` tiles under the cap `wg`: one
+// per tile when uncapped (wg == tiles), except in the 8-bit format, whose
+// uncapped kernel takes two tiles per workgroup.
+int64_t carry_grid(int fmt, int64_t tiles, int64_t wg) {
+    if (wg == tiles && fmt == APEXW_STATE_Q8) return (tiles + 1) / 2;
+    return wg;
 }
 
 // one_tile: every workgroup takes exactly one tile (the grid is not capped);
@@ -906,7 +924,8 @@ int apexw_step_ex(apexw_t h, const apexw_group *groups, int32_t n_groups, void *
         }
         if (carry) {
             hipLaunchKernelGGL(carry_kernel_for(h->fmt, L.pt, L.gt, streaming, scaled, wg == L.tile_count),
-                               dim3((unsigned)wg), dim3(kThreads), lds, st, a);
+                               dim3((unsigned)carry_grid(h->fmt, L.tile_count, wg)), dim3(kThreads),
+                               lds, st, a);
         } else if (single) {
             a.tensor_begin = L.tensor_begin;
             a.tensor_count = L.tensor_count;

@@ -870,6 +870,59 @@ __device__ __forceinline__ void tile_q8(const TensorDesc &d, const void *grad,
     }
 }
 
+// Two consecutive full blocks of one tensor (base, base + 256) in one wave:
+// one address computation for both (the second block's accesses differ by a
+// constant offset), all loads issued before any arithmetic, both blocks'
+// updates in one basic block, and their four maxima in two paired
+// reductions.  Each block gets exactly what q8_finish_full gives it.
+template <int PT, int GT, bool NT, bool SC>
+__device__ __forceinline__ void q8_pair_full(const TensorDesc &d, const void *grad, int64_t base,
+                                             const StepScalars &s) {
+    const Q8Raw<PT, GT> r0 = q8_load_full<PT, GT, NT>(d, grad, base);
+    const Q8Raw<PT, GT> r1 = q8_load_full<PT, GT, NT>(d, grad, base + kTile);
+    const int64_t e = base + threadIdx.x * kVec;
+    float th0[kVec], g0[kVec], m0[kVec], v0[kVec], th1[kVec], g1[kVec], m1[kVec], v1[kVec];
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) {
+        m0[j] = (float)(int8_t)(r0.cm >> (8 * j)) * r0.sm;
+        v0[j] = (float)(uint8_t)(r0.cv >> (8 * j)) * r0.sv;
+        m1[j] = (float)(int8_t)(r1.cm >> (8 * j)) * r1.sm;
+        v1[j] = (float)(uint8_t)(r1.cv >> (8 * j)) * r1.sv;
+    }
+    widen4<GT>(r0.g, g0);
+    widen4<PT>(r0.th, th0);
+    widen4<GT>(r1.g, g1);
+    widen4<PT>(r1.th, th1);
+    adamw_update4<SC>(th0, g0, m0, v0, s);
+    adamw_update4<SC>(th1, g1, m1, v1, s);
+    float am0 = 0.0f, av0 = 0.0f, am1 = 0.0f, av1 = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) {
+        am0 = fmaxf(am0, fabsf(m0[j]));
+        av0 = fmaxf(av0, fabsf(v0[j]));
+        am1 = fmaxf(am1, fabsf(m1[j]));
+        av1 = fmaxf(av1, fabsf(v1[j]));
+    }
+    wave_max_nonneg2(am0, am1, am0, am1);
+    wave_max_nonneg2(av0, av1, av0, av1);
+    const BlockScale bm0 = block_scale(am0, 127.0f), bv0 = block_scale(av0, 255.0f);
+    const BlockScale bm1 = block_scale(am1, 127.0f), bv1 = block_scale(av1, 255.0f);
+    const int64_t blk = base / APEXW_Q8_BLOCK;
+    if (threadIdx.x == 0) {
+        gptr<float>(static_cast<void *>(d.m_scale))[blk] = bm0.s;
+        gptr<float>(static_cast<void *>(d.v_scale))[blk] = bv0.s;
+        gptr<float>(static_cast<void *>(d.m_scale))[blk + 1] = bm1.s;
+        gptr<float>(static_cast<void *>(d.v_scale))[blk + 1] = bv1.s;
+    }
+    const bool pv = vec_aligned<PT>(d.param);
+    store_u32<NT>(d.m, e, pack_codes_signed(m0, bm0));
+    store_u32<NT>(d.v, e, pack_codes_unsigned(v0, bv0));
+    store4_any<PT, NT>(d.param, e, th0, pv);
+    store_u32<NT>(d.m, e + kTile, pack_codes_signed(m1, bm1));
+    store_u32<NT>(d.v, e + kTile, pack_codes_unsigned(v1, bv1));
+    store4_any<PT, NT>(d.param, e + kTile, th1, pv);
+}
+
 // ---------------------------------------------------------------- kernels
 
 // The fp32 scalars of a group, formed from its fp64 hyperparameters exactly
@@ -1146,18 +1199,121 @@ __global__ __launch_bounds__(kThreads) void adamw_carry_step_kernel(KernelArgs a
     carry_step<ST, PT, GT, NT, SC, ONE>(a);
 }
 
-// The 8-bit carried step under a budget of 80 scalar registers (the
-// compiler otherwise takes 93).  The 8-bit update is VALU-bound and wants
-// every wave the SIMDs can hold; at 93 SGPRs it measured 11% fewer waves
-// in flight on MI355X, although the compiler counts 8 waves per SIMD either
-// way, and ran 4-5% slower than at 78 (LoRA list, 53.7-54.5 against
-// 51.3-51.8 us per step).  The dense formats keep their allocation (their
-// residency is capped lower, and the budget's register moves cost bf16
-// moments 1%).
-template <int PT, int GT, bool NT, bool SC, bool ONE>
+// The 8-bit carried step under a workgroup cap (a grid-stride loop over the
+// tiles; uncapped launches take adamw_carry_pair_q8_kernel below).  Both
+// 8-bit carried kernels run under a budget of 80 scalar registers (the
+// compiler otherwise takes 93): the 8-bit update wants every wave the SIMDs
+// can hold, and at 93 SGPRs the one-tile kernel measured 11% fewer waves in
+// flight on MI355X, although the compiler counts 8 waves per SIMD either way,
+// and ran 4-5% slower than at 78 (LoRA list, 53.7-54.5 against 51.3-51.8 us
+// per step).  The dense formats keep their allocation (their residency is
+// capped lower, and the budget's register moves cost bf16 moments 1%).
+template <int PT, int GT, bool NT, bool SC>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_num_sgpr(80)))
 void adamw_carry_step_q8_kernel(KernelArgs a) {
-    carry_step<APEXW_STATE_Q8, PT, GT, NT, SC, ONE>(a);
+    carry_step<APEXW_STATE_Q8, PT, GT, NT, SC, false>(a);
+}
+
+// The step's scalars of a tile of tensor descriptor d in the carried step.
+__device__ __forceinline__ StepScalars carry_scalars(const KernelArgs &a, const TensorDesc &d,
+                                                     const BiasRecord &b, float inv_scale,
+                                                     float clip_coef) {
+    const GroupScalars &G = a.groups[d.group];
+    StepScalars r;
+    r.beta1 = G.beta1;
+    r.one_minus_beta1 = G.one_minus_beta1;
+    r.beta2 = G.beta2;
+    r.one_minus_beta2 = G.one_minus_beta2;
+    r.lr = G.lr;
+    r.decay = G.decay;
+    r.eps = G.eps;
+    r.bc1 = b.bc1;
+    r.bc2 = b.bc2;
+    r.rbc1 = b.rbc1;
+    r.rbc2 = b.rbc2;
+    r.div_lo = b.div_lo;
+    r.x_lo = G.x_lo;
+    r.inv_scale = inv_scale;
+    r.clip_coef = clip_coef;
+    return r;
+}
+
+// After the tile at `base` of tensor i (8-bit carried step): if it is the
+// tensor's first, advance the counter (with a grad) and write the next
+// step's corrections, after the tile.
+__device__ __forceinline__ void carry_first_tile_q8(const KernelArgs &a, int32_t i,
+                                                    const TensorDesc &d, const BiasRecord &b,
+                                                    int64_t base, const void *grad) {
+    if (base != 0 || threadIdx.x != 0) return;
+    BiasRecord nb = b;
+    if (grad != nullptr) {
+        const uint32_t t1 = (uint32_t)a.steps[i] + 1u;
+        a.steps[i] = (int32_t)t1;
+        const GroupScalars &G = a.groups[d.group];
+        nb = bias_record(G.beta1_d, G.beta2_d, (int32_t)(t1 + 1u));
+    }
+    a.bias_next[i] = nb;
+}
+
+// The 8-bit carried step with two tiles per workgroup: workgroup w takes the
+// logical tiles 2w and 2w+1.  When both lie in one tensor (every pair but at
+// most one per tensor) they are consecutive blocks, and one metadata fetch,
+// one address computation and one set of scalars serve both (q8_pair_full
+// for two full blocks); a pair that spans two tensors takes its tiles one at
+// a time, as carry_step does.  Each block gets the same bits as with one
+// tile per workgroup; the step measured 3.5% faster on MI355X (LoRA list,
+// 43.8-44.0 against 45.4-45.8 us, same machine, alternating runs): the same
+// VALU work per block, half the metadata chains and scalar work.
+template <int PT, int GT, bool NT, bool SC>
+__device__ __forceinline__ void carry_q8_one_tile(const KernelArgs &a,
+                                                  const APEXW_CONST int32_t *tile_tensor,
+                                                  int64_t k, float fi, float inv_scale,
+                                                  float clip_coef) {
+    const int32_t i = tile_owner<true>(a, tile_tensor, k);
+    const TensorDesc d = load_uniform(a.desc, i);
+    const void *g_ptr = reinterpret_cast<const void *>(cptr<uint64_t>(a.grads)[i]);
+    const BiasRecord b = load_uniform(a.bias_cur, i);
+    const int64_t base = (a.tile_begin + k - d.first_tile) * kTile;
+    const int64_t left = d.numel - base;
+    const int n = left < kTile ? (int)left : kTile;
+    const void *grad = fi != 0.0f ? nullptr : g_ptr;
+    if (grad != nullptr && n > 0)
+        tile_q8<PT, GT, NT, SC>(d, grad, base, n,
+                                [&] { return carry_scalars(a, d, b, inv_scale, clip_coef); });
+    carry_first_tile_q8(a, i, d, b, base, grad);
+}
+
+template <int PT, int GT, bool NT, bool SC>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_num_sgpr(80)))
+void adamw_carry_pair_q8_kernel(KernelArgs a) {
+    const APEXW_CONST int32_t *tile_tensor = cptr<int32_t>(a.tile_tensor);
+    const float fi = *cptr<float>(a.found_inf);
+    const float inv_scale = *cptr<float>(a.inv_scale);
+    const float clip_coef = *cptr<float>(a.clip_coef);
+    const int64_t k0 = 2 * (int64_t)blockIdx.x;           // < tile_count: grid = ceil(tiles / 2)
+    const int32_t i = tile_owner<true>(a, tile_tensor, k0);
+    const TensorDesc d = load_uniform(a.desc, i);
+    const void *g_ptr = reinterpret_cast<const void *>(cptr<uint64_t>(a.grads)[i]);
+    const BiasRecord b = load_uniform(a.bias_cur, i);
+    const int64_t base = (a.tile_begin + k0 - d.first_tile) * kTile;
+    const int64_t left = d.numel - base;
+    if (left <= kTile) {                       // tile k0 ends its tensor: one tile at a time
+        carry_q8_one_tile<PT, GT, NT, SC>(a, tile_tensor, k0, fi, inv_scale, clip_coef);
+        if (k0 + 1 < a.tile_count)
+            carry_q8_one_tile<PT, GT, NT, SC>(a, tile_tensor, k0 + 1, fi, inv_scale, clip_coef);
+        return;
+    }
+    const void *grad = fi != 0.0f ? nullptr : g_ptr;
+    if (grad != nullptr) {
+        const StepScalars s = carry_scalars(a, d, b, inv_scale, clip_coef);
+        if (left >= 2 * kTile) {
+            q8_pair_full<PT, GT, NT, SC>(d, grad, base, s);
+        } else {
+            tile_q8<PT, GT, NT, SC>(d, grad, base, kTile, [&] { return s; });
+            tile_q8<PT, GT, NT, SC>(d, grad, base + kTile, (int)(left - kTile), [&] { return s; });
+        }
+    }
+    carry_first_tile_q8(a, i, d, b, base, grad);
 }
 
 // Starts (or restarts) the carried chain: one lane per tensor writes the
