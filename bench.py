@@ -472,8 +472,10 @@ def main() -> int:
             "traffic": traffic,
             "algorithmic_bytes_per_launch": ab,
             "kernel": MODE_KERNELS[launch_mode].replace(
-                "carry_step_kernel", "carry_step_q8_kernel" if w.state_fmt == W.STATE_Q8
-                else "carry_step_kernel") + ((" + grad_norm kernels" if args.clip > 0 else " + unscale_check_kernel") if args.amp else ""),
+                "carry_step_kernel",
+                ("carry_step_q8_kernel" if args.workgroups else "carry_pair_q8_kernel")
+                if w.state_fmt == W.STATE_Q8 else "carry_step_kernel")
+            + ((" + grad_norm kernels" if args.clip > 0 else " + unscale_check_kernel") if args.amp else ""),
         },
     }
     out["context"] = {"device_copy_gbps": copy_gbps,
