@@ -1090,3 +1090,52 @@ def test_short_form_range_boundaries_against_oracle(fmt):
                     _same_bits_or_both_nan("v%d" % i, v, ref.v[i], as_s)
             assert np.array_equal(bits(opt.steps()), ref.t[:len(sizes)])
             opt.close()
+
+
+@pytest.mark.parametrize("cap", [0, 5])
+def test_q8_tile_pairs_against_oracle(cap):
+    """The uncapped 8-bit carried step gives each workgroup the tiles 2w and
+    2w+1: two full blocks of one tensor, a full block and the tensor's
+    partial last block, or two tiles of two tensors (odd tile counts, one-tile
+    and 5-element tensors), and the launch's last tile alone; with a workgroup
+    cap the grid-stride kernel takes the same list.  Five calls with absent
+    grads and a skipped call: codes, scales, theta and counters bit-exact
+    against the oracle."""
+    _need_gpu()
+    say("case: 8-bit tile pairs, cap", cap)
+    sizes = [256 * 3, 256 * 2 + 100, 256, 5, 256 * 7 + 1, 256 * 4, 256 * 5 - 3]
+    pdt = [W.F32, W.BF16, W.F32, W.BF16, W.BF16, W.F32, W.F32]
+    gdt = [W.F32, W.BF16, W.F32, W.BF16, W.BF16, W.F32, W.F32]
+    group_of = [0, 1, 0, 1, 0, 1, 0]
+    groups = [W.Group(lr=1e-3, weight_decay=0.1), W.Group(lr=5e-4, eps=1e-6)]
+    to_dev = lambda h, d: (torch.from_numpy(h.view(np.int32) if d == W.F32 else h.view(np.int16))
+                           .to(DEV).view(torch.float32 if d == W.F32 else torch.bfloat16))
+    rng = np.random.default_rng(77 + cap)
+    th_ref = [(rng.standard_normal(n) * 0.02).astype(np.float32) for n in sizes]
+    th_ref = [x if d == W.F32 else oracle.f32_to_bf16(x) for x, d in zip(th_ref, pdt)]
+    params = [to_dev(h, d) for h, d in zip(th_ref, pdt)]
+    opt = GpuOpt(sizes, pdt, gdt, group_of, len(groups), W.STATE_Q8)
+    if cap:
+        L.apexw_set_workgroups(opt.h, cap)
+    ref = oracle.OracleAdamW(sizes, pdt, gdt, group_of, W.STATE_Q8)
+    flag = torch.zeros(1, dtype=torch.float32, device=DEV)
+    for k in range(5):
+        g32 = [(rng.standard_normal(n) * 1e-3).astype(np.float32) for n in sizes]
+        g_host = [g if d == W.F32 else oracle.f32_to_bf16(g) for g, d in zip(g32, gdt)]
+        absent = {1, 3} if k == 2 else set()
+        skip = k == 3
+        flag.fill_(1.0 if skip else 0.0)
+        opt.step(groups, params, [None if i in absent else to_dev(h, d)
+                                  for i, (h, d) in enumerate(zip(g_host, gdt))], found_inf=flag)
+        ref.step(th_ref, [None if i in absent else h for i, h in enumerate(g_host)], groups,
+                 found_inf=skip)
+    torch.cuda.synchronize()
+    for i in range(len(sizes)):
+        assert n_bit_mismatch(bits(params[i]), th_ref[i]) == 0, i
+        m, v = (bits(t) for t in opt.moments(i))
+        assert np.array_equal(m, ref.m[i]) and np.array_equal(v, ref.v[i]), i
+        ms, vs = (bits(t) for t in opt.scales(i))
+        assert np.array_equal(ms.view(np.uint32), ref.m_scale[i].view(np.uint32)), i
+        assert np.array_equal(vs.view(np.uint32), ref.v_scale[i].view(np.uint32)), i
+    assert np.array_equal(bits(opt.steps()), ref.t[:len(sizes)])
+    opt.close()
