@@ -5,16 +5,19 @@
 // tile, built by apexw_plan.hpp), lays the optimizer state out in one
 // caller-owned buffer, and on every step queues, by default, one carried-step
 // launch per (parameter dtype, grad dtype) pair present, each with one
-// workgroup per tile: the bias corrections come from the previous step, and
-// each tensor's first tile advances its counter and writes the next ones.
+// workgroup per tile (per two tiles in the 8-bit format): the bias
+// corrections come from the previous step, and each tensor's first tile
+// advances its counter and writes the next ones.  It also allocates no
+// device memory of its own except one fixed static array for the
+// grad-norm entry point that allocates nothing.
 // Steps whose hyperparameters live in device memory, steps queued under
 // stream capture (and every step after one), and lists with an empty tensor
 // take a prepare launch plus the update launches, or for small lists a single
 // launch per pair (apexw_set_launch_mode).  Per call the engine only compares
 // the param / grad pointer arrays with the previous call's (one asynchronous
 // upload when they differ) and forms the per-group fp32 scalars, which travel
-// in the kernel arguments.  It never synchronises with the host inside a step
-// and allocates no device memory.
+// in the kernel arguments.  It never synchronises with the host inside a
+// step.
 //
 // Sources: "Fused optimizers and state precision" (ai-infra-kb M041),
 // sections 02-06; "Apex fused optimizers" guide (qwbw.cn), sections 二/三
@@ -264,8 +267,8 @@ int64_t carry_grid(int fmt, int64_t tiles, int64_t wg) {
     return wg;
 }
 
-// one_tile: every workgroup takes exactly one tile (the grid is not capped);
-// the kernels then run their loop-free form
+// one_tile: the grid is not capped (a workgroup per tile, or per two tiles
+// in the 8-bit format); the kernels then run their loop-free form
 template <bool NT, bool SC>
 kernel_fn pick_carry_format(int fmt, int pt, int gt, bool one_tile) {
     if (fmt == APEXW_STATE_F32)

@@ -9,8 +9,9 @@
 // once: theta, g, m, v in; theta, m, v out (28 B per fp32 element, the
 // one-pass ledger of the M041 page, section 04).  Small one-tile workgroups
 // keep many independent read and write streams in flight.  A step is one of:
-//  * adamw_carry_step_kernel (and its 8-bit form adamw_carry_step_q8_kernel)
-//    -- the default: one launch per (param, grad) dtype pair.  Every
+//  * adamw_carry_step_kernel (8-bit: adamw_carry_pair_q8_kernel, two
+//    consecutive blocks per workgroup, or adamw_carry_step_q8_kernel under a
+//    workgroup cap) -- the default: one launch per (param, grad) dtype pair.  Every
 //    workgroup takes its tensor's bias corrections 1-beta1^t, 1-beta2^t from
 //    an array the previous step wrote; the first tile of each tensor
 //    advances the tensor's step counter (only with a grad and without
@@ -26,7 +27,8 @@
 //    arrival counters, advances the counters.
 // With fp32 moments the path is HBM-bandwidth bound; with 8-bit moments the
 // exact fp32 arithmetic (the correctly rounded division and square root per
-// element, the block reductions, decode and encode) is the limit.  There is
+// element, the block reductions, decode and encode) and each block's chain
+// of memory round trips are the limit.  There is
 // no contraction in the method, so no matrix-core work; the arithmetic is
 // ordinary fp32 VALU code compiled without contraction, with exact shortcuts
 // where the hardware offers them (bf16 pair conversion, square root from
@@ -194,7 +196,7 @@ struct StepScalars {
 };
 
 // The lower bound of |lr * m_hat| for the short form of the update's last
-// division (adamw_update): 2^-96 when eps lies in [0, 2^28], else +inf (every
+// division (adamw_update4): 2^-96 when eps lies in [0, 2^28], else +inf (every
 // element then takes the division).  An integer test on the bit pattern
 // (+0 .. 2^28 are the patterns 0 .. 0x4d800000; -0, negatives and NaNs lie
 // above), so it needs no vector instruction.
@@ -261,7 +263,7 @@ __device__ __forceinline__ float rcp_rn(float b) {
 
 // x / b correctly rounded, for a wave-uniform divisor b in [2^-60, 1] with
 // y = 1/b correctly rounded (lo = 2^-96) -- and for the per-element divisor
-// of the update's last division, whose range adamw_update states: q = x*y,
+// of the update's last division, whose range adamw_update4 states: q = x*y,
 // then one correction with
 // the exact residual r = fma(-q, b, x), q + r*y rounded once -- Markstein's
 // correction step (P. Markstein, "Computation of elementary functions on the
