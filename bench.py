@@ -57,7 +57,8 @@ def kernel_source_hash() -> str:
     import re
     h = hashlib.sha256()
     for rel in ("tensor_adamw_optimizer_amd/csrc/apexw.hip",
-                "tensor_adamw_optimizer_amd/csrc/apexw_kernels.hpp", "include/apexw.h"):
+                "tensor_adamw_optimizer_amd/csrc/apexw_kernels.hpp",
+                "tensor_adamw_optimizer_amd/csrc/apexw_plan.hpp", "include/apexw.h"):
         with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
