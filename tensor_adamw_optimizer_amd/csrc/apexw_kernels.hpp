@@ -245,7 +245,10 @@ __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballo
 // exact residual x - s*s (an fma) times half the reciprocal square root
 // (v_rsq_f32), rounded once.  tests/rules/rcp_sqrt_all.hip checks the result
 // on the device against the nearest square root for every fp32 x in that
-// range (an exact fp64 test of the two midpoints; no mismatch).
+// range (an exact fp64 test of the two midpoints; no mismatch).  The rule is
+// exact for these instructions' own outputs, not for every pair of one-ulp
+// approximations (tests/rules/sqrt_rule.c finds a few x per two binades that
+// such pairs get wrong), so the device check is what establishes it.
 __device__ __forceinline__ float sqrt_rn(float x) {
     const float s = __builtin_amdgcn_sqrtf(x);
     const float h = 0.5f * __builtin_amdgcn_rsqf(x);
