@@ -247,8 +247,8 @@ __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballo
 // on the device against the nearest square root for every fp32 x in that
 // range (an exact fp64 test of the two midpoints; no mismatch).  The rule is
 // exact for these instructions' own outputs, not for every pair of one-ulp
-// approximations (tests/rules/sqrt_rule.c finds a few x per two binades that
-// such pairs get wrong), so the device check is what establishes it.
+// approximations (tests/rules/rcp_sqrt_rule.c finds a few x per two binades
+// that such pairs get wrong), so the device check is what establishes it.
 __device__ __forceinline__ float sqrt_rn(float x) {
     const float s = __builtin_amdgcn_sqrtf(x);
     const float h = 0.5f * __builtin_amdgcn_rsqf(x);
@@ -258,7 +258,9 @@ __device__ __forceinline__ float sqrt_rn(float x) {
 // 1/b rounded to nearest for b in [2^-126, 2^126]: v_rcp_f32 (within one
 // ulp) and one Newton step y + y*(1 - b*y), both products in fmas.
 // tests/rules/rcp_sqrt_all.hip checks it on the device for every fp32 b in
-// that range (no mismatch).
+// that range (no mismatch).  As with sqrt_rn, that holds for the hardware's
+// own first approximation, not for every one-ulp one (a one-ulp-high start
+// fails for 32 significands per binade in tests/rules/rcp_sqrt_rule.c).
 __device__ __forceinline__ float rcp_rn(float b) {
     const float y = __builtin_amdgcn_rcpf(b);
     return fmaf(fmaf(-b, y, 1.0f), y, y);

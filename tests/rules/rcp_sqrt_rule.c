@@ -1,4 +1,7 @@
-/* The update kernel's square root (sqrt_rn in the kernel header): from
+/* Host models of the update kernel's square root and reciprocal (sqrt_rn and
+ * rcp_rn in the kernel header).
+ *
+ * Square root: from
  * s = v_sqrt_f32(x) and t = v_rsq_f32(x), one correction
  * fma(fma(-s, s, x), t/2, s).  This host model (gcc, no contraction, libm
  * fmaf and sqrtf) runs the correction for every x of two binades ([1, 4):
@@ -7,13 +10,18 @@
  * either neighbour of each, and counts the results that differ from the
  * correctly rounded square root, per pair of offsets.
  *
- * Output, one line per s offset (-1, 0, +1), three counts each (t offset
- * -1, 0, +1):  s<offset> <k> <k> <k>
- * With both inputs correctly rounded the correction is exact; with one-ulp
- * inputs a few x of the two binades are not, so the kernel's exactness is a
- * property of the hardware's own v_sqrt_f32 and v_rsq_f32 outputs, which
+ * Reciprocal: y + y*(1 - b*y) with both products in fmas, for every b in
+ * [1, 2) (the rule scales exactly by powers of two in the normal range),
+ * from y the correctly rounded 1/b or either neighbour.
+ *
+ * Output: one line per s offset (-1, 0, +1), three counts each (t offset
+ * -1, 0, +1):  s<offset> <k> <k> <k>; then  rcp <k-1> <k0> <k+1>  (failures
+ * per starting offset of y).
+ * With correctly rounded inputs both rules are exact; from one-ulp inputs a
+ * few x (b) are not, so the kernel's exactness is a property of the
+ * hardware's own v_sqrt_f32, v_rsq_f32 and v_rcp_f32 outputs, which
  * tests/rules/rcp_sqrt_all.hip checks on the device for every input of the
- * range the kernel uses.
+ * ranges the kernel uses.
  */
 #include <math.h>
 #include <stdint.h>
@@ -45,5 +53,16 @@ int main(void) {
     }
     for (int a = 0; a < 3; ++a)
         printf("s%+d %ld %ld %ld\n", a - 1, bad[a][0], bad[a][1], bad[a][2]);
+    long rbad[3] = {0, 0, 0};
+    for (uint32_t m = 0; m < (1u << 23); ++m) {
+        const float b = f_of(0x3f800000u | m);
+        const float want = 1.0f / b;                         /* correctly rounded */
+        for (int a = -1; a <= 1; ++a) {
+            const float y = f_of(u_of(want) + (uint32_t)a);
+            const float got = fmaf(fmaf(-b, y, 1.0f), y, y);
+            rbad[a + 1] += u_of(got) != u_of(want);
+        }
+    }
+    printf("rcp %ld %ld %ld\n", rbad[0], rbad[1], rbad[2]);
     return 0;
 }

@@ -104,24 +104,26 @@ def test_near_ties_and_degenerate_scales_match_the_definition():
 
 # ------------------------------------------------------------ square root
 
-def test_sqrt_correction_model(tmp_path):
+def test_sqrt_and_reciprocal_correction_models(tmp_path):
     """sqrt_rn: one correction fma(fma(-s, s, x), t/2, s) of s = v_sqrt_f32(x)
-    with t = v_rsq_f32(x).  On the host, for every x of two binades: exact
-    when s and t are the correctly rounded root and reciprocal root; with
-    either off by one ulp, exact for all but a handful of x.  So the rule is
-    not exact for every pair of one-ulp approximations, and its exactness on
-    gfx950 rests on the hardware's own outputs, which the device check
-    (tests/test_gpu_rules.py, every input of the kernel's range) covers."""
-    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "rules", "sqrt_rule.c")
-    exe = str(tmp_path / "sqrt_rule")
+    with t = v_rsq_f32(x); rcp_rn: one Newton step y + y*(1 - b*y) of
+    y = v_rcp_f32(b).  On the host, for every x of two binades and every b of
+    one: exact from correctly rounded inputs; from one-ulp inputs, exact for
+    all but a handful.  So neither rule is exact for every one-ulp
+    approximation, and their exactness on gfx950 rests on the hardware's own
+    outputs, which the device check (tests/test_gpu_rules.py, every input of
+    the kernel's ranges) covers."""
+    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "rules", "rcp_sqrt_rule.c")
+    exe = str(tmp_path / "rcp_sqrt_rule")
     subprocess.run(["gcc", "-std=c99", "-O2", "-ffp-contract=off", "-Wall", "-o", exe, src, "-lm"],
                    check=True)
     out = subprocess.run([exe], stdout=subprocess.PIPE, text=True, timeout=300, check=True).stdout
     bad = {line.split()[0]: [int(k) for k in line.split()[1:]] for line in out.strip().splitlines()}
-    assert set(bad) == {"s-1", "s+0", "s+1"}, out
-    assert bad["s+0"][1] == 0, out                       # both correctly rounded: exact
-    total = sum(sum(v) for v in bad.values())
+    assert set(bad) == {"s-1", "s+0", "s+1", "rcp"}, out
+    assert bad["s+0"][1] == 0 and bad["rcp"][1] == 0, out     # correctly rounded inputs: exact
+    total = sum(sum(bad[k]) for k in ("s-1", "s+0", "s+1"))
     assert 0 < total < 100, out                          # one-ulp inputs: a handful of x fail
+    assert 0 < sum(bad["rcp"]) < 100, out
 
 
 def test_uniform_divisor_rule_against_ieee_division(tmp_path):
