@@ -598,9 +598,10 @@ __device__ __forceinline__ void tile_dense(const TensorDesc &d, const void *grad
 // to the code range.  The quotient is not formed per element.  When s is a
 // normal number (the usual case), inv = v_rcp_f32(s) is within one ulp of
 // 1/s (tests/rules/rcp_sqrt_all.hip checks it for every normal s whose
-// reciprocal is normal), so r = RN(x*inv) is within |x/s|*3*2^-24 of x/s, and RN(x/s) within
-// |x/s|*2^-24; every |x| <= amax has |x/s| <= 127/(1 - 2^-24) (resp. 255/..),
-// so both stay within 3e-5 of x/s and inside the code range.  When r is more
+// reciprocal is normal), so r = RN(x*inv) is within |x/s|*3*2^-24 of x/s,
+// and RN(x/s) within |x/s|*2^-24; every |x| <= amax has |x/s| <=
+// 127/(1 - 2^-24) (resp. 255/..), so both stay within 5e-5 of x/s and inside
+// the code range.  When r is more
 // than 2.5e-4 away from every half-integer, r and RN(x/s) therefore round to
 // the same integer; otherwise (rare, or a NaN), or when s is zero, denormal
 // or infinite, the quotient itself is rounded and clamped.  d = |r - rint(r)|
