@@ -354,8 +354,13 @@ __device__ __forceinline__ void adamw_update4(float (&th)[kVec], const float (&g
         const float v_hat = div_short(v[j], s.bc2, s.rbc2);
         const float denom = sqrt_rn(v_hat) + s.eps;
         th[j] = td[j] - div_short(x[j], denom, rcp_rn(denom));
+        // bitwise, not short-circuit: the comparisons are lane masks
+        // combined by scalar instructions, with no branch between them
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Wbitwise-instead-of-logical"
         ok &= ((v[j] >= s.div_lo) & (v_hat < 0x1p56f) & (fabsf(x[j]) >= s.x_lo) &
                (fabsf(x[j]) < 0x1p64f)) | (j >= valid);
+#pragma clang diagnostic pop
     }
     if (wave_any(!ok)) {
         asm volatile("");                            // not speculated
@@ -1358,7 +1363,7 @@ __device__ __forceinline__ uint32_t arrive(uint32_t *ctr, uint32_t expected) {
 
 // True in every lane of the wave whose arrival was the last of `expected`.
 __device__ __forceinline__ bool arrived_last(uint32_t before, uint32_t expected) {
-    return __builtin_amdgcn_readfirstlane(before) == expected - 1u;
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)before) == expected - 1u;
 }
 
 // The whole step in one launch per dtype pair, for lists of few tiles (where
