@@ -9,12 +9,19 @@ the whole update runs in the library's kernels.
 """
 from __future__ import annotations
 
+import contextlib
 from array import array
 from typing import Dict, Iterable, List, Optional
 
 import torch
+import torch.optim.optimizer as _torch_optimizer
 
 from . import _lib as L
+
+# torch's current stream as a raw pointer: the query torch's own kernels
+# launch with (a fraction of torch.cuda.current_stream's cost); the public
+# form where a build lacks it
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 _DT = {torch.float32: L.APEXW_F32, torch.bfloat16: L.APEXW_BF16}
 _FMT = {"f32": L.APEXW_STATE_F32, "fp32": L.APEXW_STATE_F32, "bf16": L.APEXW_STATE_BF16,
@@ -190,9 +197,17 @@ class AdamW(torch.optim.Optimizer):
         return t.data_ptr()
 
     def _stream(self) -> int:
+        if _raw_stream is not None:
+            return int(_raw_stream(self.device.index))
         return torch.cuda.current_stream(self.device).cuda_stream
 
-    @torch.no_grad()
+    def _on_device(self):
+        """The parameters' device made current for a library call (nothing to
+        do when it already is)."""
+        if torch.cuda.current_device() == self.device.index:
+            return contextlib.nullcontext()
+        return torch.cuda.device(self.device)
+
     def step(self, closure=None, found_inf: Optional[torch.Tensor] = None,
              inv_scale: Optional[torch.Tensor] = None,
              clip_coef: Optional[torch.Tensor] = None):
@@ -200,7 +215,51 @@ class AdamW(torch.optim.Optimizer):
         found_inf: one-element float32 GPU tensor, nonzero skips the step on
         the device.  inv_scale: grads are unscaled by it first.  clip_coef:
         then multiplied by it (see clip_grad_norm).  Under a GradScaler the
-        scaler's grad_scale and found_inf are used when these are not given."""
+        scaler's grad_scale and found_inf are used when these are not given.
+
+        Step pre- and post-hooks (this optimizer's and the global ones) and
+        the profiler's record of the step work as with torch's optimizers;
+        this class calls them itself (torch's own step wrapper costs several
+        microseconds of host time per call even when none is registered)."""
+        if (self._optimizer_step_pre_hooks or self._optimizer_step_post_hooks
+                or _torch_optimizer._global_optimizer_pre_hooks
+                or _torch_optimizer._global_optimizer_post_hooks
+                or torch.autograd.profiler._is_profiler_enabled):
+            return self._step_hooked(closure, found_inf, inv_scale, clip_coef)
+        return self._step(closure, found_inf, inv_scale, clip_coef)
+
+    # torch.optim.Optimizer wraps a subclass's step with its hook runner
+    # unless the step says it runs the hooks itself
+    step.hooked = True
+
+    def _step_hooked(self, closure, found_inf, inv_scale, clip_coef):
+        """step() with hooks or the profiler, as torch's own step wrapper runs
+        them: pre-hooks (which may replace the arguments), the step, then
+        post-hooks, inside a record_function named as torch names it."""
+        args = (self,)
+        kwargs = dict(closure=closure, found_inf=found_inf, inv_scale=inv_scale,
+                      clip_coef=clip_coef)
+        name = "Optimizer.step#%s.step" % self.__class__.__name__
+        with torch.autograd.profiler.record_function(name):
+            for pre_hook in list(_torch_optimizer._global_optimizer_pre_hooks.values()) + \
+                    list(self._optimizer_step_pre_hooks.values()):
+                result = pre_hook(self, args, kwargs)
+                if result is not None:
+                    if isinstance(result, tuple) and len(result) == 2:
+                        args, kwargs = result
+                    else:
+                        raise RuntimeError("a step pre-hook must return None or a tuple "
+                                           "(new_args, new_kwargs), got %r" % (result,))
+            out = self._step(*args[1:], **kwargs)
+            self._optimizer_step_code()
+            for post_hook in list(self._optimizer_step_post_hooks.values()) + \
+                    list(_torch_optimizer._global_optimizer_post_hooks.values()):
+                post_hook(self, args, kwargs)
+        return out
+
+    def _step(self, closure=None, found_inf: Optional[torch.Tensor] = None,
+              inv_scale: Optional[torch.Tensor] = None,
+              clip_coef: Optional[torch.Tensor] = None):
         loss = None
         if closure is not None:
             with torch.enable_grad():
@@ -222,7 +281,7 @@ class AdamW(torch.optim.Optimizer):
         scale = scale.to(torch.float32).reshape(1)
         if self._inv_buf is None:
             self._inv_buf = torch.empty(1, dtype=torch.float32, device=self.device)
-        with torch.cuda.device(self.device):
+        with self._on_device():
             L.apexw_inv_scale(self._dev_ptr(scale, "grad_scale"), self._inv_buf.data_ptr(),
                               self._stream())
         return self._inv_buf
@@ -236,7 +295,7 @@ class AdamW(torch.optim.Optimizer):
         per-tensor work on the host."""
         groups = [_GroupView(g) for g in self.param_groups]
         self._check_params()
-        with torch.cuda.device(self.device):
+        with self._on_device():
             L.apexw_step_ex(self._h, L.make_groups(groups), len(groups), self._params_arr,
                             grads_arr, self._dev_ptr(inv_scale, "inv_scale"),
                             self._dev_ptr(clip_coef, "clip_coef"),
@@ -245,7 +304,7 @@ class AdamW(torch.optim.Optimizer):
     def unscale_check(self, inv_scale: Optional[torch.Tensor], found_inf: torch.Tensor) -> None:
         """Set found_inf to 1 if any grad times inv_scale is not finite (never
         clears it); grads are not rewritten -- pass inv_scale to step()."""
-        with torch.cuda.device(self.device):
+        with self._on_device():
             L.apexw_unscale_check(self._h, self._grads_arr(), self._dev_ptr(inv_scale, "inv_scale"),
                                   self._dev_ptr(found_inf, "found_inf"), self._stream())
 
@@ -256,7 +315,7 @@ class AdamW(torch.optim.Optimizer):
         to step(clip_coef=...).  With found_inf the finite check runs too."""
         norm = torch.empty(1, dtype=torch.float64, device=self.device)
         coef = torch.empty(1, dtype=torch.float32, device=self.device)
-        with torch.cuda.device(self.device):
+        with self._on_device():
             L.apexw_clip_grad_norm(self._h, self._grads_arr(), self._dev_ptr(inv_scale, "inv_scale"),
                                    float(max_norm), self._dev_ptr(found_inf, "found_inf"),
                                    norm.data_ptr(), coef.data_ptr(), self._stream())
@@ -269,7 +328,7 @@ class AdamW(torch.optim.Optimizer):
         the parameter-group hyperparameters; loadable with
         torch.load(weights_only=True)."""
         groups = [_GroupView(g) for g in self.param_groups]
-        with torch.cuda.device(self.device):
+        with self._on_device():
             blob = L.apexw_export_state(self._h, L.make_groups(groups), len(groups), self._stream())
         return {
             "apexw_blob": torch.frombuffer(bytearray(blob), dtype=torch.uint8),
@@ -279,7 +338,7 @@ class AdamW(torch.optim.Optimizer):
 
     def load_state_dict(self, sd: Dict) -> None:
         blob = bytes(sd["apexw_blob"].cpu().numpy().tobytes())
-        with torch.cuda.device(self.device):
+        with self._on_device():
             L.apexw_import_state(self._h, blob, len(self.param_groups), self._stream())
         for g, h in zip(self.param_groups, sd["param_groups"]):
             g["lr"], g["betas"] = h["lr"], tuple(h["betas"])
@@ -311,7 +370,7 @@ class AdamW(torch.optim.Optimizer):
 
     def read_steps(self):
         """Step counters copied to the host (synchronises the current stream)."""
-        with torch.cuda.device(self.device):
+        with self._on_device():
             return L.apexw_read_steps(self._h, len(self._params), self._stream())
 
     def launch_info(self):

@@ -270,3 +270,76 @@ def test_flat_grads_match_the_default_path_and_backward_fills_them():
         opt_b.step()
     opt_a.close()
     opt_b.close()
+
+
+def test_step_hooks_and_profiler_record_like_torch_optimizers():
+    """The wrapper runs torch's optimizer step hooks itself: this optimizer's
+    and the global pre- and post-hooks are called with (optimizer, args,
+    kwargs), a pre-hook may replace the arguments (here it supplies a set
+    found_inf flag, so the step is skipped), removed hooks stop being called,
+    the profiler records the step under torch's name, and the steps with
+    and without hooks are the same updates (against the oracle)."""
+    import torch.optim.optimizer as topt
+    say("case: wrapper step hooks")
+    gen = torch.Generator().manual_seed(5)
+    p_cpu = [torch.randn(n, generator=gen) * 0.02 for n in (300, 17)]
+    ps = [torch.nn.Parameter(p.to(DEV)) for p in p_cpu]
+    opt = AdamW(ps, lr=1e-3, weight_decay=0.1)
+    assert getattr(AdamW.step, "hooked", False)          # torch's wrapper is not added
+    ref = oracle.OracleAdamW([p.numel() for p in p_cpu], ["f32"] * 2, ["f32"] * 2, [0, 0], "f32")
+    th_ref = [bits(p) for p in p_cpu]
+    calls = []
+    skip = torch.ones(1, dtype=torch.float32, device=DEV)
+
+    def pre(o, args, kwargs):
+        calls.append(("pre", o is opt, len(args)))
+        if kwargs.get("found_inf") is None and len(calls) == 5:
+            kwargs = dict(kwargs, found_inf=skip)        # the second hooked step is skipped
+            return args, kwargs
+        return None
+
+    def post(o, args, kwargs):
+        calls.append(("post", o is opt))
+
+    def gpre(o, args, kwargs):
+        calls.append(("gpre", o is opt))
+
+    g_all = []
+    for k in range(5):
+        g = [torch.randn(p.shape, generator=gen) * 1e-3 for p in p_cpu]
+        for p, gg in zip(ps, g):
+            p.grad = gg.to(DEV)
+        g_all.append([bits(gg) for gg in g])
+    h1 = opt.register_step_pre_hook(pre)
+    h2 = opt.register_step_post_hook(post)
+    h3 = topt.register_optimizer_step_pre_hook(gpre)
+    groups = [W.Group(lr=1e-3, weight_decay=0.1)]
+    try:
+        for k in range(3):
+            for p, gg in zip(ps, g_all[k]):
+                p.grad = torch.from_numpy(gg).to(DEV)
+            opt.step()
+            ref.step(th_ref, g_all[k], groups, found_inf=(k == 1))
+        assert [c[0] for c in calls] == ["gpre", "pre", "post"] * 3
+        assert all(c[1] for c in calls)
+    finally:
+        h1.remove()
+        h2.remove()
+        h3.remove()
+    n_calls = len(calls)
+    with torch.profiler.profile(activities=[torch.profiler.ProfilerActivity.CPU], acc_events=True) as prof:
+        for p, gg in zip(ps, g_all[3]):
+            p.grad = torch.from_numpy(gg).to(DEV)
+        opt.step()
+        ref.step(th_ref, g_all[3], groups)
+    assert any(e.name == "Optimizer.step#AdamW.step" for e in prof.events())
+    for p, gg in zip(ps, g_all[4]):
+        p.grad = torch.from_numpy(gg).to(DEV)
+    opt.step()                                           # no hooks, no profiler: the fast path
+    ref.step(th_ref, g_all[4], groups)
+    assert len(calls) == n_calls
+    torch.cuda.synchronize()
+    for i in range(2):
+        assert n_bit_mismatch(bits(ps[i].detach()), th_ref[i]) == 0, i
+    assert opt.read_steps() == [4, 4]
+    opt.close()
