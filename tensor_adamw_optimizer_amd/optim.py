@@ -23,6 +23,24 @@ from . import _lib as L
 # form where a build lacks it
 _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
+# torch's registries of global optimizer step hooks (module-level dicts in
+# torch.optim.optimizer); a build without them is treated as having hooks,
+# so every step takes the hooked path
+_NO_HOOKS: Dict = {}
+_ALWAYS: Dict = {None: None}
+
+
+def _global_pre_hooks() -> Dict:
+    return getattr(_torch_optimizer, "_global_optimizer_pre_hooks", _ALWAYS)
+
+
+def _global_post_hooks() -> Dict:
+    return getattr(_torch_optimizer, "_global_optimizer_post_hooks", _NO_HOOKS)
+
+
+def _profiling() -> bool:
+    return bool(getattr(torch.autograd.profiler, "_is_profiler_enabled", True))
+
 _DT = {torch.float32: L.APEXW_F32, torch.bfloat16: L.APEXW_BF16}
 _FMT = {"f32": L.APEXW_STATE_F32, "fp32": L.APEXW_STATE_F32, "bf16": L.APEXW_STATE_BF16,
         "q8": L.APEXW_STATE_Q8}
@@ -222,9 +240,7 @@ class AdamW(torch.optim.Optimizer):
         this class calls them itself (torch's own step wrapper costs several
         microseconds of host time per call even when none is registered)."""
         if (self._optimizer_step_pre_hooks or self._optimizer_step_post_hooks
-                or _torch_optimizer._global_optimizer_pre_hooks
-                or _torch_optimizer._global_optimizer_post_hooks
-                or torch.autograd.profiler._is_profiler_enabled):
+                or _global_pre_hooks() or _global_post_hooks() or _profiling()):
             return self._step_hooked(closure, found_inf, inv_scale, clip_coef)
         return self._step(closure, found_inf, inv_scale, clip_coef)
 
@@ -241,7 +257,8 @@ class AdamW(torch.optim.Optimizer):
                       clip_coef=clip_coef)
         name = "Optimizer.step#%s.step" % self.__class__.__name__
         with torch.autograd.profiler.record_function(name):
-            for pre_hook in list(_torch_optimizer._global_optimizer_pre_hooks.values()) + \
+            glob_pre = _global_pre_hooks()
+            for pre_hook in [h for h in glob_pre.values() if h is not None] + \
                     list(self._optimizer_step_pre_hooks.values()):
                 result = pre_hook(self, args, kwargs)
                 if result is not None:
@@ -253,7 +270,7 @@ class AdamW(torch.optim.Optimizer):
             out = self._step(*args[1:], **kwargs)
             self._optimizer_step_code()
             for post_hook in list(self._optimizer_step_post_hooks.values()) + \
-                    list(_torch_optimizer._global_optimizer_post_hooks.values()):
+                    list(_global_post_hooks().values()):
                 post_hook(self, args, kwargs)
         return out
 
