@@ -382,9 +382,10 @@ int apexw_set_workgroups(apexw_t h, int32_t workgroups);
  * time, for every update launch (enforced through the dynamic LDS each
  * workgroup reserves; the kernel uses none).  0 restores the defaults, which
  * depend on the bytes each element moves (fp32 params and moments, 28 B: 14;
- * bf16 params, fp32 grads and moments, 24 B: 16; bf16 or 8-bit moments: no
- * cap).  Fewer concurrent streams can keep the HBM read/write mix more
- * efficient; results do not depend on it.
+ * bf16 params, fp32 grads and moments, 24 B: 16; bf16 moments with fp32
+ * grads, 16-18 B: 28; all-bf16 (14 B) or 8-bit moments: no cap).  Fewer
+ * concurrent streams can keep the HBM read/write mix more efficient; results
+ * do not depend on it.
  */
 int apexw_set_occupancy(apexw_t h, int32_t workgroups_per_cu);
 
