@@ -236,24 +236,24 @@ kernel_fn pick_single(int pt, int gt) {
     return adamw_single_step_kernel<ST, APEXW_BF16, APEXW_BF16, SC>;
 }
 
-template <int ST, bool NT, bool SC, bool ONE>
+template <int ST, bool NT, bool SC, bool ONE, bool FEW>
 kernel_fn pick_carry(int pt, int gt) {
-    if (pt == APEXW_F32 && gt == APEXW_F32) return adamw_carry_step_kernel<ST, APEXW_F32, APEXW_F32, NT, SC, ONE>;
-    if (pt == APEXW_F32 && gt == APEXW_BF16) return adamw_carry_step_kernel<ST, APEXW_F32, APEXW_BF16, NT, SC, ONE>;
-    if (pt == APEXW_BF16 && gt == APEXW_F32) return adamw_carry_step_kernel<ST, APEXW_BF16, APEXW_F32, NT, SC, ONE>;
-    return adamw_carry_step_kernel<ST, APEXW_BF16, APEXW_BF16, NT, SC, ONE>;
+    if (pt == APEXW_F32 && gt == APEXW_F32) return adamw_carry_step_kernel<ST, APEXW_F32, APEXW_F32, NT, SC, ONE, FEW>;
+    if (pt == APEXW_F32 && gt == APEXW_BF16) return adamw_carry_step_kernel<ST, APEXW_F32, APEXW_BF16, NT, SC, ONE, FEW>;
+    if (pt == APEXW_BF16 && gt == APEXW_F32) return adamw_carry_step_kernel<ST, APEXW_BF16, APEXW_F32, NT, SC, ONE, FEW>;
+    return adamw_carry_step_kernel<ST, APEXW_BF16, APEXW_BF16, NT, SC, ONE, FEW>;
 }
 
 // The 8-bit carried step: under a workgroup cap the grid-stride kernel;
 // otherwise (PAIR) the kernel that takes two tiles per workgroup, whose grid
 // is half the tiles (carry_grid).
-template <bool NT, bool SC, bool PAIR>
+template <bool NT, bool SC, bool PAIR, bool FEW>
 kernel_fn pick_carry_q8(int pt, int gt) {
     if constexpr (PAIR) {
-        if (pt == APEXW_F32 && gt == APEXW_F32) return adamw_carry_pair_q8_kernel<APEXW_F32, APEXW_F32, NT, SC>;
-        if (pt == APEXW_F32 && gt == APEXW_BF16) return adamw_carry_pair_q8_kernel<APEXW_F32, APEXW_BF16, NT, SC>;
-        if (pt == APEXW_BF16 && gt == APEXW_F32) return adamw_carry_pair_q8_kernel<APEXW_BF16, APEXW_F32, NT, SC>;
-        return adamw_carry_pair_q8_kernel<APEXW_BF16, APEXW_BF16, NT, SC>;
+        if (pt == APEXW_F32 && gt == APEXW_F32) return adamw_carry_pair_q8_kernel<APEXW_F32, APEXW_F32, NT, SC, FEW>;
+        if (pt == APEXW_F32 && gt == APEXW_BF16) return adamw_carry_pair_q8_kernel<APEXW_F32, APEXW_BF16, NT, SC, FEW>;
+        if (pt == APEXW_BF16 && gt == APEXW_F32) return adamw_carry_pair_q8_kernel<APEXW_BF16, APEXW_F32, NT, SC, FEW>;
+        return adamw_carry_pair_q8_kernel<APEXW_BF16, APEXW_BF16, NT, SC, FEW>;
     } else {
         if (pt == APEXW_F32 && gt == APEXW_F32) return adamw_carry_step_q8_kernel<APEXW_F32, APEXW_F32, NT, SC>;
         if (pt == APEXW_F32 && gt == APEXW_BF16) return adamw_carry_step_q8_kernel<APEXW_F32, APEXW_BF16, NT, SC>;
@@ -271,25 +271,36 @@ int64_t carry_grid(int fmt, int64_t tiles, int64_t wg) {
 }
 
 // one_tile: the grid is not capped (a workgroup per tile, or per two tiles
-// in the 8-bit format); the kernels then run their loop-free form
+// in the 8-bit format); the kernels then run their loop-free form.  few
+// (only with one_tile): the launch's tensors are found from the few-tensor
+// bounds in the kernel arguments instead of the tile table.
+template <int ST, bool NT, bool SC>
+kernel_fn pick_carry_shape(int pt, int gt, bool one_tile, bool few) {
+    if constexpr (ST == APEXW_STATE_Q8)
+        return !one_tile ? pick_carry_q8<NT, SC, false, false>(pt, gt)
+               : few     ? pick_carry_q8<NT, SC, true, true>(pt, gt)
+                         : pick_carry_q8<NT, SC, true, false>(pt, gt);
+    else
+        return !one_tile ? pick_carry<ST, NT, SC, false, false>(pt, gt)
+               : few     ? pick_carry<ST, NT, SC, true, true>(pt, gt)
+                         : pick_carry<ST, NT, SC, true, false>(pt, gt);
+}
+
 template <bool NT, bool SC>
-kernel_fn pick_carry_format(int fmt, int pt, int gt, bool one_tile) {
-    if (fmt == APEXW_STATE_F32)
-        return one_tile ? pick_carry<APEXW_STATE_F32, NT, SC, true>(pt, gt)
-                        : pick_carry<APEXW_STATE_F32, NT, SC, false>(pt, gt);
-    if (fmt == APEXW_STATE_BF16)
-        return one_tile ? pick_carry<APEXW_STATE_BF16, NT, SC, true>(pt, gt)
-                        : pick_carry<APEXW_STATE_BF16, NT, SC, false>(pt, gt);
-    return one_tile ? pick_carry_q8<NT, SC, true>(pt, gt) : pick_carry_q8<NT, SC, false>(pt, gt);
+kernel_fn pick_carry_format(int fmt, int pt, int gt, bool one_tile, bool few) {
+    if (fmt == APEXW_STATE_F32) return pick_carry_shape<APEXW_STATE_F32, NT, SC>(pt, gt, one_tile, few);
+    if (fmt == APEXW_STATE_BF16) return pick_carry_shape<APEXW_STATE_BF16, NT, SC>(pt, gt, one_tile, few);
+    return pick_carry_shape<APEXW_STATE_Q8, NT, SC>(pt, gt, one_tile, few);
 }
 
 // The carried-step kernel (launch mode 3).
-kernel_fn carry_kernel_for(int fmt, int pt, int gt, bool streaming, bool scaled, bool one_tile) {
+kernel_fn carry_kernel_for(int fmt, int pt, int gt, bool streaming, bool scaled, bool one_tile,
+                           bool few) {
     if (streaming)
-        return scaled ? pick_carry_format<true, true>(fmt, pt, gt, one_tile)
-                      : pick_carry_format<true, false>(fmt, pt, gt, one_tile);
-    return scaled ? pick_carry_format<false, true>(fmt, pt, gt, one_tile)
-                  : pick_carry_format<false, false>(fmt, pt, gt, one_tile);
+        return scaled ? pick_carry_format<true, true>(fmt, pt, gt, one_tile, few)
+                      : pick_carry_format<true, false>(fmt, pt, gt, one_tile, few);
+    return scaled ? pick_carry_format<false, true>(fmt, pt, gt, one_tile, few)
+                  : pick_carry_format<false, false>(fmt, pt, gt, one_tile, few);
 }
 
 // The single-launch step kernel (cached accesses: such lists are small).
@@ -929,7 +940,8 @@ int apexw_step_ex(apexw_t h, const apexw_group *groups, int32_t n_groups, void *
             }
         }
         if (carry) {
-            hipLaunchKernelGGL(carry_kernel_for(h->fmt, L.pt, L.gt, streaming, scaled, wg == L.tile_count),
+            hipLaunchKernelGGL(carry_kernel_for(h->fmt, L.pt, L.gt, streaming, scaled, wg == L.tile_count,
+                                                a.few > 0),
                                dim3((unsigned)carry_grid(h->fmt, L.tile_count, wg)), dim3(kThreads),
                                lds, st, a);
         } else if (single) {

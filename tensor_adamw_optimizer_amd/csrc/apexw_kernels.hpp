@@ -176,7 +176,8 @@ struct KernelArgs {
     const BiasRecord *bias_cur;      // carried step: this step's bias corrections
     BiasRecord *bias_next;           //   and the next step's (written by first tiles)
     // carried step over a launch of at most kFewTensors tensors, none empty
-    // (0 otherwise): the tile's tensor is found from these, not the tile table
+    // (few = 0 otherwise): the few-tensor kernels find a tile's tensor from
+    // these, not the tile table; entries past `few` repeat the last tensor
     int32_t few;                     // tensors of the launch
     int32_t few_first[kFewTensors];  // launch-relative first tile of each
     int32_t few_tensor[kFewTensors]; // their tensor indices
@@ -205,15 +206,21 @@ __device__ __forceinline__ float step_x_lo(float eps) {
 }
 
 
-// beta^n in fp64: square-and-multiply from the least significant bit.
-__device__ __forceinline__ double pow_uint(double b, uint32_t n) {
-    double r = 1.0;
+// b1^n and b2^n in fp64: square-and-multiply from the least significant
+// bit, the two powers in one loop (the same products for each as two
+// separate loops would form, with their dependency chains interleaved).
+__device__ __forceinline__ void pow2_uint(double b1, double b2, uint32_t n, double &r1, double &r2) {
+    r1 = 1.0;
+    r2 = 1.0;
     while (n != 0u) {
-        if (n & 1u) r = r * b;
-        b = b * b;
+        if (n & 1u) {
+            r1 = r1 * b1;
+            r2 = r2 * b2;
+        }
+        b1 = b1 * b1;
+        b2 = b2 * b2;
         n >>= 1;
     }
-    return r;
 }
 
 __device__ __forceinline__ StepScalars step_scalars(const StepRecord &r) {
@@ -975,8 +982,10 @@ __device__ __forceinline__ T load_uniform(const T *tab, int32_t i) {
 // bound of the short division by them (div_uniform).
 __device__ __forceinline__ BiasRecord bias_record(double beta1_d, double beta2_d, int32_t t) {
     BiasRecord b = {};
-    b.bc1 = (float)(1.0 - pow_uint(beta1_d, (uint32_t)t));
-    b.bc2 = (float)(1.0 - pow_uint(beta2_d, (uint32_t)t));
+    double p1, p2;
+    pow2_uint(beta1_d, beta2_d, (uint32_t)t, p1, p2);
+    b.bc1 = (float)(1.0 - p1);
+    b.bc2 = (float)(1.0 - p2);
     b.rbc1 = 1.0f / b.bc1;
     b.rbc2 = 1.0f / b.bc2;
     b.div_lo = b.bc1 >= 0x1p-60f && b.bc2 >= 0x1p-60f ? 0x1p-96f : __builtin_inff();   // both are <= 1
@@ -1097,37 +1106,51 @@ __global__ __launch_bounds__(kThreads) void adamw_step_kernel(KernelArgs a) {
 // with the metadata, only the first tile's value counts), so no ordering
 // between workgroups is needed.  Results are bitwise those of the other
 // modes: the same fp64 and fp32 operations form the same scalars.
-// The tensor of launch-relative tile k: for a launch of a few non-empty
-// tensors, the number of tensors whose first tile is at or before k (scalar
-// compares on kernel arguments, no memory round trip before the tile's
-// metadata loads); otherwise the tile table.  Compiled in (FEW) only for
-// the loop-free kernels: across a grid-stride loop the eight bounds would
-// stay live in scalar registers.
+// The tensor of launch-relative tile k.  FEW (the loop-free kernels over a
+// launch of at most kFewTensors tensors, none empty): the last of the
+// launch's tensors whose first tile is at or before k, by scalar compares
+// on the kernel arguments.  Every bound and index sits at a constant offset,
+// so they arrive with the other arguments in one round of loads and no
+// memory round trip precedes the tile's metadata loads; the host repeats the
+// last tensor in the unused entries, which then never change the result.  A
+// separate kernel rather than a test of `few`: read unconditionally, the
+// bounds cost launches of many tensors 1.8% (many-small list), and read
+// after the test they take a second round.  Otherwise the tile table.
 template <bool FEW>
 __device__ __forceinline__ int32_t tile_owner(const KernelArgs &a, const APEXW_CONST int32_t *tile_tensor,
                                               int64_t k) {
-    if (FEW && a.few > 0) {                    // wave-uniform
+    if constexpr (FEW) {
         // launch-relative tile indices fit 32 bits (lists have < 2^31 tiles)
         const int32_t k32 = (int32_t)k;
-        int32_t j = 0;
+        int32_t t[kFewTensors];
 #pragma unroll
-        for (int u = 1; u < kFewTensors; ++u) j += (u < a.few && k32 >= a.few_first[u]) ? 1 : 0;
-        return a.few_tensor[j];
+        for (int u = 0; u < kFewTensors; ++u) {
+            t[u] = a.few_tensor[u];
+            // opaque to the optimizer: a choice between loaded values would
+            // otherwise become one load at a chosen offset, a second round
+            asm("" : "+s"(t[u]));
+        }
+        int32_t r = t[0];
+#pragma unroll
+        for (int u = 1; u < kFewTensors; ++u) r = k32 >= a.few_first[u] ? t[u] : r;
+        return r;
+    } else {
+        return tile_tensor[table_pos(a, k)];
     }
-    return tile_tensor[table_pos(a, k)];
 }
 
 // ONE: the grid has a workgroup per tile, so each takes exactly one tile and
 // the body is straight-line code (no loop, so nothing is hoisted into a
 // preheader that every wave would run for its one tile).
-template <int ST, int PT, int GT, bool NT, bool SC, bool ONE = false>
+template <int ST, int PT, int GT, bool NT, bool SC, bool ONE = false, bool FEW = false>
 __device__ __forceinline__ void carry_step(const KernelArgs &a) {
+    static_assert(ONE || !FEW, "the few-tensor lookup is for the loop-free kernels");
     const APEXW_CONST int32_t *tile_tensor = cptr<int32_t>(a.tile_tensor);
     const float fi = *cptr<float>(a.found_inf);
     const float inv_scale = *cptr<float>(a.inv_scale);
     const float clip_coef = *cptr<float>(a.clip_coef);
     int64_t k = blockIdx.x;                    // < tile_count: grid <= tiles
-    int32_t i = tile_owner<ONE>(a, tile_tensor, k);
+    int32_t i = tile_owner<FEW>(a, tile_tensor, k);
     for (;;) {
         const TensorDesc d = load_uniform(a.desc, i);
         const void *g_ptr = reinterpret_cast<const void *>(cptr<uint64_t>(a.grads)[i]);
@@ -1203,13 +1226,13 @@ __device__ __forceinline__ void carry_step(const KernelArgs &a) {
         if constexpr (ONE) break;
         k += gridDim.x;
         if (k >= a.tile_count) break;
-        i = tile_owner<ONE>(a, tile_tensor, k);
+        i = tile_owner<FEW>(a, tile_tensor, k);
     }
 }
 
-template <int ST, int PT, int GT, bool NT, bool SC, bool ONE>
+template <int ST, int PT, int GT, bool NT, bool SC, bool ONE, bool FEW>
 __global__ __launch_bounds__(kThreads) void adamw_carry_step_kernel(KernelArgs a) {
-    carry_step<ST, PT, GT, NT, SC, ONE>(a);
+    carry_step<ST, PT, GT, NT, SC, ONE, FEW>(a);
 }
 
 // The 8-bit carried step under a workgroup cap (a grid-stride loop over the
@@ -1277,12 +1300,12 @@ __device__ __forceinline__ void carry_first_tile_q8(const KernelArgs &a, int32_t
 // tile per workgroup; the step measured 3.5% faster on MI355X (LoRA list,
 // 43.8-44.0 against 45.4-45.8 us, same machine, alternating runs): the same
 // VALU work per block, half the metadata chains and scalar work.
-template <int PT, int GT, bool NT, bool SC>
+template <int PT, int GT, bool NT, bool SC, bool FEW>
 __device__ __forceinline__ void carry_q8_one_tile(const KernelArgs &a,
                                                   const APEXW_CONST int32_t *tile_tensor,
                                                   int64_t k, float fi, float inv_scale,
                                                   float clip_coef) {
-    const int32_t i = tile_owner<true>(a, tile_tensor, k);
+    const int32_t i = tile_owner<FEW>(a, tile_tensor, k);
     const TensorDesc d = load_uniform(a.desc, i);
     const void *g_ptr = reinterpret_cast<const void *>(cptr<uint64_t>(a.grads)[i]);
     const BiasRecord b = load_uniform(a.bias_cur, i);
@@ -1296,7 +1319,7 @@ __device__ __forceinline__ void carry_q8_one_tile(const KernelArgs &a,
     carry_first_tile_q8(a, i, d, b, base, grad);
 }
 
-template <int PT, int GT, bool NT, bool SC>
+template <int PT, int GT, bool NT, bool SC, bool FEW>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_num_sgpr(80)))
 void adamw_carry_pair_q8_kernel(KernelArgs a) {
     const APEXW_CONST int32_t *tile_tensor = cptr<int32_t>(a.tile_tensor);
@@ -1304,16 +1327,16 @@ void adamw_carry_pair_q8_kernel(KernelArgs a) {
     const float inv_scale = *cptr<float>(a.inv_scale);
     const float clip_coef = *cptr<float>(a.clip_coef);
     const int64_t k0 = 2 * (int64_t)blockIdx.x;           // < tile_count: grid = ceil(tiles / 2)
-    const int32_t i = tile_owner<true>(a, tile_tensor, k0);
+    const int32_t i = tile_owner<FEW>(a, tile_tensor, k0);
     const TensorDesc d = load_uniform(a.desc, i);
     const void *g_ptr = reinterpret_cast<const void *>(cptr<uint64_t>(a.grads)[i]);
     const BiasRecord b = load_uniform(a.bias_cur, i);
     const int64_t base = (a.tile_begin + k0 - d.first_tile) * kTile;
     const int64_t left = d.numel - base;
     if (left <= kTile) {                       // tile k0 ends its tensor: one tile at a time
-        carry_q8_one_tile<PT, GT, NT, SC>(a, tile_tensor, k0, fi, inv_scale, clip_coef);
+        carry_q8_one_tile<PT, GT, NT, SC, FEW>(a, tile_tensor, k0, fi, inv_scale, clip_coef);
         if (k0 + 1 < a.tile_count)
-            carry_q8_one_tile<PT, GT, NT, SC>(a, tile_tensor, k0 + 1, fi, inv_scale, clip_coef);
+            carry_q8_one_tile<PT, GT, NT, SC, FEW>(a, tile_tensor, k0 + 1, fi, inv_scale, clip_coef);
         return;
     }
     const void *grad = fi != 0.0f ? nullptr : g_ptr;
