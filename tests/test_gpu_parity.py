@@ -1139,3 +1139,67 @@ def test_q8_tile_pairs_against_oracle(cap):
         assert np.array_equal(vs.view(np.uint32), ref.v_scale[i].view(np.uint32)), i
     assert np.array_equal(bits(opt.steps()), ref.t[:len(sizes)])
     opt.close()
+
+
+@pytest.mark.parametrize("fmt", [W.STATE_F32, W.STATE_BF16, W.STATE_Q8])
+def test_few_tensor_launches_against_oracle(fmt):
+    """A carried launch of at most 8 tensors, none empty, finds each tile's
+    tensor from first-tile bounds in the kernel arguments (the unused entries
+    repeat the last tensor); a larger launch reads the tile table.  Lists of
+    1, 2, 7, 8 and 9 tensors of one dtype pair, and a mixed list whose
+    fp32/fp32 launch holds 8 tensors and whose bf16/bf16 launch holds 9, in
+    interleaved order; ragged sizes (1, 255, 256, 257 elements, several
+    tiles); four calls with an absent grad and a skipped call: every value
+    bit-exact against the oracle."""
+    _need_gpu()
+    pool = [257, 1, 256 * 3 + 7, 256, 255, 513, 3, 256 * 5, 1000]
+    lists = [[(pool[j], W.F32, W.F32) for j in range(n)] for n in (1, 2, 7, 8, 9)]
+    mixed = []
+    for j in range(9):
+        if j < 8:
+            mixed.append((pool[j], W.F32, W.F32))
+        mixed.append((pool[8 - j] + 11, W.BF16, W.BF16))
+    lists.append(mixed)
+    groups = [W.Group(lr=1e-3, weight_decay=0.1), W.Group(lr=5e-4, eps=1e-6)]
+    to_dev = lambda h, d: (torch.from_numpy(h.view(np.int32) if d == W.F32 else h.view(np.int16))
+                           .to(DEV).view(torch.float32 if d == W.F32 else torch.bfloat16))
+    f32 = lambda a: a.view(np.float32)
+    for li, spec in enumerate(lists):
+        sizes = [s for s, _, _ in spec]
+        pdt = [p for _, p, _ in spec]
+        gdt = [g for _, _, g in spec]
+        group_of = [i % 2 for i in range(len(spec))]
+        say("case: few-tensor launches", fmt, "list", li, "tensors", len(spec))
+        rng = np.random.default_rng(4242 + li)
+        th_ref = [(rng.standard_normal(n) * 0.02).astype(np.float32) for n in sizes]
+        th_ref = [x if d == W.F32 else oracle.f32_to_bf16(x) for x, d in zip(th_ref, pdt)]
+        params = [to_dev(h, d) for h, d in zip(th_ref, pdt)]
+        opt = GpuOpt(sizes, pdt, gdt, group_of, len(groups), fmt)
+        L.apexw_set_launch_mode(opt.h, 3)
+        ref = oracle.OracleAdamW(sizes, pdt, gdt, group_of, fmt)
+        flag = torch.zeros(1, dtype=torch.float32, device=DEV)
+        for k in range(4):
+            g32 = [(rng.standard_normal(n) * 1e-3).astype(np.float32) for n in sizes]
+            g_host = [g if d == W.F32 else oracle.f32_to_bf16(g) for g, d in zip(g32, gdt)]
+            absent = {len(spec) - 1} if k == 1 else set()
+            skip = k == 2
+            flag.fill_(1.0 if skip else 0.0)
+            opt.step(groups, params, [None if i in absent else to_dev(h, d)
+                                      for i, (h, d) in enumerate(zip(g_host, gdt))], found_inf=flag)
+            ref.step(th_ref, [None if i in absent else h for i, h in enumerate(g_host)], groups,
+                     found_inf=skip)
+        torch.cuda.synchronize()
+        for i in range(len(sizes)):
+            assert n_bit_mismatch(bits(params[i]), th_ref[i]) == 0, (li, i)
+            m, v = (bits(t) for t in opt.moments(i))
+            if fmt == W.STATE_Q8:
+                assert np.array_equal(m, ref.m[i]) and np.array_equal(v, ref.v[i]), (li, i)
+                ms, vs = (bits(t) for t in opt.scales(i))
+                assert np.array_equal(ms.view(np.uint32), ref.m_scale[i].view(np.uint32)), (li, i)
+                assert np.array_equal(vs.view(np.uint32), ref.v_scale[i].view(np.uint32)), (li, i)
+            else:
+                as_s = f32 if fmt == W.STATE_F32 else oracle.bf16_to_f32
+                _same_bits_or_both_nan("m%d" % i, m, ref.m[i], as_s)
+                _same_bits_or_both_nan("v%d" % i, v, ref.v[i], as_s)
+        assert np.array_equal(bits(opt.steps()), ref.t[:len(sizes)])
+        opt.close()
