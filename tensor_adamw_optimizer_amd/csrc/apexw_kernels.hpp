@@ -175,9 +175,10 @@ struct KernelArgs {
     uint32_t *done;                  // single-launch step: arrival counters
     const BiasRecord *bias_cur;      // carried step: this step's bias corrections
     BiasRecord *bias_next;           //   and the next step's (written by first tiles)
-    // carried step over a launch of at most kFewTensors tensors, none empty
-    // (few = 0 otherwise): the few-tensor kernels find a tile's tensor from
-    // these, not the tile table; entries past `few` repeat the last tensor
+    // carried step over a launch of at most kFewTensors tensors, none empty,
+    // uncapped, with cached accesses (few = 0 otherwise): the few-tensor
+    // kernels find a tile's tensor from these, not the tile table; entries
+    // past `few` repeat the last tensor
     int32_t few;                     // tensors of the launch
     int32_t few_first[kFewTensors];  // launch-relative first tile of each
     int32_t few_tensor[kFewTensors]; // their tensor indices
@@ -1107,7 +1108,8 @@ __global__ __launch_bounds__(kThreads) void adamw_step_kernel(KernelArgs a) {
 // between workgroups is needed.  Results are bitwise those of the other
 // modes: the same fp64 and fp32 operations form the same scalars.
 // The tensor of launch-relative tile k.  FEW (the loop-free kernels over a
-// launch of at most kFewTensors tensors, none empty): the last of the
+// launch of at most kFewTensors tensors, none empty, with cached accesses --
+// a small list, whose step is the latency of this chain): the last of the
 // launch's tensors whose first tile is at or before k, by scalar compares
 // on the kernel arguments.  Every bound and index sits at a constant offset,
 // so they arrive with the other arguments in one round of loads and no
