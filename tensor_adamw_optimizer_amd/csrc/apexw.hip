@@ -939,7 +939,8 @@ int apexw_step_ex(apexw_t h, const apexw_group *groups, int32_t n_groups, void *
         // streamed launch (a list past 64 MB) reads the tile table instead:
         // bandwidth-bound, it measured 0.3-0.5% faster that way (few_large
         // 1.9418 against 1.9471 ms, bf16_state 1.3406 against 1.3441 ms,
-        // four alternating runs each on MI355X)
+        // four alternating runs each on MI355X).  No tensor is empty here:
+        // the carried step takes no list with an empty tensor.
         a.few = 0;
         if (carry && !streaming && wg == L.tile_count &&
             L.tensor_count <= kFewTensors) {                      // carry_ok: none empty
