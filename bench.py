@@ -451,9 +451,15 @@ def main() -> int:
         },
         "hbm_gbps": (ab / (elapsed / args.steps)) / 1e9,
         "hbm_frac_of_peak": (ab / (elapsed / args.steps)) / 1e9 / HBM_PEAK_GBPS,
-        "kernel_ms": {"avg": avg_kernel_s * 1e3, "min": min(kernel_ms),
-                      "median": sorted(kernel_ms)[len(kernel_ms) // 2], "max": max(kernel_ms),
-                      "spread_from": "flushed steps" if args.flush_mall else
+        "kernel_ms": {"avg": avg_kernel_s * 1e3,
+                      "avg_from": "one event per flushed step" if args.flush_mall else
+                      "two HIP events around the timed steps",
+                      # per-step spread: an event after every step adds its
+                      # own time, so these can exceed the average above
+                      "per_step_min": min(kernel_ms),
+                      "per_step_median": sorted(kernel_ms)[len(kernel_ms) // 2],
+                      "per_step_max": max(kernel_ms),
+                      "per_step_from": "flushed steps" if args.flush_mall else
                       "an untimed pass with an event after every step"},
         "residency": ("cache-resident (algorithmic bytes per step below the 256 MB "
                       "Infinity Cache)" if ab < (256 << 20) and not args.flush_mall
