@@ -1203,3 +1203,65 @@ def test_few_tensor_launches_against_oracle(fmt):
                 _same_bits_or_both_nan("v%d" % i, v, ref.v[i], as_s)
         assert np.array_equal(bits(opt.steps()), ref.t[:len(sizes)])
         opt.close()
+
+
+@pytest.mark.parametrize("fmt", [W.STATE_F32, W.STATE_BF16, W.STATE_Q8])
+def test_empty_list_and_lists_of_empty_tensors(fmt):
+    """Degenerate lists: no tensor at all (every call succeeds and does
+    nothing; the grad norm is 0 and the clip coefficient the oracle's; a
+    checkpoint round-trips), and only empty tensors, with an absent grad and
+    a skipped call: the step counters advance exactly as the oracle's (a
+    present grad of no elements is a grad).  Such a list takes mode 1; modes
+    2 and 3 are refused for it with APEXW_EINVAL, as documented, and the
+    handle keeps its mode."""
+    _need_gpu()
+    groups = [W.Group(lr=1e-3, weight_decay=0.1)]
+    gr = L.make_groups(groups)
+    flag = torch.zeros(1, dtype=torch.float32, device=DEV)
+    say("case: empty list", fmt)
+    opt = GpuOpt([], [], [], [], 1, fmt)
+    for _ in range(2):
+        opt.step(groups, [], [], found_inf=flag)
+    norm = torch.full((1,), -1.0, dtype=torch.float64, device=DEV)
+    coef = torch.full((1,), -1.0, dtype=torch.float32, device=DEV)
+    L.apexw_clip_grad_norm(opt.h, L.make_ptrs([]), 0, 1.0, 0, norm.data_ptr(), coef.data_ptr(),
+                           opt.stream)
+    L.apexw_unscale_check(opt.h, L.make_ptrs([]), 0, flag.data_ptr(), opt.stream)
+    blob = L.apexw_export_state(opt.h, gr, 1, opt.stream)
+    L.apexw_import_state(opt.h, blob, 1, opt.stream)
+    torch.cuda.synchronize()
+    assert norm.item() == 0.0 and flag.item() == 0.0
+    assert coef.item() == oracle.OracleAdamW.clip_coef(0.0, 1.0)
+    opt.close()
+    for mode in (0, 1, 2, 3):
+        say("case: only empty tensors", fmt, "mode", mode)
+        sizes = [0, 0, 0]
+        pdt, gdt = [W.F32, W.BF16, W.F32], [W.F32, W.BF16, W.BF16]
+        opt = GpuOpt(sizes, pdt, gdt, [0, 0, 0], 1, fmt)
+        if mode in (2, 3):
+            with pytest.raises(L.ApexwError) as err:
+                L.apexw_set_launch_mode(opt.h, mode)
+            assert err.value.code == L.APEXW_EINVAL
+        else:
+            L.apexw_set_launch_mode(opt.h, mode)
+        assert L.apexw_get_launch_mode(opt.h) == 1
+        ref = oracle.OracleAdamW(sizes, pdt, gdt, [0, 0, 0], fmt)
+        params = [torch.empty(0, device=DEV, dtype=torch.float32 if d == W.F32 else torch.bfloat16)
+                  for d in pdt]
+        th_ref = [np.zeros(0, np.float32) if d == W.F32 else np.zeros(0, np.uint16) for d in pdt]
+        for k in range(5):
+            absent = {1} if k == 1 else set()
+            skip = k == 3
+            flag.fill_(1.0 if skip else 0.0)
+            g_dev = [None if i in absent else
+                     torch.empty(0, device=DEV, dtype=torch.float32 if d == W.F32 else torch.bfloat16)
+                     for i, d in enumerate(gdt)]
+            g_host = [None if i in absent else
+                      (np.zeros(0, np.float32) if d == W.F32 else np.zeros(0, np.uint16))
+                      for i, d in enumerate(gdt)]
+            opt.step(groups, params, g_dev, found_inf=flag)
+            ref.step(th_ref, g_host, groups, found_inf=skip)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(opt.steps()), ref.t[:3]), (bits(opt.steps()), ref.t[:3])
+        assert list(bits(opt.steps())) == [4, 3, 4]
+        opt.close()
