@@ -1265,3 +1265,73 @@ def test_empty_list_and_lists_of_empty_tensors(fmt):
         assert np.array_equal(bits(opt.steps()), ref.t[:3]), (bits(opt.steps()), ref.t[:3])
         assert list(bits(opt.steps())) == [4, 3, 4]
         opt.close()
+
+
+def test_refused_calls_write_nothing():
+    """Every refused call (wrong group count, out-of-range hyperparameters,
+    a NULL parameter pointer, out-of-range knobs) returns APEXW_EINVAL and
+    leaves parameters, state and counters bit for bit as they were; the
+    handle then steps on exactly as the oracle does."""
+    _need_gpu()
+    say("case: refused calls")
+    sizes = [1000, 257, 4096]
+    pdt, gdt = [W.F32, W.BF16, W.F32], [W.F32, W.F32, W.BF16]
+    group_of = [0, 0, 0]
+    good = [W.Group(lr=1e-3, weight_decay=0.1)]
+    to_dev = lambda h, d: (torch.from_numpy(h.view(np.int32) if d == W.F32 else h.view(np.int16))
+                           .to(DEV).view(torch.float32 if d == W.F32 else torch.bfloat16))
+    rng = np.random.default_rng(5150)
+    th_ref = [(rng.standard_normal(n) * 0.02).astype(np.float32) for n in sizes]
+    th_ref = [x if d == W.F32 else oracle.f32_to_bf16(x) for x, d in zip(th_ref, pdt)]
+    params = [to_dev(h, d) for h, d in zip(th_ref, pdt)]
+    opt = GpuOpt(sizes, pdt, gdt, group_of, 1, W.STATE_F32)
+    ref = oracle.OracleAdamW(sizes, pdt, gdt, group_of, W.STATE_F32)
+
+    def grads():
+        g32 = [(rng.standard_normal(n) * 1e-3).astype(np.float32) for n in sizes]
+        g_host = [g if d == W.F32 else oracle.f32_to_bf16(g) for g, d in zip(g32, gdt)]
+        return g_host, [to_dev(h, d) for h, d in zip(g_host, gdt)]
+
+    g_host, g_dev = grads()
+    opt.step(good, params, g_dev)
+    ref.step(th_ref, g_host, good)
+    torch.cuda.synchronize()
+    before = [p.clone() for p in params], opt.state.clone()
+    pa = L.make_ptrs([p.data_ptr() for p in params])
+    ga = L.make_ptrs([g.data_ptr() for g in g_dev])
+    bad_groups = [W.Group(lr=-1e-3), W.Group(lr=float("nan")), W.Group(lr=1e-3, eps=-1e-8),
+                  W.Group(lr=1e-3, eps=float("inf")), W.Group(lr=1e-3, weight_decay=-0.1),
+                  W.Group(lr=1e-3, beta1=1.0), W.Group(lr=1e-3, beta2=-0.5),
+                  W.Group(lr=1e-3, beta1=float("nan"))]
+    for g in bad_groups:
+        with pytest.raises(L.ApexwError) as e:
+            L.apexw_step(opt.h, L.make_groups([g]), 1, pa, ga, 0, opt.stream)
+        assert e.value.code == L.APEXW_EINVAL, g
+    with pytest.raises(L.ApexwError) as e:       # the handle was built for one group
+        L.apexw_step(opt.h, L.make_groups(good * 2), 2, pa, ga, 0, opt.stream)
+    assert e.value.code == L.APEXW_EINVAL
+    with pytest.raises(L.ApexwError) as e:       # NULL pointer for a non-empty tensor
+        L.apexw_step(opt.h, L.make_groups(good), 1,
+                     L.make_ptrs([params[0].data_ptr(), 0, params[2].data_ptr()]), ga, 0,
+                     opt.stream)
+    assert e.value.code == L.APEXW_EINVAL
+    for fn, arg in ((L.apexw_set_workgroups, -1), (L.apexw_set_occupancy, -2),
+                    (L.apexw_set_cache_policy, 3), (L.apexw_set_launch_mode, 4)):
+        with pytest.raises(L.ApexwError) as e:
+            fn(opt.h, arg)
+        assert e.value.code == L.APEXW_EINVAL, fn.__name__
+    torch.cuda.synchronize()
+    for p, q in zip(params, before[0]):
+        assert torch.equal(p.view(torch.int16 if p.dtype == torch.bfloat16 else torch.int32),
+                           q.view(torch.int16 if q.dtype == torch.bfloat16 else torch.int32))
+    assert torch.equal(opt.state, before[1])
+    g_host, g_dev = grads()
+    opt.step(good, params, g_dev)
+    ref.step(th_ref, g_host, good)
+    torch.cuda.synchronize()
+    for i in range(len(sizes)):
+        assert n_bit_mismatch(bits(params[i]), th_ref[i]) == 0, i
+        m, v = (bits(t) for t in opt.moments(i))
+        assert n_bit_mismatch(m, ref.m[i]) == 0 and n_bit_mismatch(v, ref.v[i]) == 0, i
+    assert np.array_equal(bits(opt.steps()), ref.t[:len(sizes)])
+    opt.close()
