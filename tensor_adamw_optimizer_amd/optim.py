@@ -128,6 +128,9 @@ class AdamW(torch.optim.Optimizer):
                                      stream)
         self._param_ptrs = list(map(torch.Tensor.data_ptr, self._params))
         self._params_arr = L.make_ptrs(self._param_ptrs)
+        # the groups' hyperparameters as the library reads them, refreshed in
+        # place every step (the group count is fixed with the tensor list)
+        self._groups_arr = (L.apexw_group * len(self.param_groups))()
         self._inv_buf: Optional[torch.Tensor] = None
         self._flat_bufs: List[torch.Tensor] = []
         self._flat_views: List[torch.Tensor] = []
@@ -310,10 +313,17 @@ class AdamW(torch.optim.Optimizer):
         _lib.ptr_table), or with None: the grad table of the previous call on
         this optimizer -- for grad buffers that persist across steps, with no
         per-tensor work on the host."""
-        groups = [_GroupView(g) for g in self.param_groups]
+        arr = self._groups_arr
+        for a, g in zip(arr, self.param_groups):    # a schedule may have changed them
+            a.lr = float(g["lr"])
+            b1, b2 = g["betas"]
+            a.beta1 = float(b1)
+            a.beta2 = float(b2)
+            a.eps = float(g["eps"])
+            a.weight_decay = float(g["weight_decay"])
         self._check_params()
         with self._on_device():
-            L.apexw_step_ex(self._h, L.make_groups(groups), len(groups), self._params_arr,
+            L.apexw_step_ex(self._h, arr, len(arr), self._params_arr,
                             grads_arr, self._dev_ptr(inv_scale, "inv_scale"),
                             self._dev_ptr(clip_coef, "clip_coef"),
                             self._dev_ptr(found_inf, "found_inf"), 0, self._stream())
