@@ -81,7 +81,9 @@ class AdamW(torch.optim.Optimizer):
     buffers in place whatever set_to_none says), so every parameter has a
     grad on every step -- a parameter that received none gets a zero grad,
     which decays it and counts a step, as torch does with set_to_none=False.
-    flat_grads_intact() tells whether the contract still holds.
+    flat_grads_intact() tells whether the contract still holds; step() looks
+    at two parameters' .grad each time and raises once it finds a broken one
+    (a whole list at the next step, a single one within a pass over the list).
     """
 
     # torch.amp.GradScaler: set grad_scale / found_inf on the optimizer and
@@ -152,6 +154,24 @@ class AdamW(torch.optim.Optimizer):
             self._flat_views.append(p.grad)
         self._flat_bufs = list(bufs.values())
         self._flat_arr = L.make_ptrs([g.data_ptr() or 16 for g in self._flat_views])
+        self._flat_probe = 0
+
+    def _flat_table(self):
+        """The flat buffers' pointer table, after a look at two parameters'
+        .grad (the first and one in rotation): a .grad removed or replaced
+        behind this optimizer's back (Module.zero_grad with set_to_none, an
+        assignment) would leave the step reading buffers that no longer
+        receive the grads.  A list-wide break is found on the next step, one
+        replaced .grad within one pass over the list."""
+        k = self._flat_probe
+        for i in (0, k):
+            if self._params[i].grad is not self._flat_views[i]:
+                raise RuntimeError(
+                    "flat_grads: the .grad of parameter %d is no longer the view this optimizer "
+                    "made; zero the grads with this optimizer's zero_grad() and never assign or "
+                    "delete .grad" % i)
+        self._flat_probe = k + 1 if k + 1 < len(self._params) else 0
+        return self._flat_arr
 
     def flat_grads_intact(self) -> bool:
         """True while every .grad is still the view flat_grads made."""
@@ -290,7 +310,7 @@ class AdamW(torch.optim.Optimizer):
             found_inf = scaler_inf.to(torch.float32).reshape(1)
         if inv_scale is None and scaler_scale is not None:
             inv_scale = self.inv_scale_of(scaler_scale)
-        self.step_pointers(self._flat_arr if self._flat_arr is not None else self._grads_arr(),
+        self.step_pointers(self._flat_table() if self._flat_arr is not None else self._grads_arr(),
                            found_inf, inv_scale, clip_coef)
         return loss
 

@@ -272,6 +272,34 @@ def test_flat_grads_match_the_default_path_and_backward_fills_them():
     opt_b.close()
 
 
+def test_flat_grads_broken_contract_is_an_error():
+    """With flat_grads, a .grad removed or replaced behind the optimizer's
+    back is an error at step(), not a step on buffers no longer written:
+    every .grad set to None (what Module.zero_grad does by default) is found
+    at the next step, one replaced .grad within a pass over the list; nothing
+    is queued by the refused steps."""
+    say("case: wrapper flat grads, broken contract")
+    ps = [torch.nn.Parameter(torch.randn(n, device=DEV) * 0.02) for n in (300, 7, 4096, 55, 1)]
+    opt = AdamW(ps, lr=1e-3, weight_decay=0.1, flat_grads=True)
+    before = [p.detach().clone() for p in ps]
+    saved = [p.grad for p in ps]
+    for p in ps:                                          # Module.zero_grad(set_to_none=True)
+        p.grad = None
+    with pytest.raises(RuntimeError, match="flat_grads"):
+        opt.step()
+    for p, g in zip(ps, saved):
+        p.grad = g
+    opt.step()                                            # intact again: steps
+    ps[3].grad = torch.zeros_like(ps[3])                  # one .grad replaced
+    with pytest.raises(RuntimeError, match="parameter 3"):
+        for _ in range(len(ps)):
+            opt.step()
+    torch.cuda.synchronize()
+    assert opt.read_steps()[3] < len(ps) + 1
+    assert all(not torch.equal(p, q) for p, q in zip(ps, before))
+    opt.close()
+
+
 def test_step_hooks_and_profiler_record_like_torch_optimizers():
     """The wrapper runs torch's optimizer step hooks itself: this optimizer's
     and the global pre- and post-hooks are called with (optimizer, args,
