@@ -109,6 +109,27 @@ def n_bit_mismatch(a: np.ndarray, b: np.ndarray) -> int:
                                 b.view(np.uint8).reshape(b.size, -1)) if a.size else 0)
 
 
+def _nan_mask(a: np.ndarray) -> np.ndarray:
+    if a.dtype == np.float32:
+        return np.isnan(a)
+    if a.dtype == np.uint16:                              # bf16 bit patterns
+        return (a & 0x7FFF) > 0x7F80
+    return np.zeros(a.shape, dtype=bool)
+
+
+def n_bit_mismatch_nan_equal(a: np.ndarray, b: np.ndarray) -> int:
+    """Elements whose bits differ, except where both are NaN: IEEE 754 leaves
+    the sign and payload of a NaN that an invalid operation makes (0/0,
+    inf - inf, 0 * inf) unspecified, and the host's x86 default NaN has the
+    sign set where gfx950's has it clear.  Every other value, and where the
+    NaNs are, must agree bit for bit."""
+    assert a.dtype == b.dtype and a.shape == b.shape, (a.dtype, b.dtype, a.shape, b.shape)
+    if not a.size:
+        return 0
+    diff = (a.view(np.uint8).reshape(a.size, -1) != b.view(np.uint8).reshape(b.size, -1)).any(1)
+    return int(np.count_nonzero(diff & ~(_nan_mask(a) & _nan_mask(b))))
+
+
 def assert_fp32_state_parity(name, gpu, ref, rtol=1e-5):
     """fp32 bar: elementwise relative error <= rtol (expected: bitwise)."""
     e = rel_err_elementwise(gpu, ref)
