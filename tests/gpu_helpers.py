@@ -130,6 +130,29 @@ def n_bit_mismatch_nan_equal(a: np.ndarray, b: np.ndarray) -> int:
     return int(np.count_nonzero(diff & ~(_nan_mask(a) & _nan_mask(b))))
 
 
+def norm_rel_bound(grads) -> float:
+    """Bound on |device norm - oracle norm| / oracle norm.  Both sum the same
+    N squares (u*u of fp32 values u, exact in fp64) in different orders; any
+    order of N - 1 additions of non-negative terms errs by at most
+    gamma(N-1) = (N-1)u/(1-(N-1)u) of the sum (u = 2^-53), so the two sums
+    differ by at most twice that, and the square roots (each rounded once)
+    by at most gamma(N-1) + 2u relative."""
+    n = sum(g.size for g in grads if g is not None)
+    u = 2.0 ** -53
+    return (n * u / (1.0 - n * u)) + 2.0 * u
+
+
+def stable_max_norm(ref, want: float, rel: float, max_norm: float) -> float:
+    """max_norm, nudged up until the fp32 clip coefficient is the same for
+    every norm within rel of want: a coefficient on an fp32 rounding edge
+    could then differ between two correct norms (a choice made from the
+    oracle's norm alone)."""
+    lo, hi = want * (1.0 - rel), want * (1.0 + rel)
+    while ref.clip_coef(lo, max_norm) != ref.clip_coef(hi, max_norm):
+        max_norm *= 1.0 + 2.0 ** -12
+    return max_norm
+
+
 def assert_fp32_state_parity(name, gpu, ref, rtol=1e-5):
     """fp32 bar: elementwise relative error <= rtol (expected: bitwise)."""
     e = rel_err_elementwise(gpu, ref)

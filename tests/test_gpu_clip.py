@@ -6,7 +6,7 @@ import torch
 
 import oracle
 import workloads as W
-from gpu_helpers import GpuOpt, bits, n_bit_mismatch, say
+from gpu_helpers import GpuOpt, bits, n_bit_mismatch, norm_rel_bound, say, stable_max_norm
 from tensor_adamw_optimizer_amd import _lib as L
 
 pytestmark = pytest.mark.gpu
@@ -37,14 +37,15 @@ def test_norm_and_coefficient_match_oracle(inv):
         g_cpu = [(torch.randn(s, generator=gen) * scale / inv).to(W.TORCH_DTYPE[d]) for s, d in zip(SIZES, GDT)]
         absent = [(i + trial) % 5 == 0 for i in range(n)]
         g_dev = [None if a else g.to(DEV) for g, a in zip(g_cpu, absent)]
-        max_norm = 1.0
+        g_np = [None if a else bits(g) for g, a in zip(g_cpu, absent)]
+        want = ref.grad_norm(g_np, inv)
+        rel = norm_rel_bound(g_np)
+        max_norm = stable_max_norm(ref, want, rel, 1.0)
         fi.zero_()
         L.apexw_clip_grad_norm(opt.h, _ptrs(g_dev), inv_t.data_ptr(), max_norm, fi.data_ptr(),
                                norm.data_ptr(), coef.data_ptr(), opt.stream)
         torch.cuda.synchronize()
-        g_np = [None if a else bits(g) for g, a in zip(g_cpu, absent)]
-        want = ref.grad_norm(g_np, inv)
-        assert abs(norm.item() - want) <= 1e-12 * max(want, 1e-300), (trial, norm.item(), want)
+        assert abs(norm.item() - want) <= rel * want, (trial, norm.item(), want)
         assert coef.item() == ref.clip_coef(want, max_norm), trial
         assert fi.item() == 0.0
     # a NaN anywhere: the check inside the norm pass reports it
@@ -85,14 +86,16 @@ def test_clipped_amp_loop_matches_oracle(fmt):
         if k == 5:
             g_cpu[2][3] = float("inf")
         g_dev = [g.to(DEV) for g in g_cpu]
+        g_np = [bits(g) for g in g_cpu]
+        found = ref.unscale_check(g_np, inv)
+        want = ref.grad_norm(g_np, inv)
+        mn = max_norm if found else stable_max_norm(ref, want, norm_rel_bound(g_np), max_norm)
         fi.zero_()
-        L.apexw_clip_grad_norm(opt.h, _ptrs(g_dev), inv_t.data_ptr(), max_norm, fi.data_ptr(), 0,
+        L.apexw_clip_grad_norm(opt.h, _ptrs(g_dev), inv_t.data_ptr(), mn, fi.data_ptr(), 0,
                                coef.data_ptr(), opt.stream)
         L.apexw_step_ex(opt.h, ga, 1, pa, _ptrs(g_dev), inv_scale_ptr=inv_t.data_ptr(),
                         clip_coef_ptr=coef.data_ptr(), found_inf_ptr=fi.data_ptr(), stream=opt.stream)
-        g_np = [bits(g) for g in g_cpu]
-        found = ref.unscale_check(g_np, inv)
-        c = ref.clip_coef(ref.grad_norm(g_np, inv), max_norm)
+        c = ref.clip_coef(want, mn)
         torch.cuda.synchronize()
         assert coef.item() == c or found, k
         coefs.append(c)

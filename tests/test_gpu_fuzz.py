@@ -1,4 +1,5 @@
-"""Randomised GPU parity: 48 seeded configurations, each a random tensor
+"""Randomised GPU parity: 48 seeded configurations (and 8 wider ones, see
+test_wide_random_configuration_against_oracle), each a random tensor
 list (sizes 0 .. 50,000, every (param, grad) dtype pair, 1-4 groups with
 random hyperparameters including edge values), a random state format,
 launch mode, cache policy and workgroup cap, and 4 calls with random absent
@@ -11,6 +12,7 @@ counters bit for bit against the oracle after the last call (two NaNs count
 as equal: a degenerate group -- lr = 0 with eps = 0 -- can make 0/0, and the
 sign of the NaN that makes is not fixed by IEEE 754)."""
 import ctypes
+import os
 
 import numpy as np
 import pytest
@@ -18,7 +20,8 @@ import torch
 
 import oracle
 import workloads as W
-from gpu_helpers import GpuOpt, bits, n_bit_mismatch, n_bit_mismatch_nan_equal, say
+from gpu_helpers import (GpuOpt, bits, n_bit_mismatch, n_bit_mismatch_nan_equal, norm_rel_bound,
+                         say, stable_max_norm)
 from tensor_adamw_optimizer_amd import _lib as L
 
 pytestmark = pytest.mark.gpu
@@ -55,18 +58,38 @@ def _random_group(rng):
     return W.Group(lr=lr, beta1=beta1, beta2=beta2, eps=eps, weight_decay=wd)
 
 
-@pytest.mark.parametrize("seed", range(48))
+# seeds per run: 48 and 8 by default; APEXW_FUZZ_SEEDS / APEXW_FUZZ_WIDE_SEEDS
+# ask for more (12,600 and 1,500 have been run)
+N_SEEDS = int(os.environ.get("APEXW_FUZZ_SEEDS", "48"))
+N_WIDE_SEEDS = int(os.environ.get("APEXW_FUZZ_WIDE_SEEDS", "8"))
+
+
+@pytest.mark.parametrize("seed", range(N_SEEDS))
 def test_random_configuration_against_oracle(seed):
-    rng = np.random.default_rng(1000 + seed)
-    n = int(rng.integers(1, 25))
-    sizes = [0 if rng.random() < 0.05 else int(np.exp(rng.uniform(0, np.log(50_000)))) for _ in range(n)]
+    _random_configuration(seed, wide=False)
+
+
+@pytest.mark.parametrize("seed", range(N_WIDE_SEEDS))
+def test_wide_random_configuration_against_oracle(seed):
+    """As above with up to 159 tensors (the tile table, not the few-tensor
+    lookup) of up to 300,000 elements, six calls, and the step counters of
+    some lists started far along (157, 1000, 2^20, 2^31 - 7), written into
+    the state buffer and followed by the documented resync call."""
+    _random_configuration(seed, wide=True)
+
+
+def _random_configuration(seed, wide):
+    rng = np.random.default_rng((50_000 if wide else 1000) + seed)
+    n = int(rng.integers(1, 160 if wide else 25))
+    top = 300_000 if wide else 50_000
+    sizes = [0 if rng.random() < 0.05 else int(np.exp(rng.uniform(0, np.log(top)))) for _ in range(n)]
     pdt = [str(rng.choice([W.F32, W.BF16])) for _ in range(n)]
     gdt = [str(rng.choice([W.F32, W.BF16])) for _ in range(n)]
     n_groups = int(rng.integers(1, 5))
     group_of = [int(rng.integers(0, n_groups)) for _ in range(n)]
     groups = [_random_group(rng) for _ in range(n_groups)]
     fmt = FORMATS[seed % 3]
-    say("case: fuzz", seed, "n", n, "fmt", fmt, "groups", n_groups)
+    say("case: fuzz", "wide" if wide else "", seed, "n", n, "fmt", fmt, "groups", n_groups)
     gen = torch.Generator().manual_seed(2000 + seed)
     p_cpu = [(torch.randn(s, generator=gen) * 0.02).to(W.TORCH_DTYPE[d]) for s, d in zip(sizes, pdt)]
     params = [_view(p, rng) for p in p_cpu]
@@ -83,8 +106,14 @@ def test_random_configuration_against_oracle(seed):
     fi = torch.zeros(1, device=DEV)
     inv_t = torch.zeros(1, device=DEV)
     clip_t = torch.zeros(1, device=DEV)
-    skip_call = int(rng.integers(0, 6))                 # 4 or 5: no skipped call
-    for k in range(4):
+    calls = 6 if wide else 4
+    skip_call = int(rng.integers(0, calls + 2))         # past the last call: no skipped call
+    t0 = int(rng.choice([0, 0, 157, 1000, 1 << 20, (1 << 31) - 7])) if wide else 0
+    if t0:
+        opt.steps().copy_(torch.full((n,), t0, dtype=torch.int32))
+        ref.t[:n] = t0
+        L.apexw_set_launch_mode(opt.h, L.apexw_get_launch_mode(opt.h))   # resync the chain
+    for k in range(calls):
         scaled = rng.random() < 0.5
         inv = float(np.float32(2.0 ** -int(rng.integers(0, 12)) if rng.random() < 0.7
                                else rng.uniform(0.1, 1.0))) if scaled else 1.0
@@ -103,14 +132,15 @@ def test_random_configuration_against_oracle(seed):
         g_np = [bits(g) if ok else None for g, ok in zip(g_cpu, present)]
         if clip is not None and rng.random() < 0.5:
             # the coefficient from the device norm pass instead (and its check)
-            max_norm = float(rng.uniform(1e-4, 1e-1))
+            want = ref.grad_norm(g_np, inv)
+            rel = norm_rel_bound(g_np)
+            max_norm = stable_max_norm(ref, want, rel, float(rng.uniform(1e-4, 1e-1)))
             norm_t = torch.zeros(1, dtype=torch.float64, device=DEV)
             chk = torch.zeros(1, device=DEV)
             L.apexw_clip_grad_norm(opt.h, ga, inv_t.data_ptr(), max_norm, chk.data_ptr(),
                                    norm_t.data_ptr(), clip_t.data_ptr(), opt.stream)
             torch.cuda.synchronize()
-            want = ref.grad_norm(g_np, inv)
-            assert abs(norm_t.item() - want) <= 1e-12 * max(want, 1e-300), (seed, k)
+            assert abs(norm_t.item() - want) <= rel * want, (seed, k)
             clip = ref.clip_coef(want, max_norm)
             assert clip_t.item() == clip and chk.item() == 0.0, (seed, k)
         table = _device_groups(groups) if dev_groups else None
