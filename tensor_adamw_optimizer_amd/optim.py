@@ -70,7 +70,9 @@ class AdamW(torch.optim.Optimizer):
 
     state: "f32" (or "fp32"), "bf16" (round-to-nearest-even moments) or "q8" (int8 m /
     uint8 v codes with one fp32 absmax scale per 256-element block).
-    grad_dtype: dtype the grads will have (default: each parameter's dtype).
+    grad_dtype: dtype the grads will have (default: each parameter's dtype);
+    a parameter of another dtype gets its grad_dtype attribute set to it, the
+    torch rule for such grads (backward then produces them in that dtype).
     flat_grads: give every parameter a .grad that is a view into one flat
     buffer per grad dtype (each view 64-byte aligned), made here, zero-filled.
     Autograd then accumulates into these views in place, and step() hands the
@@ -115,6 +117,12 @@ class AdamW(torch.optim.Optimizer):
         self._numel = [p.numel() for p in self._params]
         self._pdt = [_DT[p.dtype] for p in self._params]
         self._gdtype = [grad_dtype or p.dtype for p in self._params]
+        # torch accepts a .grad of another dtype than its parameter only
+        # where the parameter's grad_dtype says so; autograd then produces
+        # grads of that dtype
+        for p, d in zip(self._params, self._gdtype):
+            if d != p.dtype and hasattr(p, "grad_dtype"):
+                p.grad_dtype = d
         self._gdt = [_DT[d] for d in self._gdtype]
         fmt = _FMT[state]
         self.state_bytes = L.apexw_state_bytes(self._numel, fmt)
