@@ -314,7 +314,9 @@ class AdamW(torch.optim.Optimizer):
                 loss = closure()
         scaler_scale = getattr(self, "grad_scale", None)
         scaler_inf = getattr(self, "found_inf", None)
-        if found_inf is None and scaler_inf is not None:
+        if found_inf is None and torch.is_tensor(scaler_inf):
+            # (a step in which no parameter has a grad gets the plain number
+            # 0 from the scaler: nothing to check, nothing to skip)
             found_inf = scaler_inf.to(torch.float32).reshape(1)
         if inv_scale is None and scaler_scale is not None:
             inv_scale = self.inv_scale_of(scaler_scale)

@@ -371,3 +371,19 @@ def test_step_hooks_and_profiler_record_like_torch_optimizers():
         assert n_bit_mismatch(bits(ps[i].detach()), th_ref[i]) == 0, i
     assert opt.read_steps() == [4, 4]
     opt.close()
+
+
+def test_scaler_attributes_on_a_step_without_grads():
+    """GradScaler.step hands the optimizer the plain number 0 as found_inf
+    when no parameter has a grad; such a step does nothing and is no error."""
+    say("case: wrapper, scaler attributes without grads")
+    ps = [torch.nn.Parameter(torch.randn(300, device=DEV)), torch.nn.Parameter(torch.randn(7, device=DEV))]
+    before = [p.detach().clone() for p in ps]
+    opt = AdamW(ps, lr=1e-2, weight_decay=0.1)
+    opt.grad_scale = torch.full((1,), 1024.0, device=DEV)
+    opt.found_inf = 0
+    opt.step()
+    torch.cuda.synchronize()
+    assert opt.read_steps() == [0, 0]
+    assert all(torch.equal(p, q) for p, q in zip(ps, before))
+    opt.close()

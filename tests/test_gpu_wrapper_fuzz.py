@@ -1,9 +1,11 @@
 """Randomised runs of the torch wrapper against the oracle: random parameter
 shapes and dtypes over one to three parameter groups, a random state format,
 grad dtype and grad handling (per-parameter .grad, some absent, or flat
-grads), learning rates changed between steps as a schedule would, and on
-some runs a checkpoint through state_dict / torch.save / load_state_dict
-into a fresh optimizer halfway.  Parameters, moments and step counters bit
+grads), learning rates changed between steps as a schedule would, on
+some runs torch.amp.GradScaler driving the steps (a scale that is a power
+of two or not, an overflowing grad now and then) or the global grad norm
+clipped through clip_grad_norm, and on some runs a checkpoint through
+state_dict / torch.save / load_state_dict into a fresh optimizer halfway.  Parameters, moments and step counters bit
 for bit against the oracle after every step (NaNs compared as NaNs).
 APEXW_WRAPPER_FUZZ_SEEDS asks for more runs than the default 12."""
 import io
@@ -15,7 +17,7 @@ import torch
 
 import oracle
 import workloads as W
-from gpu_helpers import bits, n_bit_mismatch_nan_equal, say
+from gpu_helpers import bits, n_bit_mismatch_nan_equal, norm_rel_bound, say, stable_max_norm
 from tensor_adamw_optimizer_amd import AdamW
 
 pytestmark = pytest.mark.gpu
@@ -46,6 +48,9 @@ def test_random_wrapper_run_against_oracle(seed):
     state = str(rng.choice(["f32", "bf16", "q8"]))
     flat = bool(rng.random() < 0.4)
     grad_dtype = [None, torch.float32, torch.bfloat16][int(rng.integers(0, 3))]
+    drive = str(rng.choice(["plain", "amp", "clip"], p=[0.4, 0.3, 0.3]))
+    if drive == "amp":              # GradScaler's own overflow check takes no bf16 grads
+        grad_dtype = torch.float32
     n_groups = int(rng.integers(1, min(3, n) + 1))
     member = [i % n_groups for i in range(n)]
     rng.shuffle(member)
@@ -70,6 +75,9 @@ def test_random_wrapper_run_against_oracle(seed):
                              [NAME[d] for d in gdt], [member[i] for i in order], state)
     th_ref = [bits(p_cpu[i].reshape(-1)) for i in order]
     checkpoint_at = int(rng.integers(1, 5)) if rng.random() < 0.5 else -1
+    scaler = (torch.amp.GradScaler("cuda", init_scale=float(rng.choice([2.0 ** 10, 3000.0])),
+                                   growth_interval=1000) if drive == "amp" else None)
+    say("  drive", drive, "checkpoint at", checkpoint_at)
     for k in range(6):
         if k == checkpoint_at:
             buf = io.BytesIO()
@@ -81,20 +89,46 @@ def test_random_wrapper_run_against_oracle(seed):
         for g in opt.param_groups:                    # a schedule's change between steps
             if rng.random() < 0.3:
                 g["lr"] = g["lr"] * 0.5
+        scale = 1.0
+        if scaler is not None:
+            scaler.scale(torch.ones((), device=DEV))      # as a training loop scales its loss
+            scale = float(scaler.get_scale())
+        overflow = scaler is not None and rng.random() < 0.2
         g_np = []
         for j, i in enumerate(order):
-            present = flat or rng.random() < 0.85
-            g_cpu = (torch.randn(shapes[i], generator=gen) * 1e-3).to(gdt[j])
+            # (GradScaler.update needs a grad somewhere: the first is present then)
+            present = flat or rng.random() < 0.85 or (scaler is not None and j == 0)
+            g_cpu = (torch.randn(shapes[i], generator=gen) * 1e-3 * scale).to(gdt[j])
+            if overflow and j == 0 and present:
+                g_cpu.view(-1)[0] = float("inf")
             if flat:
                 params[i].grad.copy_(g_cpu.to(DEV))
             else:                                     # the optimizer set grad_dtype if it differs
                 params[i].grad = g_cpu.to(DEV) if present else None
             g_np.append(bits(g_cpu.reshape(-1)) if present else None)
+        overflow = overflow and g_np[0] is not None
         grp = [W.Group(lr=float(g["lr"]), beta1=float(g["betas"][0]), beta2=float(g["betas"][1]),
                        eps=float(g["eps"]), weight_decay=float(g["weight_decay"]))
                for g in opt.param_groups]
-        opt.step()
-        ref.step(th_ref, g_np, grp)
+        if scaler is not None:
+            scaler.step(opt)
+            scaler.update()
+            inv = float(np.float32(1.0 / np.float64(np.float32(scale))))   # fp64 reciprocal, once rounded
+            ref.step(th_ref, g_np, grp, found_inf=overflow, inv_scale=inv)
+            assert scaler.get_scale() == (scale / 2 if overflow else scale), (seed, k)
+        elif drive == "clip" and rng.random() < 0.6:
+            want = ref.grad_norm(g_np, 1.0)
+            rel = norm_rel_bound(g_np)
+            mn = stable_max_norm(ref, want, rel, float(10 ** rng.uniform(-3, 0)))
+            norm_t, coef_t = opt.clip_grad_norm(mn)
+            opt.step(clip_coef=coef_t)
+            c = ref.clip_coef(want, mn)
+            ref.step(th_ref, g_np, grp, clip_coef=c)
+            torch.cuda.synchronize()
+            assert abs(norm_t.item() - want) <= rel * want and coef_t.item() == c, (seed, k)
+        else:
+            opt.step()
+            ref.step(th_ref, g_np, grp)
         torch.cuda.synchronize()
         for j, i in enumerate(order):
             assert n_bit_mismatch_nan_equal(bits(params[i].detach().reshape(-1)), th_ref[j]) == 0, \
