@@ -163,3 +163,89 @@ def _random_configuration(seed, wide):
             assert n_bit_mismatch(bits(ms), ref.m_scale[i]) == 0, (seed, i)
             assert n_bit_mismatch(bits(vs), ref.v_scale[i]) == 0, (seed, i)
     opt.close()
+
+
+N_SESSION_SEEDS = int(os.environ.get("APEXW_FUZZ_SESSION_SEEDS", "8"))
+
+
+@pytest.mark.parametrize("seed", range(N_SESSION_SEEDS))
+def test_random_session_against_oracle(seed):
+    """One tensor list stepped ten times while the knobs change between
+    calls: the launch mode (whichever the list admits), the workgroup cap,
+    the residency cap, the cache policy, a checkpoint exported and imported
+    into the same handle or into a fresh one that takes over, a step with
+    the hyperparameters in device memory, and betas changed for a call --
+    every change the carried chain has to survive or restart after.  Theta,
+    moments, scales and counters bit for bit against the oracle after every
+    call (NaNs compared as NaNs)."""
+    rng = np.random.default_rng(90_000 + seed)
+    n = int(rng.integers(1, 40))
+    sizes = [0 if rng.random() < 0.05 else int(np.exp(rng.uniform(0, np.log(60_000)))) for _ in range(n)]
+    pdt = [str(rng.choice([W.F32, W.BF16])) for _ in range(n)]
+    gdt = [str(rng.choice([W.F32, W.BF16])) for _ in range(n)]
+    n_groups = int(rng.integers(1, 4))
+    group_of = [int(rng.integers(0, n_groups)) for _ in range(n)]
+    groups = [_random_group(rng) for _ in range(n_groups)]
+    fmt = FORMATS[seed % 3]
+    say("case: fuzz session", seed, "n", n, "fmt", fmt, "groups", n_groups)
+    gen = torch.Generator().manual_seed(91_000 + seed)
+    p_cpu = [(torch.randn(s, generator=gen) * 0.02).to(W.TORCH_DTYPE[d]) for s, d in zip(sizes, pdt)]
+    params = [p.to(DEV) for p in p_cpu]
+    th_ref = [bits(p) for p in p_cpu]
+    opt = GpuOpt(sizes, pdt, gdt, group_of, n_groups, fmt)
+    ref = oracle.OracleAdamW(sizes, pdt, gdt, group_of, fmt)
+    fi = torch.zeros(1, device=DEV)
+    pa = L.make_ptrs([p.data_ptr() for p in params])
+    for k in range(10):
+        action = str(rng.choice(["mode", "cap", "occupancy", "policy", "export_same",
+                                 "export_fresh", "device", "betas", "none"]))
+        step_groups = groups
+        if action == "mode":
+            try:
+                L.apexw_set_launch_mode(opt.h, int(rng.choice([0, 1, 2, 3])))
+            except L.ApexwError:
+                pass                                  # a mode the list does not admit
+        elif action == "cap":
+            L.apexw_set_workgroups(opt.h, int(rng.choice([0, 1, 5, 64, 1000])))
+        elif action == "occupancy":
+            L.apexw_set_occupancy(opt.h, int(rng.choice([0, 1, 4, 14, 40])))
+        elif action == "policy":
+            L.apexw_set_cache_policy(opt.h, int(rng.choice([0, 1, 2])))
+        elif action in ("export_same", "export_fresh"):
+            blob = L.apexw_export_state(opt.h, L.make_groups(groups), n_groups, opt.stream)
+            if action == "export_fresh":              # a new handle takes over from the blob
+                new = GpuOpt(sizes, pdt, gdt, group_of, n_groups, fmt)
+                opt.close()
+                opt = new
+            L.apexw_import_state(opt.h, blob, n_groups, opt.stream)
+        elif action == "betas":                       # this call only
+            step_groups = [W.Group(lr=g.lr, beta1=float(rng.choice([0.0, 0.8, 0.9])),
+                                   beta2=float(rng.choice([0.9, 0.999])), eps=g.eps,
+                                   weight_decay=g.weight_decay) for g in groups]
+        g_cpu = [(torch.randn(s, generator=gen) * 1e-3).to(W.TORCH_DTYPE[d]) for s, d in zip(sizes, gdt)]
+        present = [rng.random() < 0.85 for _ in range(n)]
+        skip = rng.random() < 0.1
+        fi.fill_(1.0 if skip else 0.0)
+        g_dev = [g.to(DEV) if ok else None for g, ok in zip(g_cpu, present)]
+        ga = L.make_ptrs([0 if g is None else (g.data_ptr() or 16) for g in g_dev])
+        g_np = [bits(g) if ok else None for g, ok in zip(g_cpu, present)]
+        if action == "device":
+            table = _device_groups(step_groups)
+            L.apexw_step_ex(opt.h, None, n_groups, pa, ga, found_inf_ptr=fi.data_ptr(),
+                            groups_dev_ptr=table.data_ptr(), stream=opt.stream)
+        else:
+            L.apexw_step(opt.h, L.make_groups(step_groups), n_groups, pa, ga, fi.data_ptr(),
+                         opt.stream)
+        ref.step(th_ref, g_np, step_groups, found_inf=skip)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(opt.steps()), ref.t[:n]), (seed, k, action)
+        for i in range(n):
+            assert n_bit_mismatch_nan_equal(bits(params[i]), th_ref[i]) == 0, (seed, k, action, i)
+            m, v = opt.moments(i)
+            assert n_bit_mismatch_nan_equal(bits(m), ref.m[i]) == 0, (seed, k, action, i)
+            assert n_bit_mismatch_nan_equal(bits(v), ref.v[i]) == 0, (seed, k, action, i)
+            if fmt == W.STATE_Q8:
+                ms, vs = opt.scales(i)
+                assert n_bit_mismatch(bits(ms), ref.m_scale[i]) == 0, (seed, k, action, i)
+                assert n_bit_mismatch(bits(vs), ref.v_scale[i]) == 0, (seed, k, action, i)
+    opt.close()
