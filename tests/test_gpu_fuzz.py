@@ -249,3 +249,86 @@ def test_random_session_against_oracle(seed):
                 assert n_bit_mismatch(bits(ms), ref.m_scale[i]) == 0, (seed, k, action, i)
                 assert n_bit_mismatch(bits(vs), ref.v_scale[i]) == 0, (seed, k, action, i)
     opt.close()
+
+
+N_GRAPH_SEEDS = int(os.environ.get("APEXW_FUZZ_GRAPH_SEEDS", "6"))
+
+
+@pytest.mark.parametrize("seed", range(N_GRAPH_SEEDS))
+def test_random_graph_session_against_oracle(seed):
+    """Twelve calls on persistent buffers in which one step is captured into
+    a graph at a random point (with the hyperparameters of that moment, or
+    read from a device table that later calls rewrite), and the calls after
+    it are eager steps or replays in random order, with learning-rate
+    changes, skipped calls, and at most one resync (apexw_set_launch_mode,
+    after which no replay follows).  Every call against the oracle."""
+    rng = np.random.default_rng(95_000 + seed)
+    n = int(rng.integers(1, 12))
+    sizes = [int(np.exp(rng.uniform(0, np.log(20_000)))) for _ in range(n)]
+    pdt = [str(rng.choice([W.F32, W.BF16])) for _ in range(n)]
+    gdt = [str(rng.choice([W.F32, W.BF16])) for _ in range(n)]
+    n_groups = int(rng.integers(1, 3))
+    group_of = [int(rng.integers(0, n_groups)) for _ in range(n)]
+    groups = [_random_group(rng) for _ in range(n_groups)]
+    fmt = FORMATS[seed % 3]
+    on_device = bool(rng.random() < 0.5)
+    capture_at = int(rng.integers(1, 6))
+    say("case: fuzz graph session", seed, "n", n, "fmt", fmt, "device groups", on_device,
+        "capture after call", capture_at)
+    gen = torch.Generator().manual_seed(96_000 + seed)
+    p_cpu = [(torch.randn(s, generator=gen) * 0.02).to(W.TORCH_DTYPE[d]) for s, d in zip(sizes, pdt)]
+    params = [p.to(DEV) for p in p_cpu]
+    grads = [torch.zeros(s, dtype=W.TORCH_DTYPE[d], device=DEV) for s, d in zip(sizes, gdt)]
+    th_ref = [bits(p) for p in p_cpu]
+    opt = GpuOpt(sizes, pdt, gdt, group_of, n_groups, fmt)
+    ref = oracle.OracleAdamW(sizes, pdt, gdt, group_of, fmt)
+    fi = torch.zeros(1, device=DEV)
+    pa = L.make_ptrs([p.data_ptr() for p in params])
+    ga = L.make_ptrs([g.data_ptr() for g in grads])
+    table = _device_groups(groups)
+    graph, captured_groups, replays_allowed = None, None, True
+    for k in range(12):
+        if rng.random() < 0.3:                        # a schedule's change
+            groups = [W.Group(lr=g.lr * 0.5, beta1=g.beta1, beta2=g.beta2, eps=g.eps,
+                              weight_decay=g.weight_decay) for g in groups]
+            table.copy_(_device_groups(groups))
+        g_cpu = [(torch.randn(s, generator=gen) * 1e-3).to(W.TORCH_DTYPE[d]) for s, d in zip(sizes, gdt)]
+        for g, x in zip(grads, g_cpu):
+            g.copy_(x.to(DEV))
+        skip = bool(rng.random() < 0.1)
+        fi.fill_(1.0 if skip else 0.0)
+        torch.cuda.synchronize()
+        replay = graph is not None and replays_allowed and rng.random() < 0.5
+        if replay:
+            graph.replay()
+            used = groups if on_device else captured_groups
+        else:
+            L.apexw_step(opt.h, L.make_groups(groups), n_groups, pa, ga, fi.data_ptr(), opt.stream)
+            used = groups
+        ref.step(th_ref, [bits(x) for x in g_cpu], used, found_inf=skip)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(opt.steps()), ref.t[:n]), (seed, k, replay)
+        for i in range(n):
+            assert n_bit_mismatch_nan_equal(bits(params[i]), th_ref[i]) == 0, (seed, k, replay, i)
+            m, v = opt.moments(i)
+            assert n_bit_mismatch_nan_equal(bits(m), ref.m[i]) == 0, (seed, k, replay, i)
+            assert n_bit_mismatch_nan_equal(bits(v), ref.v[i]) == 0, (seed, k, replay, i)
+        if k + 1 == capture_at:                       # capture one step (not run by capturing)
+            graph = torch.cuda.CUDAGraph()
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                with torch.cuda.graph(graph, stream=s):
+                    st = torch.cuda.current_stream().cuda_stream
+                    if on_device:
+                        L.apexw_step_device(opt.h, table.data_ptr(), n_groups, pa, ga, 0,
+                                            fi.data_ptr(), st)
+                    else:
+                        L.apexw_step(opt.h, L.make_groups(groups), n_groups, pa, ga,
+                                     fi.data_ptr(), st)
+            torch.cuda.synchronize()
+            captured_groups = groups
+        elif graph is not None and replays_allowed and rng.random() < 0.15:
+            L.apexw_set_launch_mode(opt.h, 0)         # no replay follows from here on
+            replays_allowed = False
+    opt.close()
