@@ -7,7 +7,9 @@ grads, a random skipped call and, on some calls, an inv_scale and a clip
 coefficient (from the device norm pass on some calls); parameters and
 grads sometimes views at odd element offsets
 into larger buffers (no vector alignment), and the hyperparameters
-sometimes read from device memory -- theta, moments, 8-bit scales and
+sometimes read from device memory, and on some calls the unscale-and-check
+pass deciding the skip (an inf or a NaN planted now and then) -- theta,
+moments, 8-bit scales and
 counters bit for bit against the oracle after the last call (two NaNs count
 as equal: a degenerate group -- lr = 0 with eps = 0 -- can make 0/0, and the
 sign of the NaN that makes is not fixed by IEEE 754)."""
@@ -113,6 +115,7 @@ def _random_configuration(seed, wide):
         opt.steps().copy_(torch.full((n,), t0, dtype=torch.int32))
         ref.t[:n] = t0
         L.apexw_set_launch_mode(opt.h, L.apexw_get_launch_mode(opt.h))   # resync the chain
+    chk_rng = np.random.default_rng((770_000 if wide else 760_000) + seed)
     for k in range(calls):
         scaled = rng.random() < 0.5
         inv = float(np.float32(2.0 ** -int(rng.integers(0, 12)) if rng.random() < 0.7
@@ -130,6 +133,24 @@ def _random_configuration(seed, wide):
             if clip is not None:
                 clip_t.fill_(clip)
         g_np = [bits(g) if ok else None for g, ok in zip(g_cpu, present)]
+        if clip is None and chk_rng.random() < 0.25:
+            # the mixed-precision check decides the skip: sometimes an inf or
+            # a NaN in one present grad (its own generator, so the other
+            # draws are those of the runs without it)
+            live = [i for i in range(n) if present[i] and sizes[i] > 0]
+            if live and chk_rng.random() < 0.5:
+                i = live[int(chk_rng.integers(0, len(live)))]
+                e = int(chk_rng.integers(0, sizes[i]))
+                bad = float("inf") if chk_rng.random() < 0.5 else float("nan")
+                g_dev[i].view(-1)[e] = bad
+                g_np[i][e] = (np.float32(bad) if gdt[i] == W.F32
+                              else np.uint16(0x7F80 if bad == float("inf") else 0x7FC0))
+            fi.zero_()
+            L.apexw_unscale_check(opt.h, ga, inv_t.data_ptr() if scaled else 0, fi.data_ptr(),
+                                  opt.stream)
+            skip = ref.unscale_check(g_np, inv)
+            torch.cuda.synchronize()
+            assert fi.item() == (1.0 if skip else 0.0), (seed, k)
         if clip is not None and rng.random() < 0.5:
             # the coefficient from the device norm pass instead (and its check)
             want = ref.grad_norm(g_np, inv)
