@@ -4,7 +4,8 @@ list (sizes 0 .. 50,000, every (param, grad) dtype pair, 1-4 groups with
 random hyperparameters including edge values), a random state format,
 launch mode, cache policy and workgroup cap, and 4 calls with random absent
 grads, a random skipped call and, on some calls, an inv_scale and a clip
-coefficient (from the device norm pass on some calls); parameters and
+coefficient (from the device norm pass on some calls, through either
+entry point); parameters and
 grads sometimes views at odd element offsets
 into larger buffers (no vector alignment), and the hyperparameters
 sometimes read from device memory, and on some calls the unscale-and-check
@@ -158,8 +159,11 @@ def _random_configuration(seed, wide):
             max_norm = stable_max_norm(ref, want, rel, float(rng.uniform(1e-4, 1e-1)))
             norm_t = torch.zeros(1, dtype=torch.float64, device=DEV)
             chk = torch.zeros(1, device=DEV)
-            L.apexw_clip_grad_norm(opt.h, ga, inv_t.data_ptr(), max_norm, chk.data_ptr(),
-                                   norm_t.data_ptr(), clip_t.data_ptr(), opt.stream)
+            # (the entry point that allocates nothing on some calls: the same bits)
+            norm_fn = (L.apexw_clip_grad_norm_noalloc if chk_rng.random() < 0.5
+                       else L.apexw_clip_grad_norm)
+            norm_fn(opt.h, ga, inv_t.data_ptr(), max_norm, chk.data_ptr(), norm_t.data_ptr(),
+                    clip_t.data_ptr(), opt.stream)
             torch.cuda.synchronize()
             assert abs(norm_t.item() - want) <= rel * want, (seed, k)
             clip = ref.clip_coef(want, max_norm)
