@@ -1335,3 +1335,67 @@ def test_refused_calls_write_nothing():
         assert n_bit_mismatch(m, ref.m[i]) == 0 and n_bit_mismatch(v, ref.v[i]) == 0, i
     assert np.array_equal(bits(opt.steps()), ref.t[:len(sizes)])
     opt.close()
+
+
+def test_two_threads_two_handles_on_two_streams():
+    """The C ABI is thread-safe on distinct handles: two host threads step
+    their own handles on their own streams at the same time (ctypes releases
+    the interpreter lock for every call), twenty steps each, one of them
+    with a failing call in between (its error stays on its thread); both
+    end bit for bit at the oracle's results."""
+    _need_gpu()
+    import threading
+    say("case: two threads, two handles")
+    specs = [([5000, 300, 4096], [W.F32, W.BF16, W.F32], [W.F32, W.F32, W.BF16], W.STATE_F32),
+             ([70000, 1], [W.BF16, W.BF16], [W.BF16, W.F32], W.STATE_Q8)]
+    groups = [W.Group(lr=1e-3, weight_decay=0.1)]
+    to_dev = lambda h, d: (torch.from_numpy(h.view(np.int32) if d == W.F32 else h.view(np.int16))
+                           .to(DEV).view(torch.float32 if d == W.F32 else torch.bfloat16))
+    jobs = []
+    for t, (sizes, pdt, gdt, fmt) in enumerate(specs):
+        rng = np.random.default_rng(600 + t)
+        th0 = [(rng.standard_normal(n) * 0.02).astype(np.float32) for n in sizes]
+        th0 = [x if d == W.F32 else oracle.f32_to_bf16(x) for x, d in zip(th0, pdt)]
+        gs = [[(rng.standard_normal(n) * 1e-3).astype(np.float32) for n in sizes] for _ in range(20)]
+        gs = [[x if d == W.F32 else oracle.f32_to_bf16(x) for x, d in zip(step, gdt)] for step in gs]
+        params = [to_dev(h, d) for h, d in zip(th0, pdt)]
+        grads = [[to_dev(h, d) for h, d in zip(step, gdt)] for step in gs]
+        opt = GpuOpt(sizes, pdt, gdt, [0] * len(sizes), 1, fmt)
+        jobs.append(dict(sizes=sizes, pdt=pdt, gdt=gdt, fmt=fmt, th0=th0, gs=gs, params=params,
+                         grads=grads, opt=opt, stream=torch.cuda.Stream(), errors=[]))
+    torch.cuda.synchronize()
+    gr = L.make_groups(groups)
+
+    def run(job, t):
+        try:
+            pa = L.make_ptrs([p.data_ptr() for p in job["params"]])
+            s = job["stream"].cuda_stream
+            for k in range(20):
+                if t == 1 and k == 10:
+                    try:                              # wrong group count: refused, this thread's error
+                        L.apexw_step(job["opt"].h, gr, 2, pa, pa, 0, s)
+                    except L.ApexwError:
+                        job["errors"].append(L.apexw_last_error())
+                ga = L.make_ptrs([g.data_ptr() for g in job["grads"][k]])
+                L.apexw_step(job["opt"].h, gr, 1, pa, ga, 0, s)
+        except Exception as e:                        # reported by the main thread
+            job["errors"].append(repr(e))
+
+    threads = [threading.Thread(target=run, args=(j, t)) for t, j in enumerate(jobs)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert jobs[0]["errors"] == [] and len(jobs[1]["errors"]) == 1, [j["errors"] for j in jobs]
+    assert "group" in jobs[1]["errors"][0]
+    for job in jobs:
+        ref = oracle.OracleAdamW(job["sizes"], job["pdt"], job["gdt"], [0] * len(job["sizes"]),
+                                 job["fmt"])
+        th = [x.copy() for x in job["th0"]]
+        for k in range(20):
+            ref.step(th, job["gs"][k], groups)
+        for i in range(len(job["sizes"])):
+            assert n_bit_mismatch(bits(job["params"][i]), th[i]) == 0, (job["fmt"], i)
+        assert np.array_equal(bits(job["opt"].steps()), ref.t[:len(job["sizes"])])
+        job["opt"].close()
