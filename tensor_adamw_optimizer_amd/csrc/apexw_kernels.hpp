@@ -1095,18 +1095,6 @@ __global__ __launch_bounds__(kThreads) void adamw_step_kernel(KernelArgs a) {
     }
 }
 
-// The carried step (launch mode 3): the whole step in one launch per dtype
-// pair at any list size, with no prepare launch and no arrival counters.
-// Every workgroup takes its tensor's bias corrections from bias_cur (formed
-// for the counter as it stands, t + 1, by the previous step or by
-// carry_init_kernel), its group's scalars from the kernel arguments and the
-// flag and scale factors from device memory.  The first tile of each tensor
-// alone advances the counter (only with a grad and without found_inf) and
-// writes the corrections for the following step, at t + 2 or unchanged, into
-// bias_next; no other workgroup uses the counter (every workgroup loads it
-// with the metadata, only the first tile's value counts), so no ordering
-// between workgroups is needed.  Results are bitwise those of the other
-// modes: the same fp64 and fp32 operations form the same scalars.
 // The tensor of launch-relative tile k.  FEW (the loop-free kernels over a
 // launch of at most kFewTensors tensors, none empty, with cached accesses --
 // a small list, whose step is the latency of this chain): the last of the
@@ -1141,6 +1129,19 @@ __device__ __forceinline__ int32_t tile_owner(const KernelArgs &a, const APEXW_C
     }
 }
 
+// The carried step (launch mode 3): the whole step in one launch per dtype
+// pair at any list size, with no prepare launch and no arrival counters.
+// Every workgroup takes its tensor's bias corrections from bias_cur (formed
+// for the counter as it stands, t + 1, by the previous step or by
+// carry_init_kernel), its group's scalars from the kernel arguments and the
+// flag and scale factors from device memory.  The first tile of each tensor
+// alone advances the counter (only with a grad and without found_inf) and
+// writes the corrections for the following step, at t + 2 or unchanged, into
+// bias_next; no other workgroup uses the counter (every workgroup loads it
+// with the metadata, only the first tile's value counts), so no ordering
+// between workgroups is needed.  Results are bitwise those of the other
+// modes: the same fp64 and fp32 operations form the same scalars.
+//
 // ONE: the grid has a workgroup per tile, so each takes exactly one tile and
 // the body is straight-line code (no loop, so nothing is hoisted into a
 // preheader that every wave would run for its one tile).
