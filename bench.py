@@ -265,7 +265,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="few_large",
-                    choices=["few_large", "many_small", "bf16_state", "lora_q8", "tiny"])
+                    choices=["few_large", "many_small", "bf16_state", "lora_q8", "tiny",
+                             "few_large_shard8"])
     ap.add_argument("--workgroups", type=int, default=0, help="cap on workgroups per launch")
     ap.add_argument("--occupancy", type=int, default=0,
                     help="update workgroups per CU (0: the format's default)")

@@ -743,6 +743,18 @@ def test_few_large_full_size_sampled():
     opt.close()
 
 
+def test_few_large_zero1_share_full_size_sampled():
+    """One of 8 ranks' ZeRO-1 share of that list (a 1024-row slice of every
+    tensor, 67.1M params), the launch configuration the benchmark times for
+    it; 60k+ elements per tensor, including the first and last tiles, against
+    the oracle."""
+    _need_gpu()
+    w = W.few_large_shard(ranks=8)
+    say("case: few_large_shard8", w.describe())
+    opt, _, _ = _few_large_check(w)
+    opt.close()
+
+
 def test_bf16_state_full_size_sampled_and_against_fp32_state():
     """The same list with bf16 moments: bitwise against the oracle's bf16
     mode, and within 1e-2 (normwise) of the fp32-state oracle on m and v."""

@@ -160,6 +160,16 @@ def few_large(seed: int = 0, n_tensors: int = 8, dim: int = 8192,
     )
 
 
+def few_large_shard(seed: int = 0, ranks: int = 8, n_tensors: int = 8, dim: int = 8192) -> Workload:
+    """One rank's share of the few-large list under ZeRO-1 ownership over
+    `ranks` GPUs: a contiguous slice of dim/ranks rows of every tensor (a
+    multiple of 256 elements), the same dtypes and hyperparameters."""
+    w = few_large(seed, n_tensors, dim)
+    w.name = "few_large_shard%d" % ranks
+    w.shapes = [(dim // ranks, dim)] * n_tensors
+    return w
+
+
 def bf16_state(seed: int = 0, n_tensors: int = 8, dim: int = 8192) -> Workload:
     return few_large(seed, n_tensors, dim, state_fmt=STATE_BF16)
 
@@ -193,6 +203,7 @@ WORKLOADS = {
     "many_small": many_small,
     "bf16_state": bf16_state,
     "lora_q8": lora_q8,
+    "few_large_shard8": few_large_shard,
 }
 
 
