@@ -427,7 +427,10 @@ def main() -> int:
     if args.amp:        # the check pass reads every grad once more
         ab += sum(n * ELEM[d] for n, d in zip(w.numels, w.grad_dtype))
     gbps = ab / avg_kernel_s / 1e9
-    traffic = None if args.amp else measured_traffic(w.name)
+    # the committed counters were taken in the default launch configuration
+    default_launch = not (args.amp or args.workgroups or args.occupancy or args.cache_policy
+                          or args.launch_mode)
+    traffic = measured_traffic(w.name) if default_launch else None
     out = {
         "metric": METRIC,
         "value": w.n_params * args.steps / elapsed,
