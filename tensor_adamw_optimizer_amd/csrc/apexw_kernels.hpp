@@ -1295,14 +1295,16 @@ __device__ __forceinline__ void carry_first_tile_q8(const KernelArgs &a, int32_t
 }
 
 // The 8-bit carried step with two tiles per workgroup: workgroup w takes the
-// logical tiles 2w and 2w+1.  When both lie in one tensor (every pair but at
-// most one per tensor) they are consecutive blocks, and one metadata fetch,
-// one address computation and one set of scalars serve both (q8_pair_full
-// for two full blocks); a pair that spans two tensors takes its tiles one at
-// a time, as carry_step does.  Each block gets the same bits as with one
-// tile per workgroup; the step measured 3.5% faster on MI355X (LoRA list,
-// 43.8-44.0 against 45.4-45.8 us, same machine, alternating runs): the same
-// VALU work per block, half the metadata chains and scalar work.
+// logical tiles 2p and 2p+1 of its pair p (q8_pair_of_workgroup: runs of 16
+// consecutive pairs per XCD, so that one L2 holds their scale lines).  When
+// both lie in one tensor (every pair but at most one per tensor) they are
+// consecutive blocks, and one metadata fetch, one address computation and
+// one set of scalars serve both (q8_pair_full for two full blocks); a pair
+// that spans two tensors takes its tiles one at a time, as carry_step does.
+// Each block gets the same bits as with one tile per workgroup; the step
+// measured 3.5% faster on MI355X (LoRA list, 43.8-44.0 against 45.4-45.8 us,
+// same machine, alternating runs): the same VALU work per block, half the
+// metadata chains and scalar work.
 template <int PT, int GT, bool NT, bool SC, bool FEW>
 __device__ __forceinline__ void carry_q8_one_tile(const KernelArgs &a,
                                                   const APEXW_CONST int32_t *tile_tensor,
@@ -1329,7 +1331,8 @@ void adamw_carry_pair_q8_kernel(KernelArgs a) {
     const float fi = *cptr<float>(a.found_inf);
     const float inv_scale = *cptr<float>(a.inv_scale);
     const float clip_coef = *cptr<float>(a.clip_coef);
-    const int64_t k0 = 2 * (int64_t)blockIdx.x;           // < tile_count: grid = ceil(tiles / 2)
+    // a permutation of the grid: k0 < tile_count, grid = ceil(tiles / 2)
+    const int64_t k0 = 2 * (int64_t)q8_pair_of_workgroup(blockIdx.x, gridDim.x);
     const int32_t i = tile_owner<FEW>(a, tile_tensor, k0);
     const TensorDesc d = load_uniform(a.desc, i);
     const void *g_ptr = reinterpret_cast<const void *>(cptr<uint64_t>(a.grads)[i]);

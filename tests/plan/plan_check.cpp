@@ -14,7 +14,12 @@
 //  3. read_window: every 4-entry load of a read group lies inside the
 //     reserved table (table_entries_reserved), its live entries are the
 //     table_position of their tiles, and the groups together visit every
-//     tile of the launch exactly once.
+//     tile of the launch exactly once;
+//  4. q8_pair_of_workgroup: over the 8-bit kernel's grid of ceil(tiles / 2)
+//     workgroups it takes every pair exactly once, its first tile inside the
+//     launch, and within each whole window every workgroup of an XCD takes a
+//     pair of that XCD's run (checked per launch and for grids of every size
+//     up to 4096 and a few large ones).
 //
 // Usage: plan_check <lists> <seed>; prints "lists N tensors T tiles K ok".
 #include <stdint.h>
@@ -40,6 +45,8 @@ static int failures = 0;
             ++failures;                                    \
         }                                                  \
     } while (0)
+
+static void check_pairs(int64_t tiles);
 
 static void check_list(const std::vector<int64_t> &numel, const std::vector<int32_t> &pdt,
                        const std::vector<int32_t> &gdt, int64_t *tiles_seen) {
@@ -120,6 +127,8 @@ static void check_list(const std::vector<int64_t> &numel, const std::vector<int3
         for (int64_t k = 0; k < L.tile_count; ++k)
             CHECK(visited[(size_t)k] == 1, "tile %lld visited %d times by the read groups",
                   (long long)k, visited[(size_t)k]);
+        // 4: the 8-bit kernel's pairs
+        check_pairs(L.tile_count);
         logical += L.tile_count;
         table_used += span;
         *tiles_seen += L.tile_count;
@@ -132,6 +141,29 @@ static void check_list(const std::vector<int64_t> &numel, const std::vector<int3
             CHECK(hits[(size_t)i][t] == 1, "tensor %d tile %zu covered %d times", i, t,
                   hits[(size_t)i][t]);
     }
+}
+
+// Check 4 for a launch of `tiles` tiles: the grid of the 8-bit carried kernel
+// (ceil(tiles / 2) workgroups) maps one-to-one onto the pairs, every pair's
+// first tile lies in the launch, and in whole windows the pair of workgroup w
+// lies in the run of w's XCD.
+static void check_pairs(int64_t tiles) {
+    const uint32_t P = (uint32_t)((tiles + 1) / 2);
+    const uint32_t W = (uint32_t)kXcds * kQ8PairRun;
+    std::vector<int> taken((size_t)P, 0);
+    for (uint32_t w = 0; w < P; ++w) {
+        const uint32_t p = q8_pair_of_workgroup(w, P);
+        CHECK(p < P, "pair %u of workgroup %u outside the grid of %u", p, w, P);
+        if (p >= P) continue;
+        taken[(size_t)p] += 1;
+        CHECK(2 * (int64_t)p < tiles, "pair %u starts past the launch's %lld tiles", p,
+              (long long)tiles);
+        if (w < P / W * W)
+            CHECK(p / W == w / W && (p % W) / kQ8PairRun == w % (uint32_t)kXcds,
+                  "workgroup %u (XCD %u) takes pair %u outside its run", w, w % (uint32_t)kXcds, p);
+    }
+    for (uint32_t p = 0; p < P; ++p)
+        CHECK(taken[(size_t)p] == 1, "pair %u taken %d times (grid %u)", p, taken[(size_t)p], P);
 }
 
 int main(int argc, char **argv) {
@@ -163,6 +195,8 @@ int main(int argc, char **argv) {
         check_list(numel, pdt, gdt, &tiles);
         tensors += 20000;
     }
+    for (int64_t t = 0; t <= 8192; ++t) check_pairs(t);
+    for (int64_t t : {94976LL, 94977LL, 2097152LL, 8388611LL}) check_pairs(t);
     printf("lists %d tensors %lld tiles %lld %s\n", lists + 1, (long long)tensors,
            (long long)tiles, failures ? "FAILED" : "ok");
     return failures ? 1 : 0;
